@@ -1,0 +1,166 @@
+"""ctypes wrapper around the fp64 CPU oracle (fd_oracle.c).
+
+TEST INFRASTRUCTURE ONLY.  Only tests/, the smoke check in __graft_entry__
+and bench.py's CPU-baseline leg may import this module.  The product path
+(split_kv_fd_amd) never imports it, and this module imports nothing from the
+product path.
+
+The oracle computes single-query decode attention as one softmax over the
+whole valid KV range in fp64 (see the header of fd_oracle.c for the formula
+and the pages it follows).  Inputs are host arrays (numpy, or torch CPU
+tensors) holding raw f32 / f16 / bf16 / f64 elements; they are decoded
+exactly to fp64 inside the C code.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "fd_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2, "f64": 3}
+
+
+def build(src: str = _SRC, out: str = _LIB, extra_flags=()) -> str:
+    """Compile the oracle with gcc (OpenMP) into a shared library."""
+    cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared", *extra_flags,
+           src, "-o", out, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+class Oracle:
+    """One loaded copy of the oracle library (the tests also load mutants)."""
+
+    def __init__(self, path: str = _LIB):
+        if not os.path.exists(path):
+            raise FileNotFoundError(f"oracle library not built: {path}")
+        self.path = path
+        self.lib = ctypes.CDLL(path)
+        f = self.lib.fdo_decode
+        f.restype = ctypes.c_int
+        f.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                                              ctypes.c_void_p, ctypes.c_int,
+                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        self.lib.fdo_decode_f16.restype = ctypes.c_double
+        self.lib.fdo_decode_f16.argtypes = [ctypes.c_uint16]
+        self.lib.fdo_decode_bf16.restype = ctypes.c_double
+        self.lib.fdo_decode_bf16.argtypes = [ctypes.c_uint16]
+        self.lib.fdo_max_threads.restype = ctypes.c_int
+
+    def max_threads(self) -> int:
+        return int(self.lib.fdo_max_threads())
+
+    def decode(self, q, k, v, scale, *, dtype=None, page_table=None, seq_lens=None,
+               page_size=0, rows=None, nthreads=0):
+        """Whole-softmax decode attention in fp64.
+
+        q: [B, Hq, D]; k, v: [B, Hkv, T, D] (contiguous) or pools
+        [num_pages, Hkv, P, D] with page_table [B, max_pages] int32 (paged).
+        seq_lens: [B] int32 valid lengths (None: all T).  For paged input T is
+        taken as max_pages * page_size unless seq_lens bounds it.
+        rows: optional list of flat b*Hq+h indices to compute.
+        Returns (out, lse) as float64 arrays: [B, Hq, D] and [B, Hq], or
+        [n_rows, D] and [n_rows] when rows is given.
+        """
+        qa, dt = _host_array(q, dtype)
+        ka, _ = _host_array(k, dt)
+        va, _ = _host_array(v, dt)
+        B, Hq, D = qa.shape
+        if page_table is None:
+            _, Hkv, T, D2 = ka.shape
+            pt = None
+            max_pages = 0
+        else:
+            _, Hkv, P, D2 = ka.shape
+            pt = np.ascontiguousarray(_to_numpy(page_table), dtype=np.int32)
+            max_pages = pt.shape[1]
+            if page_size == 0:
+                page_size = P
+            assert page_size == P
+            T = max_pages * page_size
+        assert D2 == D and ka.shape == va.shape
+        sl = None
+        if seq_lens is not None:
+            sl = np.ascontiguousarray(_to_numpy(seq_lens), dtype=np.int32)
+            if page_table is not None:
+                T = int(max(1, min(T, sl.max())))
+        rw = None
+        n_rows = 0
+        if rows is not None:
+            rw = np.ascontiguousarray(np.asarray(rows), dtype=np.int32)
+            n_rows = rw.size
+            out = np.zeros((n_rows, D), np.float64)
+            lse = np.zeros((n_rows,), np.float64)
+        else:
+            out = np.zeros((B, Hq, D), np.float64)
+            lse = np.zeros((B, Hq), np.float64)
+        rc = self.lib.fdo_decode(
+            qa.ctypes.data, ka.ctypes.data, va.ctypes.data, DTYPE_CODE[dt],
+            None if pt is None else pt.ctypes.data,
+            None if sl is None else sl.ctypes.data,
+            int(page_size), int(max_pages), int(B), int(Hq), int(Hkv), int(T), int(D),
+            float(scale), None if rw is None else rw.ctypes.data, int(n_rows),
+            out.ctypes.data, lse.ctypes.data, int(nthreads))
+        if rc != 0:
+            raise ValueError(f"oracle rejected its arguments (code {rc})")
+        return out, lse
+
+    def decode_f16_bits(self, bits: int) -> float:
+        return float(self.lib.fdo_decode_f16(bits))
+
+    def decode_bf16_bits(self, bits: int) -> float:
+        return float(self.lib.fdo_decode_bf16(bits))
+
+
+def _to_numpy(x):
+    if isinstance(x, np.ndarray):
+        return x
+    import torch  # only for host tensors handed in by the tests
+    assert isinstance(x, torch.Tensor) and x.device.type == "cpu"
+    return x.contiguous().numpy()
+
+
+def _host_array(x, dtype):
+    """Return (contiguous numpy array holding raw elements, dtype tag)."""
+    if isinstance(x, np.ndarray):
+        if dtype is None:
+            dtype = {np.dtype(np.float32): "f32", np.dtype(np.float16): "f16",
+                     np.dtype(np.float64): "f64"}[x.dtype]
+        want = {"f32": np.float32, "f16": np.float16, "f64": np.float64,
+                "bf16": np.uint16}[dtype]
+        if dtype == "bf16":
+            assert x.dtype in (np.uint16, np.int16), "bf16 arrays are passed as raw 16-bit words"
+            return np.ascontiguousarray(x).view(np.uint16), dtype
+        return np.ascontiguousarray(x, dtype=want), dtype
+    import torch
+    assert isinstance(x, torch.Tensor) and x.device.type == "cpu"
+    tag = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16",
+           torch.float64: "f64"}[x.dtype]
+    if dtype is not None:
+        assert dtype == tag, f"mixed dtypes {dtype} vs {tag}"
+    x = x.contiguous()
+    if tag == "bf16":
+        return x.view(torch.int16).numpy().view(np.uint16), tag
+    return x.numpy(), tag
+
+
+_default = None
+
+
+def default() -> Oracle:
+    """The oracle built from fd_oracle.c in this directory."""
+    global _default
+    if _default is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        _default = Oracle(_LIB)
+    return _default
