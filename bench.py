@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Benchmark one decode step of split-KV decode attention on one MI355X.
+
+A step is one full fd_decode: the split pass over every (batch, kv head,
+split) and the combine pass, on inputs already resident in HBM.  Inputs are
+seeded synthetic tensors with the workload's shapes and value distribution.
+To keep the 256 MiB last-level cache from serving KV bytes, each step reads
+a different one of several identical copies of the KV cache (together at
+least 1 GiB).
+
+Prints ONE JSON line: KV read throughput (GB/s, algorithmic bytes over wall
+time), us per step, the split kernel's roofline fraction from HIP events
+recorded around it in the timed loop, and the fp64 CPU oracle's throughput
+on a bounded sample of the same workload as a host baseline.
+
+    python bench.py [--steps K] [--warmup W] [--config NAME] [--n-splits N]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attention KV read GB/s (fraction of HBM peak) and µs/step, 1 MI355X"
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "mha32k_f16"
+ELT = {"f32": 4, "f16": 2, "bf16": 2}
+
+
+def kv_bytes_of(spec, lengths) -> int:
+    """Algorithmic KV bytes of one step: every valid K and V row read once."""
+    return 2 * sum(lengths) * spec.Hkv * spec.D * ELT[spec.dtype]
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "split_kv_fd_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str, kernel: str):
+    """HBM bytes per split launch from the committed counter summary, or None
+    when there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and line.startswith("- "):
+                k, _, v = line[2:].partition(":")
+                fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(case, seconds: float):
+    """The fp64 oracle on whole sequences of the same workload, repeated
+    until about `seconds` of host time; reported as KV GB/s."""
+    from oracle import oracle as oracle_mod
+    orc = oracle_mod.default()
+    s = case.spec
+    lens = case.lengths()
+
+    def run_seq(b):
+        q = case.q[b:b + 1].cpu()
+        if case.page_table is None:
+            k, v = case.k[b:b + 1].cpu(), case.v[b:b + 1].cpu()
+            t0 = time.perf_counter()
+            orc.decode(q, k, v, s.scale)
+        else:
+            import torch
+            n = -(-lens[b] // s.page_size)
+            pages = case.page_table[b, :n].long()
+            k, v = case.k[pages].cpu(), case.v[pages].cpu()
+            table = torch.arange(n, dtype=torch.int32)[None]
+            t0 = time.perf_counter()
+            orc.decode(q, k, v, s.scale, page_table=table, seq_lens=case.seq_lens[b:b + 1].cpu())
+        return time.perf_counter() - t0
+
+    total, done_bytes, seqs = 0.0, 0, 0
+    b = 0
+    while total < seconds and seqs < 10000:
+        total += run_seq(b)
+        done_bytes += 2 * lens[b] * s.Hkv * s.D * ELT[s.dtype]
+        seqs += 1
+        b = (b + 1) % s.B
+    full_steps = seqs / s.B
+    return {"value": round(done_bytes / total / 1e9, 4), "unit": "GB/s", "cores": orc.max_threads(),
+            "kind": "oracle",
+            "sample": (f"{seqs} sequence(s) of the workload ({full_steps:.2f} full steps; "
+                       f"all {s.Hq} query heads each), {total:.1f} s of host time, fp64 "
+                       "whole-softmax oracle, OpenMP over (batch, head)"),
+            "us_per_step": round(total / full_steps * 1e6, 1)}
+
+
+def copy_calibration(gib: float = 1.0, reps: int = 5):
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    import torch
+    n = int(gib * (1 << 30))
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "reps": reps}), flush=True)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--config", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--n-splits", type=int, default=0, help="0 = the planner's choice")
+    ap.add_argument("--path", default=None, choices=[None, "auto", "valu", "mfma"])
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (for counter scaling) and exit")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the decode runs on a single MI355X and there is no "
+              "multi-GPU path to time. Run it with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    if args.copy_calibration:
+        copy_calibration()
+        return 0
+
+    from split_kv_fd_amd import fd, inputs
+    from split_kv_fd_amd.decode import Decoder
+    fd.load()   # fails loudly if the HIP library is not built
+
+    spec = inputs.spec(args.config)
+    print(f"[bench] generating {spec.name} on the GPU", file=sys.stderr, flush=True)
+    case = inputs.make_case(spec, device="cuda")
+    lens = case.lengths()
+    kv_bytes = kv_bytes_of(spec, lens)
+    copies = max(2, min(16, math.ceil((1 << 30) / kv_bytes) + 1))
+    decs = []
+    for c in range(copies):
+        k = case.k if c == 0 else case.k.clone()
+        v = case.v if c == 0 else case.v.clone()
+        decs.append(Decoder(case.q, k, v, scale=spec.scale, page_table=case.page_table,
+                            seq_lens=case.seq_lens, T=spec.T if case.page_table is not None else None,
+                            n_splits=args.n_splits or spec.n_splits, path=args.path))
+    plan = decs[0].plan
+    print(f"[bench] plan {plan}; {copies} KV copies", file=sys.stderr, flush=True)
+
+    for i in range(args.warmup):
+        decs[i % copies]()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        d = decs[i % copies]
+        ev[i][0].record()
+        d.split()
+        ev[i][1].record()
+        d.combine()
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    split_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    comb_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    step_ms = [e[0].elapsed_time(e[2]) for e in ev]
+    ms_per_step = (t1 - t0) * 1e3 / K
+    gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    split_avg = statistics.mean(split_ms)
+    achieved = kv_bytes / (split_avg * 1e-3) / 1e9
+    kernel = "fd_split"
+    traffic = read_traffic(spec.name, kernel)
+
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic",
+        "config": {"workload": spec.name, "B": spec.B, "Hq": spec.Hq, "Hkv": spec.Hkv, "G": spec.G,
+                   "D": spec.D, "T": spec.T, "kv_dtype": spec.dtype, "accumulate": "f32",
+                   "kv_bytes_per_step": kv_bytes, "kv_copies_rotated": copies,
+                   "n_splits": plan["n_splits"], "chunk": plan["chunk"], "path": plan["path"],
+                   "seed": spec.seed},
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": kernel,
+                     "launch_us_avg": round(split_avg * 1e3, 2),
+                     "bytes_per_launch": kv_bytes},
+        "kernels_us": {"split_avg": round(split_avg * 1e3, 2),
+                       "split_median": round(statistics.median(split_ms) * 1e3, 2),
+                       "combine_avg": round(statistics.mean(comb_ms) * 1e3, 2),
+                       "step_events_median": round(statistics.median(step_ms) * 1e3, 2)},
+        "kernel_source_sha": kernel_source_sha(),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,181 @@
+/*
+ * fd.h -- C ABI of libfd: split-KV ("flash decoding") single-query decode
+ * attention for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (tinyvolt "Kernel visualization: Flash Decoding", opening
+ * section and its split / combine kernels; zenaique explainer, "What decode
+ * looks like"): for every batch row b and query head h, with kv head
+ * j = h / (Hq / Hkv) and valid length T_b,
+ *
+ *     out[b,h,:] = softmax_t( scale * q[b,h,:] . K[b,j,t,:] ) @ V[b,j,t,:]
+ *     lse[b,h]   = ln sum_t exp( scale * q[b,h,:] . K[b,j,t,:] )
+ *
+ * computed by splitting the KV axis into chunks: a split pass runs an
+ * online softmax over each chunk and keeps an unnormalised partial with its
+ * running max and sum; a combine pass aligns the partials to the global max
+ * and divides once.  The result equals the whole softmax up to fp32
+ * rounding order (zenaique explainer, interview answer on exactness).
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor arguments are DEVICE pointers on the current HIP device,
+ *     contiguous, row-major.  The caller allocates and owns every buffer,
+ *     including the workspace; the library keeps no pointer after a call
+ *     returns and allocates no device memory.
+ *   - q: [B, Hq, D]; contiguous caches: [B, Hkv, T, D]; paged pools:
+ *     [num_pages, Hkv, page_size, D] with page_table [B, max_pages_per_seq]
+ *     int32 (token t of sequence b is row t % page_size of page
+ *     page_table[b][t / page_size]); seq_lens [B] int32 with 0 <= T_b <= T.
+ *     q, K and V share one storage dtype (fd_options_t.dtype) and must be
+ *     16-byte aligned.  out is [B, Hq, D] fp32, lse [B, Hq] fp32 (natural
+ *     log; may be NULL).  A sequence with T_b = 0 yields out = 0 and
+ *     lse = -inf.
+ *   - Calls are stream-ordered on fd_options_t.stream and never synchronise;
+ *     a fault inside a kernel surfaces at the caller's next synchronisation.
+ *   - Arguments are validated on the host before any launch.  Every call
+ *     returns an fd_status_t; no exception crosses the ABI and the library
+ *     never exits the process.  fd_last_error() returns this thread's
+ *     message for the last failing call.
+ *   - Argument checking and planning are thread-safe.  Concurrent calls
+ *     that share one workspace must be ordered by the caller's streams.
+ */
+#ifndef FD_H
+#define FD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FD_F32 = 0,
+    FD_F16 = 1,
+    FD_BF16 = 2
+} fd_dtype_t;
+
+typedef enum {
+    FD_OK = 0,
+    FD_ERR_INVALID_ARG = 1,   /* a pointer, size or option is invalid        */
+    FD_ERR_UNSUPPORTED = 2,   /* valid, but no kernel instance (e.g. D=96)    */
+    FD_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required   */
+    FD_ERR_HIP = 4            /* a HIP runtime call failed (see fd_last_error) */
+} fd_status_t;
+
+typedef enum {
+    FD_PATH_AUTO = -1,        /* the planner chooses                          */
+    FD_PATH_VALU = 0,         /* vector-ALU dot products and reductions       */
+    FD_PATH_MFMA = 1          /* matrix-core path (f16/bf16 only)             */
+} fd_path_t;
+
+/* Options of a call.  Initialise with fd_options_init() and then set the
+ * fields you need; struct_size versions the layout. */
+typedef struct fd_options {
+    uint32_t struct_size;       /* sizeof(fd_options_t) of the caller         */
+    int32_t dtype;              /* fd_dtype_t of q, K and V                    */
+    int32_t page_size;          /* paged only: tokens per page, power of two  */
+    int32_t max_pages_per_seq;  /* paged only: row stride of page_table       */
+    int32_t num_pages;          /* paged only: pool size; page ids outside    */
+                                /* [0, num_pages) read as empty tokens        */
+    int32_t num_cus;            /* compute units to plan for; 0 = ask device  */
+    int32_t path;               /* fd_path_t; FD_PATH_AUTO by default          */
+    int32_t reserved;
+    void *workspace;            /* device buffer for the split partials        */
+    size_t workspace_bytes;     /* its size in bytes                          */
+    void *stream;               /* hipStream_t to launch on; NULL = null stream */
+} fd_options_t;
+
+/* What a call with these arguments will launch (see fd_plan). */
+typedef struct fd_plan {
+    int32_t n_splits;           /* effective number of KV splits              */
+    int32_t chunk;              /* tokens per split (last one may be shorter) */
+    int32_t path;               /* fd_path_t that runs                        */
+    int32_t tile;               /* tokens one workgroup consumes per step     */
+    int32_t heads_per_block;    /* query heads of one kv group per workgroup  */
+    int32_t head_blocks;        /* workgroups across one kv head's group      */
+    int32_t grid[3];            /* split-kernel grid (x: split, y: kv head *  */
+                                /* head_blocks, z: batch)                     */
+    int32_t block;              /* threads per split workgroup                */
+    int32_t combine;            /* 1 if a combine launch follows the split    */
+    int32_t reserved;
+    size_t workspace_bytes;     /* workspace this call needs (0 if n_splits=1) */
+} fd_plan_t;
+
+/* Fill *opt with defaults: dtype bf16, contiguous cache, automatic path,
+ * no workspace, null stream. */
+void fd_options_init(fd_options_t *opt);
+
+/*
+ * Choose the split count and kernel for a call (host only; no GPU work).
+ * n_splits > 0 asks for that many splits (capped so no split is empty when
+ * every sequence has length T); n_splits = 0 lets the planner size the grid
+ * to the device: enough (batch, kv head, split) workgroups to cover every
+ * compute unit, with each split long enough to amortise its partial write
+ * (the occupancy argument of the zenaique explainer, "Why decode breaks
+ * FlashAttention v2").  num_cus = 0 in *opt queries the current device.
+ * Returns FD_OK and fills *plan, or an error status.
+ */
+fd_status_t fd_plan(int B, int Hq, int Hkv, int T, int D, int n_splits,
+                    const fd_options_t *opt, fd_plan_t *plan);
+
+/* Workspace bytes fd_decode needs for these arguments (0 when the plan has
+ * one split, or when the arguments are invalid -- check fd_plan then). */
+size_t fd_workspace_bytes(int B, int Hq, int Hkv, int T, int D, int n_splits,
+                          const fd_options_t *opt);
+
+/*
+ * Decode attention: the split pass, then (when the plan has more than one
+ * split) the combine pass, both on opt->stream.
+ *   q, k_cache, v_cache : device inputs in opt->dtype (layouts above).
+ *   page_table          : NULL for contiguous caches; else [B, max_pages].
+ *   seq_lens            : NULL = every sequence has length T; else [B].
+ *   out, lse            : device outputs, fp32; lse may be NULL.
+ *   T                   : cache length, or the largest T_b for ragged input.
+ *   scale               : multiplies q.k before the softmax (finite).
+ *   n_splits            : 0 = automatic, else the requested split count.
+ * The workspace (opt->workspace, >= fd_workspace_bytes) holds the partials
+ * [B, Hq, n_splits, D] plus two [B, Hq, n_splits] rows; its contents before
+ * the call do not matter.
+ */
+fd_status_t fd_decode(const void *q, const void *k_cache, const void *v_cache,
+                      const int32_t *page_table, const int32_t *seq_lens,
+                      float *out, float *lse,
+                      int B, int Hq, int Hkv, int T, int D, float scale,
+                      int n_splits, const fd_options_t *opt);
+
+/*
+ * The split pass alone (tinyvolt, "Visualizing operations in a single
+ * block"): one workgroup per (batch, kv head, split) streams its chunk of K
+ * and V and writes the unnormalised partial, its max and its sum to the
+ * workspace.  With a one-split plan it normalises and writes out / lse
+ * itself.  Same arguments as fd_decode.
+ */
+fd_status_t fd_split(const void *q, const void *k_cache, const void *v_cache,
+                     const int32_t *page_table, const int32_t *seq_lens,
+                     float *out, float *lse,
+                     int B, int Hq, int Hkv, int T, int D, float scale,
+                     int n_splits, const fd_options_t *opt);
+
+/*
+ * The combine pass alone (tinyvolt, "Combine kernel"): one wavefront per
+ * (batch, query head) merges the partials fd_split left in the workspace by
+ * log-sum-exp and writes out / lse.  Must follow fd_split with the same
+ * B, Hq, Hkv, T, D, n_splits, seq_lens and options.  A no-op (FD_OK) when
+ * the plan has one split.
+ */
+fd_status_t fd_combine(const int32_t *seq_lens, float *out, float *lse,
+                       int B, int Hq, int Hkv, int T, int D, int n_splits,
+                       const fd_options_t *opt);
+
+/* Static text for a status code. */
+const char *fd_status_string(fd_status_t status);
+
+/* This thread's message for the last call that did not return FD_OK
+ * ("" if none).  Valid until the thread's next failing call. */
+const char *fd_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FD_H */

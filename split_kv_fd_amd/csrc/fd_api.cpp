@@ -1,0 +1,323 @@
+// Host side of libfd: argument checking, the split-count planner, workspace
+// layout and kernel dispatch.  No device memory is allocated here and no call
+// synchronises; kernels are launched on the caller's stream.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "fd_kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+fd_status_t fail(fd_status_t st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+fd_status_t hip_fail(hipError_t e, const char *what) {
+    return fail(FD_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+inline bool is_pow2(long x) { return x > 0 && (x & (x - 1)) == 0; }
+inline long ceil_div(long a, long b) { return (a + b - 1) / b; }
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+inline int ilog2(int x) { int r = 0; while ((1 << r) < x) ++r; return r; }
+
+long env_long(const char *name, long dflt) {
+    const char *s = std::getenv(name);
+    if (!s || !*s) return dflt;
+    char *end = nullptr;
+    const long v = std::strtol(s, &end, 10);
+    return (end && *end == '\0' && v > 0) ? v : dflt;
+}
+
+constexpr uint32_t kOptionsV1 = sizeof(fd_options_t);
+
+// Compute units of the current device, cached per device id.
+fd_status_t device_cus(int *cus) {
+    static std::mutex mu;
+    static int cache[64] = {0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev >= 0 && dev < 64) {
+        std::lock_guard<std::mutex> lock(mu);
+        if (cache[dev] > 0) { *cus = cache[dev]; return FD_OK; }
+    }
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(MultiprocessorCount)");
+    if (n <= 0) return fail(FD_ERR_HIP, "device reports %d compute units", n);
+    if (dev >= 0 && dev < 64) {
+        std::lock_guard<std::mutex> lock(mu);
+        cache[dev] = n;
+    }
+    *cus = n;
+    return FD_OK;
+}
+
+fd_status_t read_options(const fd_options_t *opt, fd_options_t *o) {
+    if (!opt) return fail(FD_ERR_INVALID_ARG, "options pointer is NULL (use fd_options_init)");
+    if (opt->struct_size < kOptionsV1)
+        return fail(FD_ERR_INVALID_ARG, "options struct_size %u < %u", opt->struct_size, kOptionsV1);
+    std::memcpy(o, opt, kOptionsV1);
+    if (o->dtype != FD_F32 && o->dtype != FD_F16 && o->dtype != FD_BF16)
+        return fail(FD_ERR_INVALID_ARG, "unknown dtype %d", (int)o->dtype);
+    if (o->path != FD_PATH_AUTO && o->path != FD_PATH_VALU && o->path != FD_PATH_MFMA)
+        return fail(FD_ERR_INVALID_ARG, "unknown path %d", (int)o->path);
+    if (o->num_cus < 0) return fail(FD_ERR_INVALID_ARG, "num_cus %d < 0", (int)o->num_cus);
+    return FD_OK;
+}
+
+// Shape checks and the plan.  `paged` tells whether a page table is used.
+fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_options_t &o,
+                      bool paged, fd_plan_t *p) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || T <= 0)
+        return fail(FD_ERR_INVALID_ARG, "B=%d Hq=%d Hkv=%d T=%d must all be positive", B, Hq, Hkv, T);
+    if (Hq % Hkv != 0) return fail(FD_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+    if (D <= 0) return fail(FD_ERR_INVALID_ARG, "D=%d must be positive", D);
+    if (D != 64 && D != 128) return fail(FD_ERR_UNSUPPORTED, "D=%d (supported: 64, 128)", D);
+    if (n_req < 0) return fail(FD_ERR_INVALID_ARG, "n_splits=%d < 0", n_req);
+    if (B > 65535) return fail(FD_ERR_UNSUPPORTED, "B=%d > 65535", B);
+    if ((long)B * Hq > (1L << 30)) return fail(FD_ERR_UNSUPPORTED, "B*Hq too large");
+    if (paged) {
+        if (!is_pow2(o.page_size) || o.page_size > 65536)
+            return fail(FD_ERR_INVALID_ARG, "page_size=%d is not a power of two in [1, 65536]", o.page_size);
+        if (o.max_pages_per_seq < ceil_div(T, o.page_size))
+            return fail(FD_ERR_INVALID_ARG, "max_pages_per_seq=%d < ceil(T/page_size)=%ld",
+                        o.max_pages_per_seq, ceil_div(T, o.page_size));
+        if (o.num_pages <= 0) return fail(FD_ERR_INVALID_ARG, "num_pages=%d must be positive", o.num_pages);
+    }
+    const long elt = o.dtype == FD_F32 ? 4 : 2;
+    if (!paged && (long)T * D * elt >= (1L << 32))
+        return fail(FD_ERR_UNSUPPORTED, "one (batch, kv head) cache slice of T*D*%ld bytes must be < 4 GiB", elt);
+    if (o.path == FD_PATH_MFMA)
+        return fail(FD_ERR_UNSUPPORTED, "the MFMA path is not built in this library version");
+
+    const int G = Hq / Hkv;
+    int hpb = 1;
+    while (hpb < G && hpb < 8) hpb <<= 1;
+    const int head_blocks = (int)ceil_div(G, hpb);
+    if ((long)Hkv * head_blocks > 65535) return fail(FD_ERR_UNSUPPORTED, "Hkv*head_blocks > 65535");
+    const int tile = fdk::valu_tile(o.dtype, D, hpb);
+    if (tile <= 0) return fail(FD_ERR_UNSUPPORTED, "no kernel instance for this shape");
+
+    int cus = o.num_cus;
+    if (cus == 0) {
+        fd_status_t st = device_cus(&cus);
+        if (st != FD_OK) return st;
+    }
+
+    long gran = tile;
+    if (paged && o.page_size > gran) gran = o.page_size;
+    const long max_n = ceil_div(T, gran);
+    long n;
+    if (n_req > 0) {
+        n = n_req < max_n ? n_req : max_n;
+    } else {
+        // Enough workgroups to cover every compute unit twice over, but no
+        // split shorter than min_chunk tokens (its partial write and the
+        // combine read must stay small against the chunk's KV bytes).
+        const long units = (long)B * Hkv * head_blocks;
+        const long target = env_long("FD_TARGET_WGS", 2L * cus);
+        const long min_chunk = env_long("FD_CHUNK_MIN", 512);
+        n = ceil_div(target, units);
+        const long cap = T / min_chunk > 1 ? T / min_chunk : 1;
+        if (n > cap) n = cap;
+    }
+    if (n < 1) n = 1;
+    long chunk = ceil_div(ceil_div(T, n), gran) * gran;
+    n = ceil_div(T, chunk);
+
+    std::memset(p, 0, sizeof *p);
+    p->n_splits = (int)n;
+    p->chunk = (int)chunk;
+    p->path = FD_PATH_VALU;
+    p->tile = tile;
+    p->heads_per_block = hpb;
+    p->head_blocks = head_blocks;
+    p->grid[0] = (int)n;
+    p->grid[1] = Hkv * head_blocks;
+    p->grid[2] = B;
+    p->block = 256;
+    p->combine = n > 1;
+    if (n > 1) {
+        const size_t parts = (size_t)B * Hq * (size_t)n;
+        p->workspace_bytes = align256(parts * D * sizeof(float)) + 2 * align256(parts * sizeof(float));
+    }
+    return FD_OK;
+}
+
+struct Call {
+    fd_options_t o;
+    fd_plan_t p;
+    fdk::SplitArgs s;
+    fdk::CombineArgs c;
+};
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Everything fd_decode / fd_split / fd_combine check before launching.
+fd_status_t prepare(const void *q, const void *k, const void *v, const int32_t *page_table,
+                    const int32_t *seq_lens, float *out, float *lse, int B, int Hq, int Hkv,
+                    int T, int D, float scale, int n_req, const fd_options_t *opt, bool need_inputs,
+                    Call *c) {
+    fd_status_t st = read_options(opt, &c->o);
+    if (st != FD_OK) return st;
+    if (need_inputs) {
+        if (!q || !k || !v) return fail(FD_ERR_INVALID_ARG, "q, k_cache and v_cache must be non-NULL");
+        if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
+            return fail(FD_ERR_INVALID_ARG, "q, k_cache and v_cache must be 16-byte aligned");
+        if (!std::isfinite(scale)) return fail(FD_ERR_INVALID_ARG, "scale is not finite");
+    }
+    if (!out) return fail(FD_ERR_INVALID_ARG, "out must be non-NULL");
+    if (!aligned(out, 4) || (lse && !aligned(lse, 4)))
+        return fail(FD_ERR_INVALID_ARG, "out / lse must be 4-byte aligned");
+    if (seq_lens && !aligned(seq_lens, 4)) return fail(FD_ERR_INVALID_ARG, "seq_lens must be 4-byte aligned");
+    // The page geometry in the options decides the plan; the split pass also
+    // needs the table itself.
+    const bool paged = c->o.page_size > 0;
+    if (need_inputs && paged != (page_table != nullptr))
+        return fail(FD_ERR_INVALID_ARG, "page_table and opt->page_size must be given together");
+    if (page_table && !aligned(page_table, 4)) return fail(FD_ERR_INVALID_ARG, "page_table must be 4-byte aligned");
+    st = make_plan(B, Hq, Hkv, T, D, n_req, c->o, paged, &c->p);
+    if (st != FD_OK) return st;
+
+    float *part_o = nullptr, *part_m = nullptr, *part_l = nullptr;
+    if (c->p.n_splits > 1) {
+        if (!c->o.workspace)
+            return fail(FD_ERR_WORKSPACE, "plan has %d splits: a workspace of %zu bytes is required",
+                        c->p.n_splits, c->p.workspace_bytes);
+        if (c->o.workspace_bytes < c->p.workspace_bytes)
+            return fail(FD_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", c->o.workspace_bytes,
+                        c->p.workspace_bytes);
+        if (!aligned(c->o.workspace, 256)) return fail(FD_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+        const size_t parts = (size_t)B * Hq * (size_t)c->p.n_splits;
+        char *w = static_cast<char *>(c->o.workspace);
+        part_o = reinterpret_cast<float *>(w);
+        w += align256(parts * D * sizeof(float));
+        part_m = reinterpret_cast<float *>(w);
+        w += align256(parts * sizeof(float));
+        part_l = reinterpret_cast<float *>(w);
+    }
+
+    fdk::SplitArgs &s = c->s;
+    s.q = q; s.k = k; s.v = v;
+    s.page_table = page_table;
+    s.seq_lens = seq_lens;
+    s.out = out; s.lse = lse;
+    s.part_o = part_o; s.part_m = part_m; s.part_l = part_l;
+    s.B = B; s.Hq = Hq; s.Hkv = Hkv; s.T = T; s.D = D; s.G = Hq / Hkv;
+    s.n_splits = c->p.n_splits;
+    s.chunk = c->p.chunk;
+    s.heads_per_block = c->p.heads_per_block;
+    s.head_blocks = c->p.head_blocks;
+    s.page_size = paged ? c->o.page_size : 1;
+    s.page_shift = paged ? ilog2(c->o.page_size) : 0;
+    s.max_pages = paged ? c->o.max_pages_per_seq : 0;
+    s.num_pages = paged ? c->o.num_pages : 0;
+    s.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+
+    fdk::CombineArgs &cb = c->c;
+    cb.part_o = part_o; cb.part_m = part_m; cb.part_l = part_l;
+    cb.seq_lens = seq_lens;
+    cb.out = out; cb.lse = lse;
+    cb.B = B; cb.Hq = Hq; cb.T = T; cb.D = D;
+    cb.n_splits = c->p.n_splits;
+    cb.chunk = c->p.chunk;
+    return FD_OK;
+}
+
+fd_status_t run_split(const Call &c) {
+    const hipError_t e = fdk::launch_split_valu(c.s, c.o.dtype, static_cast<hipStream_t>(c.o.stream));
+    if (e != hipSuccess) return hip_fail(e, "launching the split kernel");
+    return FD_OK;
+}
+
+fd_status_t run_combine(const Call &c) {
+    if (c.p.n_splits <= 1) return FD_OK;
+    const hipError_t e = fdk::launch_combine(c.c, static_cast<hipStream_t>(c.o.stream));
+    if (e != hipSuccess) return hip_fail(e, "launching the combine kernel");
+    return FD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void fd_options_init(fd_options_t *opt) {
+    if (!opt) return;
+    std::memset(opt, 0, sizeof *opt);
+    opt->struct_size = sizeof *opt;
+    opt->dtype = FD_BF16;
+    opt->path = FD_PATH_AUTO;
+}
+
+fd_status_t fd_plan(int B, int Hq, int Hkv, int T, int D, int n_splits, const fd_options_t *opt,
+                    fd_plan_t *plan) {
+    if (!plan) return fail(FD_ERR_INVALID_ARG, "plan pointer is NULL");
+    fd_options_t o;
+    fd_status_t st = read_options(opt, &o);
+    if (st != FD_OK) return st;
+    return make_plan(B, Hq, Hkv, T, D, n_splits, o, o.page_size > 0, plan);
+}
+
+size_t fd_workspace_bytes(int B, int Hq, int Hkv, int T, int D, int n_splits, const fd_options_t *opt) {
+    fd_plan_t p;
+    if (fd_plan(B, Hq, Hkv, T, D, n_splits, opt, &p) != FD_OK) return 0;
+    return p.workspace_bytes;
+}
+
+fd_status_t fd_decode(const void *q, const void *k_cache, const void *v_cache, const int32_t *page_table,
+                      const int32_t *seq_lens, float *out, float *lse, int B, int Hq, int Hkv, int T, int D,
+                      float scale, int n_splits, const fd_options_t *opt) {
+    Call c;
+    fd_status_t st = prepare(q, k_cache, v_cache, page_table, seq_lens, out, lse, B, Hq, Hkv, T, D, scale,
+                             n_splits, opt, true, &c);
+    if (st != FD_OK) return st;
+    st = run_split(c);
+    if (st != FD_OK) return st;
+    return run_combine(c);
+}
+
+fd_status_t fd_split(const void *q, const void *k_cache, const void *v_cache, const int32_t *page_table,
+                     const int32_t *seq_lens, float *out, float *lse, int B, int Hq, int Hkv, int T, int D,
+                     float scale, int n_splits, const fd_options_t *opt) {
+    Call c;
+    fd_status_t st = prepare(q, k_cache, v_cache, page_table, seq_lens, out, lse, B, Hq, Hkv, T, D, scale,
+                             n_splits, opt, true, &c);
+    if (st != FD_OK) return st;
+    return run_split(c);
+}
+
+fd_status_t fd_combine(const int32_t *seq_lens, float *out, float *lse, int B, int Hq, int Hkv, int T, int D,
+                       int n_splits, const fd_options_t *opt) {
+    Call c;
+    fd_status_t st = prepare(nullptr, nullptr, nullptr, nullptr, seq_lens, out, lse, B, Hq, Hkv, T, D, 1.0f,
+                             n_splits, opt, false, &c);
+    if (st != FD_OK) return st;
+    return run_combine(c);
+}
+
+const char *fd_status_string(fd_status_t status) {
+    switch (status) {
+    case FD_OK: return "FD_OK";
+    case FD_ERR_INVALID_ARG: return "FD_ERR_INVALID_ARG: invalid argument";
+    case FD_ERR_UNSUPPORTED: return "FD_ERR_UNSUPPORTED: no kernel for these arguments";
+    case FD_ERR_WORKSPACE: return "FD_ERR_WORKSPACE: workspace missing or too small";
+    case FD_ERR_HIP: return "FD_ERR_HIP: HIP runtime error";
+    default: return "unknown fd_status_t";
+    }
+}
+
+const char *fd_last_error(void) { return g_err; }
+
+}  // extern "C"

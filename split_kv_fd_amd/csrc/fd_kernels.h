@@ -1,0 +1,68 @@
+// Internal interface between the host library (fd_api.cpp) and the HIP
+// kernels.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/fd.h"
+
+namespace fdk {
+
+// Everything one split launch needs.  Passed by value as the kernel argument.
+struct SplitArgs {
+    const void *q;
+    const void *k;
+    const void *v;
+    const int32_t *page_table;   // nullptr: contiguous cache
+    const int32_t *seq_lens;     // nullptr: every sequence has length T
+    float *out;                  // written directly when n_splits == 1
+    float *lse;                  // may be nullptr
+    float *part_o;               // [B, Hq, n_splits, D] unnormalised
+    float *part_m;               // [B, Hq, n_splits] running max, log2 units
+    float *part_l;               // [B, Hq, n_splits] running sum
+    int B, Hq, Hkv, T, D, G;     // G = Hq / Hkv
+    int n_splits, chunk;
+    int heads_per_block, head_blocks;
+    int page_size, page_shift, max_pages, num_pages;
+    float scale_log2;            // scale * log2(e): logits in base-2 units
+};
+
+struct CombineArgs {
+    const float *part_o;
+    const float *part_m;
+    const float *part_l;
+    const int32_t *seq_lens;
+    float *out;
+    float *lse;
+    int B, Hq, T, D;
+    int n_splits, chunk;
+};
+
+// Shape constants of the vector-ALU split kernel.  Each 64-lane wavefront
+// reads whole 16-byte pieces of key/value rows: LPR lanes cover one row,
+// so a wave holds R rows (tokens) at a time and U tokens per row per step.
+template <int EB, int D, int GB>
+struct ValuShape {
+    static constexpr int ROWB = D * EB;                     // bytes per token row
+    static constexpr int LPR = ROWB / 16 < 16 ? ROWB / 16 : 16;
+    static constexpr int VEC = ROWB / (16 * LPR);           // 16-B pieces per lane
+    static constexpr int EPC = 16 / EB;                     // elements per piece
+    static constexpr int EPT = VEC * EPC;                   // elements per lane
+    static constexpr int R = 64 / LPR;                      // rows per wave
+    static constexpr int U = GB >= 4 ? 2 : 4;               // tokens per row per step
+    static constexpr int WAVES = 4;
+    static constexpr int TW = R * U;                        // tokens per wave step
+    static constexpr int TILE = WAVES * TW;                 // tokens per workgroup step
+    static constexpr int THREADS = 64 * WAVES;
+};
+
+// Tokens per workgroup step of the VALU kernel instance (host side).
+int valu_tile(int dtype, int D, int heads_per_block);
+// Launch the VALU split kernel.  Returns the HIP status of the launch.
+hipError_t launch_split_valu(const SplitArgs &a, int dtype, hipStream_t stream);
+// Launch the combine kernel.
+hipError_t launch_combine(const CombineArgs &a, hipStream_t stream);
+
+}  // namespace fdk

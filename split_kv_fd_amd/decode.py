@@ -1,0 +1,159 @@
+"""Torch-facing convenience over the libfd binding.
+
+Checks shapes and devices, allocates the fp32 outputs and the workspace with
+torch (device memory is torch's job here), passes raw pointers and torch's
+current HIP stream to fd_decode, and raises FDError on a failing status.
+No arithmetic of the decode happens in Python.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import torch
+
+from . import fd
+
+_DTYPE = {torch.float32: fd.FD_F32, torch.float16: fd.FD_F16, torch.bfloat16: fd.FD_BF16}
+_PATH = {None: fd.FD_PATH_AUTO, "auto": fd.FD_PATH_AUTO, "valu": fd.FD_PATH_VALU,
+         "mfma": fd.FD_PATH_MFMA}
+
+
+class FDError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {fd.fd_status_string(status)}: {fd.fd_last_error()}")
+        self.status = status
+
+
+def make_options(dtype: torch.dtype, *, page_size: int = 0, max_pages: int = 0,
+                 num_pages: int = 0, workspace: Optional[torch.Tensor] = None,
+                 stream: Optional[int] = None, num_cus: int = 0,
+                 path: Optional[str] = None) -> fd.fd_options_t:
+    opt = fd.fd_options_t()
+    fd.fd_options_init(opt)
+    opt.dtype = _DTYPE[dtype]
+    opt.page_size = page_size
+    opt.max_pages_per_seq = max_pages
+    opt.num_pages = num_pages
+    opt.num_cus = num_cus
+    opt.path = _PATH[path]
+    if workspace is not None:
+        opt.workspace = workspace.data_ptr()
+        opt.workspace_bytes = workspace.numel() * workspace.element_size()
+    opt.stream = stream
+    return opt
+
+
+def plan(B, Hq, Hkv, T, D, n_splits=0, *, dtype=torch.bfloat16, page_size=0, max_pages=0,
+         num_pages=1, num_cus=0, path=None) -> dict:
+    """What fd_decode would launch for these arguments (host only)."""
+    opt = make_options(dtype, page_size=page_size, max_pages=max_pages,
+                       num_pages=num_pages if page_size else 0, num_cus=num_cus, path=path)
+    p = fd.fd_plan_t()
+    st = fd.fd_plan(B, Hq, Hkv, T, D, n_splits, opt, p)
+    if st != fd.FD_OK:
+        raise FDError(st, "fd_plan")
+    return p.as_dict()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+class Decoder:
+    """A prepared decode call: validated shapes, plan, outputs and workspace.
+
+    Calling it launches fd_decode (or the two passes separately) on torch's
+    current stream.  The benchmark and tests use it to keep allocation out
+    of the timed region.
+    """
+
+    def __init__(self, q, k, v, *, scale: Optional[float] = None, page_table=None,
+                 seq_lens=None, T: Optional[int] = None, n_splits: int = 0,
+                 path: Optional[str] = None, out=None, lse=None, want_lse: bool = True):
+        if q.device.type != "cuda":
+            raise ValueError("q, k and v must be GPU tensors")
+        if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPE:
+            raise ValueError(f"q, k, v must share one of {list(_DTYPE)}; got {q.dtype}, {k.dtype}, {v.dtype}")
+        for name, t in (("q", q), ("k", k), ("v", v)):
+            if not t.is_contiguous() or t.device != q.device:
+                raise ValueError(f"{name} must be contiguous and on {q.device}")
+        if q.dim() != 3 or k.dim() != 4 or k.shape != v.shape:
+            raise ValueError("expected q [B, Hq, D] and k, v [B, Hkv, T, D] or [pages, Hkv, P, D]")
+        B, Hq, D = q.shape
+        Hkv = k.shape[1]
+        if k.shape[3] != D:
+            raise ValueError(f"head size mismatch: q has {D}, k has {k.shape[3]}")
+        self.paged = page_table is not None
+        page_size = max_pages = num_pages = 0
+        if self.paged:
+            if page_table.dtype != torch.int32 or page_table.dim() != 2 or page_table.shape[0] != B:
+                raise ValueError("page_table must be int32 [B, max_pages]")
+            if not page_table.is_contiguous() or page_table.device != q.device:
+                raise ValueError("page_table must be contiguous and on the GPU")
+            num_pages, _, page_size, _ = k.shape
+            max_pages = page_table.shape[1]
+            T = T if T is not None else max_pages * page_size
+        else:
+            if k.shape[0] != B:
+                raise ValueError("k, v batch differs from q")
+            if T is not None and T != k.shape[2]:
+                raise ValueError("T must equal the cache length for contiguous caches")
+            T = k.shape[2]
+        if seq_lens is not None:
+            if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,) or seq_lens.device != q.device:
+                raise ValueError("seq_lens must be int32 [B] on the GPU")
+        self.scale = float(1.0 / math.sqrt(D)) if scale is None else float(scale)
+        self.args = (B, Hq, Hkv, T, D)
+        self.n_splits = n_splits
+        self.inputs = (q, k, v, page_table, seq_lens)
+        self.opt = make_options(q.dtype, page_size=page_size, max_pages=max_pages,
+                                num_pages=num_pages, path=path)
+        p = fd.fd_plan_t()
+        st = fd.fd_plan(B, Hq, Hkv, T, D, n_splits, self.opt, p)
+        if st != fd.FD_OK:
+            raise FDError(st, "fd_plan")
+        self.plan = p.as_dict()
+        self.workspace = None
+        if p.workspace_bytes:
+            self.workspace = torch.empty(p.workspace_bytes, dtype=torch.uint8, device=q.device)
+            self.opt.workspace = self.workspace.data_ptr()
+            self.opt.workspace_bytes = p.workspace_bytes
+        self.out = out if out is not None else torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+        self.lse = lse if lse is not None else (
+            torch.empty((B, Hq), dtype=torch.float32, device=q.device) if want_lse else None)
+
+    def _call(self, fn, name):
+        q, k, v, pt, sl = self.inputs
+        self.opt.stream = torch.cuda.current_stream(q.device).cuda_stream
+        B, Hq, Hkv, T, D = self.args
+        st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(pt), _ptr(sl), _ptr(self.out), _ptr(self.lse),
+                B, Hq, Hkv, T, D, self.scale, self.n_splits, self.opt)
+        if st != fd.FD_OK:
+            raise FDError(st, name)
+
+    def __call__(self):
+        """fd_decode: split pass and (if planned) combine pass."""
+        self._call(fd.fd_decode, "fd_decode")
+        return self.out, self.lse
+
+    def split(self):
+        """fd_split alone."""
+        self._call(fd.fd_split, "fd_split")
+
+    def combine(self):
+        """fd_combine alone (no-op for a one-split plan)."""
+        q = self.inputs[0]
+        self.opt.stream = torch.cuda.current_stream(q.device).cuda_stream
+        B, Hq, Hkv, T, D = self.args
+        st = fd.fd_combine(_ptr(self.inputs[4]), _ptr(self.out), _ptr(self.lse), B, Hq, Hkv, T, D,
+                           self.n_splits, self.opt)
+        if st != fd.FD_OK:
+            raise FDError(st, "fd_combine")
+
+
+def decode(q, k, v, *, scale=None, page_table=None, seq_lens=None, T=None, n_splits=0,
+           path=None):
+    """out [B, Hq, D] fp32 and lse [B, Hq] fp32 of single-query decode attention."""
+    return Decoder(q, k, v, scale=scale, page_table=page_table, seq_lens=seq_lens, T=T,
+                   n_splits=n_splits, path=path)()

@@ -1,0 +1,121 @@
+"""Helpers shared by the GPU parity tests: run the HIP path, run the oracle on
+host copies of the same inputs, and compare with the stated tolerances.
+
+Tolerances (on max |out_gpu - out_oracle| / max |V| over the valid tokens):
+1e-5 for fp32 K/V and 2e-3 for f16/bf16 K/V with fp32 accumulation; lse
+within 1e-4 (fp32) / 1e-3 (f16, bf16) absolute.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from oracle import oracle as oracle_mod
+from split_kv_fd_amd.decode import Decoder
+
+OUT_TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3}
+LSE_TOL = {"f32": 1e-4, "f16": 1e-3, "bf16": 1e-3}
+
+
+def announce(msg: str) -> None:
+    """Name the case on stdout before a GPU step (flushed)."""
+    print(f"[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def run_gpu(case, n_splits=0, path=None, scale=None):
+    q, k, v = case.q, case.k, case.v
+    dec = Decoder(q, k, v, scale=case.spec.scale if scale is None else scale,
+                  page_table=case.page_table, seq_lens=case.seq_lens,
+                  T=case.spec.T if case.page_table is not None else None,
+                  n_splits=n_splits, path=path)
+    announce(f"decode {case.spec.name} B={case.spec.B} Hq={case.spec.Hq} Hkv={case.spec.Hkv} "
+             f"T={case.spec.T} D={case.spec.D} {case.spec.dtype} seed={case.spec.seed} "
+             f"n_splits={n_splits} plan={dec.plan}")
+    out, lse = dec()
+    torch.cuda.synchronize()
+    return out.cpu().double().numpy(), lse.cpu().double().numpy(), dec.plan
+
+
+def max_abs_v(case, b=None) -> float:
+    """max |V| over the valid tokens (of sequence b, or all)."""
+    lens = case.lengths()
+    v = case.v
+    if case.page_table is None:
+        bs = range(case.spec.B) if b is None else [b]
+        return max(float(v[bb, :, :lens[bb]].abs().max()) if lens[bb] else 0.0 for bb in bs)
+    P = case.spec.page_size
+    bs = range(case.spec.B) if b is None else [b]
+    m = 0.0
+    for bb in bs:
+        n = -(-lens[bb] // P)
+        if n == 0:
+            continue
+        pages = case.page_table[bb, :n].long()
+        blk = v[pages]                                   # [n, Hkv, P, D]
+        blk = blk.transpose(1, 2).reshape(n * P, case.spec.Hkv, case.spec.D)[:lens[bb]]
+        m = max(m, float(blk.abs().max()))
+    return m
+
+
+def oracle_full(case):
+    c = case.to("cpu")
+    return oracle_mod.default().decode(c.q, c.k, c.v, case.spec.scale, page_table=c.page_table,
+                                       seq_lens=c.seq_lens)
+
+
+def compare(case, out, lse, ref_out, ref_lse, vmax, what=""):
+    tol = OUT_TOL[case.spec.dtype]
+    ltol = LSE_TOL[case.spec.dtype]
+    assert np.all(np.isfinite(out)), f"{what}: non-finite output"
+    err = float(np.max(np.abs(out - ref_out))) / max(vmax, 1e-30)
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(fin, np.isfinite(lse)), f"{what}: lse finiteness differs"
+    assert np.all(lse[~fin] == ref_lse[~fin]), f"{what}: lse infinities differ"
+    lerr = float(np.max(np.abs(lse[fin] - ref_lse[fin]), initial=0.0))
+    announce(f"{what}: max|d out|/max|V| = {err:.3e} (tol {tol:.0e}), max|d lse| = {lerr:.3e}")
+    assert err <= tol, f"{what}: output error {err:.3e} > {tol:.0e}"
+    assert lerr <= ltol, f"{what}: lse error {lerr:.3e} > {ltol:.0e}"
+    return err, lerr
+
+
+def check_full(case, n_splits=0, path=None, what=""):
+    out, lse, plan = run_gpu(case, n_splits, path)
+    ref_out, ref_lse = oracle_full(case)
+    return compare(case, out, lse, ref_out, ref_lse, max_abs_v(case), what or case.spec.name), plan
+
+
+def sampled_rows(case, rows, out, lse, what=""):
+    """Compare selected (b, h) rows of a large case against the oracle,
+    computed one sequence at a time from host copies."""
+    s = case.spec
+    orc = oracle_mod.default()
+    by_b = {}
+    for r in rows:
+        by_b.setdefault(r // s.Hq, []).append(r % s.Hq)
+    worst = (0.0, 0.0)
+    for b, hs in sorted(by_b.items()):
+        q = case.q[b:b + 1].cpu()
+        if case.page_table is None:
+            k = case.k[b:b + 1].cpu()
+            v = case.v[b:b + 1].cpu()
+            ro, rl = orc.decode(q, k, v, s.scale, rows=hs)
+        else:
+            n = -(-case.lengths()[b] // s.page_size)
+            pages = case.page_table[b, :n].long()
+            # the sequence's own pages, renumbered 0..n-1 (same values and order)
+            k = case.k[pages].cpu()
+            v = case.v[pages].cpu()
+            table = torch.arange(n, dtype=torch.int32)[None]
+            sl = case.seq_lens[b:b + 1].cpu()
+            ro, rl = orc.decode(q, k, v, s.scale, page_table=table, seq_lens=sl, rows=hs)
+        go = np.stack([out[b, h] for h in hs])
+        gl = np.array([lse[b, h] for h in hs])
+
+        class _Sub:  # the tolerance needs only spec and dtype
+            spec = s
+        e = compare(_Sub, go, gl, ro, rl, max_abs_v(case, b), f"{what} b={b} heads={hs}")
+        worst = (max(worst[0], e[0]), max(worst[1], e[1]))
+    return worst

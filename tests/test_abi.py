@@ -1,0 +1,198 @@
+"""The C ABI on the host (no GPU work): symbols, defaults, the planner and
+argument checking.  Every call here either fails validation before any
+launch or is a host-only planning call."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from split_kv_fd_amd import fd
+from split_kv_fd_amd.inputs import SPECS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fd.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fd.LIB_PATH):
+        from split_kv_fd_amd import build
+        build.build()
+    return fd.load()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fd_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(lib):
+    declared = header_functions()
+    assert declared == sorted(fd.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), f"{name} not exported"
+
+
+def test_struct_sizes_match_header(lib):
+    # fd_options_init writes struct_size = sizeof(fd_options_t) of the library.
+    opt = fd.fd_options_t()
+    fd.fd_options_init(opt)
+    assert opt.struct_size == ctypes.sizeof(fd.fd_options_t)
+    assert opt.dtype == fd.FD_BF16 and opt.path == fd.FD_PATH_AUTO
+    assert opt.workspace is None and opt.stream is None and opt.page_size == 0
+
+
+def opts(dtype=fd.FD_BF16, **kw):
+    o = fd.fd_options_t()
+    fd.fd_options_init(o)
+    o.dtype = dtype
+    o.num_cus = kw.pop("num_cus", 256)
+    for k, v in kw.items():
+        setattr(o, k, v)
+    return o
+
+
+def plan(B, Hq, Hkv, T, D, n=0, **kw):
+    p = fd.fd_plan_t()
+    st = fd.fd_plan(B, Hq, Hkv, T, D, n, opts(**kw), p)
+    return st, p
+
+
+def test_plan_covers_sequence_and_respects_tiles(lib):
+    for (B, Hq, Hkv, T, D) in [(1, 32, 32, 32768, 128), (4, 32, 8, 131072, 128),
+                               (64, 64, 8, 32768, 128), (1, 4, 4, 1024, 64), (3, 6, 2, 1000, 64),
+                               (1, 1, 1, 1, 128)]:
+        for n in (0, 1, 3, 8, 32, 128, 100000):
+            for dt in (fd.FD_F32, fd.FD_F16, fd.FD_BF16):
+                st, p = plan(B, Hq, Hkv, T, D, n, dtype=dt)
+                assert st == fd.FD_OK, fd.fd_last_error()
+                assert p.n_splits >= 1 and p.chunk % 16 == 0
+                assert p.chunk * p.n_splits >= T > p.chunk * (p.n_splits - 1)
+                if n:
+                    assert p.n_splits <= n
+                assert p.grid[0] == p.n_splits and p.grid[2] == B
+                assert p.grid[1] == Hkv * p.head_blocks
+                assert p.heads_per_block * p.head_blocks >= Hq // Hkv
+                assert bool(p.combine) == (p.n_splits > 1)
+                parts = B * Hq * p.n_splits
+                if p.n_splits > 1:
+                    assert p.workspace_bytes >= parts * (D + 2) * 4
+                else:
+                    assert p.workspace_bytes == 0
+
+
+def test_plan_of_the_five_workloads(lib):
+    # The tiny fp32 case asks for 4 splits of 256 tokens.
+    st, p = plan(1, 4, 4, 1024, 64, 4, dtype=fd.FD_F32)
+    assert st == fd.FD_OK and (p.n_splits, p.chunk) == (4, 256)
+    # Automatic plans put at least one workgroup on every compute unit when
+    # the sequence allows it, and give high-batch GQA a single split.
+    for name in ("mha32k_f16", "gqa128k_bf16", "gqa_b64_bf16"):
+        s = SPECS[name]
+        dt = {"f16": fd.FD_F16, "bf16": fd.FD_BF16}[s.dtype]
+        st, p = plan(s.B, s.Hq, s.Hkv, s.T, s.D, 0, dtype=dt)
+        assert st == fd.FD_OK
+        assert p.grid[0] * p.grid[1] * p.grid[2] >= 256
+    s = SPECS["gqa_b64_bf16"]
+    st, p = plan(s.B, s.Hq, s.Hkv, s.T, s.D, 0)
+    assert p.n_splits == 1
+
+
+def test_plan_paged_chunks_align_to_pages(lib):
+    st, p = plan(16, 32, 8, 65536, 128, 0, page_size=256, max_pages_per_seq=256, num_pages=10)
+    assert st == fd.FD_OK and p.chunk % 256 == 0
+
+
+def test_workspace_bytes_matches_plan(lib):
+    o = opts(dtype=fd.FD_F16)
+    p = fd.fd_plan_t()
+    assert fd.fd_plan(1, 32, 32, 32768, 128, 16, o, p) == fd.FD_OK
+    assert fd.fd_workspace_bytes(1, 32, 32, 32768, 128, 16, o) == p.workspace_bytes > 0
+    assert fd.fd_workspace_bytes(1, 32, 32, 32768, 128, 1, o) == 0
+    assert fd.fd_workspace_bytes(1, 3, 2, 32768, 128, 16, o) == 0   # invalid -> 0
+
+
+@pytest.mark.parametrize("args,status", [
+    ((1, 3, 2, 100, 128), fd.FD_ERR_INVALID_ARG),     # Hq % Hkv
+    ((0, 4, 4, 100, 128), fd.FD_ERR_INVALID_ARG),
+    ((1, 4, 4, 0, 128), fd.FD_ERR_INVALID_ARG),
+    ((1, 4, 4, 100, -1), fd.FD_ERR_INVALID_ARG),
+    ((1, 4, 4, 100, 96), fd.FD_ERR_UNSUPPORTED),
+    ((1, 4, 4, 100, 256), fd.FD_ERR_UNSUPPORTED),
+    ((1, 4, 4, 1 << 30, 128), fd.FD_ERR_UNSUPPORTED),  # 256 GiB per slice
+])
+def test_plan_rejects(lib, args, status):
+    st, _ = plan(*args)
+    assert st == status
+    assert fd.fd_last_error() != ""
+
+
+def test_plan_rejects_bad_options(lib):
+    assert plan(1, 4, 4, 100, 128, -1)[0] == fd.FD_ERR_INVALID_ARG
+    assert plan(1, 4, 4, 100, 128, dtype=7)[0] == fd.FD_ERR_INVALID_ARG
+    assert plan(1, 4, 4, 100, 128, path=5)[0] == fd.FD_ERR_INVALID_ARG
+    assert plan(1, 4, 4, 100, 128, page_size=12, max_pages_per_seq=9, num_pages=1)[0] == fd.FD_ERR_INVALID_ARG
+    assert plan(1, 4, 4, 100, 128, page_size=16, max_pages_per_seq=6, num_pages=1)[0] == fd.FD_ERR_INVALID_ARG
+    assert plan(1, 4, 4, 100, 128, page_size=16, max_pages_per_seq=7, num_pages=0)[0] == fd.FD_ERR_INVALID_ARG
+    o = opts()
+    o.struct_size = 8
+    p = fd.fd_plan_t()
+    assert fd.fd_plan(1, 4, 4, 100, 128, 0, o, p) == fd.FD_ERR_INVALID_ARG
+    lib_ = fd.load()
+    assert lib_.fd_plan(1, 4, 4, 100, 128, 0, None, ctypes.byref(p)) == fd.FD_ERR_INVALID_ARG
+    assert lib_.fd_plan(1, 4, 4, 100, 128, 0, ctypes.byref(o), None) == fd.FD_ERR_INVALID_ARG
+
+
+# Pointer values below are never dereferenced: each call fails host
+# validation before anything is launched.
+A = 1 << 20          # 16-byte aligned fake address
+MIS = A + 2          # misaligned
+
+
+def decode(q=A, k=A, v=A, pt=None, sl=None, out=A, lse=A, shape=(1, 4, 4, 4096, 128), scale=0.1,
+           n=16, **kw):
+    return fd.fd_decode(q, k, v, pt, sl, out, lse, *shape, scale, n, opts(**kw))
+
+
+def test_decode_rejects_before_launch(lib):
+    assert decode(q=None) == fd.FD_ERR_INVALID_ARG
+    assert decode(v=None) == fd.FD_ERR_INVALID_ARG
+    assert decode(out=None) == fd.FD_ERR_INVALID_ARG
+    assert decode(k=MIS) == fd.FD_ERR_INVALID_ARG
+    assert decode(out=A + 1) == fd.FD_ERR_INVALID_ARG
+    assert decode(scale=float("inf")) == fd.FD_ERR_INVALID_ARG
+    assert decode(scale=float("nan")) == fd.FD_ERR_INVALID_ARG
+    assert decode(shape=(1, 4, 3, 4096, 128)) == fd.FD_ERR_INVALID_ARG
+    assert decode(shape=(1, 4, 4, 4096, 80)) == fd.FD_ERR_UNSUPPORTED
+    assert decode(n=-2) == fd.FD_ERR_INVALID_ARG
+    # paged geometry without a table, and a table without geometry
+    assert decode(page_size=16, max_pages_per_seq=256, num_pages=4) == fd.FD_ERR_INVALID_ARG
+    assert decode(pt=A) == fd.FD_ERR_INVALID_ARG
+    # a multi-split plan needs a big enough, aligned workspace
+    assert decode() == fd.FD_ERR_WORKSPACE
+    assert decode(workspace=A, workspace_bytes=100) == fd.FD_ERR_WORKSPACE
+    need = fd.fd_workspace_bytes(1, 4, 4, 4096, 128, 16, opts())
+    assert decode(workspace=A + 16, workspace_bytes=need) == fd.FD_ERR_WORKSPACE
+    assert "workspace" in fd.fd_last_error()
+    assert fd.fd_split(A, A, None, None, None, A, A, 1, 4, 4, 4096, 128, 0.1, 16, opts()) == fd.FD_ERR_INVALID_ARG
+    assert fd.fd_combine(None, None, A, 1, 4, 4, 4096, 128, 16, opts()) == fd.FD_ERR_INVALID_ARG
+    assert fd.fd_combine(None, A, A, 1, 4, 4, 4096, 128, 16, opts()) == fd.FD_ERR_WORKSPACE
+
+
+def test_status_strings(lib):
+    for st in range(5):
+        assert fd.fd_status_string(st).startswith("FD_")
+    assert "unknown" in fd.fd_status_string(99)
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
+def test_no_device_reports_hip_error(lib):
+    # Planning for the current device needs one: without a GPU this fails
+    # cleanly instead of launching.
+    need = 1 << 30
+    st = decode(num_cus=0, workspace=A, workspace_bytes=need)
+    assert st == fd.FD_ERR_HIP
+    assert "hip" in fd.fd_last_error().lower()

@@ -1,0 +1,190 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle on
+the same seeded inputs.  Small cases are compared element by element; the
+full-size workloads, in the launch configuration the benchmark times, are
+compared on sampled (batch, head) rows."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from split_kv_fd_amd import inputs
+from split_kv_fd_amd.decode import Decoder
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def small_case(name, device=DEV, **kw):
+    return inputs.make_case(inputs.spec(name, **kw), device="cpu").to(device)
+
+
+# ------------------------------------------------------------------ the five workloads, reduced
+
+def test_tiny_f32_four_splits():
+    case = small_case("tiny_f32")
+    (err, _), plan = parity.check_full(case, n_splits=4)
+    assert (plan["n_splits"], plan["chunk"]) == (4, 256)
+
+
+@pytest.mark.parametrize("n", [0, 1, 8, 32, 128])
+def test_mha_f16_split_sweep(n):
+    case = small_case("mha32k_f16", Hq=8, Hkv=8, T=4096 + 37)
+    parity.check_full(case, n_splits=n, what=f"mha f16 n={n}")
+
+
+def test_gqa_bf16_spiky_keys():
+    case = small_case("gqa128k_bf16", B=2, T=8192 + 5)
+    parity.check_full(case, what="gqa bf16 spiky")
+
+
+def test_paged_ragged_bf16():
+    case = small_case("paged_ragged_bf16", B=5, T=3000, len_lo=1, len_hi=3000)
+    for n in (0, 1, 7):
+        parity.check_full(case, n_splits=n, what=f"paged n={n}")
+
+
+def test_high_batch_gqa_hot_head():
+    case = small_case("gqa_b64_bf16", B=4, T=2048 + 100)
+    parity.check_full(case, what="b64 hot q")
+
+
+# ------------------------------------------------------------------ shapes and group sizes
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 8, 16])
+def test_group_sizes(dtype, D, G):
+    Hkv = 2
+    case = small_case("mha32k_f16", B=2, Hq=Hkv * G, Hkv=Hkv, D=D, T=700, dtype=dtype)
+    parity.check_full(case, what=f"G={G} D={D} {dtype}")
+
+
+@pytest.mark.parametrize("T", [1, 2, 15, 16, 17, 63, 64, 65, 257])
+def test_short_sequences(T):
+    case = small_case("gqa128k_bf16", B=1, Hq=8, Hkv=2, T=T)
+    for n in (0, 1, 3):
+        parity.check_full(case, n_splits=n, what=f"T={T} n={n}")
+
+
+def test_ragged_lengths_with_empty_sequences():
+    s = inputs.spec("mha32k_f16", B=4, Hq=4, Hkv=2, T=300)
+    case = inputs.make_case(s).to(DEV)
+    case.seq_lens = torch.tensor([0, 1, 299, 300], dtype=torch.int32, device=DEV)
+    for n in (0, 1, 5):
+        out, lse, _ = parity.run_gpu(case, n)
+        ref_out, ref_lse = parity.oracle_full(case)
+        parity.compare(case, out, lse, ref_out, ref_lse, parity.max_abs_v(case), f"ragged n={n}")
+        assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
+
+
+def test_paged_page_sizes():
+    for P in (1, 4, 16, 64, 256):
+        case = small_case("paged_ragged_bf16", B=3, Hq=8, Hkv=4, T=1000, page_size=P,
+                          len_lo=1, len_hi=1000)
+        parity.check_full(case, what=f"page_size={P}")
+
+
+def test_paged_equals_contiguous_gather():
+    s = inputs.spec("paged_ragged_bf16", B=3, T=900, len_lo=600, len_hi=900)
+    case = inputs.make_case(s).to(DEV)
+    out_p, lse_p, _ = parity.run_gpu(case, 4)
+    lens = case.lengths()
+    k = torch.zeros((s.B, s.Hkv, s.T, s.D), dtype=case.k.dtype, device=DEV)
+    v = torch.zeros_like(k)
+    for b in range(s.B):
+        t = torch.arange(lens[b], device=DEV)
+        pages = case.page_table[b, t // s.page_size].long()
+        k[b, :, :lens[b]] = case.k[pages, :, t % s.page_size].transpose(0, 1)
+        v[b, :, :lens[b]] = case.v[pages, :, t % s.page_size].transpose(0, 1)
+    cont = inputs.Case(s, case.q, k, v, None, case.seq_lens)
+    out_c, lse_c, _ = parity.run_gpu(cont, 4)
+    assert np.max(np.abs(out_p - out_c)) <= 1e-6 and np.max(np.abs(lse_p - lse_c)) <= 1e-6
+
+
+# ------------------------------------------------------------------ closed-form cases on the GPU
+
+def test_special_values_on_gpu():
+    s = inputs.spec("gqa128k_bf16", B=1, Hq=8, Hkv=2, T=1000)
+    case = inputs.make_case(s).to(DEV)
+    # constant V -> that constant
+    v = torch.empty_like(case.v)
+    v[:] = case.v[:, :, :1]
+    c = inputs.Case(s, case.q, case.k, v)
+    out, _, _ = parity.run_gpu(c, 4)
+    ref = case.v[:, :, 0].float().repeat_interleave(4, dim=1).cpu().numpy()
+    assert np.max(np.abs(out - ref)) <= 1e-6 * max(1.0, np.abs(ref).max())
+    # q = 0 -> mean of V, lse = ln T
+    c = inputs.Case(s, torch.zeros_like(case.q), case.k, case.v)
+    out, lse, _ = parity.run_gpu(c, 4)
+    mean = case.v.double().mean(dim=2).repeat_interleave(4, dim=1).cpu().numpy()
+    assert np.max(np.abs(out - mean)) <= 1e-5
+    assert np.max(np.abs(lse - math.log(1000))) <= 1e-5
+
+
+def test_deterministic_runs():
+    case = small_case("gqa128k_bf16", B=2, T=5000)
+    a = parity.run_gpu(case, 0)
+    b = parity.run_gpu(case, 0)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_split_and_combine_entry_points():
+    case = small_case("mha32k_f16", B=1, Hq=4, Hkv=4, T=3000)
+    dec = Decoder(case.q, case.k, case.v, scale=case.spec.scale, n_splits=6)
+    assert dec.plan["n_splits"] > 1
+    parity.announce("fd_split + fd_combine separately")
+    dec.split()
+    dec.combine()
+    torch.cuda.synchronize()
+    out1, lse1 = dec.out.clone(), dec.lse.clone()
+    dec()
+    torch.cuda.synchronize()
+    assert torch.equal(out1, dec.out) and torch.equal(lse1, dec.lse)
+
+
+# ------------------------------------------------------------------ full-size workloads, sampled rows
+
+def _full_rows(case, extra=()):
+    s = case.spec
+    g = torch.Generator().manual_seed(s.seed + 7)
+    rows = torch.randperm(s.B * s.Hq, generator=g)[:6].tolist()
+    return sorted(set(rows) | set(extra))
+
+
+def test_full_mha32k_f16_split_sweep():
+    s = inputs.spec("mha32k_f16")
+    case = inputs.make_case(s, device=DEV)
+    rows = _full_rows(case)
+    for n in (0, 1, 8, 32, 128):
+        out, lse, plan = parity.run_gpu(case, n)
+        parity.sampled_rows(case, rows, out, lse, f"mha32k n={n} ({plan['n_splits']} splits)")
+
+
+def test_full_gqa128k_bf16():
+    s = inputs.spec("gqa128k_bf16")
+    case = inputs.make_case(s, device=DEV)
+    out, lse, _ = parity.run_gpu(case, 0)
+    parity.sampled_rows(case, _full_rows(case, extra=[0, s.Hq * s.B - 1]), out, lse, "gqa128k")
+
+
+def test_full_paged_ragged_bf16():
+    s = inputs.spec("paged_ragged_bf16")
+    case = inputs.make_case(s, device=DEV)
+    out, lse, _ = parity.run_gpu(case, 0)
+    lens = case.lengths()
+    shortest = min(range(s.B), key=lambda b: lens[b])
+    odd = [b for b in range(s.B) if lens[b] % s.page_size][0]
+    parity.sampled_rows(case, _full_rows(case, extra=[shortest * s.Hq, odd * s.Hq + 5]),
+                        out, lse, "paged ragged")
+
+
+def test_full_gqa_b64_bf16_hot_heads():
+    s = inputs.spec("gqa_b64_bf16")
+    case = inputs.make_case(s, device=DEV)
+    out, lse, _ = parity.run_gpu(case, 0)
+    qn = case.q.float().norm(dim=-1)                     # [B, Hq]
+    hot = [int(b * s.Hq + int(qn[b].argmax())) for b in (0, 31, 63)]
+    parity.sampled_rows(case, _full_rows(case, extra=hot), out, lse, "b64 gqa")
