@@ -176,22 +176,31 @@ def main() -> int:
     torch.cuda.synchronize()
 
     K = args.steps
+    separate = plan["combine"] and not plan["fused"]
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(K):
-        d = decs[i % copies]
-        ev[i][0].record()
-        d.split()
-        ev[i][1].record()
-        d.combine()
-        ev[i][2].record()
+    if separate:
+        # the merge is its own kernel: time the two launches apart
+        for i in range(K):
+            d = decs[i % copies]
+            ev[i][0].record()
+            d.split()
+            ev[i][1].record()
+            d.combine()
+            ev[i][2].record()
+    else:
+        # one launch per step: the split kernel (with the fused merge)
+        for i in range(K):
+            ev[i][0].record()
+            decs[i % copies]()
+            ev[i][1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
 
     split_ms = [e[0].elapsed_time(e[1]) for e in ev]
-    comb_ms = [e[1].elapsed_time(e[2]) for e in ev]
-    step_ms = [e[0].elapsed_time(e[2]) for e in ev]
+    comb_ms = [e[1].elapsed_time(e[2]) for e in ev] if separate else [0.0]
+    step_ms = [e[0].elapsed_time(e[2 if separate else 1]) for e in ev]
     ms_per_step = (t1 - t0) * 1e3 / K
     gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
     split_avg = statistics.mean(split_ms)
@@ -216,7 +225,7 @@ def main() -> int:
                    "D": spec.D, "T": spec.T, "kv_dtype": spec.dtype, "accumulate": "f32",
                    "kv_bytes_per_step": kv_bytes, "kv_copies_rotated": copies,
                    "n_splits": plan["n_splits"], "chunk": plan["chunk"], "path": plan["path"],
-                   "seed": spec.seed},
+                   "fused_merge": plan["fused"], "seed": spec.seed},
         "us_per_step": round(ms_per_step * 1e3, 2),
         "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
@@ -225,6 +234,7 @@ def main() -> int:
                      "launch_us_avg": round(split_avg * 1e3, 2),
                      "bytes_per_launch": kv_bytes},
         "kernels_us": {"split_avg": round(split_avg * 1e3, 2),
+                       "merge": "fused into the split launch" if not separate else "combine kernel",
                        "split_median": round(statistics.median(split_ms) * 1e3, 2),
                        "combine_avg": round(statistics.mean(comb_ms) * 1e3, 2),
                        "step_events_median": round(statistics.median(step_ms) * 1e3, 2)},

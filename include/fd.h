@@ -73,7 +73,8 @@ typedef enum {
 typedef struct fd_options {
     uint32_t struct_size;       /* sizeof(fd_options_t) of the caller         */
     int32_t dtype;              /* fd_dtype_t of q, K and V                    */
-    int32_t page_size;          /* paged only: tokens per page, power of two  */
+    int32_t page_size;          /* > 0 selects the paged layout (page_table   */
+                                /* required): tokens per page, power of two   */
     int32_t max_pages_per_seq;  /* paged only: row stride of page_table       */
     int32_t num_pages;          /* paged only: pool size; page ids outside    */
                                 /* [0, num_pages) read as empty tokens        */
@@ -85,7 +86,9 @@ typedef struct fd_options {
     void *stream;               /* hipStream_t to launch on; NULL = null stream */
 } fd_options_t;
 
-/* What a call with these arguments will launch (see fd_plan). */
+/* What a call with these arguments will launch (see fd_plan).  Paged calls
+ * (opt->page_size > 0) are planned as ragged batches: shorter chunks, so
+ * sequences of very different lengths spread evenly over the device. */
 typedef struct fd_plan {
     int32_t n_splits;           /* effective number of KV splits              */
     int32_t chunk;              /* tokens per split (last one may be shorter) */
@@ -96,8 +99,10 @@ typedef struct fd_plan {
     int32_t grid[3];            /* split-kernel grid (x: split, y: kv head *  */
                                 /* head_blocks, z: batch)                     */
     int32_t block;              /* threads per split workgroup                */
-    int32_t combine;            /* 1 if a combine launch follows the split    */
-    int32_t reserved;
+    int32_t combine;            /* 1 if the splits are merged (n_splits > 1)   */
+    int32_t fused;              /* 1 if fd_decode merges them inside the split */
+                                /* launch (its last workgroup per kv head);   */
+                                /* 0: fd_decode launches the combine kernel   */
     size_t workspace_bytes;     /* workspace this call needs (0 if n_splits=1) */
 } fd_plan_t;
 
@@ -124,8 +129,11 @@ size_t fd_workspace_bytes(int B, int Hq, int Hkv, int T, int D, int n_splits,
                           const fd_options_t *opt);
 
 /*
- * Decode attention: the split pass, then (when the plan has more than one
- * split) the combine pass, both on opt->stream.
+ * Decode attention: the split pass and, when the plan has more than one
+ * split, the merge of the splits, on opt->stream.  With plan.fused the
+ * merge runs inside the split launch (the last workgroup of each kv head
+ * combines its group's splits), so one kernel is launched; otherwise the
+ * combine kernel follows.
  *   q, k_cache, v_cache : device inputs in opt->dtype (layouts above).
  *   page_table          : NULL for contiguous caches; else [B, max_pages].
  *   seq_lens            : NULL = every sequence has length T; else [B].
@@ -133,9 +141,12 @@ size_t fd_workspace_bytes(int B, int Hq, int Hkv, int T, int D, int n_splits,
  *   T                   : cache length, or the largest T_b for ragged input.
  *   scale               : multiplies q.k before the softmax (finite).
  *   n_splits            : 0 = automatic, else the requested split count.
- * The workspace (opt->workspace, >= fd_workspace_bytes) holds the partials
- * [B, Hq, n_splits, D] plus two [B, Hq, n_splits] rows; its contents before
- * the call do not matter.
+ * The workspace (opt->workspace, >= fd_workspace_bytes, 256-byte aligned)
+ * holds one arrival counter per (batch, kv head, head block), the partials
+ * [B, Hq, n_splits, D] and two [B, Hq, n_splits] rows.  Its contents before
+ * the call do not matter: counters carry a per-call tag, so values left by
+ * any earlier call are ignored.  Calls that share a workspace must not
+ * overlap in time.
  */
 fd_status_t fd_decode(const void *q, const void *k_cache, const void *v_cache,
                       const int32_t *page_table, const int32_t *seq_lens,

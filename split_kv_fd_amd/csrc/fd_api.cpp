@@ -6,6 +6,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <atomic>
 #include <mutex>
 
 #include "fd_kernels.h"
@@ -99,15 +100,26 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
     const long elt = o.dtype == FD_F32 ? 4 : 2;
     if (!paged && (long)T * D * elt >= (1L << 32))
         return fail(FD_ERR_UNSUPPORTED, "one (batch, kv head) cache slice of T*D*%ld bytes must be < 4 GiB", elt);
-    if (o.path == FD_PATH_MFMA)
-        return fail(FD_ERR_UNSUPPORTED, "the MFMA path is not built in this library version");
 
+    // Path: the matrix-core kernel once a kv head's query group makes the
+    // logit and value updates real small-M contractions (f16 / bf16 only).
     const int G = Hq / Hkv;
-    int hpb = 1;
-    while (hpb < G && hpb < 8) hpb <<= 1;
+    int path = o.path;
+    if (path == FD_PATH_MFMA && o.dtype == FD_F32)
+        return fail(FD_ERR_UNSUPPORTED, "the MFMA path needs f16 or bf16 inputs");
+    if (path == FD_PATH_AUTO)
+        path = (o.dtype != FD_F32 && G >= env_long("FD_MFMA_MIN_G", 4)) ? FD_PATH_MFMA : FD_PATH_VALU;
+    int hpb, tile;
+    if (path == FD_PATH_MFMA) {
+        hpb = fdk::kMfmaHeads;
+        tile = fdk::kMfmaTile;
+    } else {
+        hpb = 1;
+        while (hpb < G && hpb < 8) hpb <<= 1;
+        tile = fdk::valu_tile(o.dtype, D, hpb);
+    }
     const int head_blocks = (int)ceil_div(G, hpb);
     if ((long)Hkv * head_blocks > 65535) return fail(FD_ERR_UNSUPPORTED, "Hkv*head_blocks > 65535");
-    const int tile = fdk::valu_tile(o.dtype, D, hpb);
     if (tile <= 0) return fail(FD_ERR_UNSUPPORTED, "no kernel instance for this shape");
 
     int cus = o.num_cus;
@@ -123,15 +135,22 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
     if (n_req > 0) {
         n = n_req < max_n ? n_req : max_n;
     } else {
-        // Enough workgroups to cover every compute unit twice over, but no
-        // split shorter than min_chunk tokens (its partial write and the
-        // combine read must stay small against the chunk's KV bytes).
+        // Enough workgroups to cover every compute unit several times over,
+        // but no split shorter than min_chunk tokens (its partial write and
+        // the merge must stay small against the chunk's KV bytes).  Paged
+        // (ragged) batches get shorter chunks so the hardware scheduler can
+        // balance sequences of very different lengths.
         const long units = (long)B * Hkv * head_blocks;
         const long target = env_long("FD_TARGET_WGS", 2L * cus);
         const long min_chunk = env_long("FD_CHUNK_MIN", 512);
         n = ceil_div(target, units);
         const long cap = T / min_chunk > 1 ? T / min_chunk : 1;
         if (n > cap) n = cap;
+        if (paged) {
+            const long ragged_chunk = env_long("FD_RAGGED_CHUNK", 2048);
+            const long nr = ceil_div(T, ragged_chunk);
+            if (n < nr) n = nr;
+        }
     }
     if (n < 1) n = 1;
     long chunk = ceil_div(ceil_div(T, n), gran) * gran;
@@ -140,7 +159,7 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
     std::memset(p, 0, sizeof *p);
     p->n_splits = (int)n;
     p->chunk = (int)chunk;
-    p->path = FD_PATH_VALU;
+    p->path = path;
     p->tile = tile;
     p->heads_per_block = hpb;
     p->head_blocks = head_blocks;
@@ -149,9 +168,14 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
     p->grid[2] = B;
     p->block = 256;
     p->combine = n > 1;
+    // The last workgroup of a group merges the splits itself when their
+    // weights fit its LDS (n * heads <= 4 * D * heads_per_block).
+    p->fused = n > 1 && n <= 4L * D && env_long("FD_FUSED", 1) == 1;
     if (n > 1) {
         const size_t parts = (size_t)B * Hq * (size_t)n;
-        p->workspace_bytes = align256(parts * D * sizeof(float)) + 2 * align256(parts * sizeof(float));
+        const size_t counters = (size_t)B * Hkv * head_blocks * sizeof(unsigned long long);
+        p->workspace_bytes = align256(counters) + align256(parts * D * sizeof(float)) +
+                             2 * align256(parts * sizeof(float));
     }
     return FD_OK;
 }
@@ -192,6 +216,7 @@ fd_status_t prepare(const void *q, const void *k, const void *v, const int32_t *
     if (st != FD_OK) return st;
 
     float *part_o = nullptr, *part_m = nullptr, *part_l = nullptr;
+    unsigned long long *counters = nullptr;
     if (c->p.n_splits > 1) {
         if (!c->o.workspace)
             return fail(FD_ERR_WORKSPACE, "plan has %d splits: a workspace of %zu bytes is required",
@@ -202,6 +227,8 @@ fd_status_t prepare(const void *q, const void *k, const void *v, const int32_t *
         if (!aligned(c->o.workspace, 256)) return fail(FD_ERR_WORKSPACE, "workspace must be 256-byte aligned");
         const size_t parts = (size_t)B * Hq * (size_t)c->p.n_splits;
         char *w = static_cast<char *>(c->o.workspace);
+        counters = reinterpret_cast<unsigned long long *>(w);
+        w += align256((size_t)B * Hkv * c->p.head_blocks * sizeof(unsigned long long));
         part_o = reinterpret_cast<float *>(w);
         w += align256(parts * D * sizeof(float));
         part_m = reinterpret_cast<float *>(w);
@@ -225,6 +252,9 @@ fd_status_t prepare(const void *q, const void *k, const void *v, const int32_t *
     s.max_pages = paged ? c->o.max_pages_per_seq : 0;
     s.num_pages = paged ? c->o.num_pages : 0;
     s.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+    s.fused = 0;
+    s.epoch = 0;
+    s.counters = counters;
 
     fdk::CombineArgs &cb = c->c;
     cb.part_o = part_o; cb.part_m = part_m; cb.part_l = part_l;
@@ -236,8 +266,21 @@ fd_status_t prepare(const void *q, const void *k, const void *v, const int32_t *
     return FD_OK;
 }
 
-fd_status_t run_split(const Call &c) {
-    const hipError_t e = fdk::launch_split_valu(c.s, c.o.dtype, static_cast<hipStream_t>(c.o.stream));
+// Epoch of a fused call: distinct per call (never 0), so arrival counters
+// left in a workspace by any earlier call are recognised as stale.
+unsigned next_epoch() {
+    static std::atomic<unsigned> epoch{0x5eed0000u};
+    unsigned e;
+    do { e = epoch.fetch_add(1, std::memory_order_relaxed) + 1; } while (e == 0);
+    return e;
+}
+
+fd_status_t run_split(Call &c, bool fused) {
+    c.s.fused = fused ? 1 : 0;
+    c.s.epoch = fused ? next_epoch() : 0;
+    const hipStream_t stream = static_cast<hipStream_t>(c.o.stream);
+    const hipError_t e = c.p.path == FD_PATH_MFMA ? fdk::launch_split_mfma(c.s, c.o.dtype, stream)
+                                                  : fdk::launch_split_valu(c.s, c.o.dtype, stream);
     if (e != hipSuccess) return hip_fail(e, "launching the split kernel");
     return FD_OK;
 }
@@ -283,8 +326,9 @@ fd_status_t fd_decode(const void *q, const void *k_cache, const void *v_cache, c
     fd_status_t st = prepare(q, k_cache, v_cache, page_table, seq_lens, out, lse, B, Hq, Hkv, T, D, scale,
                              n_splits, opt, true, &c);
     if (st != FD_OK) return st;
-    st = run_split(c);
-    if (st != FD_OK) return st;
+    const bool fused = c.p.fused != 0;
+    st = run_split(c, fused);
+    if (st != FD_OK || fused) return st;
     return run_combine(c);
 }
 
@@ -295,7 +339,7 @@ fd_status_t fd_split(const void *q, const void *k_cache, const void *v_cache, co
     fd_status_t st = prepare(q, k_cache, v_cache, page_table, seq_lens, out, lse, B, Hq, Hkv, T, D, scale,
                              n_splits, opt, true, &c);
     if (st != FD_OK) return st;
-    return run_split(c);
+    return run_split(c, false);
 }
 
 fd_status_t fd_combine(const int32_t *seq_lens, float *out, float *lse, int B, int Hq, int Hkv, int T, int D,

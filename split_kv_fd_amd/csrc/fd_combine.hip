@@ -7,7 +7,8 @@
 // One 64-lane wavefront per (batch, query head), four per workgroup.  The
 // global max and normaliser are wave reductions over the splits (lanes
 // stride over splits); the weighted sum over splits runs with each lane
-// owning D/64 output elements, reading the partial rows coalesced.  Split
+// owning D/64 output elements, reading eight partial rows at a time so the
+// loop is not bound by one memory round trip per split.  Split
 // maxima are in base-2 units (the split kernel folds log2(e) into the
 // scale).  Splits that start past a sequence's length were never written
 // and are not read.
@@ -34,6 +35,7 @@ __device__ __forceinline__ float wave_sum(float x) {
 template <int D>
 __global__ __launch_bounds__(256) void combine(CombineArgs a) {
     constexpr int DPL = D / 64;   // output elements per lane
+    constexpr int UNR = 8;        // partial rows in flight per lane
     const int lane = threadIdx.x & 63;
     const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (bh >= a.B * a.Hq) return;   // whole wave exits together
@@ -57,18 +59,33 @@ __global__ __launch_bounds__(256) void combine(CombineArgs a) {
     const float mu = M == kNegInf ? 0.f : M;
 
     float L = 0.f;
-    for (int s = lane; s < n; s += 64) L += __builtin_amdgcn_exp2f(pm[s] - mu) * pl[s];
-    L = wave_sum(L);
-
     float acc[DPL];
 #pragma unroll
     for (int j = 0; j < DPL; ++j) acc[j] = 0.f;
-    for (int s = 0; s < n; ++s) {
-        const float w = __builtin_amdgcn_exp2f(pm[s] - mu);
-        const float *row = po + (size_t)s * D + lane * DPL;
+    // Lanes hold the weights of 64 splits at a time; each weight is
+    // broadcast while UNR partial rows are read at once.
+    for (int s0 = 0; s0 < n; s0 += 64) {
+        const int s = s0 + lane;
+        const float w = s < n ? __builtin_amdgcn_exp2f(pm[s] - mu) : 0.f;
+        if (s < n) L += w * pl[s];
+        const int cnt = n - s0 < 64 ? n - s0 : 64;
+        for (int j0 = 0; j0 < cnt; j0 += UNR) {
+            float v[UNR][DPL], wj[UNR];
 #pragma unroll
-        for (int j = 0; j < DPL; ++j) acc[j] = fmaf(w, row[j], acc[j]);
+            for (int u = 0; u < UNR; ++u) {
+                const bool in = j0 + u < cnt;
+                wj[u] = __shfl(w, j0 + u < 64 ? j0 + u : 63);
+                const float *row = po + (size_t)(s0 + (in ? j0 + u : 0)) * D + lane * DPL;
+#pragma unroll
+                for (int j = 0; j < DPL; ++j) v[u][j] = in ? row[j] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < UNR; ++u)
+#pragma unroll
+                for (int j = 0; j < DPL; ++j) acc[j] = fmaf(j0 + u < cnt ? wj[u] : 0.f, v[u][j], acc[j]);
+        }
     }
+    L = wave_sum(L);
 
     float *o = a.out + (size_t)bh * D + lane * DPL;
 #pragma unroll

@@ -1,0 +1,160 @@
+// Device code shared by the split kernels: merging the per-wave softmax
+// states of one workgroup, writing a split's partial (or the final result
+// when there is a single split), and -- in the fused mode -- letting the
+// last workgroup of a (batch, kv head, head block) merge all of its splits.
+//
+// The merge rule is the combine of tinyvolt's "Combine kernel" section:
+// align every partial to the largest running max, sum the rescaled
+// normalisers and accumulators, divide once.  Maxima are in base-2 units.
+#pragma once
+
+#include "fd_kernels.h"
+
+namespace fdk {
+
+constexpr float kEpNegInf = -__builtin_inff();
+constexpr float kEpLn2 = 0.693147180559945309417f;
+
+__device__ __forceinline__ float ep_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Count this workgroup's arrival at its group's counter.  The counter holds
+// (call epoch << 32 | arrivals); a value left by any other call (another
+// epoch) restarts the count, so the workspace needs no clearing between
+// calls.  Returns true for the workgroup that completes the group.  The loop
+// ends: every failed exchange means another workgroup's exchange succeeded.
+__device__ __forceinline__ bool arrive_last(unsigned long long *cnt, unsigned epoch, int n_active) {
+    unsigned long long old = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    unsigned long long next;
+    for (;;) {
+        next = ((unsigned)(old >> 32) == epoch) ? old + 1ull
+                                                 : (((unsigned long long)epoch << 32) | 1ull);
+        if (__hip_atomic_compare_exchange_strong(cnt, &old, next, __ATOMIC_ACQ_REL, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT))
+            break;
+    }
+    return (unsigned)(next & 0xffffffffull) == (unsigned)n_active;
+}
+
+__device__ __forceinline__ float ld_agent(const float *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// LDS the epilogue works in: per-wave states, reused for the split weights.
+template <int WAVES, int GB, int D>
+struct EpilogueLds {
+    float o[WAVES][GB][D];
+    float m[WAVES][GB];
+    float l[WAVES][GB];
+    float gm[GB];      // combine: global max of each head
+    float gl[GB];      // combine: global normaliser of each head
+    int last;
+};
+
+// Splits that hold tokens of a sequence of length Tb.
+__device__ __forceinline__ int active_splits(const SplitArgs &a, int Tb) {
+    const int n = (Tb + a.chunk - 1) / a.chunk;
+    return n < a.n_splits ? n : a.n_splits;
+}
+
+// Merge the last workgroup's group: for every valid head g of the block,
+// out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s over the n active
+// splits, read back from the workspace.
+template <int WAVES, int GB, int D>
+__device__ void combine_group(const SplitArgs &a, EpilogueLds<WAVES, GB, D> &sm, int b, int h0, int ng,
+                              int n) {
+    constexpr int NT = WAVES * 64;
+    float *w = &sm.o[0][0][0];                       // [GB][n] split weights
+    constexpr int WCAP = WAVES * GB * D;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // maxima and weights, one wave per head
+    for (int g = wave; g < ng; g += WAVES) {
+        const size_t row = (size_t)(b * a.Hq + h0 + g) * a.n_splits;
+        float M = kEpNegInf;
+        for (int s = lane; s < n; s += 64) {
+            const float m = ld_agent(a.part_m + row + s);
+            w[g * n + s] = m;
+            M = fmaxf(M, m);
+        }
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+        const float mu = M == kEpNegInf ? 0.f : M;
+        float L = 0.f;
+        for (int s = lane; s < n; s += 64) {
+            const float c = ep_exp2(w[g * n + s] - mu);
+            w[g * n + s] = c;
+            L += c * ld_agent(a.part_l + row + s);
+        }
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) L += __shfl_xor(L, off);
+        if (lane == 0) { sm.gm[g] = M; sm.gl[g] = L; }
+    }
+    __syncthreads();
+    (void)WCAP;
+    for (int idx = threadIdx.x; idx < ng * D; idx += NT) {
+        const int g = idx / D, d = idx - (idx / D) * D;
+        const int bh = b * a.Hq + h0 + g;
+        const float *po = a.part_o + (size_t)bh * a.n_splits * D + d;
+        const float *wg = w + g * n;
+        float acc = 0.f;
+        int s = 0;
+        for (; s + 8 <= n; s += 8) {
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = ld_agent(po + (size_t)(s + j) * D);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc = fmaf(wg[s + j], v[j], acc);
+        }
+        for (; s < n; ++s) acc = fmaf(wg[s], ld_agent(po + (size_t)s * D), acc);
+        const float L = sm.gl[g];
+        a.out[(size_t)bh * D + d] = L > 0.f ? acc / L : 0.f;
+        if (d == 0 && a.lse) a.lse[bh] = L > 0.f ? (sm.gm[g] + log2f(L)) * kEpLn2 : kEpNegInf;
+    }
+}
+
+// Called by every thread after sm.o / sm.m / sm.l hold each wave's state
+// (the caller has synchronised).  Writes this split's result and, in fused
+// mode, completes the group when this workgroup arrives last.
+template <int WAVES, int GB, int D>
+__device__ void finish_split(const SplitArgs &a, EpilogueLds<WAVES, GB, D> &sm, int b, int kvh, int hb,
+                             int split, int h0, int ng, int Tb) {
+    constexpr int NT = WAVES * 64;
+    for (int idx = threadIdx.x; idx < ng * D; idx += NT) {
+        const int g = idx / D, d = idx - (idx / D) * D;
+        float M = sm.m[0][g];
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w) M = fmaxf(M, sm.m[w][g]);
+        const float mu = M == kEpNegInf ? 0.f : M;
+        float acc = 0.f, L = 0.f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) {
+            const float c = ep_exp2(sm.m[w][g] - mu);
+            acc += c * sm.o[w][g][d];
+            L += c * sm.l[w][g];
+        }
+        const int bh = b * a.Hq + h0 + g;
+        if (a.n_splits == 1) {
+            a.out[(size_t)bh * D + d] = L > 0.f ? acc / L : 0.f;
+            if (d == 0 && a.lse) a.lse[bh] = L > 0.f ? (M + log2f(L)) * kEpLn2 : kEpNegInf;
+        } else {
+            const size_t pi = (size_t)bh * a.n_splits + split;
+            a.part_o[pi * D + d] = acc;
+            if (d == 0) { a.part_m[pi] = M; a.part_l[pi] = L; }
+        }
+    }
+    if (a.n_splits == 1 || !a.fused) return;
+
+    // Fused combine: publish this split, count arrivals, and let the last
+    // workgroup of the group merge every split.
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        unsigned long long *cnt = a.counters + (size_t)b * a.Hkv * a.head_blocks + (size_t)kvh * a.head_blocks + hb;
+        sm.last = arrive_last(cnt, a.epoch, active_splits(a, Tb)) ? 1 : 0;
+    }
+    __syncthreads();
+    if (!sm.last) return;
+    __threadfence();
+    combine_group<WAVES, GB, D>(a, sm, b, h0, ng, active_splits(a, Tb));
+}
+
+}  // namespace fdk

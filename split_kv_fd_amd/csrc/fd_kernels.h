@@ -8,6 +8,15 @@
 
 #include "../../include/fd.h"
 
+// Tokens each row of a wave takes per step in the VALU kernel (G <= 2).
+#ifndef FD_VALU_U
+#define FD_VALU_U 4
+#endif
+// 1: stream K/V with non-temporal loads.
+#ifndef FD_NT_LOADS
+#define FD_NT_LOADS 0
+#endif
+
 namespace fdk {
 
 // Everything one split launch needs.  Passed by value as the kernel argument.
@@ -27,6 +36,9 @@ struct SplitArgs {
     int heads_per_block, head_blocks;
     int page_size, page_shift, max_pages, num_pages;
     float scale_log2;            // scale * log2(e): logits in base-2 units
+    int fused;                   // last workgroup of a group merges its splits
+    unsigned epoch;              // per-call tag of the arrival counters
+    unsigned long long *counters;  // [B, Hkv, head_blocks] arrival counters
 };
 
 struct CombineArgs {
@@ -51,7 +63,7 @@ struct ValuShape {
     static constexpr int EPC = 16 / EB;                     // elements per piece
     static constexpr int EPT = VEC * EPC;                   // elements per lane
     static constexpr int R = 64 / LPR;                      // rows per wave
-    static constexpr int U = GB >= 4 ? 2 : 4;               // tokens per row per step
+    static constexpr int U = GB >= 4 ? 2 : FD_VALU_U;       // tokens per row per step
     static constexpr int WAVES = 4;
     static constexpr int TW = R * U;                        // tokens per wave step
     static constexpr int TILE = WAVES * TW;                 // tokens per workgroup step
@@ -62,6 +74,12 @@ struct ValuShape {
 int valu_tile(int dtype, int D, int heads_per_block);
 // Launch the VALU split kernel.  Returns the HIP status of the launch.
 hipError_t launch_split_valu(const SplitArgs &a, int dtype, hipStream_t stream);
+
+// Matrix-core split kernel (f16 / bf16): up to 16 query heads of one kv head
+// per workgroup, 32 tokens per wave step, four waves.
+constexpr int kMfmaHeads = 16;
+constexpr int kMfmaTile = 128;
+hipError_t launch_split_mfma(const SplitArgs &a, int dtype, hipStream_t stream);
 // Launch the combine kernel.
 hipError_t launch_combine(const CombineArgs &a, hipStream_t stream);
 

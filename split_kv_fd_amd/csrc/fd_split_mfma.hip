@@ -1,0 +1,278 @@
+// Split pass of flash decoding on the gfx950 matrix cores, for GQA groups.
+//
+// Same contract as the VALU split kernel (tinyvolt "Kernel visualization:
+// Flash Decoding", single-block walkthrough): one workgroup per (batch, kv
+// head, head block, split) streams its chunk of K and V once and leaves an
+// unnormalised partial with its running max and sum.  With a GQA group of G
+// query heads per kv head, the logits of a 16-token tile are a real
+// (16 tokens x D) . (D x G) contraction and the value update a (D x tokens)
+// . (tokens x G) one, so both run on MFMA; G is padded to 16.
+//
+// Per 64-lane wave and 32-token step (two 16-token tiles):
+//  * logits: v_mfma_f32_16x16x32_{bf16,f16} with the tile's tokens as the M
+//    rows (lane i16 = lane % 16 loads token i16's 16-byte pieces) and the
+//    query heads as the N columns (the B operand is the q pieces, loaded
+//    once).  Products of two 16-bit values are exact in fp32.  The output
+//    leaves lane (i16, kb = lane / 16) holding head i16's logits of tokens
+//    4*kb .. 4*kb+3 of the tile, so each lane owns one head;
+//  * online softmax: per-lane max over its 8 logits, then across the four
+//    lanes of the head (xor 16, xor 32); every lane keeps its own partial
+//    sum (all four share the max), summed once at the end;
+//  * values: v_mfma_f32_16x16x4f32 in fp32 with P straight from the logit
+//    registers as the B operand (no rounding of P, no data movement): for
+//    the token group of row r, lane (i16, kb) supplies p of its head and
+//    token 4*kb+r, and V of that token as the A operand -- 8 (D=128) or 4
+//    (D=64) consecutive elements of the row, one per MFMA, so element i of
+//    lane i16 is dimension (D/16)*i16 + i.  Each V load instruction reads
+//    four whole rows.
+// The next step's K/V pieces are prefetched into registers while the current
+// step is consumed (two buffers used in turn).
+#include <type_traits>
+
+#include "fd_epilogue.h"
+
+namespace fdk {
+namespace {
+
+typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_v __attribute__((ext_vector_type(8)));
+typedef float f32x4_v __attribute__((ext_vector_type(4)));
+
+constexpr float kNegInf = -__builtin_inff();
+
+template <int DT>
+__device__ __forceinline__ f32x4_v mfma_logits(const uint4 &k, const uint4 &q, f32x4_v c) {
+    if constexpr (DT == FD_BF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, k),
+                                                       __builtin_bit_cast(bf16x8_v, q), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_v, k),
+                                                      __builtin_bit_cast(f16x8_v, q), c, 0, 0, 0);
+}
+
+template <int DT>
+__device__ __forceinline__ float widen1(uint32_t w, int hi) {
+    if constexpr (DT == FD_BF16) {
+        return __uint_as_float(hi ? (w & 0xffff0000u) : (w << 16));
+    } else {
+        return (float)__builtin_bit_cast(_Float16, (unsigned short)(hi ? (w >> 16) : (w & 0xffffu)));
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ void widen(const uint4 &p, float *f) {
+    const uint32_t w[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { f[2 * i] = widen1<DT>(w[i], 0); f[2 * i + 1] = widen1<DT>(w[i], 1); }
+}
+
+template <int DT>
+__device__ __forceinline__ void widen(const uint2 &p, float *f) {
+    const uint32_t w[2] = {p.x, p.y};
+#pragma unroll
+    for (int i = 0; i < 2; ++i) { f[2 * i] = widen1<DT>(w[i], 0); f[2 * i + 1] = widen1<DT>(w[i], 1); }
+}
+
+template <typename V>
+__device__ __forceinline__ V load_piece(const char *p) {
+#if FD_NT_LOADS
+    return __builtin_nontemporal_load(reinterpret_cast<const V *>(p));
+#else
+    return *reinterpret_cast<const V *>(p);
+#endif
+}
+
+template <int DT, int D, bool PAGED>
+__global__ __launch_bounds__(256) void split_mfma(SplitArgs a) {
+    constexpr int EB = 2;
+    constexpr int ROWB = D * EB;
+    constexpr int KS = D / 32;          // 16-byte q/k pieces per lane per tile
+    constexpr int PVE = D / 16;         // V elements per lane per token
+    constexpr int VB = PVE * EB;        // V bytes per lane per token
+    constexpr int WAVES = 4;
+    constexpr int TOK = 32;             // tokens per wave step
+    constexpr int TILE = WAVES * TOK;
+    constexpr int GB = kMfmaHeads;
+    static_assert(TILE == kMfmaTile, "host and kernel disagree on the tile");
+    using VP = typename std::conditional<VB == 16, uint4, uint2>::type;
+    using Off = typename std::conditional<PAGED, size_t, uint32_t>::type;
+
+    const int split = blockIdx.x;
+    const int kvh = blockIdx.y / a.head_blocks;
+    const int hb = blockIdx.y - kvh * a.head_blocks;
+    const int b = blockIdx.z;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int i16 = lane & 15;
+    const int kb = lane >> 4;
+
+    int Tb = a.T;
+    if (a.seq_lens) {
+        Tb = a.seq_lens[b];
+        Tb = Tb < 0 ? 0 : (Tb > a.T ? a.T : Tb);
+    }
+    const int c0 = split * a.chunk;
+    const int c1 = min(c0 + a.chunk, Tb);
+    if (a.n_splits > 1 && c0 >= Tb) return;   // empty split: never counted or read
+
+    const int g0 = hb * GB;
+    const int ng = min(GB, a.G - g0);
+    const int h0 = kvh * a.G + g0;
+
+    // B operand of the logit MFMAs: q pieces 4*ks + kb of head i16.
+    uint4 qb[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        qb[ks] = make_uint4(0, 0, 0, 0);
+        if (i16 < ng)
+            qb[ks] = *reinterpret_cast<const uint4 *>(static_cast<const char *>(a.q) +
+                                                       (size_t)(b * a.Hq + h0 + i16) * ROWB + (4 * ks + kb) * 16);
+    }
+
+    f32x4_v acc[PVE];
+#pragma unroll
+    for (int i = 0; i < PVE; ++i) acc[i] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+    float m = kNegInf, l = 0.f;
+
+    const char *kbase = static_cast<const char *>(a.k);
+    const char *vbase = static_cast<const char *>(a.v);
+    if constexpr (!PAGED) {
+        const size_t seq = (size_t)(b * a.Hkv + kvh) * (size_t)a.T * ROWB;
+        kbase += seq;
+        vbase += seq;
+    }
+    auto row_offset = [&](int t, bool &ok) -> Off {
+        ok = t < c1;
+        const int tc = ok ? t : c1 - 1;        // clamped: always a valid token
+        if constexpr (PAGED) {
+            int page = a.page_table[(size_t)b * a.max_pages + (tc >> a.page_shift)];
+            if ((unsigned)page >= (unsigned)a.num_pages) { ok = false; page = 0; }
+            return (((size_t)page * a.Hkv + kvh) * a.page_size + (tc & (a.page_size - 1))) * ROWB;
+        } else {
+            return (uint32_t)tc * (uint32_t)ROWB;
+        }
+    };
+
+    struct Buf {
+        uint4 k[2][KS];
+        VP v[2][4];
+        bool ok[2][4];
+    };
+
+    auto load_step = [&](int base, Buf &f) {
+        const int tb = base + wave * TOK;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            bool okk;
+            const Off ko = row_offset(tb + 16 * h + i16, okk);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) f.k[h][ks] = load_piece<uint4>(kbase + (ko + (Off)((4 * ks + kb) * 16)));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const Off vo = row_offset(tb + 16 * h + 4 * kb + r, f.ok[h][r]);
+                f.v[h][r] = load_piece<VP>(vbase + (vo + (Off)(i16 * VB)));
+            }
+        }
+    };
+
+    auto consume_step = [&](const Buf &f) {
+        float s[2][4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            f32x4_v c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) c = mfma_logits<DT>(f.k[h][ks], qb[ks], c);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s[h][r] = f.ok[h][r] ? c[r] * a.scale_log2 : kNegInf;
+        }
+        float mt = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                         fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+        mt = fmaxf(mt, __shfl_xor(mt, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float mn = fmaxf(m, mt);
+        const float mu = mn == kNegInf ? 0.f : mn;
+        const float alpha = __builtin_amdgcn_exp2f(m - mu);
+        float p[2][4];
+        float ps = 0.f;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) { p[h][r] = __builtin_amdgcn_exp2f(s[h][r] - mu); ps += p[h][r]; }
+        l = l * alpha + ps;
+        m = mn;
+#pragma unroll
+        for (int i = 0; i < PVE; ++i) acc[i] *= alpha;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float vf[PVE];
+                widen<DT>(f.v[h][r], vf);
+#pragma unroll
+                for (int i = 0; i < PVE; ++i)
+                    acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[i], p[h][r], acc[i], 0, 0, 0);
+            }
+    };
+
+    if (c0 < c1) {
+        Buf fa, fb;
+        load_step(c0, fa);
+        for (int base = c0;; base += 2 * TILE) {
+            load_step(base + TILE, fb);            // clamped past the end
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            consume_step(fa);
+            if (base + TILE >= c1) break;
+            load_step(base + 2 * TILE, fa);
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            consume_step(fb);
+            if (base + 2 * TILE >= c1) break;
+        }
+    }
+
+    // The four lanes of a head share m; their sums cover different tokens.
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+
+    __shared__ EpilogueLds<WAVES, GB, D> sm;
+#pragma unroll
+    for (int i = 0; i < PVE; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sm.o[wave][i16][PVE * (4 * kb + r) + i] = acc[i][r];
+    if (kb == 0) { sm.m[wave][i16] = m; sm.l[wave][i16] = l; }
+    __syncthreads();
+    finish_split<WAVES, GB, D>(a, sm, b, kvh, hb, split, h0, ng, Tb);
+}
+
+template <int DT, int D>
+hipError_t launch_dim(const SplitArgs &a, hipStream_t stream) {
+    const dim3 grid(a.n_splits, a.Hkv * a.head_blocks, a.B);
+    if (a.page_table)
+        hipLaunchKernelGGL((split_mfma<DT, D, true>), grid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((split_mfma<DT, D, false>), grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_dtype(const SplitArgs &a, hipStream_t stream) {
+    switch (a.D) {
+    case 64: return launch_dim<DT, 64>(a, stream);
+    case 128: return launch_dim<DT, 128>(a, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_split_mfma(const SplitArgs &a, int dtype, hipStream_t stream) {
+    if (a.heads_per_block != kMfmaHeads) return hipErrorInvalidValue;
+    switch (dtype) {
+    case FD_F16: return launch_dtype<FD_F16>(a, stream);
+    case FD_BF16: return launch_dtype<FD_BF16>(a, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace fdk

@@ -24,7 +24,7 @@
 // a -inf logit, which keeps every load unconditional.
 #include <type_traits>
 
-#include "fd_kernels.h"
+#include "fd_epilogue.h"
 
 namespace fdk {
 namespace {
@@ -33,7 +33,6 @@ typedef _Float16 half2_v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf162_v __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInf = -__builtin_inff();
-constexpr float kLn2 = 0.693147180559945309417f;
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
@@ -104,7 +103,11 @@ __device__ __forceinline__ void widen(const uint4 &p, float *f) {
 }
 
 __device__ __forceinline__ uint4 load16(const char *p) {
+#if FD_NT_LOADS
+    return __builtin_nontemporal_load(reinterpret_cast<const uint4 *>(p));
+#else
     return *reinterpret_cast<const uint4 *>(p);
+#endif
 }
 
 template <int DT, int D, int GB, bool PAGED>
@@ -280,10 +283,8 @@ __global__ __launch_bounds__(256) void split_valu(SplitArgs a) {
         }
     }
 
-    // Merge the waves through LDS and write the split's result.
-    __shared__ float sm_o[WAVES][GB][D];
-    __shared__ float sm_m[WAVES][GB];
-    __shared__ float sm_l[WAVES][GB];
+    // Merge the waves through LDS and finish the split.
+    __shared__ EpilogueLds<WAVES, GB, D> sm;
     if (row == 0) {
 #pragma unroll
         for (int g = 0; g < GB; ++g) {
@@ -291,35 +292,12 @@ __global__ __launch_bounds__(256) void split_valu(SplitArgs a) {
             for (int v = 0; v < VEC; ++v)
 #pragma unroll
                 for (int j = 0; j < EPC; ++j)
-                    sm_o[wave][g][(v * LPR + sub) * EPC + j] = o[g][v * EPC + j];
-            if (sub == 0) { sm_m[wave][g] = m[g]; sm_l[wave][g] = l[g]; }
+                    sm.o[wave][g][(v * LPR + sub) * EPC + j] = o[g][v * EPC + j];
+            if (sub == 0) { sm.m[wave][g] = m[g]; sm.l[wave][g] = l[g]; }
         }
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < GB * D; idx += 64 * WAVES) {
-        const int g = idx / D, d = idx - (idx / D) * D;
-        if (g >= ng) continue;
-        float M = sm_m[0][g];
-#pragma unroll
-        for (int w = 1; w < WAVES; ++w) M = fmaxf(M, sm_m[w][g]);
-        const float mu = M == kNegInf ? 0.f : M;
-        float acc = 0.f, L = 0.f;
-#pragma unroll
-        for (int w = 0; w < WAVES; ++w) {
-            const float c = exp2_fast(sm_m[w][g] - mu);
-            acc += c * sm_o[w][g][d];
-            L += c * sm_l[w][g];
-        }
-        const int bh = b * a.Hq + h0 + g;
-        if (a.n_splits == 1) {
-            a.out[(size_t)bh * D + d] = L > 0.f ? acc / L : 0.f;
-            if (d == 0 && a.lse) a.lse[bh] = L > 0.f ? (M + log2f(L)) * kLn2 : kNegInf;
-        } else {
-            const size_t pi = (size_t)bh * a.n_splits + split;
-            a.part_o[pi * D + d] = acc;
-            if (d == 0) { a.part_m[pi] = M; a.part_l[pi] = L; }
-        }
-    }
+    finish_split<WAVES, GB, D>(a, sm, b, kvh, hb, split, h0, ng, Tb);
 }
 
 template <int DT, int D, int GB, bool PAGED>

@@ -83,6 +83,8 @@ def compare(case, out, lse, ref_out, ref_lse, vmax, what=""):
 
 def check_full(case, n_splits=0, path=None, what=""):
     out, lse, plan = run_gpu(case, n_splits, path)
+    if path in ("valu", "mfma"):
+        assert plan["path"] == path
     ref_out, ref_lse = oracle_full(case)
     return compare(case, out, lse, ref_out, ref_lse, max_abs_v(case), what or case.spec.name), plan
 

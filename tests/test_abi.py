@@ -77,11 +77,16 @@ def test_plan_covers_sequence_and_respects_tiles(lib):
                 assert p.grid[1] == Hkv * p.head_blocks
                 assert p.heads_per_block * p.head_blocks >= Hq // Hkv
                 assert bool(p.combine) == (p.n_splits > 1)
+                assert not p.fused or (p.combine and p.n_splits <= 4 * D)
                 parts = B * Hq * p.n_splits
                 if p.n_splits > 1:
-                    assert p.workspace_bytes >= parts * (D + 2) * 4
+                    assert p.workspace_bytes >= parts * (D + 2) * 4 + B * Hkv * p.head_blocks * 8
                 else:
                     assert p.workspace_bytes == 0
+                G = Hq // Hkv
+                want_mfma = dt != fd.FD_F32 and G >= 4
+                assert p.path == (fd.FD_PATH_MFMA if want_mfma else fd.FD_PATH_VALU)
+                assert p.heads_per_block == (16 if want_mfma else min(8, 1 << (G - 1).bit_length()))
 
 
 def test_plan_of_the_five_workloads(lib):
@@ -104,6 +109,19 @@ def test_plan_of_the_five_workloads(lib):
 def test_plan_paged_chunks_align_to_pages(lib):
     st, p = plan(16, 32, 8, 65536, 128, 0, page_size=256, max_pages_per_seq=256, num_pages=10)
     assert st == fd.FD_OK and p.chunk % 256 == 0
+    # ragged (paged) batches are cut into short chunks for balance
+    st, p = plan(16, 32, 8, 65536, 128, 0, page_size=16, max_pages_per_seq=4096, num_pages=10)
+    assert st == fd.FD_OK and p.chunk <= 2048 and p.fused
+
+
+def test_plan_paths(lib):
+    assert plan(1, 32, 8, 4096, 128, 0, path=fd.FD_PATH_MFMA, dtype=fd.FD_F32)[0] == fd.FD_ERR_UNSUPPORTED
+    st, p = plan(1, 8, 8, 4096, 128, 0, path=fd.FD_PATH_MFMA, dtype=fd.FD_F16)
+    assert st == fd.FD_OK and p.path == fd.FD_PATH_MFMA and p.heads_per_block == 16
+    st, p = plan(1, 64, 2, 4096, 128, 0, path=fd.FD_PATH_MFMA)   # G = 32: two head blocks
+    assert st == fd.FD_OK and p.head_blocks == 2 and p.grid[1] == 4
+    st, p = plan(1, 64, 8, 4096, 64, 0, path=fd.FD_PATH_VALU)     # G = 8 on the VALU path
+    assert st == fd.FD_OK and p.path == fd.FD_PATH_VALU and p.heads_per_block == 8
 
 
 def test_workspace_bytes_matches_plan(lib):

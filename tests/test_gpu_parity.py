@@ -55,18 +55,22 @@ def test_high_batch_gqa_hot_head():
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 8, 16])
-def test_group_sizes(dtype, D, G):
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 8, 16, 32])
+@pytest.mark.parametrize("path", ["valu", "mfma"])
+def test_group_sizes(dtype, D, G, path):
+    if path == "mfma" and dtype == "f32":
+        pytest.skip("the matrix-core path takes f16 / bf16 inputs")
     Hkv = 2
     case = small_case("mha32k_f16", B=2, Hq=Hkv * G, Hkv=Hkv, D=D, T=700, dtype=dtype)
-    parity.check_full(case, what=f"G={G} D={D} {dtype}")
+    parity.check_full(case, path=path, what=f"G={G} D={D} {dtype} {path}")
 
 
-@pytest.mark.parametrize("T", [1, 2, 15, 16, 17, 63, 64, 65, 257])
-def test_short_sequences(T):
+@pytest.mark.parametrize("T", [1, 2, 15, 16, 17, 63, 64, 65, 127, 128, 129, 257])
+@pytest.mark.parametrize("path", ["valu", "mfma"])
+def test_short_sequences(T, path):
     case = small_case("gqa128k_bf16", B=1, Hq=8, Hkv=2, T=T)
     for n in (0, 1, 3):
-        parity.check_full(case, n_splits=n, what=f"T={T} n={n}")
+        parity.check_full(case, n_splits=n, path=path, what=f"T={T} n={n} {path}")
 
 
 def test_ragged_lengths_with_empty_sequences():
@@ -80,11 +84,27 @@ def test_ragged_lengths_with_empty_sequences():
         assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
 
 
-def test_paged_page_sizes():
+@pytest.mark.parametrize("path", ["valu", "mfma"])
+def test_paged_page_sizes(path):
     for P in (1, 4, 16, 64, 256):
         case = small_case("paged_ragged_bf16", B=3, Hq=8, Hkv=4, T=1000, page_size=P,
                           len_lo=1, len_hi=1000)
-        parity.check_full(case, what=f"page_size={P}")
+        parity.check_full(case, path=path, what=f"page_size={P} {path}")
+
+
+def test_paged_invalid_page_ids_read_as_empty():
+    # Page ids outside [0, num_pages) are skipped instead of read; a table
+    # whose second page is invalid equals the sequence cut after page one.
+    s = inputs.spec("paged_ragged_bf16", B=1, Hq=8, Hkv=2, T=64, len_lo=64, len_hi=64)
+    case = inputs.make_case(s).to(DEV)
+    bad = case.page_table.clone()
+    bad[0, 1:] = case.k.shape[0] + 5
+    cut = inputs.Case(s, case.q, case.k, case.v, case.page_table,
+                      torch.tensor([16], dtype=torch.int32, device=DEV))
+    for path in ("valu", "mfma"):
+        a = parity.run_gpu(inputs.Case(s, case.q, case.k, case.v, bad, case.seq_lens), 1, path)
+        b = parity.run_gpu(cut, 1, path)
+        assert np.max(np.abs(a[0] - b[0])) <= 1e-6 and np.max(np.abs(a[1] - b[1])) <= 1e-6
 
 
 def test_paged_equals_contiguous_gather():
@@ -124,25 +144,52 @@ def test_special_values_on_gpu():
     assert np.max(np.abs(lse - math.log(1000))) <= 1e-5
 
 
-def test_deterministic_runs():
+@pytest.mark.parametrize("path", ["valu", "mfma"])
+def test_deterministic_runs(path):
     case = small_case("gqa128k_bf16", B=2, T=5000)
-    a = parity.run_gpu(case, 0)
-    b = parity.run_gpu(case, 0)
+    a = parity.run_gpu(case, 0, path)
+    b = parity.run_gpu(case, 0, path)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
-def test_split_and_combine_entry_points():
-    case = small_case("mha32k_f16", B=1, Hq=4, Hkv=4, T=3000)
-    dec = Decoder(case.q, case.k, case.v, scale=case.spec.scale, n_splits=6)
-    assert dec.plan["n_splits"] > 1
-    parity.announce("fd_split + fd_combine separately")
-    dec.split()
-    dec.combine()
-    torch.cuda.synchronize()
-    out1, lse1 = dec.out.clone(), dec.lse.clone()
-    dec()
-    torch.cuda.synchronize()
-    assert torch.equal(out1, dec.out) and torch.equal(lse1, dec.lse)
+@pytest.mark.parametrize("path", ["valu", "mfma"])
+def test_fused_merge_with_stale_workspace(path):
+    # The arrival counters carry a per-call tag: a workspace full of garbage,
+    # or left by a call with another split count, must not change results.
+    case = small_case("gqa128k_bf16", B=3, T=6000)
+    ref_out, ref_lse = parity.oracle_full(case)
+    vmax = parity.max_abs_v(case)
+    for n in (7, 20, 7):
+        dec = Decoder(case.q, case.k, case.v, scale=case.spec.scale, n_splits=n, path=path)
+        assert dec.plan["fused"]
+        dec.workspace.fill_(0xFF)
+        for rep in range(3):
+            parity.announce(f"fused merge n={n} rep={rep} {path}")
+            out, lse = dec()
+            torch.cuda.synchronize()
+            parity.compare(case, out.cpu().double().numpy(), lse.cpu().double().numpy(),
+                           ref_out, ref_lse, vmax, f"stale workspace n={n} rep={rep}")
+
+
+@pytest.mark.parametrize("path", ["valu", "mfma"])
+def test_split_and_combine_entry_points(path):
+    case = small_case("gqa128k_bf16", B=2, Hq=8, Hkv=2, T=3000)
+    ref_out, ref_lse = parity.oracle_full(case)
+    vmax = parity.max_abs_v(case)
+    for n in (6, 100):
+        dec = Decoder(case.q, case.k, case.v, scale=case.spec.scale, n_splits=n, path=path)
+        assert dec.plan["n_splits"] > 1
+        parity.announce(f"fd_split + fd_combine separately n={n} {path}")
+        dec.split()
+        dec.combine()
+        torch.cuda.synchronize()
+        out1, lse1 = dec.out.cpu().double().numpy(), dec.lse.cpu().double().numpy()
+        parity.compare(case, out1, lse1, ref_out, ref_lse, vmax, f"separate passes n={n}")
+        dec()
+        torch.cuda.synchronize()
+        out2, lse2 = dec.out.cpu().double().numpy(), dec.lse.cpu().double().numpy()
+        parity.compare(case, out2, lse2, ref_out, ref_lse, vmax, f"fd_decode n={n}")
+        assert np.max(np.abs(out1 - out2)) <= 1e-6 and np.max(np.abs(lse1 - lse2)) <= 1e-6
 
 
 # ------------------------------------------------------------------ full-size workloads, sampled rows
