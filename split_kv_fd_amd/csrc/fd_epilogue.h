@@ -50,6 +50,19 @@ struct EpilogueLds {
     int last;
 };
 
+// A sequence with no tokens: out = 0 and lse = -inf for the block's heads.
+// In fused mode no split of such a sequence reaches the merge, so split 0
+// writes this instead.
+template <int D>
+__device__ void write_empty_group(const SplitArgs &a, int b, int h0, int ng) {
+    for (int idx = threadIdx.x; idx < ng * D; idx += blockDim.x) {
+        const int g = idx / D, d = idx - (idx / D) * D;
+        const int bh = b * a.Hq + h0 + g;
+        a.out[(size_t)bh * D + d] = 0.f;
+        if (d == 0 && a.lse) a.lse[bh] = kEpNegInf;
+    }
+}
+
 // Splits that hold tokens of a sequence of length Tb.
 __device__ __forceinline__ int active_splits(const SplitArgs &a, int Tb) {
     const int n = (Tb + a.chunk - 1) / a.chunk;

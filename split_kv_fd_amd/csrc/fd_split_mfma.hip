@@ -113,11 +113,13 @@ __global__ __launch_bounds__(256) void split_mfma(SplitArgs a) {
     }
     const int c0 = split * a.chunk;
     const int c1 = min(c0 + a.chunk, Tb);
-    if (a.n_splits > 1 && c0 >= Tb) return;   // empty split: never counted or read
-
     const int g0 = hb * GB;
     const int ng = min(GB, a.G - g0);
     const int h0 = kvh * a.G + g0;
+    if (a.n_splits > 1 && c0 >= Tb) {          // empty split: never counted or read
+        if (a.fused && split == 0) write_empty_group<D>(a, b, h0, ng);
+        return;
+    }
 
     // B operand of the logit MFMAs: q pieces 4*ks + kb of head i16.
     uint4 qb[KS];
