@@ -131,6 +131,8 @@ def main() -> int:
     ap.add_argument("--config", default=DEFAULT_WORKLOAD)
     ap.add_argument("--n-splits", type=int, default=0, help="0 = the planner's choice")
     ap.add_argument("--path", default=None, choices=[None, "auto", "valu", "mfma"])
+    ap.add_argument("--fused-merge", action="store_true",
+                    help="merge the splits inside the split launch (FD_FLAG_FUSED_MERGE)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -167,7 +169,8 @@ def main() -> int:
         v = case.v if c == 0 else case.v.clone()
         decs.append(Decoder(case.q, k, v, scale=spec.scale, page_table=case.page_table,
                             seq_lens=case.seq_lens, T=spec.T if case.page_table is not None else None,
-                            n_splits=args.n_splits or spec.n_splits, path=args.path))
+                            n_splits=args.n_splits or spec.n_splits, path=args.path,
+                            fused_merge=args.fused_merge))
     plan = decs[0].plan
     print(f"[bench] plan {plan}; {copies} KV copies", file=sys.stderr, flush=True)
 

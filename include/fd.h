@@ -25,8 +25,8 @@
  *     [num_pages, Hkv, page_size, D] with page_table [B, max_pages_per_seq]
  *     int32 (token t of sequence b is row t % page_size of page
  *     page_table[b][t / page_size]); seq_lens [B] int32 with 0 <= T_b <= T.
- *     q, K and V share one storage dtype (fd_options_t.dtype) and must be
- *     16-byte aligned.  out is [B, Hq, D] fp32, lse [B, Hq] fp32 (natural
+ *     q, K and V share one storage dtype (fd_options_t.dtype); q, K, V and
+ *     out must be 16-byte aligned.  out is [B, Hq, D] fp32, lse [B, Hq] fp32 (natural
  *     log; may be NULL).  A sequence with T_b = 0 yields out = 0 and
  *     lse = -inf.
  *   - Calls are stream-ordered on fd_options_t.stream and never synchronise;
@@ -68,6 +68,12 @@ typedef enum {
     FD_PATH_MFMA = 1          /* matrix-core path (f16/bf16 only)             */
 } fd_path_t;
 
+/* fd_options_t.flags: merge the splits inside the split launch (the last
+ * workgroup of each kv head combines its group) instead of launching the
+ * combine kernel.  Saves one launch; the partials then travel through
+ * device-coherent stores and loads. */
+#define FD_FLAG_FUSED_MERGE 0x1
+
 /* Options of a call.  Initialise with fd_options_init() and then set the
  * fields you need; struct_size versions the layout. */
 typedef struct fd_options {
@@ -80,7 +86,7 @@ typedef struct fd_options {
                                 /* [0, num_pages) read as empty tokens        */
     int32_t num_cus;            /* compute units to plan for; 0 = ask device  */
     int32_t path;               /* fd_path_t; FD_PATH_AUTO by default          */
-    int32_t reserved;
+    int32_t flags;              /* FD_FLAG_* bits; 0 by default               */
     void *workspace;            /* device buffer for the split partials        */
     size_t workspace_bytes;     /* its size in bytes                          */
     void *stream;               /* hipStream_t to launch on; NULL = null stream */
@@ -113,7 +119,8 @@ void fd_options_init(fd_options_t *opt);
 /*
  * Choose the split count and kernel for a call (host only; no GPU work).
  * n_splits > 0 asks for that many splits (capped so no split is empty when
- * every sequence has length T); n_splits = 0 lets the planner size the grid
+ * every sequence has length T, and raised for paged layouts so one split
+ * covers at most 2048 pages); n_splits = 0 lets the planner size the grid
  * to the device: enough (batch, kv head, split) workgroups to cover every
  * compute unit, with each split long enough to amortise its partial write
  * (the occupancy argument of the zenaique explainer, "Why decode breaks

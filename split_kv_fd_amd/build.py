@@ -27,22 +27,25 @@ CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
           f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}"]
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, out: str = LIB, defines=(), build_dir: str = BUILD) -> str:
+    """Compile every source and link `out`.  `defines` are extra -D flags
+    (compile-time variants); objects go to `build_dir`."""
+    os.makedirs(build_dir, exist_ok=True)
     procs = []
     objs = []
     for src in SOURCES:
-        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+        obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [HIPCC, *CFLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *CFLAGS, *[f"-D{d}" for d in defines], *lang, "-c",
+               os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
     failed = []
     for src, p in procs:
-        out, _ = p.communicate()
-        text = out.decode(errors="replace")
+        log, _ = p.communicate()
+        text = log.decode(errors="replace")
         # The host pass does not know the device-only feature flag; that note is noise.
         lines = [ln for ln in text.splitlines() if "packed-fp32-ops" not in ln]
         if lines and (verbose or p.returncode):
@@ -51,13 +54,13 @@ def build(verbose: bool = False) -> str:
             failed.append(src)
     if failed:
         raise RuntimeError(f"hipcc failed for {failed}")
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

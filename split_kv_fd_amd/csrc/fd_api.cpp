@@ -6,6 +6,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 
@@ -32,12 +33,14 @@ inline long ceil_div(long a, long b) { return (a + b - 1) / b; }
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 inline int ilog2(int x) { int r = 0; while ((1 << r) < x) ++r; return r; }
 
+// Integer environment override (experiments only); malformed values and
+// negatives fall back to the default.
 long env_long(const char *name, long dflt) {
     const char *s = std::getenv(name);
     if (!s || !*s) return dflt;
     char *end = nullptr;
     const long v = std::strtol(s, &end, 10);
-    return (end && *end == '\0' && v > 0) ? v : dflt;
+    return (end && *end == '\0' && v >= 0) ? v : dflt;
 }
 
 constexpr uint32_t kOptionsV1 = sizeof(fd_options_t);
@@ -75,6 +78,7 @@ fd_status_t read_options(const fd_options_t *opt, fd_options_t *o) {
     if (o->path != FD_PATH_AUTO && o->path != FD_PATH_VALU && o->path != FD_PATH_MFMA)
         return fail(FD_ERR_INVALID_ARG, "unknown path %d", (int)o->path);
     if (o->num_cus < 0) return fail(FD_ERR_INVALID_ARG, "num_cus %d < 0", (int)o->num_cus);
+    if (o->flags & ~FD_FLAG_FUSED_MERGE) return fail(FD_ERR_INVALID_ARG, "unknown flags 0x%x", (unsigned)o->flags);
     return FD_OK;
 }
 
@@ -135,25 +139,34 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
     if (n_req > 0) {
         n = n_req < max_n ? n_req : max_n;
     } else {
-        // Enough workgroups to cover every compute unit several times over,
-        // but no split shorter than min_chunk tokens (its partial write and
+        // About one workgroup per compute unit (measured best for streaming;
+        // more, shorter splits only add partial traffic), but no split
+        // shorter than min_chunk tokens (its partial write and
         // the merge must stay small against the chunk's KV bytes).  Paged
         // (ragged) batches get shorter chunks so the hardware scheduler can
         // balance sequences of very different lengths.
         const long units = (long)B * Hkv * head_blocks;
-        const long target = env_long("FD_TARGET_WGS", 2L * cus);
-        const long min_chunk = env_long("FD_CHUNK_MIN", 512);
+        const long target = std::max(1L, env_long("FD_TARGET_WGS", (long)cus));
+        const long min_chunk = std::max(1L, env_long("FD_CHUNK_MIN", 512));
         n = ceil_div(target, units);
         const long cap = T / min_chunk > 1 ? T / min_chunk : 1;
         if (n > cap) n = cap;
         if (paged) {
-            const long ragged_chunk = env_long("FD_RAGGED_CHUNK", 2048);
+            const long ragged_chunk = std::max(1L, env_long("FD_RAGGED_CHUNK", 1024));
             const long nr = ceil_div(T, ragged_chunk);
             if (n < nr) n = nr;
         }
     }
+    if (paged) {
+        // a split stages its page ids on chip: at most kMaxSplitPages pages
+        const long max_chunk = (long)fdk::kMaxSplitPages * o.page_size;
+        const long n_min = ceil_div(T, max_chunk);
+        if (n < n_min) n = n_min;
+    }
     if (n < 1) n = 1;
     long chunk = ceil_div(ceil_div(T, n), gran) * gran;
+    if (paged && chunk > (long)fdk::kMaxSplitPages * o.page_size)
+        chunk = (long)fdk::kMaxSplitPages * o.page_size;
     n = ceil_div(T, chunk);
 
     std::memset(p, 0, sizeof *p);
@@ -168,9 +181,10 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
     p->grid[2] = B;
     p->block = 256;
     p->combine = n > 1;
-    // The last workgroup of a group merges the splits itself when their
-    // weights fit its LDS (n * heads <= 4 * D * heads_per_block).
-    p->fused = n > 1 && n <= 4L * D && env_long("FD_FUSED", 1) == 1;
+    // On request, the last workgroup of a group merges the splits itself
+    // when their weights fit its LDS (n * heads <= 4 * D * heads_per_block).
+    const bool want_fused = (o.flags & FD_FLAG_FUSED_MERGE) != 0 || env_long("FD_FUSED", 0) == 1;
+    p->fused = n > 1 && n <= 4L * D && want_fused;
     if (n > 1) {
         const size_t parts = (size_t)B * Hq * (size_t)n;
         const size_t counters = (size_t)B * Hkv * head_blocks * sizeof(unsigned long long);
@@ -203,8 +217,8 @@ fd_status_t prepare(const void *q, const void *k, const void *v, const int32_t *
         if (!std::isfinite(scale)) return fail(FD_ERR_INVALID_ARG, "scale is not finite");
     }
     if (!out) return fail(FD_ERR_INVALID_ARG, "out must be non-NULL");
-    if (!aligned(out, 4) || (lse && !aligned(lse, 4)))
-        return fail(FD_ERR_INVALID_ARG, "out / lse must be 4-byte aligned");
+    if (!aligned(out, 16) || (lse && !aligned(lse, 4)))
+        return fail(FD_ERR_INVALID_ARG, "out must be 16-byte and lse 4-byte aligned");
     if (seq_lens && !aligned(seq_lens, 4)) return fail(FD_ERR_INVALID_ARG, "seq_lens must be 4-byte aligned");
     // The page geometry in the options decides the plan; the split pass also
     // needs the table itself.

@@ -4,14 +4,15 @@
 // normaliser.  Shift invariance of softmax makes this exact (zenaique
 // explainer, interview answer on exactness).
 //
-// One 64-lane wavefront per (batch, query head), four per workgroup.  The
-// global max and normaliser are wave reductions over the splits (lanes
-// stride over splits); the weighted sum over splits runs with each lane
-// owning D/64 output elements, reading eight partial rows at a time so the
-// loop is not bound by one memory round trip per split.  Split
-// maxima are in base-2 units (the split kernel folds log2(e) into the
-// scale).  Splits that start past a sequence's length were never written
-// and are not read.
+// One 256-thread workgroup per (batch, query head).  Thread t owns four
+// output elements (quad t % (D/4)) for the splits s = t / (D/4) (mod SG),
+// SG = 256 / (D/4).  The partial rows of its first PRE splits are loaded
+// together with the split maxima and sums, so a merge of up to PRE*SG
+// splits costs one memory round trip; the global max and normaliser are
+// workgroup reductions, and the SG partial sums of each quad are added in
+// split-group order (deterministic).  Split maxima are in base-2 units (the
+// split kernel folds log2(e) into the scale).  Splits that start past a
+// sequence's length were never written and are not read.
 #include "fd_kernels.h"
 
 namespace fdk {
@@ -34,11 +35,14 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 template <int D>
 __global__ __launch_bounds__(256) void combine(CombineArgs a) {
-    constexpr int DPL = D / 64;   // output elements per lane
-    constexpr int UNR = 8;        // partial rows in flight per lane
-    const int lane = threadIdx.x & 63;
-    const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (bh >= a.B * a.Hq) return;   // whole wave exits together
+    constexpr int NT = 256;
+    constexpr int Q = D / 4;          // float4 quads per row
+    constexpr int SG = NT / Q;        // split groups
+    constexpr int PRE = 4;            // partial rows preloaded per thread
+    constexpr int WCH = 2048;         // split weights staged per pass
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int q = t % Q, sg = t / Q;
+    const int bh = blockIdx.x;
     const int b = bh / a.Hq;
 
     int Tb = a.T;
@@ -51,53 +55,77 @@ __global__ __launch_bounds__(256) void combine(CombineArgs a) {
 
     const float *pm = a.part_m + (size_t)bh * a.n_splits;
     const float *pl = a.part_l + (size_t)bh * a.n_splits;
-    const float *po = a.part_o + (size_t)bh * a.n_splits * D;
+    const float4 *po = reinterpret_cast<const float4 *>(a.part_o + (size_t)bh * a.n_splits * D);
 
+    // Issue the first partial rows together with the maxima.
+    float4 pre[PRE];
+#pragma unroll
+    for (int j = 0; j < PRE; ++j) {
+        const int s = sg + j * SG;
+        pre[j] = s < n ? po[(size_t)s * Q + q] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
     float M = kNegInf;
-    for (int s = lane; s < n; s += 64) M = fmaxf(M, pm[s]);
+    for (int s = t; s < n; s += NT) M = fmaxf(M, pm[s]);
+
+    __shared__ float s_red[2][4];
+    __shared__ float s_w[WCH];
+    __shared__ float4 s_acc[SG][Q];
     M = wave_max(M);
+    if (lane == 0) s_red[0][wave] = M;
+    __syncthreads();
+    M = fmaxf(fmaxf(s_red[0][0], s_red[0][1]), fmaxf(s_red[0][2], s_red[0][3]));
     const float mu = M == kNegInf ? 0.f : M;
 
     float L = 0.f;
-    float acc[DPL];
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s0 = 0; s0 < n; s0 += WCH) {
+        const int cnt = n - s0 < WCH ? n - s0 : WCH;
+        if (s0 > 0) __syncthreads();          // previous weights consumed
+        for (int i = t; i < cnt; i += NT) {
+            const float w = __builtin_amdgcn_exp2f(pm[s0 + i] - mu);
+            s_w[i] = w;
+            L += w * pl[s0 + i];
+        }
+        __syncthreads();
+        int s = sg;
+        if (s0 == 0) {
 #pragma unroll
-    for (int j = 0; j < DPL; ++j) acc[j] = 0.f;
-    // Lanes hold the weights of 64 splits at a time; each weight is
-    // broadcast while UNR partial rows are read at once.
-    for (int s0 = 0; s0 < n; s0 += 64) {
-        const int s = s0 + lane;
-        const float w = s < n ? __builtin_amdgcn_exp2f(pm[s] - mu) : 0.f;
-        if (s < n) L += w * pl[s];
-        const int cnt = n - s0 < 64 ? n - s0 : 64;
-        for (int j0 = 0; j0 < cnt; j0 += UNR) {
-            float v[UNR][DPL], wj[UNR];
-#pragma unroll
-            for (int u = 0; u < UNR; ++u) {
-                const bool in = j0 + u < cnt;
-                wj[u] = __shfl(w, j0 + u < 64 ? j0 + u : 63);
-                const float *row = po + (size_t)(s0 + (in ? j0 + u : 0)) * D + lane * DPL;
-#pragma unroll
-                for (int j = 0; j < DPL; ++j) v[u][j] = in ? row[j] : 0.f;
+            for (int j = 0; j < PRE; ++j, s += SG) {
+                if (s < cnt) {
+                    const float w = s_w[s];
+                    acc.x = fmaf(w, pre[j].x, acc.x); acc.y = fmaf(w, pre[j].y, acc.y);
+                    acc.z = fmaf(w, pre[j].z, acc.z); acc.w = fmaf(w, pre[j].w, acc.w);
+                }
             }
-#pragma unroll
-            for (int u = 0; u < UNR; ++u)
-#pragma unroll
-                for (int j = 0; j < DPL; ++j) acc[j] = fmaf(j0 + u < cnt ? wj[u] : 0.f, v[u][j], acc[j]);
+        }
+        for (; s < cnt; s += SG) {
+            const float4 v = po[(size_t)(s0 + s) * Q + q];
+            const float w = s_w[s];
+            acc.x = fmaf(w, v.x, acc.x); acc.y = fmaf(w, v.y, acc.y);
+            acc.z = fmaf(w, v.z, acc.z); acc.w = fmaf(w, v.w, acc.w);
         }
     }
+    s_acc[sg][q] = acc;
     L = wave_sum(L);
-
-    float *o = a.out + (size_t)bh * D + lane * DPL;
-#pragma unroll
-    for (int j = 0; j < DPL; ++j) o[j] = L > 0.f ? acc[j] / L : 0.f;
-    if (lane == 0 && a.lse) a.lse[bh] = L > 0.f ? (M + log2f(L)) * kLn2 : kNegInf;
+    if (lane == 0) s_red[1][wave] = L;
+    __syncthreads();
+    L = (s_red[1][0] + s_red[1][1]) + (s_red[1][2] + s_red[1][3]);
+    if (t < Q) {
+        float4 r = s_acc[0][t];
+        for (int g = 1; g < SG; ++g) {
+            const float4 v = s_acc[g][t];
+            r.x += v.x; r.y += v.y; r.z += v.z; r.w += v.w;
+        }
+        float4 o = L > 0.f ? make_float4(r.x / L, r.y / L, r.z / L, r.w / L) : make_float4(0.f, 0.f, 0.f, 0.f);
+        reinterpret_cast<float4 *>(a.out + (size_t)bh * D)[t] = o;
+    }
+    if (t == 0 && a.lse) a.lse[bh] = L > 0.f ? (M + log2f(L)) * kLn2 : kNegInf;
 }
 
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs &a, hipStream_t stream) {
-    const int rows = a.B * a.Hq;
-    const dim3 grid((rows + 3) / 4);
+    const dim3 grid(a.B * a.Hq);
     switch (a.D) {
     case 64: hipLaunchKernelGGL(combine<64>, grid, dim3(256), 0, stream, a); break;
     case 128: hipLaunchKernelGGL(combine<128>, grid, dim3(256), 0, stream, a); break;

@@ -22,17 +22,32 @@ __device__ __forceinline__ float ep_exp2(float x) { return __builtin_amdgcn_exp2
 // epoch) restarts the count, so the workspace needs no clearing between
 // calls.  Returns true for the workgroup that completes the group.  The loop
 // ends: every failed exchange means another workgroup's exchange succeeded.
+//
+// Ordering.  A device-scope release here would write back the whole L2 of
+// the XCD for every workgroup (about 1.7 us each, serialised), which costs
+// more than the separate combine launch it replaces.  Instead the partials
+// are written and read only with device-coherent (sc1) accesses, which go to
+// the coherent level instead of a per-XCD L2 copy; every thread waits for
+// its stores to complete (vmcnt 0) before the barrier, so all partials of
+// the workgroup are at the coherent level before this exchange is issued,
+// and the last workgroup issues its coherent loads only after the exchange
+// that completed the count has returned.
 __device__ __forceinline__ bool arrive_last(unsigned long long *cnt, unsigned epoch, int n_active) {
     unsigned long long old = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     unsigned long long next;
     for (;;) {
         next = ((unsigned)(old >> 32) == epoch) ? old + 1ull
                                                  : (((unsigned long long)epoch << 32) | 1ull);
-        if (__hip_atomic_compare_exchange_strong(cnt, &old, next, __ATOMIC_ACQ_REL, __ATOMIC_RELAXED,
+        if (__hip_atomic_compare_exchange_strong(cnt, &old, next, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT))
             break;
     }
     return (unsigned)(next & 0xffffffffull) == (unsigned)n_active;
+}
+
+// Device-coherent accesses of the partials in fused mode.
+__device__ __forceinline__ void st_agent(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ float ld_agent(const float *p) {
@@ -148,6 +163,10 @@ __device__ void finish_split(const SplitArgs &a, EpilogueLds<WAVES, GB, D> &sm, 
         if (a.n_splits == 1) {
             a.out[(size_t)bh * D + d] = L > 0.f ? acc / L : 0.f;
             if (d == 0 && a.lse) a.lse[bh] = L > 0.f ? (M + log2f(L)) * kEpLn2 : kEpNegInf;
+        } else if (a.fused) {
+            const size_t pi = (size_t)bh * a.n_splits + split;
+            st_agent(a.part_o + pi * D + d, acc);
+            if (d == 0) { st_agent(a.part_m + pi, M); st_agent(a.part_l + pi, L); }
         } else {
             const size_t pi = (size_t)bh * a.n_splits + split;
             a.part_o[pi * D + d] = acc;
@@ -156,9 +175,10 @@ __device__ void finish_split(const SplitArgs &a, EpilogueLds<WAVES, GB, D> &sm, 
     }
     if (a.n_splits == 1 || !a.fused) return;
 
-    // Fused combine: publish this split, count arrivals, and let the last
-    // workgroup of the group merge every split.
-    __threadfence();
+    // Fused combine: every thread's coherent partial stores complete
+    // (vmcnt 0), the barrier gathers the workgroup, one exchange counts the
+    // arrival, and the workgroup that completes the group merges its splits.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0) {
         unsigned long long *cnt = a.counters + (size_t)b * a.Hkv * a.head_blocks + (size_t)kvh * a.head_blocks + hb;
@@ -166,7 +186,6 @@ __device__ void finish_split(const SplitArgs &a, EpilogueLds<WAVES, GB, D> &sm, 
     }
     __syncthreads();
     if (!sm.last) return;
-    __threadfence();
     combine_group<WAVES, GB, D>(a, sm, b, h0, ng, active_splits(a, Tb));
 }
 

@@ -12,12 +12,18 @@
 #ifndef FD_VALU_U
 #define FD_VALU_U 4
 #endif
-// 1: stream K/V with non-temporal loads.
+// 1: stream K/V with non-temporal loads (each byte is read once; keeping
+// it out of the caches measured 13-19% faster on MI355X).
 #ifndef FD_NT_LOADS
-#define FD_NT_LOADS 0
+#define FD_NT_LOADS 1
 #endif
 
 namespace fdk {
+
+// Page ids one split workgroup stages in LDS (paged layout): a paged split
+// covers at most kMaxSplitPages pages, so the planner keeps paged chunks at
+// or below kMaxSplitPages * page_size tokens.
+constexpr int kMaxSplitPages = 2048;
 
 // Everything one split launch needs.  Passed by value as the kernel argument.
 struct SplitArgs {

@@ -73,12 +73,29 @@ __device__ __forceinline__ void widen(const uint2 &p, float *f) {
     for (int i = 0; i < 2; ++i) { f[2 * i] = widen1<DT>(w[i], 0); f[2 * i + 1] = widen1<DT>(w[i], 1); }
 }
 
+typedef unsigned int u32x4_v __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_v __attribute__((ext_vector_type(2)));
+
 template <typename V>
-__device__ __forceinline__ V load_piece(const char *p) {
+__device__ __forceinline__ V load_piece(const char *p);
+
+template <>
+__device__ __forceinline__ uint4 load_piece<uint4>(const char *p) {
 #if FD_NT_LOADS
-    return __builtin_nontemporal_load(reinterpret_cast<const V *>(p));
+    const u32x4_v v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_v *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
 #else
-    return *reinterpret_cast<const V *>(p);
+    return *reinterpret_cast<const uint4 *>(p);
+#endif
+}
+
+template <>
+__device__ __forceinline__ uint2 load_piece<uint2>(const char *p) {
+#if FD_NT_LOADS
+    const u32x2_v v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_v *>(p));
+    return make_uint2(v.x, v.y);
+#else
+    return *reinterpret_cast<const uint2 *>(p);
 #endif
 }
 
@@ -143,12 +160,24 @@ __global__ __launch_bounds__(256) void split_mfma(SplitArgs a) {
         kbase += seq;
         vbase += seq;
     }
+    // Paged: this split's page ids, staged once in LDS so that no K/V load
+    // waits on a dependent page-table read (ids outside the pool become -1).
+    __shared__ int s_pages[PAGED ? kMaxSplitPages : 1];
+    const int p0 = PAGED ? (c0 >> a.page_shift) : 0;
+    if constexpr (PAGED) {
+        const int npg = c1 > c0 ? ((c1 - 1) >> a.page_shift) - p0 + 1 : 0;
+        for (int i = threadIdx.x; i < npg; i += 64 * WAVES) {
+            const int pg = a.page_table[(size_t)b * a.max_pages + p0 + i];
+            s_pages[i] = (unsigned)pg < (unsigned)a.num_pages ? pg : -1;
+        }
+        __syncthreads();
+    }
     auto row_offset = [&](int t, bool &ok) -> Off {
         ok = t < c1;
         const int tc = ok ? t : c1 - 1;        // clamped: always a valid token
         if constexpr (PAGED) {
-            int page = a.page_table[(size_t)b * a.max_pages + (tc >> a.page_shift)];
-            if ((unsigned)page >= (unsigned)a.num_pages) { ok = false; page = 0; }
+            int page = s_pages[(tc >> a.page_shift) - p0];
+            if (page < 0) { ok = false; page = 0; }
             return (((size_t)page * a.Hkv + kvh) * a.page_size + (tc & (a.page_size - 1))) * ROWB;
         } else {
             return (uint32_t)tc * (uint32_t)ROWB;

@@ -28,7 +28,7 @@ class FDError(RuntimeError):
 def make_options(dtype: torch.dtype, *, page_size: int = 0, max_pages: int = 0,
                  num_pages: int = 0, workspace: Optional[torch.Tensor] = None,
                  stream: Optional[int] = None, num_cus: int = 0,
-                 path: Optional[str] = None) -> fd.fd_options_t:
+                 path: Optional[str] = None, fused_merge: bool = False) -> fd.fd_options_t:
     opt = fd.fd_options_t()
     fd.fd_options_init(opt)
     opt.dtype = _DTYPE[dtype]
@@ -37,6 +37,7 @@ def make_options(dtype: torch.dtype, *, page_size: int = 0, max_pages: int = 0,
     opt.num_pages = num_pages
     opt.num_cus = num_cus
     opt.path = _PATH[path]
+    opt.flags = fd.FD_FLAG_FUSED_MERGE if fused_merge else 0
     if workspace is not None:
         opt.workspace = workspace.data_ptr()
         opt.workspace_bytes = workspace.numel() * workspace.element_size()
@@ -45,10 +46,11 @@ def make_options(dtype: torch.dtype, *, page_size: int = 0, max_pages: int = 0,
 
 
 def plan(B, Hq, Hkv, T, D, n_splits=0, *, dtype=torch.bfloat16, page_size=0, max_pages=0,
-         num_pages=1, num_cus=0, path=None) -> dict:
+         num_pages=1, num_cus=0, path=None, fused_merge=False) -> dict:
     """What fd_decode would launch for these arguments (host only)."""
     opt = make_options(dtype, page_size=page_size, max_pages=max_pages,
-                       num_pages=num_pages if page_size else 0, num_cus=num_cus, path=path)
+                       num_pages=num_pages if page_size else 0, num_cus=num_cus, path=path,
+                       fused_merge=fused_merge)
     p = fd.fd_plan_t()
     st = fd.fd_plan(B, Hq, Hkv, T, D, n_splits, opt, p)
     if st != fd.FD_OK:
@@ -70,7 +72,8 @@ class Decoder:
 
     def __init__(self, q, k, v, *, scale: Optional[float] = None, page_table=None,
                  seq_lens=None, T: Optional[int] = None, n_splits: int = 0,
-                 path: Optional[str] = None, out=None, lse=None, want_lse: bool = True):
+                 path: Optional[str] = None, fused_merge: bool = False, out=None, lse=None,
+                 want_lse: bool = True):
         if q.device.type != "cuda":
             raise ValueError("q, k and v must be GPU tensors")
         if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPE:
@@ -108,7 +111,7 @@ class Decoder:
         self.n_splits = n_splits
         self.inputs = (q, k, v, page_table, seq_lens)
         self.opt = make_options(q.dtype, page_size=page_size, max_pages=max_pages,
-                                num_pages=num_pages, path=path)
+                                num_pages=num_pages, path=path, fused_merge=fused_merge)
         p = fd.fd_plan_t()
         st = fd.fd_plan(B, Hq, Hkv, T, D, n_splits, self.opt, p)
         if st != fd.FD_OK:
@@ -153,7 +156,7 @@ class Decoder:
 
 
 def decode(q, k, v, *, scale=None, page_table=None, seq_lens=None, T=None, n_splits=0,
-           path=None):
+           path=None, fused_merge=False):
     """out [B, Hq, D] fp32 and lse [B, Hq] fp32 of single-query decode attention."""
     return Decoder(q, k, v, scale=scale, page_table=page_table, seq_lens=seq_lens, T=T,
-                   n_splits=n_splits, path=path)()
+                   n_splits=n_splits, path=path, fused_merge=fused_merge)()

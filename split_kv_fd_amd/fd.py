@@ -9,11 +9,15 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfd.so")
+# The in-tree build; FD_LIBRARY may name another build of the same sources
+# (for comparing compile-time variants).
+LIB_PATH = os.environ.get("FD_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libfd.so")
 
 FD_F32, FD_F16, FD_BF16 = 0, 1, 2
 FD_OK, FD_ERR_INVALID_ARG, FD_ERR_UNSUPPORTED, FD_ERR_WORKSPACE, FD_ERR_HIP = range(5)
 FD_PATH_AUTO, FD_PATH_VALU, FD_PATH_MFMA = -1, 0, 1
+FD_FLAG_FUSED_MERGE = 0x1
 
 # Every function include/fd.h declares.
 EXPORTS = ("fd_options_init", "fd_plan", "fd_workspace_bytes", "fd_decode", "fd_split",
@@ -24,7 +28,7 @@ class fd_options_t(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32), ("dtype", ctypes.c_int32),
                 ("page_size", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
                 ("num_pages", ctypes.c_int32), ("num_cus", ctypes.c_int32),
-                ("path", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("path", ctypes.c_int32), ("flags", ctypes.c_int32),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
                 ("stream", ctypes.c_void_p)]
 

@@ -25,12 +25,14 @@ def announce(msg: str) -> None:
     sys.stdout.flush()
 
 
-def run_gpu(case, n_splits=0, path=None, scale=None):
+def run_gpu(case, n_splits=0, path=None, scale=None, fused_merge=False, poison=False):
     q, k, v = case.q, case.k, case.v
     dec = Decoder(q, k, v, scale=case.spec.scale if scale is None else scale,
                   page_table=case.page_table, seq_lens=case.seq_lens,
                   T=case.spec.T if case.page_table is not None else None,
-                  n_splits=n_splits, path=path)
+                  n_splits=n_splits, path=path, fused_merge=fused_merge)
+    if poison and dec.workspace is not None:
+        dec.workspace.fill_(0xFF)          # NaN partials, foreign counter tags
     announce(f"decode {case.spec.name} B={case.spec.B} Hq={case.spec.Hq} Hkv={case.spec.Hkv} "
              f"T={case.spec.T} D={case.spec.D} {case.spec.dtype} seed={case.spec.seed} "
              f"n_splits={n_splits} plan={dec.plan}")
@@ -81,8 +83,8 @@ def compare(case, out, lse, ref_out, ref_lse, vmax, what=""):
     return err, lerr
 
 
-def check_full(case, n_splits=0, path=None, what=""):
-    out, lse, plan = run_gpu(case, n_splits, path)
+def check_full(case, n_splits=0, path=None, what="", fused_merge=False):
+    out, lse, plan = run_gpu(case, n_splits, path, fused_merge=fused_merge, poison=fused_merge)
     if path in ("valu", "mfma"):
         assert plan["path"] == path
     ref_out, ref_lse = oracle_full(case)

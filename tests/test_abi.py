@@ -111,7 +111,11 @@ def test_plan_paged_chunks_align_to_pages(lib):
     assert st == fd.FD_OK and p.chunk % 256 == 0
     # ragged (paged) batches are cut into short chunks for balance
     st, p = plan(16, 32, 8, 65536, 128, 0, page_size=16, max_pages_per_seq=4096, num_pages=10)
-    assert st == fd.FD_OK and p.chunk <= 2048 and p.fused
+    assert st == fd.FD_OK and p.chunk <= 2048 and not p.fused
+    st, p = plan(16, 32, 8, 65536, 128, 0, page_size=16, max_pages_per_seq=4096, num_pages=10,
+                 flags=fd.FD_FLAG_FUSED_MERGE)
+    assert st == fd.FD_OK and p.fused
+    assert plan(1, 4, 4, 100, 128, flags=6)[0] == fd.FD_ERR_INVALID_ARG
 
 
 def test_plan_paths(lib):
@@ -181,6 +185,7 @@ def test_decode_rejects_before_launch(lib):
     assert decode(out=None) == fd.FD_ERR_INVALID_ARG
     assert decode(k=MIS) == fd.FD_ERR_INVALID_ARG
     assert decode(out=A + 1) == fd.FD_ERR_INVALID_ARG
+    assert decode(out=A + 4) == fd.FD_ERR_INVALID_ARG
     assert decode(scale=float("inf")) == fd.FD_ERR_INVALID_ARG
     assert decode(scale=float("nan")) == fd.FD_ERR_INVALID_ARG
     assert decode(shape=(1, 4, 3, 4096, 128)) == fd.FD_ERR_INVALID_ARG

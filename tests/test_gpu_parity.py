@@ -73,13 +73,14 @@ def test_short_sequences(T, path):
         parity.check_full(case, n_splits=n, path=path, what=f"T={T} n={n} {path}")
 
 
-def test_ragged_lengths_with_empty_sequences():
+@pytest.mark.parametrize("fused", [False, True])
+def test_ragged_lengths_with_empty_sequences(fused):
     s = inputs.spec("mha32k_f16", B=4, Hq=4, Hkv=2, T=300)
     case = inputs.make_case(s).to(DEV)
     case.seq_lens = torch.tensor([0, 1, 299, 300], dtype=torch.int32, device=DEV)
+    ref_out, ref_lse = parity.oracle_full(case)
     for n in (0, 1, 5):
-        out, lse, _ = parity.run_gpu(case, n)
-        ref_out, ref_lse = parity.oracle_full(case)
+        out, lse, _ = parity.run_gpu(case, n, fused_merge=fused, poison=True)
         parity.compare(case, out, lse, ref_out, ref_lse, parity.max_abs_v(case), f"ragged n={n}")
         assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
 
@@ -154,21 +155,58 @@ def test_deterministic_runs(path):
 
 @pytest.mark.parametrize("path", ["valu", "mfma"])
 def test_fused_merge_with_stale_workspace(path):
-    # The arrival counters carry a per-call tag: a workspace full of garbage,
-    # or left by a call with another split count, must not change results.
-    case = small_case("gqa128k_bf16", B=3, T=6000)
-    ref_out, ref_lse = parity.oracle_full(case)
-    vmax = parity.max_abs_v(case)
-    for n in (7, 20, 7):
-        dec = Decoder(case.q, case.k, case.v, scale=case.spec.scale, n_splits=n, path=path)
-        assert dec.plan["fused"]
-        dec.workspace.fill_(0xFF)
-        for rep in range(3):
-            parity.announce(f"fused merge n={n} rep={rep} {path}")
-            out, lse = dec()
-            torch.cuda.synchronize()
-            parity.compare(case, out.cpu().double().numpy(), lse.cpu().double().numpy(),
-                           ref_out, ref_lse, vmax, f"stale workspace n={n} rep={rep}")
+    # The arrival counters carry a per-call tag: a workspace full of garbage
+    # (NaN partials, foreign tags) before every call, or left by a call with
+    # another split count or other inputs, must not change results.  Inputs
+    # alternate so a stale partial could not pass for a fresh one.
+    cases = [small_case("gqa128k_bf16", B=3, T=6000),
+             small_case("gqa128k_bf16", B=3, T=6000, seed=301)]
+    refs = [parity.oracle_full(c) for c in cases]
+    vmax = [parity.max_abs_v(c) for c in cases]
+    decs = {}
+    for rep in range(4):
+        for n in (7, 20):
+            for i, c in enumerate(cases):
+                key = (n, i)
+                if key not in decs:
+                    decs[key] = Decoder(c.q, c.k, c.v, scale=c.spec.scale, n_splits=n, path=path,
+                                        fused_merge=True)
+                dec = decs[key]
+                assert dec.plan["fused"]
+                if rep % 2 == 0:
+                    dec.workspace.fill_(0xFF)
+                parity.announce(f"fused merge n={n} case={i} rep={rep} {path}")
+                out, lse = dec()
+                torch.cuda.synchronize()
+                parity.compare(c, out.cpu().double().numpy(), lse.cpu().double().numpy(),
+                               refs[i][0], refs[i][1], vmax[i], f"fused n={n} case={i} rep={rep}")
+
+
+@pytest.mark.parametrize("path", ["valu", "mfma"])
+def test_fused_merge_matches_combine_kernel(path):
+    # Many groups and splits finishing in arbitrary order: the fused merge
+    # must agree with the separate combine kernel on every run.
+    case = small_case("mha32k_f16", B=2, Hq=32, Hkv=8, T=20000)
+    base = Decoder(case.q, case.k, case.v, scale=case.spec.scale, n_splits=40, path=path)
+    fused = Decoder(case.q, case.k, case.v, scale=case.spec.scale, n_splits=40, path=path,
+                    fused_merge=True)
+    assert not base.plan["fused"] and fused.plan["fused"]
+    ref_out, ref_lse = (x.clone() for x in base())
+    torch.cuda.synchronize()
+    for rep in range(20):
+        fused.workspace.fill_(0xFF)
+        out, lse = fused()
+        torch.cuda.synchronize()
+        assert torch.isfinite(out).all(), f"rep {rep}: non-finite output"
+        assert torch.allclose(out, ref_out, rtol=0, atol=2e-6) and torch.allclose(lse, ref_lse, rtol=0, atol=2e-6), f"rep {rep}"
+
+
+@pytest.mark.parametrize("path", ["valu", "mfma"])
+def test_fused_merge_ragged_and_paged(path):
+    case = small_case("paged_ragged_bf16", B=6, T=5000, len_lo=0, len_hi=5000)
+    case.seq_lens[1] = 0
+    for n in (0, 3, 11):
+        parity.check_full(case, n_splits=n, path=path, fused_merge=True, what=f"fused paged n={n}")
 
 
 @pytest.mark.parametrize("path", ["valu", "mfma"])
@@ -177,7 +215,8 @@ def test_split_and_combine_entry_points(path):
     ref_out, ref_lse = parity.oracle_full(case)
     vmax = parity.max_abs_v(case)
     for n in (6, 100):
-        dec = Decoder(case.q, case.k, case.v, scale=case.spec.scale, n_splits=n, path=path)
+        dec = Decoder(case.q, case.k, case.v, scale=case.spec.scale, n_splits=n, path=path,
+                      fused_merge=True)
         assert dec.plan["n_splits"] > 1
         parity.announce(f"fd_split + fd_combine separately n={n} {path}")
         dec.split()
