@@ -131,10 +131,12 @@ def main() -> int:
     ap.add_argument("--config", default=DEFAULT_WORKLOAD)
     ap.add_argument("--n-splits", type=int, default=0, help="0 = the planner's choice")
     ap.add_argument("--path", default=None, choices=[None, "auto", "valu", "mfma"])
-    ap.add_argument("--fused-merge", action="store_true",
-                    help="merge the splits inside the split launch (FD_FLAG_FUSED_MERGE)")
+    ap.add_argument("--merge", default="auto", choices=["auto", "fused", "combine"],
+                    help="force the fused merge or the combine kernel (default: library's choice)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--set", action="append", default=[], metavar="KEY=VALUE",
+                    help="override a workload field (experiments; e.g. T=65536)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (for counter scaling) and exit")
     args = ap.parse_args()
@@ -157,7 +159,13 @@ def main() -> int:
     from split_kv_fd_amd.decode import Decoder
     fd.load()   # fails loudly if the HIP library is not built
 
-    spec = inputs.spec(args.config)
+    overrides = {}
+    for kv in args.set:
+        key, _, val = kv.partition("=")
+        cur = getattr(inputs.SPECS[args.config], key)
+        overrides[key] = type(cur)(float(val)) if not isinstance(cur, (str, bool)) else (
+            val if isinstance(cur, str) else val.lower() in ("1", "true", "yes"))
+    spec = inputs.spec(args.config, **overrides)
     print(f"[bench] generating {spec.name} on the GPU", file=sys.stderr, flush=True)
     case = inputs.make_case(spec, device="cuda")
     lens = case.lengths()
@@ -170,7 +178,7 @@ def main() -> int:
         decs.append(Decoder(case.q, k, v, scale=spec.scale, page_table=case.page_table,
                             seq_lens=case.seq_lens, T=spec.T if case.page_table is not None else None,
                             n_splits=args.n_splits or spec.n_splits, path=args.path,
-                            fused_merge=args.fused_merge))
+                            fused_merge={"auto": None, "fused": True, "combine": False}[args.merge]))
     plan = decs[0].plan
     print(f"[bench] plan {plan}; {copies} KV copies", file=sys.stderr, flush=True)
 
@@ -211,6 +219,9 @@ def main() -> int:
     kernel = "fd_split"
     traffic = read_traffic(spec.name, kernel)
 
+    if overrides:
+        print(f"[bench] workload overrides {overrides}: not the reference workload",
+              file=sys.stderr, flush=True)
     result = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -224,7 +235,8 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": spec.dtype,
         "data": "synthetic",
-        "config": {"workload": spec.name, "B": spec.B, "Hq": spec.Hq, "Hkv": spec.Hkv, "G": spec.G,
+        "config": {"workload": spec.name + ("" if not overrides else f" (overrides {overrides})"),
+                   "B": spec.B, "Hq": spec.Hq, "Hkv": spec.Hkv, "G": spec.G,
                    "D": spec.D, "T": spec.T, "kv_dtype": spec.dtype, "accumulate": "f32",
                    "kv_bytes_per_step": kv_bytes, "kv_copies_rotated": copies,
                    "n_splits": plan["n_splits"], "chunk": plan["chunk"], "path": plan["path"],

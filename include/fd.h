@@ -68,11 +68,13 @@ typedef enum {
     FD_PATH_MFMA = 1          /* matrix-core path (f16/bf16 only)             */
 } fd_path_t;
 
-/* fd_options_t.flags: merge the splits inside the split launch (the last
- * workgroup of each kv head combines its group) instead of launching the
- * combine kernel.  Saves one launch; the partials then travel through
- * device-coherent stores and loads. */
+/* fd_options_t.flags.  By default fd_decode merges the splits inside the
+ * split launch (the last workgroup of each kv head combines its group, the
+ * partials travelling through device-coherent stores and loads) when the
+ * grid runs in about one round of workgroups, and launches the combine
+ * kernel otherwise.  These flags force one or the other. */
 #define FD_FLAG_FUSED_MERGE 0x1
+#define FD_FLAG_COMBINE_KERNEL 0x2
 
 /* Options of a call.  Initialise with fd_options_init() and then set the
  * fields you need; struct_size versions the layout. */

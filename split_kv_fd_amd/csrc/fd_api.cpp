@@ -78,7 +78,10 @@ fd_status_t read_options(const fd_options_t *opt, fd_options_t *o) {
     if (o->path != FD_PATH_AUTO && o->path != FD_PATH_VALU && o->path != FD_PATH_MFMA)
         return fail(FD_ERR_INVALID_ARG, "unknown path %d", (int)o->path);
     if (o->num_cus < 0) return fail(FD_ERR_INVALID_ARG, "num_cus %d < 0", (int)o->num_cus);
-    if (o->flags & ~FD_FLAG_FUSED_MERGE) return fail(FD_ERR_INVALID_ARG, "unknown flags 0x%x", (unsigned)o->flags);
+    if (o->flags & ~(FD_FLAG_FUSED_MERGE | FD_FLAG_COMBINE_KERNEL))
+        return fail(FD_ERR_INVALID_ARG, "unknown flags 0x%x", (unsigned)o->flags);
+    if ((o->flags & FD_FLAG_FUSED_MERGE) && (o->flags & FD_FLAG_COMBINE_KERNEL))
+        return fail(FD_ERR_INVALID_ARG, "FD_FLAG_FUSED_MERGE and FD_FLAG_COMBINE_KERNEL exclude each other");
     return FD_OK;
 }
 
@@ -111,8 +114,14 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
     int path = o.path;
     if (path == FD_PATH_MFMA && o.dtype == FD_F32)
         return fail(FD_ERR_UNSUPPORTED, "the MFMA path needs f16 or bf16 inputs");
-    if (path == FD_PATH_AUTO)
-        path = (o.dtype != FD_F32 && G >= env_long("FD_MFMA_MIN_G", 4)) ? FD_PATH_MFMA : FD_PATH_VALU;
+    if (path == FD_PATH_AUTO) {
+        // Measured: the matrix-core kernel wins from G = 4 on contiguous
+        // caches; with paged (ragged) batches, whose short splits expose the
+        // per-workgroup pipeline fill, the VALU kernel's higher occupancy
+        // wins at G = 4.
+        const long min_g = env_long("FD_MFMA_MIN_G", paged ? 8 : 4);
+        path = (o.dtype != FD_F32 && G >= min_g) ? FD_PATH_MFMA : FD_PATH_VALU;
+    }
     int hpb, tile;
     if (path == FD_PATH_MFMA) {
         hpb = fdk::kMfmaHeads;
@@ -155,6 +164,10 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
             const long ragged_chunk = std::max(1L, env_long("FD_RAGGED_CHUNK", 1024));
             const long nr = ceil_div(T, ragged_chunk);
             if (n < nr) n = nr;
+            // Workgroups go to the 8 XCDs round-robin by linear id, with the
+            // split index fastest: a multiple of 8 splits spreads each
+            // sequence's active (leading) splits evenly over the XCDs.
+            n = ceil_div(n, 8) * 8;
         }
     }
     if (paged) {
@@ -181,9 +194,16 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
     p->grid[2] = B;
     p->block = 256;
     p->combine = n > 1;
-    // On request, the last workgroup of a group merges the splits itself
-    // when their weights fit its LDS (n * heads <= 4 * D * heads_per_block).
-    const bool want_fused = (o.flags & FD_FLAG_FUSED_MERGE) != 0 || env_long("FD_FUSED", 0) == 1;
+    // The last workgroup of a group merges the splits itself when their
+    // weights fit its LDS (n * heads <= 4 * D * heads_per_block).  By
+    // default this is chosen when the grid runs in about one round (at most
+    // two workgroups per compute unit): then it saves the combine launch,
+    // while with many rounds the per-workgroup publish latency costs more.
+    bool want_fused = (long)B * Hkv * head_blocks * n <= 2L * cus;
+    if (o.flags & FD_FLAG_FUSED_MERGE) want_fused = true;
+    if (o.flags & FD_FLAG_COMBINE_KERNEL) want_fused = false;
+    const long env_fused = env_long("FD_FUSED", -1);
+    if (env_fused == 0 || env_fused == 1) want_fused = env_fused == 1;
     p->fused = n > 1 && n <= 4L * D && want_fused;
     if (n > 1) {
         const size_t parts = (size_t)B * Hq * (size_t)n;

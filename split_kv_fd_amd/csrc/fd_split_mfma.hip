@@ -99,8 +99,11 @@ __device__ __forceinline__ uint2 load_piece<uint2>(const char *p) {
 #endif
 }
 
-template <int DT, int D, bool PAGED>
+// PG: 0 contiguous cache, 1 paged with per-token page lookups (pages under
+// 16 tokens), 2 paged with one lookup per 16-token block (pages of 16+).
+template <int DT, int D, int PG>
 __global__ __launch_bounds__(256) void split_mfma(SplitArgs a) {
+    constexpr bool PAGED = PG != 0;
     constexpr int EB = 2;
     constexpr int ROWB = D * EB;
     constexpr int KS = D / 32;          // 16-byte q/k pieces per lane per tile
@@ -119,7 +122,7 @@ __global__ __launch_bounds__(256) void split_mfma(SplitArgs a) {
     const int hb = blockIdx.y - kvh * a.head_blocks;
     const int b = blockIdx.z;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
     const int i16 = lane & 15;
     const int kb = lane >> 4;
 
@@ -190,18 +193,54 @@ __global__ __launch_bounds__(256) void split_mfma(SplitArgs a) {
         bool ok[2][4];
     };
 
+    // Pages of 16 tokens or more: a 16-token block (16-aligned, as every
+    // split starts on a multiple of the tile) lies in one page, so one page
+    // lookup serves the block's K and V rows.  The page is the same for the
+    // whole wave, so the block's base address is kept in scalar registers and
+    // each lane adds a fixed 32-bit offset -- the same load form as the
+    // contiguous path (64-bit per-lane addresses measurably cut the number of
+    // loads a wave keeps in flight).  A block past the split end is
+    // redirected to the split's last block; its rows are read but masked.
+    constexpr bool block_pages = PG == 2;
+    const uint32_t k_lane = (uint32_t)(i16 * ROWB + kb * 16);         // + 64 * ks
+    const uint32_t v_lane = (uint32_t)(4 * kb * ROWB + i16 * VB);     // + ROWB * r
+    auto block_base = [&](int t16, bool &page_ok) -> size_t {
+        const int tcl = t16 < c1 ? t16 : ((c1 - 1) & ~15);
+        int page = __builtin_amdgcn_readfirstlane(s_pages[(tcl >> a.page_shift) - p0]);
+        page_ok = page >= 0;
+        page = page_ok ? page : 0;
+        return (((size_t)page * a.Hkv + kvh) * a.page_size + (tcl & (a.page_size - 1))) * ROWB;
+    };
+
     auto load_step = [&](int base, Buf &f) {
         const int tb = base + wave * TOK;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            bool okk;
-            const Off ko = row_offset(tb + 16 * h + i16, okk);
+            const int t16 = tb + 16 * h;
+            if constexpr (block_pages) {
+                bool pok;
+                const size_t bo = block_base(t16, pok);
+                const char *kblk = kbase + bo;
+                const char *vblk = vbase + bo;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) f.k[h][ks] = load_piece<uint4>(kbase + (ko + (Off)((4 * ks + kb) * 16)));
+                for (int ks = 0; ks < KS; ++ks)
+                    f.k[h][ks] = load_piece<uint4>(kblk + (k_lane + (uint32_t)(64 * ks)));
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const Off vo = row_offset(tb + 16 * h + 4 * kb + r, f.ok[h][r]);
-                f.v[h][r] = load_piece<VP>(vbase + (vo + (Off)(i16 * VB)));
+                for (int r = 0; r < 4; ++r) {
+                    f.ok[h][r] = pok && (t16 + 4 * kb + r < c1);
+                    f.v[h][r] = load_piece<VP>(vblk + (v_lane + (uint32_t)(ROWB * r)));
+                }
+            } else {
+                bool okk;
+                const Off ko = row_offset(t16 + i16, okk);
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    f.k[h][ks] = load_piece<uint4>(kbase + (ko + (Off)((4 * ks + kb) * 16)));
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const Off vo = row_offset(t16 + 4 * kb + r, f.ok[h][r]);
+                    f.v[h][r] = load_piece<VP>(vbase + (vo + (Off)(i16 * VB)));
+                }
             }
         }
     };
@@ -279,10 +318,12 @@ __global__ __launch_bounds__(256) void split_mfma(SplitArgs a) {
 template <int DT, int D>
 hipError_t launch_dim(const SplitArgs &a, hipStream_t stream) {
     const dim3 grid(a.n_splits, a.Hkv * a.head_blocks, a.B);
-    if (a.page_table)
-        hipLaunchKernelGGL((split_mfma<DT, D, true>), grid, dim3(256), 0, stream, a);
+    if (!a.page_table)
+        hipLaunchKernelGGL((split_mfma<DT, D, 0>), grid, dim3(256), 0, stream, a);
+    else if (a.page_size >= 16)
+        hipLaunchKernelGGL((split_mfma<DT, D, 2>), grid, dim3(256), 0, stream, a);
     else
-        hipLaunchKernelGGL((split_mfma<DT, D, false>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((split_mfma<DT, D, 1>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

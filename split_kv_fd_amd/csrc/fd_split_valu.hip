@@ -127,7 +127,7 @@ __global__ __launch_bounds__(256) void split_valu(SplitArgs a) {
     const int hb = blockIdx.y - kvh * a.head_blocks;
     const int b = blockIdx.z;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
     const int row = lane / LPR;
     const int sub = lane % LPR;
 

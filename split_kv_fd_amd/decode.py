@@ -28,7 +28,7 @@ class FDError(RuntimeError):
 def make_options(dtype: torch.dtype, *, page_size: int = 0, max_pages: int = 0,
                  num_pages: int = 0, workspace: Optional[torch.Tensor] = None,
                  stream: Optional[int] = None, num_cus: int = 0,
-                 path: Optional[str] = None, fused_merge: bool = False) -> fd.fd_options_t:
+                 path: Optional[str] = None, fused_merge: Optional[bool] = None) -> fd.fd_options_t:
     opt = fd.fd_options_t()
     fd.fd_options_init(opt)
     opt.dtype = _DTYPE[dtype]
@@ -37,7 +37,9 @@ def make_options(dtype: torch.dtype, *, page_size: int = 0, max_pages: int = 0,
     opt.num_pages = num_pages
     opt.num_cus = num_cus
     opt.path = _PATH[path]
-    opt.flags = fd.FD_FLAG_FUSED_MERGE if fused_merge else 0
+    # None: the library chooses; True / False force the fused merge / the
+    # combine kernel.
+    opt.flags = {None: 0, True: fd.FD_FLAG_FUSED_MERGE, False: fd.FD_FLAG_COMBINE_KERNEL}[fused_merge]
     if workspace is not None:
         opt.workspace = workspace.data_ptr()
         opt.workspace_bytes = workspace.numel() * workspace.element_size()
@@ -46,7 +48,7 @@ def make_options(dtype: torch.dtype, *, page_size: int = 0, max_pages: int = 0,
 
 
 def plan(B, Hq, Hkv, T, D, n_splits=0, *, dtype=torch.bfloat16, page_size=0, max_pages=0,
-         num_pages=1, num_cus=0, path=None, fused_merge=False) -> dict:
+         num_pages=1, num_cus=0, path=None, fused_merge=None) -> dict:
     """What fd_decode would launch for these arguments (host only)."""
     opt = make_options(dtype, page_size=page_size, max_pages=max_pages,
                        num_pages=num_pages if page_size else 0, num_cus=num_cus, path=path,
@@ -72,7 +74,7 @@ class Decoder:
 
     def __init__(self, q, k, v, *, scale: Optional[float] = None, page_table=None,
                  seq_lens=None, T: Optional[int] = None, n_splits: int = 0,
-                 path: Optional[str] = None, fused_merge: bool = False, out=None, lse=None,
+                 path: Optional[str] = None, fused_merge: Optional[bool] = None, out=None, lse=None,
                  want_lse: bool = True):
         if q.device.type != "cuda":
             raise ValueError("q, k and v must be GPU tensors")
@@ -156,7 +158,7 @@ class Decoder:
 
 
 def decode(q, k, v, *, scale=None, page_table=None, seq_lens=None, T=None, n_splits=0,
-           path=None, fused_merge=False):
+           path=None, fused_merge=None):
     """out [B, Hq, D] fp32 and lse [B, Hq] fp32 of single-query decode attention."""
     return Decoder(q, k, v, scale=scale, page_table=page_table, seq_lens=seq_lens, T=T,
                    n_splits=n_splits, path=path, fused_merge=fused_merge)()

@@ -18,6 +18,7 @@ FD_F32, FD_F16, FD_BF16 = 0, 1, 2
 FD_OK, FD_ERR_INVALID_ARG, FD_ERR_UNSUPPORTED, FD_ERR_WORKSPACE, FD_ERR_HIP = range(5)
 FD_PATH_AUTO, FD_PATH_VALU, FD_PATH_MFMA = -1, 0, 1
 FD_FLAG_FUSED_MERGE = 0x1
+FD_FLAG_COMBINE_KERNEL = 0x2
 
 # Every function include/fd.h declares.
 EXPORTS = ("fd_options_init", "fd_plan", "fd_workspace_bytes", "fd_decode", "fd_split",

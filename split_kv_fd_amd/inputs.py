@@ -53,6 +53,7 @@ class Spec:
     page_size: int = 16
     len_lo: int = 0             # ragged lengths ~ U{len_lo .. len_hi}
     len_hi: int = 0
+    page_shuffle: bool = True   # hand out pool pages in random order
 
     @property
     def G(self) -> int:
@@ -170,6 +171,8 @@ def paged_layout(s: Spec):
     npages = [-(-int(n) // P) for n in lens]
     num_pages = sum(npages)
     perm = torch.randperm(num_pages, generator=_gen("cpu", s.seed, _AUX, 4)).to(torch.int32)
+    if not s.page_shuffle:
+        perm = torch.arange(num_pages, dtype=torch.int32)
     table = torch.zeros((s.B, max_pages), dtype=torch.int32)
     off = 0
     for b, n in enumerate(npages):

@@ -25,7 +25,7 @@ def announce(msg: str) -> None:
     sys.stdout.flush()
 
 
-def run_gpu(case, n_splits=0, path=None, scale=None, fused_merge=False, poison=False):
+def run_gpu(case, n_splits=0, path=None, scale=None, fused_merge=None, poison=False):
     q, k, v = case.q, case.k, case.v
     dec = Decoder(q, k, v, scale=case.spec.scale if scale is None else scale,
                   page_table=case.page_table, seq_lens=case.seq_lens,
@@ -83,8 +83,8 @@ def compare(case, out, lse, ref_out, ref_lse, vmax, what=""):
     return err, lerr
 
 
-def check_full(case, n_splits=0, path=None, what="", fused_merge=False):
-    out, lse, plan = run_gpu(case, n_splits, path, fused_merge=fused_merge, poison=fused_merge)
+def check_full(case, n_splits=0, path=None, what="", fused_merge=None):
+    out, lse, plan = run_gpu(case, n_splits, path, fused_merge=fused_merge, poison=True)
     if path in ("valu", "mfma"):
         assert plan["path"] == path
     ref_out, ref_lse = oracle_full(case)

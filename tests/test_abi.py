@@ -78,13 +78,14 @@ def test_plan_covers_sequence_and_respects_tiles(lib):
                 assert p.heads_per_block * p.head_blocks >= Hq // Hkv
                 assert bool(p.combine) == (p.n_splits > 1)
                 assert not p.fused or (p.combine and p.n_splits <= 4 * D)
+                assert not p.fused or B * Hkv * p.head_blocks * p.n_splits <= 512
                 parts = B * Hq * p.n_splits
                 if p.n_splits > 1:
                     assert p.workspace_bytes >= parts * (D + 2) * 4 + B * Hkv * p.head_blocks * 8
                 else:
                     assert p.workspace_bytes == 0
                 G = Hq // Hkv
-                want_mfma = dt != fd.FD_F32 and G >= 4
+                want_mfma = dt != fd.FD_F32 and G >= 4   # contiguous caches
                 assert p.path == (fd.FD_PATH_MFMA if want_mfma else fd.FD_PATH_VALU)
                 assert p.heads_per_block == (16 if want_mfma else min(8, 1 << (G - 1).bit_length()))
 
@@ -111,11 +112,24 @@ def test_plan_paged_chunks_align_to_pages(lib):
     assert st == fd.FD_OK and p.chunk % 256 == 0
     # ragged (paged) batches are cut into short chunks for balance
     st, p = plan(16, 32, 8, 65536, 128, 0, page_size=16, max_pages_per_seq=4096, num_pages=10)
-    assert st == fd.FD_OK and p.chunk <= 2048 and not p.fused
+    assert st == fd.FD_OK and p.chunk <= 2048 and not p.fused and p.n_splits % 8 == 0
     st, p = plan(16, 32, 8, 65536, 128, 0, page_size=16, max_pages_per_seq=4096, num_pages=10,
                  flags=fd.FD_FLAG_FUSED_MERGE)
     assert st == fd.FD_OK and p.fused
-    assert plan(1, 4, 4, 100, 128, flags=6)[0] == fd.FD_ERR_INVALID_ARG
+    assert plan(1, 4, 4, 100, 128, flags=4)[0] == fd.FD_ERR_INVALID_ARG
+    assert plan(1, 4, 4, 100, 128, flags=3)[0] == fd.FD_ERR_INVALID_ARG
+
+
+def test_plan_merge_choice(lib):
+    # one round of workgroups: fused merge; many rounds: combine kernel
+    st, p = plan(1, 32, 32, 32768, 128, 0, dtype=fd.FD_F16)
+    assert st == fd.FD_OK and p.n_splits > 1 and p.fused
+    st, p = plan(1, 32, 32, 32768, 128, 64, dtype=fd.FD_F16)
+    assert st == fd.FD_OK and not p.fused
+    st, p = plan(1, 32, 32, 32768, 128, 64, dtype=fd.FD_F16, flags=fd.FD_FLAG_FUSED_MERGE)
+    assert st == fd.FD_OK and p.fused
+    st, p = plan(1, 32, 32, 32768, 128, 0, dtype=fd.FD_F16, flags=fd.FD_FLAG_COMBINE_KERNEL)
+    assert st == fd.FD_OK and not p.fused
 
 
 def test_plan_paths(lib):

@@ -80,7 +80,9 @@ def test_ragged_lengths_with_empty_sequences(fused):
     case.seq_lens = torch.tensor([0, 1, 299, 300], dtype=torch.int32, device=DEV)
     ref_out, ref_lse = parity.oracle_full(case)
     for n in (0, 1, 5):
-        out, lse, _ = parity.run_gpu(case, n, fused_merge=fused, poison=True)
+        out, lse, plan = parity.run_gpu(case, n, fused_merge=fused, poison=True)
+        if plan["n_splits"] > 1:
+            assert plan["fused"] == fused
         parity.compare(case, out, lse, ref_out, ref_lse, parity.max_abs_v(case), f"ragged n={n}")
         assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
 
@@ -187,7 +189,8 @@ def test_fused_merge_matches_combine_kernel(path):
     # Many groups and splits finishing in arbitrary order: the fused merge
     # must agree with the separate combine kernel on every run.
     case = small_case("mha32k_f16", B=2, Hq=32, Hkv=8, T=20000)
-    base = Decoder(case.q, case.k, case.v, scale=case.spec.scale, n_splits=40, path=path)
+    base = Decoder(case.q, case.k, case.v, scale=case.spec.scale, n_splits=40, path=path,
+                   fused_merge=False)
     fused = Decoder(case.q, case.k, case.v, scale=case.spec.scale, n_splits=40, path=path,
                     fused_merge=True)
     assert not base.plan["fused"] and fused.plan["fused"]
