@@ -133,6 +133,8 @@ def main() -> int:
     ap.add_argument("--path", default=None, choices=[None, "auto", "valu", "mfma"])
     ap.add_argument("--merge", default="auto", choices=["auto", "fused", "combine"],
                     help="force the fused merge or the combine kernel (default: library's choice)")
+    ap.add_argument("--event-every", type=int, default=4,
+                    help="record HIP events around every N-th step's launches")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--set", action="append", default=[], metavar="KEY=VALUE",
@@ -188,24 +190,30 @@ def main() -> int:
 
     K = args.steps
     separate = plan["combine"] and not plan["fused"]
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    # HIP events bracket the launches of every EVERY-th step (the others run
+    # without markers, which would otherwise add their own gaps).
+    every = max(1, args.event_every)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(0, K, every)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    if separate:
-        # the merge is its own kernel: time the two launches apart
-        for i in range(K):
-            d = decs[i % copies]
-            ev[i][0].record()
+    for i in range(K):
+        d = decs[i % copies]
+        e = ev[i // every] if i % every == 0 else None
+        if e:
+            e[0].record()
+        if separate:
+            # the merge is its own kernel: time the two launches apart
             d.split()
-            ev[i][1].record()
+            if e:
+                e[1].record()
             d.combine()
-            ev[i][2].record()
-    else:
-        # one launch per step: the split kernel (with the fused merge)
-        for i in range(K):
-            ev[i][0].record()
-            decs[i % copies]()
-            ev[i][1].record()
+            if e:
+                e[2].record()
+        else:
+            # one launch per step: the split kernel (with the fused merge)
+            d()
+            if e:
+                e[1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
 

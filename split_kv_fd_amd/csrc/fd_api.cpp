@@ -195,7 +195,7 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
     p->block = 256;
     p->combine = n > 1;
     // The last workgroup of a group merges the splits itself when their
-    // weights fit its LDS (n * heads <= 4 * D * heads_per_block).  By
+    // maxima and sums fit its LDS (n * heads <= 1024).  By
     // default this is chosen when the grid runs in about one round (at most
     // two workgroups per compute unit): then it saves the combine launch,
     // while with many rounds the per-workgroup publish latency costs more.
@@ -204,7 +204,8 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
     if (o.flags & FD_FLAG_COMBINE_KERNEL) want_fused = false;
     const long env_fused = env_long("FD_FUSED", -1);
     if (env_fused == 0 || env_fused == 1) want_fused = env_fused == 1;
-    p->fused = n > 1 && n <= 4L * D && want_fused;
+    const long merge_heads = G < hpb ? G : hpb;
+    p->fused = n > 1 && n * merge_heads <= fdk::kMergeMaxPairsHost && want_fused;
     if (n > 1) {
         const size_t parts = (size_t)B * Hq * (size_t)n;
         const size_t counters = (size_t)B * Hkv * head_blocks * sizeof(unsigned long long);

@@ -54,14 +54,22 @@ __device__ __forceinline__ float ld_agent(const float *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// LDS the epilogue works in: per-wave states, reused for the split weights.
+// Largest heads x splits one fused merge handles (the planner keeps fused
+// plans within it).
+constexpr int kMergeMaxPairs = (int)kMergeMaxPairsHost;
+
+// LDS the epilogue works in: per-wave states, then the fused merge's split
+// maxima / weights, sums and per-split-group partial rows.
 template <int WAVES, int GB, int D>
 struct EpilogueLds {
     float o[WAVES][GB][D];
     float m[WAVES][GB];
     float l[WAVES][GB];
-    float gm[GB];      // combine: global max of each head
-    float gl[GB];      // combine: global normaliser of each head
+    float gm[GB];                  // merge: global max of each head
+    float gl[GB];                  // merge: global normaliser of each head
+    float w[kMergeMaxPairs];       // merge: split maxima, then weights
+    float sl[kMergeMaxPairs];      // merge: split sums
+    float4 red[WAVES * 64];        // merge: per split-group partial rows
     int last;
 };
 
@@ -86,56 +94,115 @@ __device__ __forceinline__ int active_splits(const SplitArgs &a, int Tb) {
 
 // Merge the last workgroup's group: for every valid head g of the block,
 // out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s over the n active
-// splits, read back from the workspace.
+// splits, read back from the workspace.  The loads of the split maxima and
+// sums and of each thread's first PRE partial rows are issued together, so
+// a merge of up to PRE*SG splits costs one memory round trip.  Thread t owns
+// one (head, float4 quad) pair and every SG-th split of it; sums run in
+// split order within a thread and in split-group order across threads
+// (deterministic).  ng * n <= kMergeMaxPairs.
 template <int WAVES, int GB, int D>
 __device__ void combine_group(const SplitArgs &a, EpilogueLds<WAVES, GB, D> &sm, int b, int h0, int ng,
                               int n) {
     constexpr int NT = WAVES * 64;
-    float *w = &sm.o[0][0][0];                       // [GB][n] split weights
-    constexpr int WCAP = WAVES * GB * D;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    // maxima and weights, one wave per head
-    for (int g = wave; g < ng; g += WAVES) {
-        const size_t row = (size_t)(b * a.Hq + h0 + g) * a.n_splits;
-        float M = kEpNegInf;
-        for (int s = lane; s < n; s += 64) {
-            const float m = ld_agent(a.part_m + row + s);
-            w[g * n + s] = m;
-            M = fmaxf(M, m);
-        }
+    constexpr int Q = D / 4;
+    constexpr int PRE = 8;
+    constexpr int MLR = kMergeMaxPairs / NT;            // maxima/sums per thread
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int nml = ng * n;
+    const int pairs = ng * Q;
+    int SG = 1;                                         // split groups per pair:
+    while (SG * 2 * pairs <= NT) SG *= 2;               // a power of two, so NT % SG == 0
+    const int per_pass = NT / SG;                       // pairs per pass
+
+    float mr[MLR], lr[MLR];
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
-        const float mu = M == kEpNegInf ? 0.f : M;
-        float L = 0.f;
-        for (int s = lane; s < n; s += 64) {
-            const float c = ep_exp2(w[g * n + s] - mu);
-            w[g * n + s] = c;
-            L += c * ld_agent(a.part_l + row + s);
+    for (int k = 0; k < MLR; ++k) {
+        const int i = t + k * NT;
+        mr[k] = kEpNegInf;
+        lr[k] = 0.f;
+        if (i < nml) {
+            const int g = i / n, s = i - (i / n) * n;
+            const size_t row = (size_t)(b * a.Hq + h0 + g) * a.n_splits + s;
+            mr[k] = ld_agent(a.part_m + row);
+            lr[k] = ld_agent(a.part_l + row);
         }
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) L += __shfl_xor(L, off);
-        if (lane == 0) { sm.gm[g] = M; sm.gl[g] = L; }
     }
-    __syncthreads();
-    (void)WCAP;
-    for (int idx = threadIdx.x; idx < ng * D; idx += NT) {
-        const int g = idx / D, d = idx - (idx / D) * D;
+    for (int p0 = 0; p0 < pairs; p0 += per_pass) {
+        const int p = p0 + t / SG, sg = t - (t / SG) * SG;
+        const bool active = p < pairs;
+        const int g = active ? p / Q : 0, q = active ? p - (p / Q) * Q : 0;
         const int bh = b * a.Hq + h0 + g;
-        const float *po = a.part_o + (size_t)bh * a.n_splits * D + d;
-        const float *wg = w + g * n;
-        float acc = 0.f;
-        int s = 0;
-        for (; s + 8 <= n; s += 8) {
-            float v[8];
+        const float *po = a.part_o + (size_t)bh * a.n_splits * D + 4 * q;
+        float4 pre[PRE];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) v[j] = ld_agent(po + (size_t)(s + j) * D);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) acc = fmaf(wg[s + j], v[j], acc);
+        for (int j = 0; j < PRE; ++j) {
+            const int s = sg + j * SG;
+            pre[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (active && s < n) {
+                const float *src = po + (size_t)s * D;
+                pre[j] = make_float4(ld_agent(src), ld_agent(src + 1), ld_agent(src + 2), ld_agent(src + 3));
+            }
         }
-        for (; s < n; ++s) acc = fmaf(wg[s], ld_agent(po + (size_t)s * D), acc);
-        const float L = sm.gl[g];
-        a.out[(size_t)bh * D + d] = L > 0.f ? acc / L : 0.f;
-        if (d == 0 && a.lse) a.lse[bh] = L > 0.f ? (sm.gm[g] + log2f(L)) * kEpLn2 : kEpNegInf;
+        if (p0 == 0) {
+            // global max, weights and normaliser of each head (one wave per head)
+#pragma unroll
+            for (int k = 0; k < MLR; ++k) {
+                const int i = t + k * NT;
+                if (i < nml) { sm.w[i] = mr[k]; sm.sl[i] = lr[k]; }
+            }
+            __syncthreads();
+            for (int g2 = wave; g2 < ng; g2 += WAVES) {
+                float M = kEpNegInf;
+                for (int s2 = lane; s2 < n; s2 += 64) M = fmaxf(M, sm.w[g2 * n + s2]);
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+                const float mu = M == kEpNegInf ? 0.f : M;
+                float L = 0.f;
+                for (int s2 = lane; s2 < n; s2 += 64) {
+                    const float c = ep_exp2(sm.w[g2 * n + s2] - mu);
+                    sm.w[g2 * n + s2] = c;
+                    L = fmaf(c, sm.sl[g2 * n + s2], L);
+                }
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) L += __shfl_xor(L, off);
+                if (lane == 0) { sm.gm[g2] = M; sm.gl[g2] = L; }
+            }
+            __syncthreads();
+        }
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (active) {
+            const float *wg = sm.w + g * n;
+            int s = sg;
+#pragma unroll
+            for (int j = 0; j < PRE; ++j, s += SG) {
+                if (s < n) {
+                    const float c = wg[s];
+                    acc.x = fmaf(c, pre[j].x, acc.x); acc.y = fmaf(c, pre[j].y, acc.y);
+                    acc.z = fmaf(c, pre[j].z, acc.z); acc.w = fmaf(c, pre[j].w, acc.w);
+                }
+            }
+            for (; s < n; s += SG) {
+                const float *src = po + (size_t)s * D;
+                const float c = wg[s];
+                acc.x = fmaf(c, ld_agent(src), acc.x); acc.y = fmaf(c, ld_agent(src + 1), acc.y);
+                acc.z = fmaf(c, ld_agent(src + 2), acc.z); acc.w = fmaf(c, ld_agent(src + 3), acc.w);
+            }
+        }
+        sm.red[sg * per_pass + (t / SG)] = acc;
+        __syncthreads();
+        if (active && sg == 0) {
+            float4 r = sm.red[t / SG];
+            for (int k2 = 1; k2 < SG; ++k2) {
+                const float4 v = sm.red[k2 * per_pass + t / SG];
+                r.x += v.x; r.y += v.y; r.z += v.z; r.w += v.w;
+            }
+            const float L = sm.gl[g];
+            const float4 o = L > 0.f ? make_float4(r.x / L, r.y / L, r.z / L, r.w / L)
+                                     : make_float4(0.f, 0.f, 0.f, 0.f);
+            reinterpret_cast<float4 *>(a.out + (size_t)bh * D)[q] = o;
+            if (q == 0 && a.lse) a.lse[bh] = L > 0.f ? (sm.gm[g] + log2f(L)) * kEpLn2 : kEpNegInf;
+        }
+        __syncthreads();
     }
 }
 

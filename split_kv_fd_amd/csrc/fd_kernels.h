@@ -24,6 +24,8 @@ namespace fdk {
 // covers at most kMaxSplitPages pages, so the planner keeps paged chunks at
 // or below kMaxSplitPages * page_size tokens.
 constexpr int kMaxSplitPages = 2048;
+// Largest heads x splits a fused merge handles (its LDS arrays).
+constexpr long kMergeMaxPairsHost = 1024;
 
 // Everything one split launch needs.  Passed by value as the kernel argument.
 struct SplitArgs {

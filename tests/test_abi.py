@@ -77,7 +77,7 @@ def test_plan_covers_sequence_and_respects_tiles(lib):
                 assert p.grid[1] == Hkv * p.head_blocks
                 assert p.heads_per_block * p.head_blocks >= Hq // Hkv
                 assert bool(p.combine) == (p.n_splits > 1)
-                assert not p.fused or (p.combine and p.n_splits <= 4 * D)
+                assert not p.fused or (p.combine and p.n_splits * min(Hq // Hkv, p.heads_per_block) <= 1024)
                 assert not p.fused or B * Hkv * p.head_blocks * p.n_splits <= 512
                 parts = B * Hq * p.n_splits
                 if p.n_splits > 1:
