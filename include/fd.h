@@ -95,7 +95,8 @@ typedef struct fd_options {
 } fd_options_t;
 
 /* What a call with these arguments will launch (see fd_plan).  Paged calls
- * (opt->page_size > 0) are planned as ragged batches: shorter chunks, so
+ * (opt->page_size > 0) are planned as ragged batches: with the automatic
+ * split count (and B <= 2048) in stream mode, else with short chunks, so
  * sequences of very different lengths spread evenly over the device. */
 typedef struct fd_plan {
     int32_t n_splits;           /* effective number of KV splits              */
@@ -111,6 +112,12 @@ typedef struct fd_plan {
     int32_t fused;              /* 1 if fd_decode merges them inside the split */
                                 /* launch (its last workgroup per kv head);   */
                                 /* 0: fd_decode launches the combine kernel   */
+    int32_t stream;             /* 1: balanced stream mode (paged, automatic  */
+                                /* split count): grid[0] workgroups each take */
+                                /* an equal share of all rows' tokens; chunk  */
+                                /* is 0 and n_splits = grid[0]; the merge is  */
+                                /* always inside the split launch             */
+    int32_t reserved;
     size_t workspace_bytes;     /* workspace this call needs (0 if n_splits=1) */
 } fd_plan_t;
 
@@ -152,7 +159,8 @@ size_t fd_workspace_bytes(int B, int Hq, int Hkv, int T, int D, int n_splits,
  *   n_splits            : 0 = automatic, else the requested split count.
  * The workspace (opt->workspace, >= fd_workspace_bytes, 256-byte aligned)
  * holds one arrival counter per (batch, kv head, head block), the partials
- * [B, Hq, n_splits, D] and two [B, Hq, n_splits] rows.  Its contents before
+ * [B, Hq, n_splits, D] and two [B, Hq, n_splits] rows (a stream plan: one
+ * partial slot per (row + workgroup) pair instead).  Its contents before
  * the call do not matter: counters carry a per-call tag, so values left by
  * any earlier call are ignored.  Calls that share a workspace must not
  * overlap in time.
@@ -168,7 +176,8 @@ fd_status_t fd_decode(const void *q, const void *k_cache, const void *v_cache,
  * block"): one workgroup per (batch, kv head, split) streams its chunk of K
  * and V and writes the unnormalised partial, its max and its sum to the
  * workspace.  With a one-split plan it normalises and writes out / lse
- * itself.  Same arguments as fd_decode.
+ * itself; a stream plan always merges inside this launch, so its out / lse
+ * are final.  Same arguments as fd_decode.
  */
 fd_status_t fd_split(const void *q, const void *k_cache, const void *v_cache,
                      const int32_t *page_table, const int32_t *seq_lens,
@@ -177,11 +186,11 @@ fd_status_t fd_split(const void *q, const void *k_cache, const void *v_cache,
                      int n_splits, const fd_options_t *opt);
 
 /*
- * The combine pass alone (tinyvolt, "Combine kernel"): one wavefront per
+ * The combine pass alone (tinyvolt, "Combine kernel"): one workgroup per
  * (batch, query head) merges the partials fd_split left in the workspace by
  * log-sum-exp and writes out / lse.  Must follow fd_split with the same
  * B, Hq, Hkv, T, D, n_splits, seq_lens and options.  A no-op (FD_OK) when
- * the plan has one split.
+ * the plan has one split or is a stream plan (whose split launch merges).
  */
 fd_status_t fd_combine(const int32_t *seq_lens, float *out, float *lse,
                        int B, int Hq, int Hkv, int T, int D, int n_splits,

@@ -115,11 +115,12 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
     if (path == FD_PATH_MFMA && o.dtype == FD_F32)
         return fail(FD_ERR_UNSUPPORTED, "the MFMA path needs f16 or bf16 inputs");
     if (path == FD_PATH_AUTO) {
-        // Measured: the matrix-core kernel wins from G = 4 on contiguous
-        // caches; with paged (ragged) batches, whose short splits expose the
-        // per-workgroup pipeline fill, the VALU kernel's higher occupancy
-        // wins at G = 4.
-        const long min_g = env_long("FD_MFMA_MIN_G", paged ? 8 : 4);
+        // Measured: the matrix-core kernel wins from G = 4.  With an
+        // explicit split count on a paged (ragged) batch, whose short splits
+        // expose the per-workgroup pipeline fill, the VALU kernel's higher
+        // occupancy wins at G = 4; the automatic paged plan uses the
+        // balanced stream mode instead.
+        const long min_g = env_long("FD_MFMA_MIN_G", (paged && n_req > 0) ? 8 : 4);
         path = (o.dtype != FD_F32 && G >= min_g) ? FD_PATH_MFMA : FD_PATH_VALU;
     }
     int hpb, tile;
@@ -139,6 +140,36 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
     if (cus == 0) {
         fd_status_t st = device_cus(&cus);
         if (st != FD_OK) return st;
+    }
+
+    std::memset(p, 0, sizeof *p);
+
+    // Stream mode for ragged (paged) batches: the rows are laid end to end
+    // and cut into one equal range per resident workgroup, so sequences of
+    // any lengths spread evenly and no workgroup is launched for an empty
+    // split.  Taken on the automatic split count only; an explicit n_splits
+    // keeps the split grid.
+    const bool stream = paged && n_req == 0 && B <= fdk::kStreamMaxB && env_long("FD_STREAM", 1) == 1;
+    if (stream) {
+        const long rows = (long)B * Hkv * head_blocks;
+        const long nw = std::max(1L, env_long("FD_STREAM_WGS", 2L * cus));
+        p->n_splits = (int)nw;
+        p->chunk = 0;
+        p->path = path;
+        p->tile = tile;
+        p->heads_per_block = hpb;
+        p->head_blocks = head_blocks;
+        p->grid[0] = (int)nw;
+        p->grid[1] = 1;
+        p->grid[2] = 1;
+        p->block = 256;
+        p->combine = 1;
+        p->fused = 1;
+        p->stream = 1;
+        const size_t slots = (size_t)(rows + nw) * hpb;
+        p->workspace_bytes = align256(rows * sizeof(unsigned long long)) + align256(slots * D * sizeof(float)) +
+                             2 * align256(slots * sizeof(float));
+        return FD_OK;
     }
 
     long gran = tile;
@@ -182,7 +213,6 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
         chunk = (long)fdk::kMaxSplitPages * o.page_size;
     n = ceil_div(T, chunk);
 
-    std::memset(p, 0, sizeof *p);
     p->n_splits = (int)n;
     p->chunk = (int)chunk;
     p->path = path;
@@ -252,7 +282,24 @@ fd_status_t prepare(const void *q, const void *k, const void *v, const int32_t *
 
     float *part_o = nullptr, *part_m = nullptr, *part_l = nullptr;
     unsigned long long *counters = nullptr;
-    if (c->p.n_splits > 1) {
+    if (c->p.stream) {
+        if (!c->o.workspace)
+            return fail(FD_ERR_WORKSPACE, "stream plan: a workspace of %zu bytes is required", c->p.workspace_bytes);
+        if (c->o.workspace_bytes < c->p.workspace_bytes)
+            return fail(FD_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", c->o.workspace_bytes,
+                        c->p.workspace_bytes);
+        if (!aligned(c->o.workspace, 256)) return fail(FD_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+        const size_t rows = (size_t)B * Hkv * c->p.head_blocks;
+        const size_t slots = (rows + (size_t)c->p.n_splits) * c->p.heads_per_block;
+        char *w = static_cast<char *>(c->o.workspace);
+        counters = reinterpret_cast<unsigned long long *>(w);
+        w += align256(rows * sizeof(unsigned long long));
+        part_o = reinterpret_cast<float *>(w);
+        w += align256(slots * D * sizeof(float));
+        part_m = reinterpret_cast<float *>(w);
+        w += align256(slots * sizeof(float));
+        part_l = reinterpret_cast<float *>(w);
+    } else if (c->p.n_splits > 1) {
         if (!c->o.workspace)
             return fail(FD_ERR_WORKSPACE, "plan has %d splits: a workspace of %zu bytes is required",
                         c->p.n_splits, c->p.workspace_bytes);
@@ -290,6 +337,12 @@ fd_status_t prepare(const void *q, const void *k, const void *v, const int32_t *
     s.fused = 0;
     s.epoch = 0;
     s.counters = counters;
+    s.stream = c->p.stream;
+    s.stream_align = c->p.tile;
+    {
+        const int merge_heads = s.G < c->p.heads_per_block ? s.G : c->p.heads_per_block;
+        s.merge_cap = (int)(fdk::kMergeMaxPairsHost / merge_heads);
+    }
 
     fdk::CombineArgs &cb = c->c;
     cb.part_o = part_o; cb.part_m = part_m; cb.part_l = part_l;
@@ -311,6 +364,7 @@ unsigned next_epoch() {
 }
 
 fd_status_t run_split(Call &c, bool fused) {
+    fused = fused || c.p.stream;            // stream mode always merges in the launch
     c.s.fused = fused ? 1 : 0;
     c.s.epoch = fused ? next_epoch() : 0;
     const hipStream_t stream = static_cast<hipStream_t>(c.o.stream);
@@ -321,7 +375,7 @@ fd_status_t run_split(Call &c, bool fused) {
 }
 
 fd_status_t run_combine(const Call &c) {
-    if (c.p.n_splits <= 1) return FD_OK;
+    if (c.p.n_splits <= 1 || c.p.stream) return FD_OK;
     const hipError_t e = fdk::launch_combine(c.c, static_cast<hipStream_t>(c.o.stream));
     if (e != hipSuccess) return hip_fail(e, "launching the combine kernel");
     return FD_OK;

@@ -92,6 +92,31 @@ __device__ __forceinline__ int active_splits(const SplitArgs &a, int Tb) {
     return n < a.n_splits ? n : a.n_splits;
 }
 
+// Where one segment (a split, or a stream range of one row) leaves its
+// result.  Partial row of head g for segment s: base + g*gs + s*ss.
+struct SegOut {
+    int final_out;                 // the segment is the whole row: write out / lse
+    size_t base;
+    int gs, ss, s;
+    int fused;                     // the last arriving segment merges the group
+    unsigned long long *cnt;       // the group's arrival counter
+    int arrivals;                  // segments of the group (its merge count)
+};
+
+__device__ __forceinline__ SegOut split_segment(const SplitArgs &a, int b, int kvh, int hb, int h0,
+                                                int split, int Tb) {
+    SegOut so;
+    so.final_out = a.n_splits == 1;
+    so.base = (size_t)(b * a.Hq + h0) * a.n_splits;
+    so.gs = a.n_splits;
+    so.ss = 1;
+    so.s = split;
+    so.fused = a.fused;
+    so.cnt = a.counters + ((size_t)b * a.Hkv + kvh) * a.head_blocks + hb;
+    so.arrivals = active_splits(a, Tb);
+    return so;
+}
+
 // Merge the last workgroup's group: for every valid head g of the block,
 // out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s over the n active
 // splits, read back from the workspace.  The loads of the split maxima and
@@ -101,8 +126,8 @@ __device__ __forceinline__ int active_splits(const SplitArgs &a, int Tb) {
 // split order within a thread and in split-group order across threads
 // (deterministic).  ng * n <= kMergeMaxPairs.
 template <int WAVES, int GB, int D>
-__device__ void combine_group(const SplitArgs &a, EpilogueLds<WAVES, GB, D> &sm, int b, int h0, int ng,
-                              int n) {
+__device__ void combine_group(const SplitArgs &a, EpilogueLds<WAVES, GB, D> &sm, const SegOut &so, int b,
+                              int h0, int ng, int n) {
     constexpr int NT = WAVES * 64;
     constexpr int Q = D / 4;
     constexpr int PRE = 8;
@@ -122,7 +147,7 @@ __device__ void combine_group(const SplitArgs &a, EpilogueLds<WAVES, GB, D> &sm,
         lr[k] = 0.f;
         if (i < nml) {
             const int g = i / n, s = i - (i / n) * n;
-            const size_t row = (size_t)(b * a.Hq + h0 + g) * a.n_splits + s;
+            const size_t row = so.base + (size_t)g * so.gs + (size_t)s * so.ss;
             mr[k] = ld_agent(a.part_m + row);
             lr[k] = ld_agent(a.part_l + row);
         }
@@ -132,14 +157,15 @@ __device__ void combine_group(const SplitArgs &a, EpilogueLds<WAVES, GB, D> &sm,
         const bool active = p < pairs;
         const int g = active ? p / Q : 0, q = active ? p - (p / Q) * Q : 0;
         const int bh = b * a.Hq + h0 + g;
-        const float *po = a.part_o + (size_t)bh * a.n_splits * D + 4 * q;
+        const float *po = a.part_o + (so.base + (size_t)g * so.gs) * D + 4 * q;
+        const size_t srow = (size_t)so.ss * D;
         float4 pre[PRE];
 #pragma unroll
         for (int j = 0; j < PRE; ++j) {
             const int s = sg + j * SG;
             pre[j] = make_float4(0.f, 0.f, 0.f, 0.f);
             if (active && s < n) {
-                const float *src = po + (size_t)s * D;
+                const float *src = po + (size_t)s * srow;
                 pre[j] = make_float4(ld_agent(src), ld_agent(src + 1), ld_agent(src + 2), ld_agent(src + 3));
             }
         }
@@ -182,7 +208,7 @@ __device__ void combine_group(const SplitArgs &a, EpilogueLds<WAVES, GB, D> &sm,
                 }
             }
             for (; s < n; s += SG) {
-                const float *src = po + (size_t)s * D;
+                const float *src = po + (size_t)s * srow;
                 const float c = wg[s];
                 acc.x = fmaf(c, ld_agent(src), acc.x); acc.y = fmaf(c, ld_agent(src + 1), acc.y);
                 acc.z = fmaf(c, ld_agent(src + 2), acc.z); acc.w = fmaf(c, ld_agent(src + 3), acc.w);
@@ -207,11 +233,11 @@ __device__ void combine_group(const SplitArgs &a, EpilogueLds<WAVES, GB, D> &sm,
 }
 
 // Called by every thread after sm.o / sm.m / sm.l hold each wave's state
-// (the caller has synchronised).  Writes this split's result and, in fused
+// (the caller has synchronised).  Writes this segment's result and, in fused
 // mode, completes the group when this workgroup arrives last.
 template <int WAVES, int GB, int D>
-__device__ void finish_split(const SplitArgs &a, EpilogueLds<WAVES, GB, D> &sm, int b, int kvh, int hb,
-                             int split, int h0, int ng, int Tb) {
+__device__ void finish_split(const SplitArgs &a, EpilogueLds<WAVES, GB, D> &sm, const SegOut &so, int b,
+                             int h0, int ng) {
     constexpr int NT = WAVES * 64;
     for (int idx = threadIdx.x; idx < ng * D; idx += NT) {
         const int g = idx / D, d = idx - (idx / D) * D;
@@ -227,33 +253,135 @@ __device__ void finish_split(const SplitArgs &a, EpilogueLds<WAVES, GB, D> &sm, 
             L += c * sm.l[w][g];
         }
         const int bh = b * a.Hq + h0 + g;
-        if (a.n_splits == 1) {
+        const size_t pi = so.base + (size_t)g * so.gs + (size_t)so.s * so.ss;
+        if (so.final_out) {
             a.out[(size_t)bh * D + d] = L > 0.f ? acc / L : 0.f;
             if (d == 0 && a.lse) a.lse[bh] = L > 0.f ? (M + log2f(L)) * kEpLn2 : kEpNegInf;
-        } else if (a.fused) {
-            const size_t pi = (size_t)bh * a.n_splits + split;
+        } else if (so.fused) {
             st_agent(a.part_o + pi * D + d, acc);
             if (d == 0) { st_agent(a.part_m + pi, M); st_agent(a.part_l + pi, L); }
         } else {
-            const size_t pi = (size_t)bh * a.n_splits + split;
             a.part_o[pi * D + d] = acc;
             if (d == 0) { a.part_m[pi] = M; a.part_l[pi] = L; }
         }
     }
-    if (a.n_splits == 1 || !a.fused) return;
+    if (so.final_out || !so.fused) return;
 
     // Fused combine: every thread's coherent partial stores complete
     // (vmcnt 0), the barrier gathers the workgroup, one exchange counts the
     // arrival, and the workgroup that completes the group merges its splits.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (threadIdx.x == 0) {
-        unsigned long long *cnt = a.counters + (size_t)b * a.Hkv * a.head_blocks + (size_t)kvh * a.head_blocks + hb;
-        sm.last = arrive_last(cnt, a.epoch, active_splits(a, Tb)) ? 1 : 0;
-    }
+    if (threadIdx.x == 0) sm.last = arrive_last(so.cnt, a.epoch, so.arrivals) ? 1 : 0;
     __syncthreads();
     if (!sm.last) return;
-    combine_group<WAVES, GB, D>(a, sm, b, h0, ng, active_splits(a, Tb));
+    combine_group<WAVES, GB, D>(a, sm, so, b, h0, ng, so.arrivals);
+}
+
+// Stream mode.  Rows (batch, kv head, head block) are padded to
+// a.stream_align tokens and laid end to end; workgroup w takes the stream
+// range [w*per, (w+1)*per), which may cover the end of one row, whole rows
+// and the start of another.  Every workgroup scans the sequence lengths to
+// find its range (B <= kStreamMaxB).  The segment of row r taken by
+// workgroup w writes partial slot r + w (distinct for all rows and
+// workgroups, and consecutive within a row); a row's last arriving segment
+// merges it, and a row covered by one segment writes out directly.
+// `seg(b, kvh, hb, c0, c1, so)` runs one segment (tokens [c0, c1) of the
+// row; c0 == c1 for a range that only covers padding).  Sequences of
+// length 0 have no segments: their outputs are written here.
+template <int NT, int D, typename Seg>
+__device__ void drive_stream(const SplitArgs &a, long long *pref, int hpb, Seg &&seg) {
+    const int t = threadIdx.x;
+    const int RB = a.Hkv * a.head_blocks;             // rows per sequence
+    const int align = a.stream_align;
+    auto real_len = [&](int b) {
+        int Tb = a.seq_lens ? a.seq_lens[b] : a.T;
+        return Tb < 0 ? 0 : (Tb > a.T ? a.T : Tb);
+    };
+    auto pad_len = [&](int b) { return (long long)((real_len(b) + align - 1) / align) * align; };
+
+    // exclusive prefix over sequences of RB * padded length, and the longest row
+    __shared__ long long s_scan[NT];
+    __shared__ long long s_max[NT];
+    long long carry = 0, lmax = 0;
+    for (int c = 0; c < a.B; c += NT) {
+        const int b = c + t;
+        const long long v = b < a.B ? pad_len(b) : 0;
+        lmax = v > lmax ? v : lmax;
+        s_scan[t] = v * RB;
+        __syncthreads();
+        for (int off = 1; off < NT; off <<= 1) {
+            const long long x = t >= off ? s_scan[t - off] : 0;
+            __syncthreads();
+            s_scan[t] += x;
+            __syncthreads();
+        }
+        if (b < a.B) pref[b + 1] = carry + s_scan[t];
+        carry += s_scan[NT - 1];
+        __syncthreads();
+    }
+    s_max[t] = lmax;
+    if (t == 0) pref[0] = 0;
+    __syncthreads();
+    for (int off = NT / 2; off > 0; off >>= 1) {
+        if (t < off) s_max[t] = s_max[t] > s_max[t + off] ? s_max[t] : s_max[t + off];
+        __syncthreads();
+    }
+    const long long total = pref[a.B];
+    const long long longest = s_max[0];
+    const int w = blockIdx.x, NW = gridDim.x;
+    long long per = (total + NW - 1) / NW;
+    // keep every row within merge_cap segments
+    const long long min_per = (longest + a.merge_cap - 2) / (a.merge_cap - 1);
+    per = per > min_per ? per : min_per;
+    per = (per + align - 1) / align * align;
+    if (per < align) per = align;
+
+    // sequences of length 0: out = 0, lse = -inf
+    for (int b = w; b < a.B; b += NW)
+        if (real_len(b) == 0)
+            for (int idx = t; idx < a.Hq * D; idx += NT) {
+                const int h = idx / D, d = idx - (idx / D) * D;
+                a.out[((size_t)b * a.Hq + h) * D + d] = 0.f;
+                if (d == 0 && a.lse) a.lse[(size_t)b * a.Hq + h] = kEpNegInf;
+            }
+
+    const long long g0 = (long long)w * per;
+    const long long g1 = g0 + per < total ? g0 + per : total;
+    if (g0 >= g1) return;
+    // the sequence holding stream position g0: the last b with pref[b] <= g0
+    int lo = 0, hi = a.B - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (pref[mid] <= g0) lo = mid; else hi = mid - 1;
+    }
+    for (int b = lo; b < a.B && pref[b] < g1; ++b) {
+        const long long lb = pad_len(b);
+        if (lb == 0) continue;
+        const int Tb = real_len(b);
+        long long k = g0 > pref[b] ? (g0 - pref[b]) / lb : 0;
+        for (; k < RB; ++k) {
+            const long long rs = pref[b] + k * lb;     // row start in the stream
+            if (rs >= g1) return;
+            const long long c0 = g0 > rs ? g0 - rs : 0;
+            const long long c1p = g1 - rs < lb ? g1 - rs : lb;
+            const int c1 = (int)(c1p < Tb ? c1p : Tb);
+            const int r = b * RB + (int)k;
+            const int kvh = (int)k / a.head_blocks, hb = (int)k - kvh * a.head_blocks;
+            const long long wf = rs / per, wl = (rs + lb - 1) / per;
+            SegOut so;
+            so.final_out = wf == wl;
+            so.base = (size_t)(r + wf) * hpb;
+            so.gs = 1;
+            so.ss = hpb;
+            so.s = (int)(w - wf);
+            so.fused = 1;
+            so.cnt = a.counters + r;
+            so.arrivals = (int)(wl - wf + 1);
+            __syncthreads();                       // LDS of the previous segment is free
+            seg(b, kvh, hb, (int)c0, c1 > (int)c0 ? c1 : (int)c0, so);
+        }
+    }
 }
 
 }  // namespace fdk

@@ -46,8 +46,16 @@ struct SplitArgs {
     float scale_log2;            // scale * log2(e): logits in base-2 units
     int fused;                   // last workgroup of a group merges its splits
     unsigned epoch;              // per-call tag of the arrival counters
-    unsigned long long *counters;  // [B, Hkv, head_blocks] arrival counters
+    unsigned long long *counters;  // arrival counters, one per group (row)
+    // Stream mode (ragged batches): rows padded to stream_align tokens and
+    // laid end to end, one equal range per workgroup (gridDim.x of them).
+    int stream;
+    int stream_align;
+    int merge_cap;               // most segments one row may have (fused merge)
 };
+
+// Most sequences a stream-mode launch handles (its LDS prefix array).
+constexpr int kStreamMaxB = 2048;
 
 struct CombineArgs {
     const float *part_o;

@@ -101,8 +101,10 @@ __device__ __forceinline__ uint2 load_piece<uint2>(const char *p) {
 
 // PG: 0 contiguous cache, 1 paged with per-token page lookups (pages under
 // 16 tokens), 2 paged with one lookup per 16-token block (pages of 16+).
-template <int DT, int D, int PG>
-__global__ __launch_bounds__(256) void split_mfma(SplitArgs a) {
+// STREAM: balanced stream mode (ragged batches), else one workgroup per
+// (batch, kv head, head block, split).
+template <int DT, int D, int PG, bool STREAM>
+__global__ __launch_bounds__(256, 2) void split_mfma(SplitArgs a) {
     constexpr bool PAGED = PG != 0;
     constexpr int EB = 2;
     constexpr int ROWB = D * EB;
@@ -117,213 +119,251 @@ __global__ __launch_bounds__(256) void split_mfma(SplitArgs a) {
     using VP = typename std::conditional<VB == 16, uint4, uint2>::type;
     using Off = typename std::conditional<PAGED, size_t, uint32_t>::type;
 
-    const int split = blockIdx.x;
-    const int kvh = blockIdx.y / a.head_blocks;
-    const int hb = blockIdx.y - kvh * a.head_blocks;
-    const int b = blockIdx.z;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
     const int i16 = lane & 15;
     const int kb = lane >> 4;
 
-    int Tb = a.T;
-    if (a.seq_lens) {
-        Tb = a.seq_lens[b];
-        Tb = Tb < 0 ? 0 : (Tb > a.T ? a.T : Tb);
-    }
-    const int c0 = split * a.chunk;
-    const int c1 = min(c0 + a.chunk, Tb);
-    const int g0 = hb * GB;
-    const int ng = min(GB, a.G - g0);
-    const int h0 = kvh * a.G + g0;
-    if (a.n_splits > 1 && c0 >= Tb) {          // empty split: never counted or read
-        if (a.fused && split == 0) write_empty_group<D>(a, b, h0, ng);
-        return;
-    }
-
-    // B operand of the logit MFMAs: q pieces 4*ks + kb of head i16.
-    uint4 qb[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        qb[ks] = make_uint4(0, 0, 0, 0);
-        if (i16 < ng)
-            qb[ks] = *reinterpret_cast<const uint4 *>(static_cast<const char *>(a.q) +
-                                                       (size_t)(b * a.Hq + h0 + i16) * ROWB + (4 * ks + kb) * 16);
-    }
-
-    f32x4_v acc[PVE];
-#pragma unroll
-    for (int i = 0; i < PVE; ++i) acc[i] = f32x4_v{0.f, 0.f, 0.f, 0.f};
-    float m = kNegInf, l = 0.f;
-
-    const char *kbase = static_cast<const char *>(a.k);
-    const char *vbase = static_cast<const char *>(a.v);
-    if constexpr (!PAGED) {
-        const size_t seq = (size_t)(b * a.Hkv + kvh) * (size_t)a.T * ROWB;
-        kbase += seq;
-        vbase += seq;
-    }
-    // Paged: this split's page ids, staged once in LDS so that no K/V load
-    // waits on a dependent page-table read (ids outside the pool become -1).
     __shared__ int s_pages[PAGED ? kMaxSplitPages : 1];
-    const int p0 = PAGED ? (c0 >> a.page_shift) : 0;
-    if constexpr (PAGED) {
-        const int npg = c1 > c0 ? ((c1 - 1) >> a.page_shift) - p0 + 1 : 0;
-        for (int i = threadIdx.x; i < npg; i += 64 * WAVES) {
-            const int pg = a.page_table[(size_t)b * a.max_pages + p0 + i];
-            s_pages[i] = (unsigned)pg < (unsigned)a.num_pages ? pg : -1;
-        }
-        __syncthreads();
-    }
-    auto row_offset = [&](int t, bool &ok) -> Off {
-        ok = t < c1;
-        const int tc = ok ? t : c1 - 1;        // clamped: always a valid token
-        if constexpr (PAGED) {
-            int page = s_pages[(tc >> a.page_shift) - p0];
-            if (page < 0) { ok = false; page = 0; }
-            return (((size_t)page * a.Hkv + kvh) * a.page_size + (tc & (a.page_size - 1))) * ROWB;
-        } else {
-            return (uint32_t)tc * (uint32_t)ROWB;
-        }
-    };
-
-    struct Buf {
-        uint4 k[2][KS];
-        VP v[2][4];
-        bool ok[2][4];
-    };
-
-    // Pages of 16 tokens or more: a 16-token block (16-aligned, as every
-    // split starts on a multiple of the tile) lies in one page, so one page
-    // lookup serves the block's K and V rows.  The page is the same for the
-    // whole wave, so the block's base address is kept in scalar registers and
-    // each lane adds a fixed 32-bit offset -- the same load form as the
-    // contiguous path (64-bit per-lane addresses measurably cut the number of
-    // loads a wave keeps in flight).  A block past the split end is
-    // redirected to the split's last block; its rows are read but masked.
-    constexpr bool block_pages = PG == 2;
-    const uint32_t k_lane = (uint32_t)(i16 * ROWB + kb * 16);         // + 64 * ks
-    const uint32_t v_lane = (uint32_t)(4 * kb * ROWB + i16 * VB);     // + ROWB * r
-    auto block_base = [&](int t16, bool &page_ok) -> size_t {
-        const int tcl = t16 < c1 ? t16 : ((c1 - 1) & ~15);
-        int page = __builtin_amdgcn_readfirstlane(s_pages[(tcl >> a.page_shift) - p0]);
-        page_ok = page >= 0;
-        page = page_ok ? page : 0;
-        return (((size_t)page * a.Hkv + kvh) * a.page_size + (tcl & (a.page_size - 1))) * ROWB;
-    };
-
-    auto load_step = [&](int base, Buf &f) {
-        const int tb = base + wave * TOK;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int t16 = tb + 16 * h;
-            if constexpr (block_pages) {
-                bool pok;
-                const size_t bo = block_base(t16, pok);
-                const char *kblk = kbase + bo;
-                const char *vblk = vbase + bo;
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    f.k[h][ks] = load_piece<uint4>(kblk + (k_lane + (uint32_t)(64 * ks)));
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    f.ok[h][r] = pok && (t16 + 4 * kb + r < c1);
-                    f.v[h][r] = load_piece<VP>(vblk + (v_lane + (uint32_t)(ROWB * r)));
-                }
-            } else {
-                bool okk;
-                const Off ko = row_offset(t16 + i16, okk);
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    f.k[h][ks] = load_piece<uint4>(kbase + (ko + (Off)((4 * ks + kb) * 16)));
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const Off vo = row_offset(t16 + 4 * kb + r, f.ok[h][r]);
-                    f.v[h][r] = load_piece<VP>(vbase + (vo + (Off)(i16 * VB)));
-                }
-            }
-        }
-    };
-
-    auto consume_step = [&](const Buf &f) {
-        float s[2][4];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            f32x4_v c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) c = mfma_logits<DT>(f.k[h][ks], qb[ks], c);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) s[h][r] = f.ok[h][r] ? c[r] * a.scale_log2 : kNegInf;
-        }
-        float mt = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                         fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-        mt = fmaxf(mt, __shfl_xor(mt, 16));
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const float mn = fmaxf(m, mt);
-        const float mu = mn == kNegInf ? 0.f : mn;
-        const float alpha = __builtin_amdgcn_exp2f(m - mu);
-        float p[2][4];
-        float ps = 0.f;
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) { p[h][r] = __builtin_amdgcn_exp2f(s[h][r] - mu); ps += p[h][r]; }
-        l = l * alpha + ps;
-        m = mn;
-#pragma unroll
-        for (int i = 0; i < PVE; ++i) acc[i] *= alpha;
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float vf[PVE];
-                widen<DT>(f.v[h][r], vf);
-#pragma unroll
-                for (int i = 0; i < PVE; ++i)
-                    acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[i], p[h][r], acc[i], 0, 0, 0);
-            }
-    };
-
-    if (c0 < c1) {
-        Buf fa, fb;
-        load_step(c0, fa);
-        for (int base = c0;; base += 2 * TILE) {
-            load_step(base + TILE, fb);            // clamped past the end
-            asm volatile("" ::: "memory");
-            __builtin_amdgcn_sched_barrier(0);
-            consume_step(fa);
-            if (base + TILE >= c1) break;
-            load_step(base + 2 * TILE, fa);
-            asm volatile("" ::: "memory");
-            __builtin_amdgcn_sched_barrier(0);
-            consume_step(fb);
-            if (base + 2 * TILE >= c1) break;
-        }
-    }
-
-    // The four lanes of a head share m; their sums cover different tokens.
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-
     __shared__ EpilogueLds<WAVES, GB, D> sm;
+
+    // One segment: tokens [c0, c1) of row (b, kvh, hb) into `so`.
+    auto segment = [&](int b, int kvh, int hb, int c0, int c1, const SegOut &so) {
+        const int g0 = hb * GB;
+        const int ng = min(GB, a.G - g0);
+        const int h0 = kvh * a.G + g0;
+
+        // B operand of the logit MFMAs: q pieces 4*ks + kb of head i16.
+        uint4 qb[KS];
 #pragma unroll
-    for (int i = 0; i < PVE; ++i)
+        for (int ks = 0; ks < KS; ++ks) {
+            qb[ks] = make_uint4(0, 0, 0, 0);
+            if (i16 < ng)
+                qb[ks] = *reinterpret_cast<const uint4 *>(static_cast<const char *>(a.q) +
+                                                           (size_t)(b * a.Hq + h0 + i16) * ROWB +
+                                                           (4 * ks + kb) * 16);
+        }
+
+        f32x4_v acc[PVE];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sm.o[wave][i16][PVE * (4 * kb + r) + i] = acc[i][r];
-    if (kb == 0) { sm.m[wave][i16] = m; sm.l[wave][i16] = l; }
-    __syncthreads();
-    finish_split<WAVES, GB, D>(a, sm, b, kvh, hb, split, h0, ng, Tb);
+        for (int i = 0; i < PVE; ++i) acc[i] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+        float m = kNegInf, l = 0.f;
+
+        const char *kbase = static_cast<const char *>(a.k);
+        const char *vbase = static_cast<const char *>(a.v);
+        if constexpr (!PAGED) {
+            const size_t seq = (size_t)(b * a.Hkv + kvh) * (size_t)a.T * ROWB;
+            kbase += seq;
+            vbase += seq;
+        }
+
+        // Paged: page ids of the range being streamed, staged in LDS so that
+        // no K/V load waits on a dependent page-table read (ids outside the
+        // pool become -1).  A range spans at most kMaxSplitPages pages.
+        int p0 = 0;
+        auto stage_pages = [&](int r0, int r1) {
+            if constexpr (PAGED) {
+                p0 = r0 >> a.page_shift;
+                const int npg = r1 > r0 ? ((r1 - 1) >> a.page_shift) - p0 + 1 : 0;
+                __syncthreads();
+                for (int i = threadIdx.x; i < npg; i += 64 * WAVES) {
+                    const int pg = a.page_table[(size_t)b * a.max_pages + p0 + i];
+                    s_pages[i] = (unsigned)pg < (unsigned)a.num_pages ? pg : -1;
+                }
+                __syncthreads();
+            }
+        };
+
+        auto stream_range = [&](int r0, int r1) {
+            auto row_offset = [&](int t, bool &ok) -> Off {
+                ok = t < r1;
+                const int tc = ok ? t : r1 - 1;        // clamped: always a valid token
+                if constexpr (PAGED) {
+                    int page = s_pages[(tc >> a.page_shift) - p0];
+                    if (page < 0) { ok = false; page = 0; }
+                    return (((size_t)page * a.Hkv + kvh) * a.page_size + (tc & (a.page_size - 1))) * ROWB;
+                } else {
+                    return (uint32_t)tc * (uint32_t)ROWB;
+                }
+            };
+
+            struct Buf {
+                uint4 k[2][KS];
+                VP v[2][4];
+                bool ok[2][4];
+            };
+
+            // Pages of 16 tokens or more: a 16-token block (16-aligned, as every
+            // range starts on a multiple of the tile) lies in one page, so one
+            // page lookup serves the block's K and V rows.  The page is the
+            // same for the whole wave, so the block's base address is kept in
+            // scalar registers and each lane adds a fixed 32-bit offset -- the
+            // same load form as the contiguous path.  A block past the range
+            // end is redirected to the range's last block; its rows are read
+            // but masked.
+            constexpr bool block_pages = PG == 2;
+            const uint32_t k_lane = (uint32_t)(i16 * ROWB + kb * 16);         // + 64 * ks
+            const uint32_t v_lane = (uint32_t)(4 * kb * ROWB + i16 * VB);     // + ROWB * r
+            auto block_base = [&](int t16, bool &page_ok) -> size_t {
+                const int tcl = t16 < r1 ? t16 : ((r1 - 1) & ~15);
+                int page = __builtin_amdgcn_readfirstlane(s_pages[(tcl >> a.page_shift) - p0]);
+                page_ok = page >= 0;
+                page = page_ok ? page : 0;
+                return (((size_t)page * a.Hkv + kvh) * a.page_size + (tcl & (a.page_size - 1))) * ROWB;
+            };
+
+            auto load_step = [&](int base, Buf &f) {
+                const int tb = base + wave * TOK;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int t16 = tb + 16 * h;
+                    if constexpr (block_pages) {
+                        bool pok;
+                        const size_t bo = block_base(t16, pok);
+                        const char *kblk = kbase + bo;
+                        const char *vblk = vbase + bo;
+#pragma unroll
+                        for (int ks = 0; ks < KS; ++ks)
+                            f.k[h][ks] = load_piece<uint4>(kblk + (k_lane + (uint32_t)(64 * ks)));
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            f.ok[h][r] = pok && (t16 + 4 * kb + r < r1);
+                            f.v[h][r] = load_piece<VP>(vblk + (v_lane + (uint32_t)(ROWB * r)));
+                        }
+                    } else {
+                        bool okk;
+                        const Off ko = row_offset(t16 + i16, okk);
+#pragma unroll
+                        for (int ks = 0; ks < KS; ++ks)
+                            f.k[h][ks] = load_piece<uint4>(kbase + (ko + (Off)((4 * ks + kb) * 16)));
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const Off vo = row_offset(t16 + 4 * kb + r, f.ok[h][r]);
+                            f.v[h][r] = load_piece<VP>(vbase + (vo + (Off)(i16 * VB)));
+                        }
+                    }
+                }
+            };
+
+            auto consume_step = [&](const Buf &f) {
+                float s[2][4];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    f32x4_v c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) c = mfma_logits<DT>(f.k[h][ks], qb[ks], c);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) s[h][r] = f.ok[h][r] ? c[r] * a.scale_log2 : kNegInf;
+                }
+                float mt = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                                 fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+                mt = fmaxf(mt, __shfl_xor(mt, 16));
+                mt = fmaxf(mt, __shfl_xor(mt, 32));
+                const float mn = fmaxf(m, mt);
+                const float mu = mn == kNegInf ? 0.f : mn;
+                const float alpha = __builtin_amdgcn_exp2f(m - mu);
+                float p[2][4];
+                float ps = 0.f;
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) { p[h][r] = __builtin_amdgcn_exp2f(s[h][r] - mu); ps += p[h][r]; }
+                l = l * alpha + ps;
+                m = mn;
+#pragma unroll
+                for (int i = 0; i < PVE; ++i) acc[i] *= alpha;
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        float vf[PVE];
+                        widen<DT>(f.v[h][r], vf);
+#pragma unroll
+                        for (int i = 0; i < PVE; ++i)
+                            acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[i], p[h][r], acc[i], 0, 0, 0);
+                    }
+            };
+
+            Buf fa, fb;
+            load_step(r0, fa);
+            for (int base = r0;; base += 2 * TILE) {
+                load_step(base + TILE, fb);            // clamped past the end
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+                consume_step(fa);
+                if (base + TILE >= r1) break;
+                load_step(base + 2 * TILE, fa);
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+                consume_step(fb);
+                if (base + 2 * TILE >= r1) break;
+            }
+        };
+
+        if constexpr (PAGED) {
+            // ranges of at most kMaxSplitPages pages: each ends on a page
+            // boundary, so a start inside a page still fits the stage
+            for (int r0 = c0, r1; r0 < c1; r0 = r1) {
+                const long long e = ((long long)(r0 >> a.page_shift) + kMaxSplitPages) << a.page_shift;
+                r1 = e < c1 ? (int)e : c1;
+                stage_pages(r0, r1);
+                stream_range(r0, r1);
+            }
+        } else {
+            if (c0 < c1) stream_range(c0, c1);
+        }
+
+        // The four lanes of a head share m; their sums cover different tokens.
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+
+        __syncthreads();                               // sm is free (previous segment)
+#pragma unroll
+        for (int i = 0; i < PVE; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sm.o[wave][i16][PVE * (4 * kb + r) + i] = acc[i][r];
+        if (kb == 0) { sm.m[wave][i16] = m; sm.l[wave][i16] = l; }
+        __syncthreads();
+        finish_split<WAVES, GB, D>(a, sm, so, b, h0, ng);
+    };
+
+    if constexpr (STREAM) {
+        __shared__ long long s_pref[kStreamMaxB + 1];
+        drive_stream<64 * WAVES, D>(a, s_pref, GB, segment);
+    } else {
+        const int split = blockIdx.x;
+        const int kvh = blockIdx.y / a.head_blocks;
+        const int hb = blockIdx.y - kvh * a.head_blocks;
+        const int b = blockIdx.z;
+        int Tb = a.T;
+        if (a.seq_lens) {
+            Tb = a.seq_lens[b];
+            Tb = Tb < 0 ? 0 : (Tb > a.T ? a.T : Tb);
+        }
+        const int c0 = split * a.chunk;
+        const int c1 = min(c0 + a.chunk, Tb);
+        const int h0 = kvh * a.G + hb * GB;
+        if (a.n_splits > 1 && c0 >= Tb) {          // empty split: never counted or read
+            if (a.fused && split == 0) write_empty_group<D>(a, b, h0, min(GB, a.G - hb * GB));
+            return;
+        }
+        segment(b, kvh, hb, c0, c1 > c0 ? c1 : c0, split_segment(a, b, kvh, hb, h0, split, Tb));
+    }
 }
 
 template <int DT, int D>
 hipError_t launch_dim(const SplitArgs &a, hipStream_t stream) {
-    const dim3 grid(a.n_splits, a.Hkv * a.head_blocks, a.B);
-    if (!a.page_table)
-        hipLaunchKernelGGL((split_mfma<DT, D, 0>), grid, dim3(256), 0, stream, a);
-    else if (a.page_size >= 16)
-        hipLaunchKernelGGL((split_mfma<DT, D, 2>), grid, dim3(256), 0, stream, a);
-    else
-        hipLaunchKernelGGL((split_mfma<DT, D, 1>), grid, dim3(256), 0, stream, a);
+    const dim3 grid = a.stream ? dim3(a.n_splits) : dim3(a.n_splits, a.Hkv * a.head_blocks, a.B);
+    const int pg = !a.page_table ? 0 : (a.page_size >= 16 ? 2 : 1);
+    if (a.stream) {
+        if (pg == 2) hipLaunchKernelGGL((split_mfma<DT, D, 2, true>), grid, dim3(256), 0, stream, a);
+        else if (pg == 1) hipLaunchKernelGGL((split_mfma<DT, D, 1, true>), grid, dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((split_mfma<DT, D, 0, true>), grid, dim3(256), 0, stream, a);
+    } else {
+        if (pg == 2) hipLaunchKernelGGL((split_mfma<DT, D, 2, false>), grid, dim3(256), 0, stream, a);
+        else if (pg == 1) hipLaunchKernelGGL((split_mfma<DT, D, 1, false>), grid, dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((split_mfma<DT, D, 0, false>), grid, dim3(256), 0, stream, a);
+    }
     return hipGetLastError();
 }
 

@@ -113,7 +113,9 @@ __device__ __forceinline__ uint4 load16(const char *p) {
 #endif
 }
 
-template <int DT, int D, int GB, bool PAGED>
+// STREAM: balanced stream mode (ragged batches), else one workgroup per
+// (batch, kv head, head block, split).
+template <int DT, int D, int GB, bool PAGED, bool STREAM>
 __global__ __launch_bounds__(256) void split_valu(SplitArgs a) {
     constexpr int EB = DT == FD_F32 ? 4 : 2;
     using S = ValuShape<EB, D, GB>;
@@ -122,206 +124,242 @@ __global__ __launch_bounds__(256) void split_valu(SplitArgs a) {
     constexpr int ROWB = S::ROWB;
     static_assert(WAVES * 64 == 256, "launch bounds assume 256 threads");
 
-    const int split = blockIdx.x;
-    const int kvh = blockIdx.y / a.head_blocks;
-    const int hb = blockIdx.y - kvh * a.head_blocks;
-    const int b = blockIdx.z;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
     const int row = lane / LPR;
     const int sub = lane % LPR;
 
-    int Tb = a.T;
-    if (a.seq_lens) {
-        Tb = a.seq_lens[b];
-        Tb = Tb < 0 ? 0 : (Tb > a.T ? a.T : Tb);
-    }
-    const int c0 = split * a.chunk;
-    const int c1 = min(c0 + a.chunk, Tb);
-    const int g0 = hb * GB;
-    const int ng = min(GB, a.G - g0);          // valid query heads in this block
-    const int h0 = kvh * a.G + g0;
-    if (a.n_splits > 1 && c0 >= Tb) {          // empty split: never counted or read
-        if (a.fused && split == 0) write_empty_group<D>(a, b, h0, ng);
-        return;
-    }
-
-    // This lane's pieces of the query rows (raw storage words).
-    uint4 qv[GB][VEC];
-#pragma unroll
-    for (int g = 0; g < GB; ++g)
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) {
-            qv[g][v] = make_uint4(0, 0, 0, 0);
-            if (g < ng)
-                qv[g][v] = load16(static_cast<const char *>(a.q) +
-                                  (size_t)(b * a.Hq + h0 + g) * ROWB + (v * LPR + sub) * 16);
-        }
-
-    float m[GB], l[GB], o[GB][EPT];
-#pragma unroll
-    for (int g = 0; g < GB; ++g) {
-        m[g] = kNegInf;
-        l[g] = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPT; ++e) o[g][e] = 0.f;
-    }
-
-    const char *kb = static_cast<const char *>(a.k);
-    const char *vb = static_cast<const char *>(a.v);
-    if constexpr (!PAGED) {
-        const size_t seq = (size_t)(b * a.Hkv + kvh) * (size_t)a.T * ROWB;
-        kb += seq;
-        vb += seq;
-    }
-
-    // Paged: this split's page ids, staged once in LDS so that no K/V load
-    // waits on a dependent page-table read (ids outside the pool become -1).
     __shared__ int s_pages[PAGED ? kMaxSplitPages : 1];
-    const int p0 = PAGED ? (c0 >> a.page_shift) : 0;
-    if constexpr (PAGED) {
-        const int npg = c1 > c0 ? ((c1 - 1) >> a.page_shift) - p0 + 1 : 0;
-        for (int i = threadIdx.x; i < npg; i += 64 * WAVES) {
-            const int pg = a.page_table[(size_t)b * a.max_pages + p0 + i];
-            s_pages[i] = (unsigned)pg < (unsigned)a.num_pages ? pg : -1;
-        }
-        __syncthreads();
-    }
+    __shared__ EpilogueLds<WAVES, GB, D> sm;
 
-    // Byte offset of token t's row and whether the token is real.  A
-    // contiguous (batch, kv head) slice is below 4 GiB (checked on the host),
-    // so its offsets are 32-bit: the loads then take a scalar base address
-    // plus one vector register.
-    using Off = typename std::conditional<PAGED, size_t, uint32_t>::type;
-    auto row_offset = [&](int t, bool &ok) -> Off {
-        ok = t < c1;
-        const int tc = ok ? t : c1 - 1;        // clamped: always a valid token
-        if constexpr (PAGED) {
-            int page = s_pages[(tc >> a.page_shift) - p0];
-            if (page < 0) { ok = false; page = 0; }
-            return (((size_t)page * a.Hkv + kvh) * a.page_size + (tc & (a.page_size - 1))) * ROWB;
-        } else {
-            return (uint32_t)tc * (uint32_t)ROWB;
-        }
-    };
+    // One segment: tokens [c0, c1) of row (b, kvh, hb) into `so`.
+    auto segment = [&](int b, int kvh, int hb, int c0, int c1, const SegOut &so) {
+        const int g0 = hb * GB;
+        const int ng = min(GB, a.G - g0);          // valid query heads in this block
+        const int h0 = kvh * a.G + g0;
 
-    auto load_step = [&](int base, uint4 (&kr)[U][VEC], uint4 (&vr)[U][VEC], bool (&ok)[U]) {
+        // This lane's pieces of the query rows (raw storage words).
+        uint4 qv[GB][VEC];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const Off off = row_offset(base + wave * TW + u * R + row, ok[u]);
+        for (int g = 0; g < GB; ++g)
 #pragma unroll
             for (int v = 0; v < VEC; ++v) {
-                kr[u][v] = load16(kb + (off + (Off)((v * LPR + sub) * 16)));
-                vr[u][v] = load16(vb + (off + (Off)((v * LPR + sub) * 16)));
+                qv[g][v] = make_uint4(0, 0, 0, 0);
+                if (g < ng)
+                    qv[g][v] = *reinterpret_cast<const uint4 *>(static_cast<const char *>(a.q) +
+                                                                 (size_t)(b * a.Hq + h0 + g) * ROWB +
+                                                                 (v * LPR + sub) * 16);
             }
-        }
-    };
 
-    auto consume_step = [&](const uint4 (&kr)[U][VEC], const uint4 (&vr)[U][VEC], const bool (&ok)[U]) {
-        float s[U][GB];
+        float m[GB], l[GB], o[GB][EPT];
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+        for (int g = 0; g < GB; ++g) {
+            m[g] = kNegInf;
+            l[g] = 0.f;
+#pragma unroll
+            for (int e = 0; e < EPT; ++e) o[g][e] = 0.f;
+        }
+
+        const char *kb = static_cast<const char *>(a.k);
+        const char *vb = static_cast<const char *>(a.v);
+        if constexpr (!PAGED) {
+            const size_t seq = (size_t)(b * a.Hkv + kvh) * (size_t)a.T * ROWB;
+            kb += seq;
+            vb += seq;
+        }
+
+        // Paged: page ids of the range being streamed, staged in LDS so that
+        // no K/V load waits on a dependent page-table read (ids outside the
+        // pool become -1).  A range spans at most kMaxSplitPages pages.
+        int p0 = 0;
+        auto stage_pages = [&](int r0, int r1) {
+            if constexpr (PAGED) {
+                p0 = r0 >> a.page_shift;
+                const int npg = r1 > r0 ? ((r1 - 1) >> a.page_shift) - p0 + 1 : 0;
+                __syncthreads();
+                for (int i = threadIdx.x; i < npg; i += 64 * WAVES) {
+                    const int pg = a.page_table[(size_t)b * a.max_pages + p0 + i];
+                    s_pages[i] = (unsigned)pg < (unsigned)a.num_pages ? pg : -1;
+                }
+                __syncthreads();
+            }
+        };
+
+        auto stream_range = [&](int r0, int r1) {
+            // Byte offset of token t's row and whether the token is real.  A
+            // contiguous (batch, kv head) slice is below 4 GiB (checked on the
+            // host), so its offsets are 32-bit: the loads then take a scalar
+            // base address plus one vector register.
+            using Off = typename std::conditional<PAGED, size_t, uint32_t>::type;
+            auto row_offset = [&](int t, bool &ok) -> Off {
+                ok = t < r1;
+                const int tc = ok ? t : r1 - 1;        // clamped: always a valid token
+                if constexpr (PAGED) {
+                    int page = s_pages[(tc >> a.page_shift) - p0];
+                    if (page < 0) { ok = false; page = 0; }
+                    return (((size_t)page * a.Hkv + kvh) * a.page_size + (tc & (a.page_size - 1))) * ROWB;
+                } else {
+                    return (uint32_t)tc * (uint32_t)ROWB;
+                }
+            };
+
+            auto load_step = [&](int base, uint4 (&kr)[U][VEC], uint4 (&vr)[U][VEC], bool (&ok)[U]) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const Off off = row_offset(base + wave * TW + u * R + row, ok[u]);
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v) {
+                        kr[u][v] = load16(kb + (off + (Off)((v * LPR + sub) * 16)));
+                        vr[u][v] = load16(vb + (off + (Off)((v * LPR + sub) * 16)));
+                    }
+                }
+            };
+
+            auto consume_step = [&](const uint4 (&kr)[U][VEC], const uint4 (&vr)[U][VEC], const bool (&ok)[U]) {
+                float s[U][GB];
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int g = 0; g < GB; ++g) {
+                        float acc = 0.f;
+#pragma unroll
+                        for (int v = 0; v < VEC; ++v) acc = dot_piece<DT>(qv[g][v], kr[u][v], acc);
+                        acc = row_sum<LPR>(acc) * a.scale_log2;
+                        s[u][g] = ok[u] ? acc : kNegInf;
+                    }
+                float vf[U][EPT];
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v) widen<DT>(vr[u][v], &vf[u][v * EPC]);
+#pragma unroll
+                for (int g = 0; g < GB; ++g) {
+                    float mt = s[0][g];
+#pragma unroll
+                    for (int u = 1; u < U; ++u) mt = fmaxf(mt, s[u][g]);
+                    const float mn = fmaxf(m[g], mt);
+                    const float mu = mn == kNegInf ? 0.f : mn;
+                    const float alpha = exp2_fast(m[g] - mu);
+                    float p[U];
+                    float ps = 0.f;
+#pragma unroll
+                    for (int u = 0; u < U; ++u) { p[u] = exp2_fast(s[u][g] - mu); ps += p[u]; }
+                    l[g] = l[g] * alpha + ps;
+#pragma unroll
+                    for (int e = 0; e < EPT; ++e) {
+                        float acc = o[g][e] * alpha;
+#pragma unroll
+                        for (int u = 0; u < U; ++u) acc = fmaf(p[u], vf[u][e], acc);
+                        o[g][e] = acc;
+                    }
+                    m[g] = mn;
+                }
+            };
+
+            // Two register buffers used in turn: while one step is consumed
+            // the next one is in flight.  The fence keeps each prefetch where
+            // it is issued (otherwise the compiler sinks every load next to
+            // its first use one step later), and the scheduling barrier stops
+            // the consumer's arithmetic from being hoisted above it.
+            uint4 ka[U][VEC], va[U][VEC], kb2[U][VEC], vb2[U][VEC];
+            bool oka[U], okb[U];
+            load_step(r0, ka, va, oka);
+            for (int base = r0;; base += 2 * TILE) {
+                load_step(base + TILE, kb2, vb2, okb);   // clamped past the end
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+                consume_step(ka, va, oka);
+                if (base + TILE >= r1) break;
+                load_step(base + 2 * TILE, ka, va, oka);
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+                consume_step(kb2, vb2, okb);
+                if (base + 2 * TILE >= r1) break;
+            }
+        };
+
+        if constexpr (PAGED) {
+            // ranges of at most kMaxSplitPages pages: each ends on a page
+            // boundary, so a start inside a page still fits the stage
+            for (int r0 = c0, r1; r0 < c1; r0 = r1) {
+                const long long e = ((long long)(r0 >> a.page_shift) + kMaxSplitPages) << a.page_shift;
+                r1 = e < c1 ? (int)e : c1;
+                stage_pages(r0, r1);
+                stream_range(r0, r1);
+            }
+        } else {
+            if (c0 < c1) stream_range(c0, c1);
+        }
+
+        // Merge the rows of this wave (log-sum-exp, rows LPR, 2*LPR, ... apart).
+#pragma unroll
+        for (int off = LPR; off < 64; off <<= 1) {
 #pragma unroll
             for (int g = 0; g < GB; ++g) {
-                float acc = 0.f;
+                const float m2 = __shfl_xor(m[g], off);
+                const float l2 = __shfl_xor(l[g], off);
+                const float mn = fmaxf(m[g], m2);
+                const float mu = mn == kNegInf ? 0.f : mn;
+                const float a1 = exp2_fast(m[g] - mu), a2 = exp2_fast(m2 - mu);
+                l[g] = l[g] * a1 + l2 * a2;
 #pragma unroll
-                for (int v = 0; v < VEC; ++v) acc = dot_piece<DT>(qv[g][v], kr[u][v], acc);
-                acc = row_sum<LPR>(acc) * a.scale_log2;
-                s[u][g] = ok[u] ? acc : kNegInf;
+                for (int e = 0; e < EPT; ++e) {
+                    const float o2 = __shfl_xor(o[g][e], off);
+                    o[g][e] = o[g][e] * a1 + o2 * a2;
+                }
+                m[g] = mn;
             }
-        float vf[U][EPT];
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) widen<DT>(vr[u][v], &vf[u][v * EPC]);
-#pragma unroll
-        for (int g = 0; g < GB; ++g) {
-            float mt = s[0][g];
-#pragma unroll
-            for (int u = 1; u < U; ++u) mt = fmaxf(mt, s[u][g]);
-            const float mn = fmaxf(m[g], mt);
-            const float mu = mn == kNegInf ? 0.f : mn;
-            const float alpha = exp2_fast(m[g] - mu);
-            float p[U];
-            float ps = 0.f;
-#pragma unroll
-            for (int u = 0; u < U; ++u) { p[u] = exp2_fast(s[u][g] - mu); ps += p[u]; }
-            l[g] = l[g] * alpha + ps;
-#pragma unroll
-            for (int e = 0; e < EPT; ++e) {
-                float acc = o[g][e] * alpha;
-#pragma unroll
-                for (int u = 0; u < U; ++u) acc = fmaf(p[u], vf[u][e], acc);
-                o[g][e] = acc;
-            }
-            m[g] = mn;
         }
+
+        // Merge the waves through LDS and finish the segment.
+        __syncthreads();                               // sm is free (previous segment)
+        if (row == 0) {
+#pragma unroll
+            for (int g = 0; g < GB; ++g) {
+#pragma unroll
+                for (int v = 0; v < VEC; ++v)
+#pragma unroll
+                    for (int j = 0; j < EPC; ++j)
+                        sm.o[wave][g][(v * LPR + sub) * EPC + j] = o[g][v * EPC + j];
+                if (sub == 0) { sm.m[wave][g] = m[g]; sm.l[wave][g] = l[g]; }
+            }
+        }
+        __syncthreads();
+        finish_split<WAVES, GB, D>(a, sm, so, b, h0, ng);
     };
 
-    // Two register buffers used in turn: while one step is consumed the
-    // next one is in flight.  The fence keeps each prefetch where it is
-    // issued (otherwise the compiler sinks every load next to its first use
-    // one step later), and the scheduling barrier stops the consumer's
-    // arithmetic from being hoisted above it.
-    if (c0 < c1) {
-        uint4 ka[U][VEC], va[U][VEC], kb2[U][VEC], vb2[U][VEC];
-        bool oka[U], okb[U];
-        load_step(c0, ka, va, oka);
-        for (int base = c0;; base += 2 * TILE) {
-            load_step(base + TILE, kb2, vb2, okb);   // clamped past the end
-            asm volatile("" ::: "memory");
-            __builtin_amdgcn_sched_barrier(0);
-            consume_step(ka, va, oka);
-            if (base + TILE >= c1) break;
-            load_step(base + 2 * TILE, ka, va, oka);
-            asm volatile("" ::: "memory");
-            __builtin_amdgcn_sched_barrier(0);
-            consume_step(kb2, vb2, okb);
-            if (base + 2 * TILE >= c1) break;
+    if constexpr (STREAM) {
+        __shared__ long long s_pref[kStreamMaxB + 1];
+        drive_stream<64 * WAVES, D>(a, s_pref, GB, segment);
+    } else {
+        const int split = blockIdx.x;
+        const int kvh = blockIdx.y / a.head_blocks;
+        const int hb = blockIdx.y - kvh * a.head_blocks;
+        const int b = blockIdx.z;
+        int Tb = a.T;
+        if (a.seq_lens) {
+            Tb = a.seq_lens[b];
+            Tb = Tb < 0 ? 0 : (Tb > a.T ? a.T : Tb);
         }
-    }
-
-    // Merge the rows of this wave (log-sum-exp, rows LPR, 2*LPR, ... apart).
-#pragma unroll
-    for (int off = LPR; off < 64; off <<= 1) {
-#pragma unroll
-        for (int g = 0; g < GB; ++g) {
-            const float m2 = __shfl_xor(m[g], off);
-            const float l2 = __shfl_xor(l[g], off);
-            const float mn = fmaxf(m[g], m2);
-            const float mu = mn == kNegInf ? 0.f : mn;
-            const float a1 = exp2_fast(m[g] - mu), a2 = exp2_fast(m2 - mu);
-            l[g] = l[g] * a1 + l2 * a2;
-#pragma unroll
-            for (int e = 0; e < EPT; ++e) {
-                const float o2 = __shfl_xor(o[g][e], off);
-                o[g][e] = o[g][e] * a1 + o2 * a2;
-            }
-            m[g] = mn;
+        const int c0 = split * a.chunk;
+        const int c1 = min(c0 + a.chunk, Tb);
+        const int h0 = kvh * a.G + hb * GB;
+        if (a.n_splits > 1 && c0 >= Tb) {          // empty split: never counted or read
+            if (a.fused && split == 0) write_empty_group<D>(a, b, h0, min(GB, a.G - hb * GB));
+            return;
         }
+        segment(b, kvh, hb, c0, c1 > c0 ? c1 : c0, split_segment(a, b, kvh, hb, h0, split, Tb));
     }
-
-    // Merge the waves through LDS and finish the split.
-    __shared__ EpilogueLds<WAVES, GB, D> sm;
-    if (row == 0) {
-#pragma unroll
-        for (int g = 0; g < GB; ++g) {
-#pragma unroll
-            for (int v = 0; v < VEC; ++v)
-#pragma unroll
-                for (int j = 0; j < EPC; ++j)
-                    sm.o[wave][g][(v * LPR + sub) * EPC + j] = o[g][v * EPC + j];
-            if (sub == 0) { sm.m[wave][g] = m[g]; sm.l[wave][g] = l[g]; }
-        }
-    }
-    __syncthreads();
-    finish_split<WAVES, GB, D>(a, sm, b, kvh, hb, split, h0, ng, Tb);
 }
 
 template <int DT, int D, int GB, bool PAGED>
 hipError_t launch_instance(const SplitArgs &a, hipStream_t stream) {
-    const dim3 grid(a.n_splits, a.Hkv * a.head_blocks, a.B);
-    hipLaunchKernelGGL((split_valu<DT, D, GB, PAGED>), grid, dim3(256), 0, stream, a);
+    if (a.stream) {
+        hipLaunchKernelGGL((split_valu<DT, D, GB, PAGED, true>), dim3(a.n_splits), dim3(256), 0, stream, a);
+    } else {
+        const dim3 grid(a.n_splits, a.Hkv * a.head_blocks, a.B);
+        hipLaunchKernelGGL((split_valu<DT, D, GB, PAGED, false>), grid, dim3(256), 0, stream, a);
+    }
     return hipGetLastError();
 }
 

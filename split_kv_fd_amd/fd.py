@@ -39,14 +39,15 @@ class fd_plan_t(ctypes.Structure):
                 ("tile", ctypes.c_int32), ("heads_per_block", ctypes.c_int32),
                 ("head_blocks", ctypes.c_int32), ("grid", ctypes.c_int32 * 3),
                 ("block", ctypes.c_int32), ("combine", ctypes.c_int32),
-                ("fused", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t)]
+                ("fused", ctypes.c_int32), ("stream", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t)]
 
     def as_dict(self) -> dict:
         return {"n_splits": self.n_splits, "chunk": self.chunk,
                 "path": {0: "valu", 1: "mfma"}.get(self.path, self.path), "tile": self.tile,
                 "heads_per_block": self.heads_per_block, "head_blocks": self.head_blocks,
                 "grid": list(self.grid), "block": self.block, "combine": bool(self.combine),
-                "fused": bool(self.fused),
+                "fused": bool(self.fused), "stream": bool(self.stream),
                 "workspace_bytes": self.workspace_bytes}
 
 

@@ -108,16 +108,35 @@ def test_plan_of_the_five_workloads(lib):
 
 
 def test_plan_paged_chunks_align_to_pages(lib):
-    st, p = plan(16, 32, 8, 65536, 128, 0, page_size=256, max_pages_per_seq=256, num_pages=10)
-    assert st == fd.FD_OK and p.chunk % 256 == 0
-    # ragged (paged) batches are cut into short chunks for balance
-    st, p = plan(16, 32, 8, 65536, 128, 0, page_size=16, max_pages_per_seq=4096, num_pages=10)
-    assert st == fd.FD_OK and p.chunk <= 2048 and not p.fused and p.n_splits % 8 == 0
-    st, p = plan(16, 32, 8, 65536, 128, 0, page_size=16, max_pages_per_seq=4096, num_pages=10,
-                 flags=fd.FD_FLAG_FUSED_MERGE)
-    assert st == fd.FD_OK and p.fused
+    # explicit split counts keep the split grid: chunks are whole pages
+    st, p = plan(16, 32, 8, 65536, 128, 40, page_size=256, max_pages_per_seq=256, num_pages=10)
+    assert st == fd.FD_OK and p.chunk % 256 == 0 and not p.stream
+    assert p.chunk * p.n_splits >= 65536 and p.chunk <= 2048 * 256
+    # a split stages at most 2048 page ids on chip
+    st, p = plan(1, 8, 8, 65536, 128, 1, page_size=16, max_pages_per_seq=4096, num_pages=10)
+    assert st == fd.FD_OK and p.chunk <= 2048 * 16 and p.n_splits >= 2
     assert plan(1, 4, 4, 100, 128, flags=4)[0] == fd.FD_ERR_INVALID_ARG
     assert plan(1, 4, 4, 100, 128, flags=3)[0] == fd.FD_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("G,dtype", [(4, fd.FD_BF16), (1, fd.FD_F16), (8, fd.FD_F32), (32, fd.FD_BF16)])
+def test_plan_paged_stream_mode(lib, G, dtype):
+    # automatic plans of paged (ragged) batches use the balanced stream mode:
+    # one workgroup per stream range, two per compute unit, merged in-launch
+    B, Hkv, D = 16, 2, 128
+    st, p = plan(B, G * Hkv, Hkv, 65536, D, 0, dtype=dtype, page_size=16,
+                 max_pages_per_seq=4096, num_pages=10, num_cus=100)
+    assert st == fd.FD_OK, fd.fd_last_error()
+    assert p.stream and p.fused and p.combine and p.chunk == 0
+    assert (p.n_splits, p.grid[0], p.grid[1], p.grid[2]) == (200, 200, 1, 1)
+    rows = B * Hkv * p.head_blocks
+    slots = (rows + p.n_splits) * p.heads_per_block
+    assert p.workspace_bytes >= rows * 8 + slots * (D + 2) * 4
+    assert p.tile > 0 and p.tile % 16 == 0
+    # too many sequences for the on-chip prefix scan: the split grid
+    st, p = plan(4096, G * Hkv, Hkv, 1024, D, 0, dtype=dtype, page_size=16,
+                 max_pages_per_seq=64, num_pages=10)
+    assert st == fd.FD_OK and not p.stream and p.chunk > 0
 
 
 def test_plan_merge_choice(lib):

@@ -212,6 +212,49 @@ def test_fused_merge_ragged_and_paged(path):
         parity.check_full(case, n_splits=n, path=path, fused_merge=True, what=f"fused paged n={n}")
 
 
+# ------------------------------------------------------------------ balanced stream mode (paged, automatic plans)
+
+@pytest.mark.parametrize("path", ["valu", "mfma"])
+@pytest.mark.parametrize("wgs", [1, 3, 8, 64, 1000])
+def test_stream_mode_workgroup_counts(monkeypatch, path, wgs):
+    # Rows laid end to end and cut into `wgs` equal ranges: one workgroup
+    # covering everything, rows split over several workgroups, rows shorter
+    # than a range, and more workgroups than tiles.  Empty sequences and a
+    # poisoned workspace included.
+    monkeypatch.setenv("FD_STREAM_WGS", str(wgs))
+    for P in (16, 256):
+        case = small_case("paged_ragged_bf16", B=7, Hq=8, Hkv=2, T=5000, page_size=P,
+                          len_lo=0, len_hi=5000)
+        case.seq_lens[2] = 0
+        case.seq_lens[4] = 1
+        (_, _), plan = parity.check_full(case, path=path, what=f"stream wgs={wgs} P={P} {path}")
+        assert plan["stream"] and plan["n_splits"] == wgs
+
+
+@pytest.mark.parametrize("path", ["valu", "mfma"])
+def test_stream_mode_merge_cap(monkeypatch, path):
+    # Many workgroups over one long row: ranges are widened so that no row
+    # is cut into more pieces than the in-launch merge holds.
+    monkeypatch.setenv("FD_STREAM_WGS", "1000")
+    case = small_case("paged_ragged_bf16", B=2, Hq=32, Hkv=1, T=40000, len_lo=30000, len_hi=40000)
+    (_, _), plan = parity.check_full(case, path=path, what=f"stream merge cap {path}")
+    assert plan["stream"]
+
+
+@pytest.mark.parametrize("path", ["valu", "mfma"])
+def test_stream_mode_long_ranges_restage_pages(monkeypatch, path):
+    # A range longer than the on-chip page-id stage (2048 pages), starting
+    # inside a page: 256-token pages, ranges cut at multiples of the tile.
+    # Two workgroups: each range spans a little over 2048 pages and the
+    # second one starts three quarters into a page.
+    monkeypatch.setenv("FD_STREAM_WGS", "2")
+    T = 2 * (2048 * 256 + 128 * 3) + 50
+    case = small_case("paged_ragged_bf16", B=1, Hq=4, Hkv=1, D=64, T=T, page_size=256,
+                      len_lo=T, len_hi=T)
+    (_, _), plan = parity.check_full(case, path=path, what=f"stream restage {path}")
+    assert plan["stream"]
+
+
 @pytest.mark.parametrize("path", ["valu", "mfma"])
 def test_split_and_combine_entry_points(path):
     case = small_case("gqa128k_bf16", B=2, Hq=8, Hkv=2, T=3000)
