@@ -158,12 +158,14 @@ size_t fd_workspace_bytes(int B, int Hq, int Hkv, int T, int D, int n_splits,
  *   scale               : multiplies q.k before the softmax (finite).
  *   n_splits            : 0 = automatic, else the requested split count.
  * The workspace (opt->workspace, >= fd_workspace_bytes, 256-byte aligned)
- * holds one arrival counter per (batch, kv head, head block), the partials
+ * holds two arrival counter words per (batch, kv head, head block), the partials
  * [B, Hq, n_splits, D] and two [B, Hq, n_splits] rows (a stream plan: one
  * partial slot per (row + workgroup) pair instead).  Its contents before
  * the call do not matter: counters carry a per-call tag, so values left by
- * any earlier call are ignored.  Calls that share a workspace must not
- * overlap in time.
+ * any other call are ignored (a fused call leaves its counters tagged for
+ * the next call on the same workspace, which then counts arrivals with one
+ * atomic add each; anything else is counted once through a slower exchange
+ * loop).  Calls that share a workspace must not overlap in time.
  */
 fd_status_t fd_decode(const void *q, const void *k_cache, const void *v_cache,
                       const int32_t *page_table, const int32_t *seq_lens,

@@ -167,7 +167,7 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
         p->fused = 1;
         p->stream = 1;
         const size_t slots = (size_t)(rows + nw) * hpb;
-        p->workspace_bytes = align256(rows * sizeof(unsigned long long)) + align256(slots * D * sizeof(float)) +
+        p->workspace_bytes = align256(rows * 2 * sizeof(unsigned long long)) + align256(slots * D * sizeof(float)) +
                              2 * align256(slots * sizeof(float));
         return FD_OK;
     }
@@ -238,7 +238,7 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
     p->fused = n > 1 && n * merge_heads <= fdk::kMergeMaxPairsHost && want_fused;
     if (n > 1) {
         const size_t parts = (size_t)B * Hq * (size_t)n;
-        const size_t counters = (size_t)B * Hkv * head_blocks * sizeof(unsigned long long);
+        const size_t counters = (size_t)B * Hkv * head_blocks * 2 * sizeof(unsigned long long);
         p->workspace_bytes = align256(counters) + align256(parts * D * sizeof(float)) +
                              2 * align256(parts * sizeof(float));
     }
@@ -293,7 +293,7 @@ fd_status_t prepare(const void *q, const void *k, const void *v, const int32_t *
         const size_t slots = (rows + (size_t)c->p.n_splits) * c->p.heads_per_block;
         char *w = static_cast<char *>(c->o.workspace);
         counters = reinterpret_cast<unsigned long long *>(w);
-        w += align256(rows * sizeof(unsigned long long));
+        w += align256(rows * 2 * sizeof(unsigned long long));
         part_o = reinterpret_cast<float *>(w);
         w += align256(slots * D * sizeof(float));
         part_m = reinterpret_cast<float *>(w);
@@ -310,7 +310,7 @@ fd_status_t prepare(const void *q, const void *k, const void *v, const int32_t *
         const size_t parts = (size_t)B * Hq * (size_t)c->p.n_splits;
         char *w = static_cast<char *>(c->o.workspace);
         counters = reinterpret_cast<unsigned long long *>(w);
-        w += align256((size_t)B * Hkv * c->p.head_blocks * sizeof(unsigned long long));
+        w += align256((size_t)B * Hkv * c->p.head_blocks * 2 * sizeof(unsigned long long));
         part_o = reinterpret_cast<float *>(w);
         w += align256(parts * D * sizeof(float));
         part_m = reinterpret_cast<float *>(w);
@@ -336,6 +336,7 @@ fd_status_t prepare(const void *q, const void *k, const void *v, const int32_t *
     s.scale_log2 = (float)((double)scale * 1.4426950408889634074);
     s.fused = 0;
     s.epoch = 0;
+    s.next_epoch = 0;
     s.counters = counters;
     s.stream = c->p.stream;
     s.stream_align = c->p.tile;
@@ -354,23 +355,66 @@ fd_status_t prepare(const void *q, const void *k, const void *v, const int32_t *
     return FD_OK;
 }
 
-// Epoch of a fused call: distinct per call (never 0), so arrival counters
-// left in a workspace by any earlier call are recognised as stale.
-unsigned next_epoch() {
+// Epochs of fused calls.  A fresh epoch is distinct from every other one
+// this process hands out (never 0 and never all ones, the values a cleared
+// or poisoned word reads), so counters left by any other call are stale.
+unsigned fresh_epoch() {
     static std::atomic<unsigned> epoch{0x5eed0000u};
     unsigned e;
-    do { e = epoch.fetch_add(1, std::memory_order_relaxed) + 1; } while (e == 0);
+    do { e = epoch.fetch_add(1, std::memory_order_relaxed) + 1; } while (e == 0 || e == ~0u);
     return e;
 }
+
+// The epoch each recent workspace's counters were left at by its last fused
+// call: the next call on that workspace uses it, so its arrivals take the
+// one-fetch-add path.  A workspace not found here (first use, or evicted)
+// gets a fresh epoch and counts once through the exchange loop; results do
+// not depend on this table, only the cost of the count does.
+struct EpochTable {
+    static constexpr int kSlots = 64;
+    std::mutex mu;
+    const void *ws[kSlots] = {};
+    unsigned left[kSlots] = {};
+    int victim = 0;
+
+    // (epoch for this call, epoch its completing workgroups leave behind)
+    void take(const void *w, unsigned *cur, unsigned *next) {
+        std::lock_guard<std::mutex> g(mu);
+        *next = fresh_epoch();
+        for (int i = 0; i < kSlots; ++i)
+            if (ws[i] == w) {
+                *cur = left[i];
+                left[i] = *next;
+                return;
+            }
+        *cur = fresh_epoch();
+        ws[victim] = w;
+        left[victim] = *next;
+        victim = (victim + 1) % kSlots;
+    }
+
+    // the launch failed: the counters were not touched
+    void forget(const void *w) {
+        std::lock_guard<std::mutex> g(mu);
+        for (int i = 0; i < kSlots; ++i)
+            if (ws[i] == w) ws[i] = nullptr;
+    }
+};
+
+EpochTable g_epochs;
 
 fd_status_t run_split(Call &c, bool fused) {
     fused = fused || c.p.stream;            // stream mode always merges in the launch
     c.s.fused = fused ? 1 : 0;
-    c.s.epoch = fused ? next_epoch() : 0;
+    c.s.epoch = c.s.next_epoch = 0;
+    if (fused) g_epochs.take(c.s.counters, &c.s.epoch, &c.s.next_epoch);
     const hipStream_t stream = static_cast<hipStream_t>(c.o.stream);
     const hipError_t e = c.p.path == FD_PATH_MFMA ? fdk::launch_split_mfma(c.s, c.o.dtype, stream)
                                                   : fdk::launch_split_valu(c.s, c.o.dtype, stream);
-    if (e != hipSuccess) return hip_fail(e, "launching the split kernel");
+    if (e != hipSuccess) {
+        if (fused) g_epochs.forget(c.s.counters);
+        return hip_fail(e, "launching the split kernel");
+    }
     return FD_OK;
 }
 

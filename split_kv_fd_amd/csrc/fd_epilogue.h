@@ -17,11 +17,20 @@ constexpr float kEpLn2 = 0.693147180559945309417f;
 
 __device__ __forceinline__ float ep_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Count this workgroup's arrival at its group's counter.  The counter holds
-// (call epoch << 32 | arrivals); a value left by any other call (another
-// epoch) restarts the count, so the workspace needs no clearing between
-// calls.  Returns true for the workgroup that completes the group.  The loop
-// ends: every failed exchange means another workgroup's exchange succeeded.
+// Count this workgroup's arrival at its group's counters and return true for
+// the workgroup that completes the group (n_active arrivals).
+//
+// Each group has two 64-bit words holding (epoch << 32 | arrivals).  The
+// first is counted with one fetch-add per workgroup: it is valid when it
+// already carries this call's epoch, which the previous call on the same
+// workspace leaves there (its last workgroup stores next_epoch << 32 with a
+// zero count).  A word that carries anything else -- a new workspace,
+// foreign data, a group the previous call did not finish -- sends every
+// arrival of the call to the second word, counted with an exchange loop
+// that restarts the count on a foreign epoch.  Within one call all arrivals
+// see the same epoch in the first word (only the completing workgroup
+// changes it, after every fetch-add), so they all take the same path.  The
+// loop ends: every failed exchange means another workgroup's succeeded.
 //
 // Ordering.  A device-scope release here would write back the whole L2 of
 // the XCD for every workgroup (about 1.7 us each, serialised), which costs
@@ -29,20 +38,33 @@ __device__ __forceinline__ float ep_exp2(float x) { return __builtin_amdgcn_exp2
 // are written and read only with device-coherent (sc1) accesses, which go to
 // the coherent level instead of a per-XCD L2 copy; every thread waits for
 // its stores to complete (vmcnt 0) before the barrier, so all partials of
-// the workgroup are at the coherent level before this exchange is issued,
-// and the last workgroup issues its coherent loads only after the exchange
-// that completed the count has returned.
-__device__ __forceinline__ bool arrive_last(unsigned long long *cnt, unsigned epoch, int n_active) {
-    unsigned long long old = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    unsigned long long next;
-    for (;;) {
-        next = ((unsigned)(old >> 32) == epoch) ? old + 1ull
-                                                 : (((unsigned long long)epoch << 32) | 1ull);
-        if (__hip_atomic_compare_exchange_strong(cnt, &old, next, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT))
-            break;
+// the workgroup are at the coherent level before the count is issued, and
+// the last workgroup issues its coherent loads only after the count that
+// completed the group has returned.
+__device__ __forceinline__ bool arrive_last(unsigned long long *cnt, unsigned epoch, unsigned next_epoch,
+                                            int n_active) {
+    const unsigned long long old =
+        __hip_atomic_fetch_add(cnt, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bool last;
+    if ((unsigned)(old >> 32) == epoch) {
+        last = (unsigned)(old & 0xffffffffull) + 1u == (unsigned)n_active;
+    } else {
+        unsigned long long *slow = cnt + 1;
+        unsigned long long prev = __hip_atomic_load(slow, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        unsigned long long next;
+        for (;;) {
+            next = ((unsigned)(prev >> 32) == epoch) ? prev + 1ull
+                                                      : (((unsigned long long)epoch << 32) | 1ull);
+            if (__hip_atomic_compare_exchange_strong(slow, &prev, next, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT))
+                break;
+        }
+        last = (unsigned)(next & 0xffffffffull) == (unsigned)n_active;
     }
-    return (unsigned)(next & 0xffffffffull) == (unsigned)n_active;
+    if (last)   // every arrival of the group has counted: hand the word to the next call
+        __hip_atomic_store(cnt, (unsigned long long)next_epoch << 32, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    return last;
 }
 
 // Device-coherent accesses of the partials in fused mode.
@@ -99,7 +121,7 @@ struct SegOut {
     size_t base;
     int gs, ss, s;
     int fused;                     // the last arriving segment merges the group
-    unsigned long long *cnt;       // the group's arrival counter
+    unsigned long long *cnt;       // the group's two arrival counter words
     int arrivals;                  // segments of the group (its merge count)
 };
 
@@ -112,7 +134,7 @@ __device__ __forceinline__ SegOut split_segment(const SplitArgs &a, int b, int k
     so.ss = 1;
     so.s = split;
     so.fused = a.fused;
-    so.cnt = a.counters + ((size_t)b * a.Hkv + kvh) * a.head_blocks + hb;
+    so.cnt = a.counters + 2 * (((size_t)b * a.Hkv + kvh) * a.head_blocks + hb);
     so.arrivals = active_splits(a, Tb);
     return so;
 }
@@ -272,7 +294,7 @@ __device__ void finish_split(const SplitArgs &a, EpilogueLds<WAVES, GB, D> &sm, 
     // arrival, and the workgroup that completes the group merges its splits.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (threadIdx.x == 0) sm.last = arrive_last(so.cnt, a.epoch, so.arrivals) ? 1 : 0;
+    if (threadIdx.x == 0) sm.last = arrive_last(so.cnt, a.epoch, a.next_epoch, so.arrivals) ? 1 : 0;
     __syncthreads();
     if (!sm.last) return;
     combine_group<WAVES, GB, D>(a, sm, so, b, h0, ng, so.arrivals);
@@ -376,7 +398,7 @@ __device__ void drive_stream(const SplitArgs &a, long long *pref, int hpb, Seg &
             so.ss = hpb;
             so.s = (int)(w - wf);
             so.fused = 1;
-            so.cnt = a.counters + r;
+            so.cnt = a.counters + 2 * (size_t)r;
             so.arrivals = (int)(wl - wf + 1);
             __syncthreads();                       // LDS of the previous segment is free
             seg(b, kvh, hb, (int)c0, c1 > (int)c0 ? c1 : (int)c0, so);

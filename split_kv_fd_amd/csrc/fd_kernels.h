@@ -46,7 +46,8 @@ struct SplitArgs {
     float scale_log2;            // scale * log2(e): logits in base-2 units
     int fused;                   // last workgroup of a group merges its splits
     unsigned epoch;              // per-call tag of the arrival counters
-    unsigned long long *counters;  // arrival counters, one per group (row)
+    unsigned next_epoch;         // tag the completing workgroup leaves for the next call
+    unsigned long long *counters;  // arrival counters, two words per group (row)
     // Stream mode (ragged batches): rows padded to stream_align tokens and
     // laid end to end, one equal range per workgroup (gridDim.x of them).
     int stream;

@@ -197,7 +197,8 @@ def test_fused_merge_matches_combine_kernel(path):
     ref_out, ref_lse = (x.clone() for x in base())
     torch.cuda.synchronize()
     for rep in range(20):
-        fused.workspace.fill_(0xFF)
+        if rep % 3 == 0:       # garbage counters: the exchange-loop count; else one add each
+            fused.workspace.fill_(0xFF)
         out, lse = fused()
         torch.cuda.synchronize()
         assert torch.isfinite(out).all(), f"rep {rep}: non-finite output"
@@ -253,6 +254,36 @@ def test_stream_mode_long_ranges_restage_pages(monkeypatch, path):
                       len_lo=T, len_hi=T)
     (_, _), plan = parity.check_full(case, path=path, what=f"stream restage {path}")
     assert plan["stream"]
+
+
+def test_fused_plans_sharing_one_workspace():
+    # A stream plan and a split-grid plan with other row counts take turns
+    # on one workspace: each call must count its arrivals correctly from the
+    # counters the other plan left (tagged for another call, or untouched).
+    case = small_case("paged_ragged_bf16", B=6, Hq=8, Hkv=2, T=4000, len_lo=0, len_hi=4000)
+    case.seq_lens[3] = 0
+    other = small_case("mha32k_f16", B=3, Hq=16, Hkv=4, T=3000, dtype="bf16")
+    decs = [Decoder(case.q, case.k, case.v, scale=case.spec.scale, page_table=case.page_table,
+                    seq_lens=case.seq_lens, T=case.spec.T),
+            Decoder(case.q, case.k, case.v, scale=case.spec.scale, page_table=case.page_table,
+                    seq_lens=case.seq_lens, T=case.spec.T, n_splits=7, fused_merge=True),
+            Decoder(other.q, other.k, other.v, scale=other.spec.scale, n_splits=9, fused_merge=True)]
+    assert decs[0].plan["stream"] and decs[1].plan["fused"] and decs[2].plan["fused"]
+    size = max(d.plan["workspace_bytes"] for d in decs)
+    shared = torch.empty(size, dtype=torch.uint8, device=DEV)
+    shared.fill_(0xFF)
+    for d in decs:
+        d.opt.workspace = shared.data_ptr()
+        d.opt.workspace_bytes = size
+    cases = [case, case, other]
+    refs = [parity.oracle_full(c) for c in cases]
+    vmax = [parity.max_abs_v(c) for c in cases]
+    for rep, i in enumerate([0, 1, 0, 0, 2, 1, 1, 2, 0, 2, 2, 1]):
+        parity.announce(f"shared workspace rep={rep} plan={i}")
+        out, lse = decs[i]()
+        torch.cuda.synchronize()
+        parity.compare(cases[i], out.cpu().double().numpy(), lse.cpu().double().numpy(),
+                       refs[i][0], refs[i][1], vmax[i], f"shared workspace rep={rep} plan={i}")
 
 
 @pytest.mark.parametrize("path", ["valu", "mfma"])
