@@ -114,6 +114,88 @@ class Oracle:
             raise ValueError(f"oracle rejected its arguments (code {rc})")
         return out, lse
 
+    def append_decode(self, q, k_new, v_new, k, v, scale, seq_lens, *, dtype=None,
+                      page_table=None, page_size=0, rows=None, nthreads=0):
+        """Append the step's new key and value rows to the cache, then decode
+        over the grown sequence, in fp64.
+
+        This is the fused append-KV step a serving engine runs per decode
+        token (dupenodi guide "FlashDecoding and split-KV", "Walking through
+        it", lists fused append-KV paths beside paged layouts and GQA): with
+        T_b = seq_lens[b] tokens already cached, the rows k_new[b, j, :] and
+        v_new[b, j, :] become token T_b of every kv head j, and attention
+        runs over tokens 0 .. T_b (T_b + 1 of them).
+
+        Storage slot of token T_b: K[b, j, T_b, :] of a contiguous cache
+        (when T_b < T), or row T_b % P of page page_table[b, T_b // P] of a
+        paged pool (when T_b // P < max_pages; that page id must be in the
+        pool).  A sequence whose cache is full (T_b = T, or T_b = max_pages *
+        P) has no slot: it still attends to its new token, and its cache is
+        left unchanged.
+
+        Returns (out, lse, k_after, v_after): the fp64 results as decode()
+        gives them, and host copies of the caches after the store (raw
+        elements, same dtype and layout as k, v).
+        """
+        qa, dt = _host_array(q, dtype)
+        kn, _ = _host_array(k_new, dt)
+        vn, _ = _host_array(v_new, dt)
+        ka = _host_array(k, dt)[0].copy()
+        va = _host_array(v, dt)[0].copy()
+        sl = np.ascontiguousarray(_to_numpy(seq_lens), dtype=np.int64)
+        B = qa.shape[0]
+        assert kn.shape == vn.shape == (B, ka.shape[1], ka.shape[3])
+        grown = (sl + 1).astype(np.int32)
+        if page_table is None:
+            T = ka.shape[2]
+            # attention reads a cache one token longer, so a full sequence
+            # still has a place for its new token
+            k_att = np.zeros(ka.shape[:2] + (T + 1,) + ka.shape[3:], ka.dtype)
+            v_att = np.zeros_like(k_att)
+            k_att[:, :, :T] = ka
+            v_att[:, :, :T] = va
+            for b in range(B):
+                t = int(sl[b])
+                assert 0 <= t <= T, "seq_lens must lie in [0, T]"
+                k_att[b, :, t] = kn[b]
+                v_att[b, :, t] = vn[b]
+                if t < T:
+                    ka[b, :, t] = kn[b]
+                    va[b, :, t] = vn[b]
+            out, lse = self.decode(qa, k_att, v_att, scale, dtype=dt, seq_lens=grown,
+                                   rows=rows, nthreads=nthreads)
+            return out, lse, ka, va
+        pt = np.ascontiguousarray(_to_numpy(page_table), dtype=np.int64)
+        num_pages, _, P, _ = ka.shape
+        if page_size:
+            assert page_size == P
+        max_pages = pt.shape[1]
+        # attention: the stored pool plus one spare page per sequence that
+        # has no slot, and a table one column wider
+        pt_att = np.zeros((B, max_pages + 1), np.int32)
+        pt_att[:, :max_pages] = pt
+        spare = []
+        for b in range(B):
+            t = int(sl[b])
+            assert 0 <= t <= max_pages * P, "seq_lens must lie in [0, max_pages * page_size]"
+            col = t // P
+            if col < max_pages:
+                assert 0 <= pt[b, col] < num_pages, "the page of the new token must be in the pool"
+                ka[pt[b, col], :, t % P] = kn[b]
+                va[pt[b, col], :, t % P] = vn[b]
+            else:
+                spare.append(b)
+                pt_att[b, col] = num_pages + len(spare) - 1
+        k_att = np.concatenate([ka, np.zeros((len(spare),) + ka.shape[1:], ka.dtype)])
+        v_att = np.concatenate([va, np.zeros((len(spare),) + va.shape[1:], va.dtype)])
+        for i, b in enumerate(spare):
+            t = int(sl[b])
+            k_att[num_pages + i, :, t % P] = kn[b]
+            v_att[num_pages + i, :, t % P] = vn[b]
+        out, lse = self.decode(qa, k_att, v_att, scale, dtype=dt, page_table=pt_att,
+                               seq_lens=grown, rows=rows, nthreads=nthreads)
+        return out, lse, ka, va
+
     def decode_f16_bits(self, bits: int) -> float:
         return float(self.lib.fdo_decode_f16(bits))
 

@@ -426,6 +426,144 @@ def pin_golden_fixtures(orc):
         _close(lse, exp_lse, c["tol"], f"golden {name} lse")
 
 
+# ---------------------------------------------------------------- append, then decode
+
+def _sigmoid(x):
+    return 1.0 / (1.0 + math.exp(-x))
+
+
+def pin_append_to_empty(orc):
+    """T_b = 0: after the append the sequence is the new token alone, so out
+    = v_new exactly and lse = its logit (exact: integer operands); the cache
+    changes at token 0 only."""
+    rng = _rng(41)
+    B, Hq, Hkv, T, D = 2, 4, 2, 5, 8
+    q = _ints(rng, (B, Hq, D))
+    kn = _ints(rng, (B, Hkv, D))
+    vn = rng.standard_normal((B, Hkv, D))
+    k = rng.standard_normal((B, Hkv, T, D))
+    v = rng.standard_normal((B, Hkv, T, D))
+    out, lse, ka, va = orc.append_decode(q, kn, vn, k, v, 0.5, np.zeros(B, np.int32))
+    G = Hq // Hkv
+    for b in range(B):
+        for h in range(Hq):
+            assert np.array_equal(out[b, h], vn[b, h // G]), "append to empty: out != v_new"
+            assert lse[b, h] == 0.5 * float(np.dot(q[b, h], kn[b, h // G])), "append to empty: lse"
+    assert np.array_equal(ka[:, :, 0], kn) and np.array_equal(va[:, :, 0], vn), "append: token 0 not stored"
+    assert np.array_equal(ka[:, :, 1:], k[:, :, 1:]) and np.array_equal(va[:, :, 1:], v[:, :, 1:]), \
+        "append: other tokens changed"
+
+
+def pin_append_two_tokens(orc):
+    """T_b = 1: two tokens, so out = sigma(s0 - s1) V0 + sigma(s1 - s0) v_new
+    and lse = s1 + log(1 + exp(s0 - s1)) (logistic closed form)."""
+    rng = _rng(42)
+    B, Hq, Hkv, T, D = 1, 3, 1, 4, 6
+    q = rng.standard_normal((B, Hq, D))
+    k = rng.standard_normal((B, Hkv, T, D))
+    v = rng.standard_normal((B, Hkv, T, D))
+    kn = rng.standard_normal((B, Hkv, D))
+    vn = rng.standard_normal((B, Hkv, D))
+    scale = 0.7
+    out, lse, _, _ = orc.append_decode(q, kn, vn, k, v, scale, np.ones(B, np.int32))
+    for h in range(Hq):
+        s0 = scale * float(np.dot(q[0, h], k[0, 0, 0]))
+        s1 = scale * float(np.dot(q[0, h], kn[0, 0]))
+        ref = _sigmoid(s0 - s1) * v[0, 0, 0] + _sigmoid(s1 - s0) * vn[0, 0]
+        _close(out[0, h], ref, 1e-14, "append T_b=1 out")
+        _close(lse[0, h], s1 + math.log1p(math.exp(s0 - s1)), 1e-14, "append T_b=1 lse")
+
+
+def pin_append_mpmath(orc):
+    """50-digit brute force over the cached tokens 0 .. T_b-1 and the new
+    token, on ragged tiny cases, contiguous and paged with shuffled pages;
+    the stored rows sit exactly at the new token's slot."""
+    import mpmath
+    mpmath.mp.dps = 50
+    rng = _rng(43)
+    B, Hq, Hkv, T, D, P = 3, 4, 2, 8, 3, 2
+    G = Hq // Hkv
+    q = rng.standard_normal((B, Hq, D)) * 2
+    k = rng.standard_normal((B, Hkv, T, D)) * 2
+    v = rng.standard_normal((B, Hkv, T, D))
+    kn = rng.standard_normal((B, Hkv, D)) * 2
+    vn = rng.standard_normal((B, Hkv, D))
+    lens = np.array([3, 0, 7], np.int32)
+    scale = 0.8
+    # paged copy of the same caches: page i of sequence b is pool page perm[b*n + i]
+    n = T // P
+    perm = rng.permutation(B * n)
+    table = perm.reshape(B, n).astype(np.int32)
+    kp = np.zeros((B * n, Hkv, P, D))
+    vp = np.zeros((B * n, Hkv, P, D))
+    for b in range(B):
+        for i in range(n):
+            kp[table[b, i]] = k[b, :, i * P:(i + 1) * P]
+            vp[table[b, i]] = v[b, :, i * P:(i + 1) * P]
+    res_c = orc.append_decode(q, kn, vn, k, v, scale, lens)
+    res_p = orc.append_decode(q, kn, vn, kp, vp, scale, lens, page_table=table)
+    for out, lse, _, _ in (res_c, res_p):
+        for b in range(B):
+            for h in range(Hq):
+                j = h // G
+                keys = [k[b, j, t] for t in range(lens[b])] + [kn[b, j]]
+                vals = [v[b, j, t] for t in range(lens[b])] + [vn[b, j]]
+                logits = [mpmath.mpf(scale) * mpmath.fsum(mpmath.mpf(q[b, h, d]) * mpmath.mpf(x[d])
+                                                         for d in range(D)) for x in keys]
+                w = [mpmath.e ** s for s in logits]
+                z = mpmath.fsum(w)
+                for d in range(D):
+                    ref = float(mpmath.fsum(w[t] * mpmath.mpf(vals[t][d]) for t in range(len(w))) / z)
+                    assert abs(out[b, h, d] - ref) <= 1e-14 * max(1.0, abs(ref)), "append mpmath out"
+                ref_l = float(mpmath.log(z))
+                assert abs(lse[b, h] - ref_l) <= 1e-14 * max(1.0, abs(ref_l)), "append mpmath lse"
+    _, _, kc, vc = res_c
+    _, _, kpa, vpa = res_p
+    for b in range(B):
+        t = int(lens[b])
+        assert np.array_equal(kc[b, :, t], kn[b]) and np.array_equal(vc[b, :, t], vn[b]), "contiguous slot"
+        pg, row = table[b, t // P], t % P
+        assert np.array_equal(kpa[pg, :, row], kn[b]) and np.array_equal(vpa[pg, :, row], vn[b]), "paged slot"
+    assert int(np.sum(kc != k)) == B * Hkv * D and int(np.sum(vc != v)) == B * Hkv * D, "contiguous: one row per (b, j)"
+    assert int(np.sum(kpa != kp)) == B * Hkv * D and int(np.sum(vpa != vp)) == B * Hkv * D, "paged: one row per (b, j)"
+
+
+def pin_append_full_cache(orc):
+    """A full cache (T_b = T, or every page of the table in use) has no slot:
+    the new token is still attended and nothing is stored.  Checked against
+    a decode over caches one token longer built by concatenation."""
+    rng = _rng(44)
+    B, Hq, Hkv, T, D, P = 2, 2, 1, 6, 4, 3
+    q = rng.standard_normal((B, Hq, D))
+    k = rng.standard_normal((B, Hkv, T, D))
+    v = rng.standard_normal((B, Hkv, T, D))
+    kn = rng.standard_normal((B, Hkv, D))
+    vn = rng.standard_normal((B, Hkv, D))
+    lens = np.array([T, 2], np.int32)
+    out, lse, ka, va = orc.append_decode(q, kn, vn, k, v, 1.1, lens)
+    k2 = np.concatenate([k, kn[:, :, None]], axis=2)
+    v2 = np.concatenate([v, vn[:, :, None]], axis=2)
+    ref, ref_l = orc.decode(q[0:1], k2[0:1], v2[0:1], 1.1)
+    _close(out[0:1], ref, 1e-15, "full cache out")
+    _close(lse[0:1], ref_l, 1e-15, "full cache lse")
+    assert np.array_equal(ka[0], k[0]) and np.array_equal(va[0], v[0]), "full cache must stay unchanged"
+    # paged: a table of T / P pages all in use
+    table = np.array([[1, 0], [3, 2]], np.int32)
+    kp = np.zeros((4, Hkv, P, D))
+    vp = np.zeros((4, Hkv, P, D))
+    for b in range(B):
+        for i in range(2):
+            kp[table[b, i]] = k[b, :, i * P:(i + 1) * P]
+            vp[table[b, i]] = v[b, :, i * P:(i + 1) * P]
+    out_p, lse_p, kpa, vpa = orc.append_decode(q, kn, vn, kp, vp, 1.1, lens, page_table=table)
+    _close(out_p, out, 1e-15, "full paged table == full contiguous cache")
+    _close(lse_p, lse, 1e-15, "full paged table lse")
+    assert np.array_equal(kpa[table[0]], kp[table[0]]), "full paged cache must stay unchanged"
+
+
+APPEND_PINS = [pin_append_to_empty, pin_append_two_tokens, pin_append_mpmath, pin_append_full_cache]
+
+
 ALL_PINS = [
     pin_single_token, pin_constant_values, pin_uniform_weights, pin_two_tokens,
     pin_dominant_logit, pin_torch_sdpa, pin_mpmath_bruteforce, pin_f16_decoder,

@@ -67,3 +67,40 @@ def test_mutant_is_caught(tmp_path, name, old, new):
             caught.append(pin.__name__)
     assert caught, f"mutant {name} passed every pin"
     shutil.rmtree(str(tmp_path), ignore_errors=True)
+
+
+# Mistakes planted in the oracle's append-then-decode step (oracle.py).
+PY_SRC = oracle_mod.__file__
+APPEND_MUTANTS = [
+    ("append_not_attended", "grown = (sl + 1).astype(np.int32)", "grown = sl.astype(np.int32)"),
+    ("append_values_from_k", "v_att[b, :, t] = vn[b]", "v_att[b, :, t] = kn[b]"),
+    ("append_heads_reversed", "k_att[b, :, t] = kn[b]", "k_att[b, :, t] = kn[b, ::-1]"),
+    ("append_store_next_slot", "                    ka[b, :, t] = kn[b]",
+     "                    ka[b, :, min(t + 1, T - 1)] = kn[b]"),
+    ("append_store_skipped", "                    va[b, :, t] = vn[b]\n", "\n"),
+    ("append_paged_row", "ka[pt[b, col], :, t % P] = kn[b]", "ka[pt[b, col], :, (t + 1) % P] = kn[b]"),
+    ("append_spare_row", "k_att[num_pages + i, :, t % P] = kn[b]",
+     "k_att[num_pages + i, :, (t + 1) % P] = kn[b]"),
+]
+
+
+def _load_py_mutant(name, old, new):
+    import types
+    text = open(PY_SRC).read()
+    assert text.count(old) == 1, f"mutant {name}: pattern must occur once"
+    mod = types.ModuleType(f"oracle_mut_{name}")
+    mod.__file__ = PY_SRC                      # same directory: the same C library
+    exec(compile(text.replace(old, new), PY_SRC, "exec"), mod.__dict__)
+    return mod.Oracle(oracle_mod.default().path)
+
+
+@pytest.mark.parametrize("name,old,new", APPEND_MUTANTS, ids=[m[0] for m in APPEND_MUTANTS])
+def test_append_mutant_is_caught(name, old, new):
+    orc = _load_py_mutant(name, old, new)
+    caught = []
+    for pin in oracle_pins.APPEND_PINS:
+        try:
+            pin(orc)
+        except (AssertionError, ValueError, FloatingPointError):
+            caught.append(pin.__name__)
+    assert caught, f"mutant {name} passed every append pin"

@@ -15,6 +15,11 @@ def test_pin(orc, pin):
     pin(orc)
 
 
+@pytest.mark.parametrize("pin", oracle_pins.APPEND_PINS, ids=lambda f: f.__name__)
+def test_append_pin(orc, pin):
+    pin(orc)
+
+
 def test_rejects_bad_arguments(orc):
     import numpy as np
     q = np.zeros((1, 3, 4))
