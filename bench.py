@@ -139,6 +139,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--set", action="append", default=[], metavar="KEY=VALUE",
                     help="override a workload field (experiments; e.g. T=65536)")
+    ap.add_argument("--append", action="store_true",
+                    help="time fd_append_decode: each sequence caches T_b - 1 tokens and the step "
+                         "stores and attends to token T_b (same KV bytes as the plain step)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (for counter scaling) and exit")
     args = ap.parse_args()
@@ -172,15 +175,22 @@ def main() -> int:
     case = inputs.make_case(spec, device="cuda")
     lens = case.lengths()
     kv_bytes = kv_bytes_of(spec, lens)
+    new_rows = (None, None)
+    seq_lens = case.seq_lens
+    if args.append:
+        # the step's new token is the last of each sequence's T_b tokens
+        seq_lens = torch.tensor([max(0, n - 1) for n in lens], dtype=torch.int32, device="cuda")
+        new_rows = inputs.make_new_token(spec, 0, device="cuda")
     copies = max(2, min(16, math.ceil((1 << 30) / kv_bytes) + 1))
     decs = []
     for c in range(copies):
         k = case.k if c == 0 else case.k.clone()
         v = case.v if c == 0 else case.v.clone()
         decs.append(Decoder(case.q, k, v, scale=spec.scale, page_table=case.page_table,
-                            seq_lens=case.seq_lens, T=spec.T if case.page_table is not None else None,
+                            seq_lens=seq_lens, T=spec.T if case.page_table is not None else None,
                             n_splits=args.n_splits or spec.n_splits, path=args.path,
-                            fused_merge={"auto": None, "fused": True, "combine": False}[args.merge]))
+                            fused_merge={"auto": None, "fused": True, "combine": False}[args.merge],
+                            k_new=new_rows[0], v_new=new_rows[1]))
     plan = decs[0].plan
     print(f"[bench] plan {plan}; {copies} KV copies", file=sys.stderr, flush=True)
 
@@ -189,7 +199,8 @@ def main() -> int:
     torch.cuda.synchronize()
 
     K = args.steps
-    separate = plan["combine"] and not plan["fused"]
+    # fd_append_decode has no separate passes: its step is timed as a whole
+    separate = plan["combine"] and not plan["fused"] and not args.append
     # HIP events bracket the launches of every EVERY-th step (the others run
     # without markers, which would otherwise add their own gaps).
     every = max(1, args.event_every)
@@ -248,7 +259,8 @@ def main() -> int:
                    "D": spec.D, "T": spec.T, "kv_dtype": spec.dtype, "accumulate": "f32",
                    "kv_bytes_per_step": kv_bytes, "kv_copies_rotated": copies,
                    "n_splits": plan["n_splits"], "chunk": plan["chunk"], "path": plan["path"],
-                   "fused_merge": plan["fused"], "seed": spec.seed},
+                   "fused_merge": plan["fused"], "seed": spec.seed,
+                   "step": "fd_append_decode" if args.append else "fd_decode"},
         "us_per_step": round(ms_per_step * 1e3, 2),
         "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,

@@ -75,6 +75,12 @@ typedef enum {
  * kernel otherwise.  These flags force one or the other. */
 #define FD_FLAG_FUSED_MERGE 0x1
 #define FD_FLAG_COMBINE_KERNEL 0x2
+/* Plan for fd_append_decode: every sequence attends to one more token than
+ * it has cached (plans cover T + 1 tokens).  Pass it to fd_plan /
+ * fd_workspace_bytes to size the workspace of an append call;
+ * fd_append_decode sets it itself, and fd_decode / fd_split / fd_combine
+ * reject it. */
+#define FD_FLAG_APPEND 0x4
 
 /* Options of a call.  Initialise with fd_options_init() and then set the
  * fields you need; struct_size versions the layout. */
@@ -172,6 +178,34 @@ fd_status_t fd_decode(const void *q, const void *k_cache, const void *v_cache,
                       float *out, float *lse,
                       int B, int Hq, int Hkv, int T, int D, float scale,
                       int n_splits, const fd_options_t *opt);
+
+/*
+ * Fused append-KV decode step (dupenodi guide "FlashDecoding and split-KV",
+ * "Walking through it": serving stacks pair split-KV decode with fused
+ * append-KV paths).  In one pass over the cache, for every sequence b with
+ * T_b = seq_lens[b] cached tokens (T when seq_lens is NULL):
+ *   - the new token's rows k_new[b, j, :] and v_new[b, j, :] (every kv
+ *     head j) are stored as token T_b of the cache: row T_b of a contiguous
+ *     cache, or row T_b % page_size of page page_table[b, T_b / page_size];
+ *   - out / lse are decode attention over tokens 0 .. T_b, the new one
+ *     included (read from k_new / v_new, not from the cache).
+ *   k_new, v_new : device, [B, Hkv, D] in opt->dtype, 16-byte aligned; they
+ *                  must not overlap the caches.
+ *   k_cache, v_cache : written at the new token's slot only.  A sequence
+ *                  whose cache is full (T_b = T; paged: no table column
+ *                  T_b / page_size, or a column naming no pool page) stores
+ *                  nothing but still attends to its new token.
+ *   seq_lens     : lengths before the append; the library does not update
+ *                  them (the caller adds one for the next step).
+ * Everything else as fd_decode; the workspace is sized by fd_workspace_bytes
+ * with FD_FLAG_APPEND in opt->flags.
+ */
+fd_status_t fd_append_decode(const void *q, const void *k_new, const void *v_new,
+                             void *k_cache, void *v_cache,
+                             const int32_t *page_table, const int32_t *seq_lens,
+                             float *out, float *lse,
+                             int B, int Hq, int Hkv, int T, int D, float scale,
+                             int n_splits, const fd_options_t *opt);
 
 /*
  * The split pass alone (tinyvolt, "Visualizing operations in a single

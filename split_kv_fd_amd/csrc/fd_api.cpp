@@ -78,7 +78,7 @@ fd_status_t read_options(const fd_options_t *opt, fd_options_t *o) {
     if (o->path != FD_PATH_AUTO && o->path != FD_PATH_VALU && o->path != FD_PATH_MFMA)
         return fail(FD_ERR_INVALID_ARG, "unknown path %d", (int)o->path);
     if (o->num_cus < 0) return fail(FD_ERR_INVALID_ARG, "num_cus %d < 0", (int)o->num_cus);
-    if (o->flags & ~(FD_FLAG_FUSED_MERGE | FD_FLAG_COMBINE_KERNEL))
+    if (o->flags & ~(FD_FLAG_FUSED_MERGE | FD_FLAG_COMBINE_KERNEL | FD_FLAG_APPEND))
         return fail(FD_ERR_INVALID_ARG, "unknown flags 0x%x", (unsigned)o->flags);
     if ((o->flags & FD_FLAG_FUSED_MERGE) && (o->flags & FD_FLAG_COMBINE_KERNEL))
         return fail(FD_ERR_INVALID_ARG, "FD_FLAG_FUSED_MERGE and FD_FLAG_COMBINE_KERNEL exclude each other");
@@ -172,9 +172,11 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
         return FD_OK;
     }
 
+    // Tokens a sequence may attend to: T, plus the appended one.
+    const long Tp = (long)T + ((o.flags & FD_FLAG_APPEND) ? 1 : 0);
     long gran = tile;
     if (paged && o.page_size > gran) gran = o.page_size;
-    const long max_n = ceil_div(T, gran);
+    const long max_n = ceil_div(Tp, gran);
     long n;
     if (n_req > 0) {
         n = n_req < max_n ? n_req : max_n;
@@ -189,11 +191,11 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
         const long target = std::max(1L, env_long("FD_TARGET_WGS", (long)cus));
         const long min_chunk = std::max(1L, env_long("FD_CHUNK_MIN", 512));
         n = ceil_div(target, units);
-        const long cap = T / min_chunk > 1 ? T / min_chunk : 1;
+        const long cap = Tp / min_chunk > 1 ? Tp / min_chunk : 1;
         if (n > cap) n = cap;
         if (paged) {
             const long ragged_chunk = std::max(1L, env_long("FD_RAGGED_CHUNK", 1024));
-            const long nr = ceil_div(T, ragged_chunk);
+            const long nr = ceil_div(Tp, ragged_chunk);
             if (n < nr) n = nr;
             // Workgroups go to the 8 XCDs round-robin by linear id, with the
             // split index fastest: a multiple of 8 splits spreads each
@@ -204,14 +206,14 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
     if (paged) {
         // a split stages its page ids on chip: at most kMaxSplitPages pages
         const long max_chunk = (long)fdk::kMaxSplitPages * o.page_size;
-        const long n_min = ceil_div(T, max_chunk);
+        const long n_min = ceil_div(Tp, max_chunk);
         if (n < n_min) n = n_min;
     }
     if (n < 1) n = 1;
-    long chunk = ceil_div(ceil_div(T, n), gran) * gran;
+    long chunk = ceil_div(ceil_div(Tp, n), gran) * gran;
     if (paged && chunk > (long)fdk::kMaxSplitPages * o.page_size)
         chunk = (long)fdk::kMaxSplitPages * o.page_size;
-    n = ceil_div(T, chunk);
+    n = ceil_div(Tp, chunk);
 
     p->n_splits = (int)n;
     p->chunk = (int)chunk;
@@ -255,12 +257,24 @@ struct Call {
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // Everything fd_decode / fd_split / fd_combine check before launching.
+// k_new / v_new: the appended token's rows (fd_append_decode), else nullptr.
 fd_status_t prepare(const void *q, const void *k, const void *v, const int32_t *page_table,
                     const int32_t *seq_lens, float *out, float *lse, int B, int Hq, int Hkv,
                     int T, int D, float scale, int n_req, const fd_options_t *opt, bool need_inputs,
-                    Call *c) {
+                    const void *k_new, const void *v_new, Call *c) {
     fd_status_t st = read_options(opt, &c->o);
     if (st != FD_OK) return st;
+    const bool append = k_new != nullptr;
+    if (append) {
+        c->o.flags |= FD_FLAG_APPEND;
+        if (!v_new) return fail(FD_ERR_INVALID_ARG, "k_new and v_new must be non-NULL");
+        if (!aligned(k_new, 16) || !aligned(v_new, 16))
+            return fail(FD_ERR_INVALID_ARG, "k_new and v_new must be 16-byte aligned");
+        if (k_new == k || v_new == v || k_new == v || v_new == k)
+            return fail(FD_ERR_INVALID_ARG, "k_new and v_new must not be the caches");
+    } else if (c->o.flags & FD_FLAG_APPEND) {
+        return fail(FD_ERR_INVALID_ARG, "FD_FLAG_APPEND plans are run by fd_append_decode");
+    }
     if (need_inputs) {
         if (!q || !k || !v) return fail(FD_ERR_INVALID_ARG, "q, k_cache and v_cache must be non-NULL");
         if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
@@ -340,6 +354,11 @@ fd_status_t prepare(const void *q, const void *k, const void *v, const int32_t *
     s.counters = counters;
     s.stream = c->p.stream;
     s.stream_align = c->p.tile;
+    s.append = append ? 1 : 0;
+    s.k_new = k_new;
+    s.v_new = v_new;
+    s.k_store = const_cast<void *>(k);
+    s.v_store = const_cast<void *>(v);
     {
         const int merge_heads = s.G < c->p.heads_per_block ? s.G : c->p.heads_per_block;
         s.merge_cap = (int)(fdk::kMergeMaxPairsHost / merge_heads);
@@ -352,6 +371,7 @@ fd_status_t prepare(const void *q, const void *k, const void *v, const int32_t *
     cb.B = B; cb.Hq = Hq; cb.T = T; cb.D = D;
     cb.n_splits = c->p.n_splits;
     cb.chunk = c->p.chunk;
+    cb.append = append ? 1 : 0;
     return FD_OK;
 }
 
@@ -457,7 +477,21 @@ fd_status_t fd_decode(const void *q, const void *k_cache, const void *v_cache, c
                       float scale, int n_splits, const fd_options_t *opt) {
     Call c;
     fd_status_t st = prepare(q, k_cache, v_cache, page_table, seq_lens, out, lse, B, Hq, Hkv, T, D, scale,
-                             n_splits, opt, true, &c);
+                             n_splits, opt, true, nullptr, nullptr, &c);
+    if (st != FD_OK) return st;
+    const bool fused = c.p.fused != 0;
+    st = run_split(c, fused);
+    if (st != FD_OK || fused) return st;
+    return run_combine(c);
+}
+
+fd_status_t fd_append_decode(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                             const int32_t *page_table, const int32_t *seq_lens, float *out, float *lse, int B,
+                             int Hq, int Hkv, int T, int D, float scale, int n_splits, const fd_options_t *opt) {
+    Call c;
+    if (!k_new) return fail(FD_ERR_INVALID_ARG, "k_new and v_new must be non-NULL");
+    fd_status_t st = prepare(q, k_cache, v_cache, page_table, seq_lens, out, lse, B, Hq, Hkv, T, D, scale,
+                             n_splits, opt, true, k_new, v_new, &c);
     if (st != FD_OK) return st;
     const bool fused = c.p.fused != 0;
     st = run_split(c, fused);
@@ -470,7 +504,7 @@ fd_status_t fd_split(const void *q, const void *k_cache, const void *v_cache, co
                      float scale, int n_splits, const fd_options_t *opt) {
     Call c;
     fd_status_t st = prepare(q, k_cache, v_cache, page_table, seq_lens, out, lse, B, Hq, Hkv, T, D, scale,
-                             n_splits, opt, true, &c);
+                             n_splits, opt, true, nullptr, nullptr, &c);
     if (st != FD_OK) return st;
     return run_split(c, false);
 }
@@ -479,7 +513,7 @@ fd_status_t fd_combine(const int32_t *seq_lens, float *out, float *lse, int B, i
                        int n_splits, const fd_options_t *opt) {
     Call c;
     fd_status_t st = prepare(nullptr, nullptr, nullptr, nullptr, seq_lens, out, lse, B, Hq, Hkv, T, D, 1.0f,
-                             n_splits, opt, false, &c);
+                             n_splits, opt, false, nullptr, nullptr, &c);
     if (st != FD_OK) return st;
     return run_combine(c);
 }

@@ -50,6 +50,7 @@ __global__ __launch_bounds__(256) void combine(CombineArgs a) {
         Tb = a.seq_lens[b];
         Tb = Tb < 0 ? 0 : (Tb > a.T ? a.T : Tb);
     }
+    Tb += a.append;                          // the appended token
     int n = (Tb + a.chunk - 1) / a.chunk;   // splits that hold tokens
     n = n < a.n_splits ? n : a.n_splits;
 

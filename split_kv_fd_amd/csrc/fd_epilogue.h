@@ -108,6 +108,45 @@ __device__ void write_empty_group(const SplitArgs &a, int b, int h0, int ng) {
     }
 }
 
+// Tokens of sequence b already in the cache (clamped to [0, T]).
+__device__ __forceinline__ int cached_len(const SplitArgs &a, int b) {
+    const int Tb = a.seq_lens ? a.seq_lens[b] : a.T;
+    return Tb < 0 ? 0 : (Tb > a.T ? a.T : Tb);
+}
+
+// Tokens sequence b attends to: the cached ones, plus the new one when
+// appending.
+__device__ __forceinline__ int attended_len(const SplitArgs &a, int b) { return cached_len(a, b) + a.append; }
+
+// Append: store the new token's key and value rows of (b, kvh) at token Tc
+// of the cache -- row Tc of a contiguous cache when Tc < T, or row Tc % P of
+// page page_table[b, Tc / P] when that column exists and names a pool page.
+// Without such a slot nothing is stored (the token is still attended).  No
+// workgroup of the launch reads that slot: every one that covers token Tc
+// takes it from k_new / v_new.
+template <int ROWB>
+__device__ void store_new_token(const SplitArgs &a, int b, int kvh, int Tc) {
+    size_t row;
+    if (a.page_table) {
+        const int col = Tc >> a.page_shift;
+        const int page = col < a.max_pages ? a.page_table[(size_t)b * a.max_pages + col] : -1;
+        if ((unsigned)page >= (unsigned)a.num_pages) return;
+        row = ((size_t)page * a.Hkv + kvh) * (size_t)a.page_size + (size_t)(Tc & (a.page_size - 1));
+    } else {
+        if (Tc >= a.T) return;
+        row = ((size_t)b * a.Hkv + kvh) * (size_t)a.T + (size_t)Tc;
+    }
+    const size_t src = ((size_t)b * a.Hkv + kvh) * (ROWB / 16);
+    const uint4 *ks = static_cast<const uint4 *>(a.k_new) + src;
+    const uint4 *vs = static_cast<const uint4 *>(a.v_new) + src;
+    uint4 *kd = static_cast<uint4 *>(a.k_store) + row * (ROWB / 16);
+    uint4 *vd = static_cast<uint4 *>(a.v_store) + row * (ROWB / 16);
+    for (int i = threadIdx.x; i < ROWB / 16; i += blockDim.x) {
+        kd[i] = ks[i];
+        vd[i] = vs[i];
+    }
+}
+
 // Splits that hold tokens of a sequence of length Tb.
 __device__ __forceinline__ int active_splits(const SplitArgs &a, int Tb) {
     const int n = (Tb + a.chunk - 1) / a.chunk;
@@ -316,10 +355,7 @@ __device__ void drive_stream(const SplitArgs &a, long long *pref, int hpb, Seg &
     const int t = threadIdx.x;
     const int RB = a.Hkv * a.head_blocks;             // rows per sequence
     const int align = a.stream_align;
-    auto real_len = [&](int b) {
-        int Tb = a.seq_lens ? a.seq_lens[b] : a.T;
-        return Tb < 0 ? 0 : (Tb > a.T ? a.T : Tb);
-    };
+    auto real_len = [&](int b) { return attended_len(a, b); };
     auto pad_len = [&](int b) { return (long long)((real_len(b) + align - 1) / align) * align; };
 
     // exclusive prefix over sequences of RB * padded length, and the longest row

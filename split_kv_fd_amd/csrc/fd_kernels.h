@@ -53,6 +53,14 @@ struct SplitArgs {
     int stream;
     int stream_align;
     int merge_cap;               // most segments one row may have (fused merge)
+    // Append (fused append-KV): the new token's rows k_new / v_new [B, Hkv,
+    // D] are token T_b = seq_lens[b] of each sequence, which then has T_b + 1
+    // tokens; the workgroup that covers it also stores them into the caches.
+    int append;
+    const void *k_new;
+    const void *v_new;
+    void *k_store;               // the caches again, writable
+    void *v_store;
 };
 
 // Most sequences a stream-mode launch handles (its LDS prefix array).
@@ -67,6 +75,7 @@ struct CombineArgs {
     float *lse;
     int B, Hq, T, D;
     int n_splits, chunk;
+    int append;                  // sequences hold seq_lens[b] + 1 tokens
 };
 
 // Shape constants of the vector-ALU split kernel.  Each 64-lane wavefront

@@ -174,6 +174,52 @@ __global__ __launch_bounds__(256, 2) void split_mfma(SplitArgs a) {
             }
         };
 
+        // K/V pieces of one 32-token wave step (two 16-token tiles).
+        struct Buf {
+            uint4 k[2][KS];
+            VP v[2][4];
+            bool ok[2][4];
+        };
+
+        auto consume_step = [&](const Buf &f) {
+            float s[2][4];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                f32x4_v c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) c = mfma_logits<DT>(f.k[h][ks], qb[ks], c);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) s[h][r] = f.ok[h][r] ? c[r] * a.scale_log2 : kNegInf;
+            }
+            float mt = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                             fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+            mt = fmaxf(mt, __shfl_xor(mt, 16));
+            mt = fmaxf(mt, __shfl_xor(mt, 32));
+            const float mn = fmaxf(m, mt);
+            const float mu = mn == kNegInf ? 0.f : mn;
+            const float alpha = __builtin_amdgcn_exp2f(m - mu);
+            float p[2][4];
+            float ps = 0.f;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) { p[h][r] = __builtin_amdgcn_exp2f(s[h][r] - mu); ps += p[h][r]; }
+            l = l * alpha + ps;
+            m = mn;
+#pragma unroll
+            for (int i = 0; i < PVE; ++i) acc[i] *= alpha;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float vf[PVE];
+                    widen<DT>(f.v[h][r], vf);
+#pragma unroll
+                    for (int i = 0; i < PVE; ++i)
+                        acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[i], p[h][r], acc[i], 0, 0, 0);
+                }
+        };
+
         auto stream_range = [&](int r0, int r1) {
             auto row_offset = [&](int t, bool &ok) -> Off {
                 ok = t < r1;
@@ -185,12 +231,6 @@ __global__ __launch_bounds__(256, 2) void split_mfma(SplitArgs a) {
                 } else {
                     return (uint32_t)tc * (uint32_t)ROWB;
                 }
-            };
-
-            struct Buf {
-                uint4 k[2][KS];
-                VP v[2][4];
-                bool ok[2][4];
             };
 
             // Pages of 16 tokens or more: a 16-token block (16-aligned, as every
@@ -245,45 +285,6 @@ __global__ __launch_bounds__(256, 2) void split_mfma(SplitArgs a) {
                 }
             };
 
-            auto consume_step = [&](const Buf &f) {
-                float s[2][4];
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    f32x4_v c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int ks = 0; ks < KS; ++ks) c = mfma_logits<DT>(f.k[h][ks], qb[ks], c);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) s[h][r] = f.ok[h][r] ? c[r] * a.scale_log2 : kNegInf;
-                }
-                float mt = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                                 fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-                mt = fmaxf(mt, __shfl_xor(mt, 16));
-                mt = fmaxf(mt, __shfl_xor(mt, 32));
-                const float mn = fmaxf(m, mt);
-                const float mu = mn == kNegInf ? 0.f : mn;
-                const float alpha = __builtin_amdgcn_exp2f(m - mu);
-                float p[2][4];
-                float ps = 0.f;
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) { p[h][r] = __builtin_amdgcn_exp2f(s[h][r] - mu); ps += p[h][r]; }
-                l = l * alpha + ps;
-                m = mn;
-#pragma unroll
-                for (int i = 0; i < PVE; ++i) acc[i] *= alpha;
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        float vf[PVE];
-                        widen<DT>(f.v[h][r], vf);
-#pragma unroll
-                        for (int i = 0; i < PVE; ++i)
-                            acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[i], p[h][r], acc[i], 0, 0, 0);
-                    }
-            };
-
             Buf fa, fb;
             load_step(r0, fa);
             for (int base = r0;; base += 2 * TILE) {
@@ -300,17 +301,49 @@ __global__ __launch_bounds__(256, 2) void split_mfma(SplitArgs a) {
             }
         };
 
+        // Appending: the segment that reaches token Tc (the new one) streams
+        // the cached tokens before it and takes the new token from k_new /
+        // v_new below.
+        int e1 = c1;
+        int Tc = 0;
+        if (a.append) {
+            Tc = cached_len(a, b);
+            e1 = c1 < Tc ? c1 : Tc;
+        }
+
         if constexpr (PAGED) {
             // ranges of at most kMaxSplitPages pages: each ends on a page
             // boundary, so a start inside a page still fits the stage
-            for (int r0 = c0, r1; r0 < c1; r0 = r1) {
+            for (int r0 = c0, r1; r0 < e1; r0 = r1) {
                 const long long e = ((long long)(r0 >> a.page_shift) + kMaxSplitPages) << a.page_shift;
-                r1 = e < c1 ? (int)e : c1;
+                r1 = e < e1 ? (int)e : e1;
                 stage_pages(r0, r1);
                 stream_range(r0, r1);
             }
         } else {
-            if (c0 < c1) stream_range(c0, c1);
+            if (c0 < e1) stream_range(c0, e1);
+        }
+
+        if (a.append && c1 > Tc) {
+            // The new token as token 0 of wave 0's first tile: every row of
+            // the tile reads the new rows, all but that one are masked.
+            const size_t nr = ((size_t)b * a.Hkv + kvh) * ROWB;
+            const char *kn = static_cast<const char *>(a.k_new) + nr;
+            const char *vn = static_cast<const char *>(a.v_new) + nr;
+            Buf f;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    f.k[h][ks] = *reinterpret_cast<const uint4 *>(kn + (4 * ks + kb) * 16);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    f.v[h][r] = *reinterpret_cast<const VP *>(vn + i16 * VB);
+                    f.ok[h][r] = wave == 0 && h == 0 && kb == 0 && r == 0;
+                }
+            }
+            consume_step(f);
+            if (hb == 0) store_new_token<ROWB>(a, b, kvh, Tc);
         }
 
         // The four lanes of a head share m; their sums cover different tokens.
@@ -335,11 +368,7 @@ __global__ __launch_bounds__(256, 2) void split_mfma(SplitArgs a) {
         const int kvh = blockIdx.y / a.head_blocks;
         const int hb = blockIdx.y - kvh * a.head_blocks;
         const int b = blockIdx.z;
-        int Tb = a.T;
-        if (a.seq_lens) {
-            Tb = a.seq_lens[b];
-            Tb = Tb < 0 ? 0 : (Tb > a.T ? a.T : Tb);
-        }
+        const int Tb = attended_len(a, b);
         const int c0 = split * a.chunk;
         const int c1 = min(c0 + a.chunk, Tb);
         const int h0 = kvh * a.G + hb * GB;

@@ -185,6 +185,47 @@ __global__ __launch_bounds__(256) void split_valu(SplitArgs a) {
             }
         };
 
+        auto consume_step = [&](const uint4 (&kr)[U][VEC], const uint4 (&vr)[U][VEC], const bool (&ok)[U]) {
+            float s[U][GB];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int g = 0; g < GB; ++g) {
+                    float acc = 0.f;
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v) acc = dot_piece<DT>(qv[g][v], kr[u][v], acc);
+                    acc = row_sum<LPR>(acc) * a.scale_log2;
+                    s[u][g] = ok[u] ? acc : kNegInf;
+                }
+            float vf[U][EPT];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) widen<DT>(vr[u][v], &vf[u][v * EPC]);
+#pragma unroll
+            for (int g = 0; g < GB; ++g) {
+                float mt = s[0][g];
+#pragma unroll
+                for (int u = 1; u < U; ++u) mt = fmaxf(mt, s[u][g]);
+                const float mn = fmaxf(m[g], mt);
+                const float mu = mn == kNegInf ? 0.f : mn;
+                const float alpha = exp2_fast(m[g] - mu);
+                float p[U];
+                float ps = 0.f;
+#pragma unroll
+                for (int u = 0; u < U; ++u) { p[u] = exp2_fast(s[u][g] - mu); ps += p[u]; }
+                l[g] = l[g] * alpha + ps;
+#pragma unroll
+                for (int e = 0; e < EPT; ++e) {
+                    float acc = o[g][e] * alpha;
+#pragma unroll
+                    for (int u = 0; u < U; ++u) acc = fmaf(p[u], vf[u][e], acc);
+                    o[g][e] = acc;
+                }
+                m[g] = mn;
+            }
+        };
+
         auto stream_range = [&](int r0, int r1) {
             // Byte offset of token t's row and whether the token is real.  A
             // contiguous (batch, kv head) slice is below 4 GiB (checked on the
@@ -215,47 +256,6 @@ __global__ __launch_bounds__(256) void split_valu(SplitArgs a) {
                 }
             };
 
-            auto consume_step = [&](const uint4 (&kr)[U][VEC], const uint4 (&vr)[U][VEC], const bool (&ok)[U]) {
-                float s[U][GB];
-#pragma unroll
-                for (int u = 0; u < U; ++u)
-#pragma unroll
-                    for (int g = 0; g < GB; ++g) {
-                        float acc = 0.f;
-#pragma unroll
-                        for (int v = 0; v < VEC; ++v) acc = dot_piece<DT>(qv[g][v], kr[u][v], acc);
-                        acc = row_sum<LPR>(acc) * a.scale_log2;
-                        s[u][g] = ok[u] ? acc : kNegInf;
-                    }
-                float vf[U][EPT];
-#pragma unroll
-                for (int u = 0; u < U; ++u)
-#pragma unroll
-                    for (int v = 0; v < VEC; ++v) widen<DT>(vr[u][v], &vf[u][v * EPC]);
-#pragma unroll
-                for (int g = 0; g < GB; ++g) {
-                    float mt = s[0][g];
-#pragma unroll
-                    for (int u = 1; u < U; ++u) mt = fmaxf(mt, s[u][g]);
-                    const float mn = fmaxf(m[g], mt);
-                    const float mu = mn == kNegInf ? 0.f : mn;
-                    const float alpha = exp2_fast(m[g] - mu);
-                    float p[U];
-                    float ps = 0.f;
-#pragma unroll
-                    for (int u = 0; u < U; ++u) { p[u] = exp2_fast(s[u][g] - mu); ps += p[u]; }
-                    l[g] = l[g] * alpha + ps;
-#pragma unroll
-                    for (int e = 0; e < EPT; ++e) {
-                        float acc = o[g][e] * alpha;
-#pragma unroll
-                        for (int u = 0; u < U; ++u) acc = fmaf(p[u], vf[u][e], acc);
-                        o[g][e] = acc;
-                    }
-                    m[g] = mn;
-                }
-            };
-
             // Two register buffers used in turn: while one step is consumed
             // the next one is in flight.  The fence keeps each prefetch where
             // it is issued (otherwise the compiler sinks every load next to
@@ -278,17 +278,48 @@ __global__ __launch_bounds__(256) void split_valu(SplitArgs a) {
             }
         };
 
+        // Appending: the segment that reaches token Tc (the new one) streams
+        // the cached tokens before it and takes the new token from k_new /
+        // v_new below.
+        int e1 = c1;
+        int Tc = 0;
+        if (a.append) {
+            Tc = cached_len(a, b);
+            e1 = c1 < Tc ? c1 : Tc;
+        }
+
         if constexpr (PAGED) {
             // ranges of at most kMaxSplitPages pages: each ends on a page
             // boundary, so a start inside a page still fits the stage
-            for (int r0 = c0, r1; r0 < c1; r0 = r1) {
+            for (int r0 = c0, r1; r0 < e1; r0 = r1) {
                 const long long e = ((long long)(r0 >> a.page_shift) + kMaxSplitPages) << a.page_shift;
-                r1 = e < c1 ? (int)e : c1;
+                r1 = e < e1 ? (int)e : e1;
                 stage_pages(r0, r1);
                 stream_range(r0, r1);
             }
         } else {
-            if (c0 < c1) stream_range(c0, c1);
+            if (c0 < e1) stream_range(c0, e1);
+        }
+
+        if (a.append && c1 > Tc) {
+            // The new token as row 0 of wave 0's first step: every row reads
+            // the new rows, all but that one are masked.
+            const size_t nr = ((size_t)b * a.Hkv + kvh) * ROWB;
+            const char *kn = static_cast<const char *>(a.k_new) + nr;
+            const char *vn = static_cast<const char *>(a.v_new) + nr;
+            uint4 kr[U][VEC], vr[U][VEC];
+            bool ok[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) {
+                    kr[u][v] = *reinterpret_cast<const uint4 *>(kn + (v * LPR + sub) * 16);
+                    vr[u][v] = *reinterpret_cast<const uint4 *>(vn + (v * LPR + sub) * 16);
+                }
+                ok[u] = wave == 0 && u == 0 && row == 0;
+            }
+            consume_step(kr, vr, ok);
+            if (hb == 0) store_new_token<ROWB>(a, b, kvh, Tc);
         }
 
         // Merge the rows of this wave (log-sum-exp, rows LPR, 2*LPR, ... apart).
@@ -336,11 +367,7 @@ __global__ __launch_bounds__(256) void split_valu(SplitArgs a) {
         const int kvh = blockIdx.y / a.head_blocks;
         const int hb = blockIdx.y - kvh * a.head_blocks;
         const int b = blockIdx.z;
-        int Tb = a.T;
-        if (a.seq_lens) {
-            Tb = a.seq_lens[b];
-            Tb = Tb < 0 ? 0 : (Tb > a.T ? a.T : Tb);
-        }
+        const int Tb = attended_len(a, b);
         const int c0 = split * a.chunk;
         const int c1 = min(c0 + a.chunk, Tb);
         const int h0 = kvh * a.G + hb * GB;

@@ -28,7 +28,8 @@ class FDError(RuntimeError):
 def make_options(dtype: torch.dtype, *, page_size: int = 0, max_pages: int = 0,
                  num_pages: int = 0, workspace: Optional[torch.Tensor] = None,
                  stream: Optional[int] = None, num_cus: int = 0,
-                 path: Optional[str] = None, fused_merge: Optional[bool] = None) -> fd.fd_options_t:
+                 path: Optional[str] = None, fused_merge: Optional[bool] = None,
+                 append: bool = False) -> fd.fd_options_t:
     opt = fd.fd_options_t()
     fd.fd_options_init(opt)
     opt.dtype = _DTYPE[dtype]
@@ -40,6 +41,8 @@ def make_options(dtype: torch.dtype, *, page_size: int = 0, max_pages: int = 0,
     # None: the library chooses; True / False force the fused merge / the
     # combine kernel.
     opt.flags = {None: 0, True: fd.FD_FLAG_FUSED_MERGE, False: fd.FD_FLAG_COMBINE_KERNEL}[fused_merge]
+    if append:
+        opt.flags |= fd.FD_FLAG_APPEND
     if workspace is not None:
         opt.workspace = workspace.data_ptr()
         opt.workspace_bytes = workspace.numel() * workspace.element_size()
@@ -48,11 +51,12 @@ def make_options(dtype: torch.dtype, *, page_size: int = 0, max_pages: int = 0,
 
 
 def plan(B, Hq, Hkv, T, D, n_splits=0, *, dtype=torch.bfloat16, page_size=0, max_pages=0,
-         num_pages=1, num_cus=0, path=None, fused_merge=None) -> dict:
-    """What fd_decode would launch for these arguments (host only)."""
+         num_pages=1, num_cus=0, path=None, fused_merge=None, append=False) -> dict:
+    """What fd_decode (fd_append_decode with append=True) would launch for
+    these arguments (host only)."""
     opt = make_options(dtype, page_size=page_size, max_pages=max_pages,
                        num_pages=num_pages if page_size else 0, num_cus=num_cus, path=path,
-                       fused_merge=fused_merge)
+                       fused_merge=fused_merge, append=append)
     p = fd.fd_plan_t()
     st = fd.fd_plan(B, Hq, Hkv, T, D, n_splits, opt, p)
     if st != fd.FD_OK:
@@ -68,14 +72,15 @@ class Decoder:
     """A prepared decode call: validated shapes, plan, outputs and workspace.
 
     Calling it launches fd_decode (or the two passes separately) on torch's
-    current stream.  The benchmark and tests use it to keep allocation out
-    of the timed region.
+    current stream; given k_new and v_new ([B, Hkv, D]) it launches
+    fd_append_decode instead, which also stores them into k, v.  The
+    benchmark and tests use it to keep allocation out of the timed region.
     """
 
     def __init__(self, q, k, v, *, scale: Optional[float] = None, page_table=None,
                  seq_lens=None, T: Optional[int] = None, n_splits: int = 0,
                  path: Optional[str] = None, fused_merge: Optional[bool] = None, out=None, lse=None,
-                 want_lse: bool = True):
+                 want_lse: bool = True, k_new=None, v_new=None):
         if q.device.type != "cuda":
             raise ValueError("q, k and v must be GPU tensors")
         if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPE:
@@ -108,12 +113,21 @@ class Decoder:
         if seq_lens is not None:
             if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,) or seq_lens.device != q.device:
                 raise ValueError("seq_lens must be int32 [B] on the GPU")
+        self.append = k_new is not None
+        if self.append:
+            if v_new is None:
+                raise ValueError("k_new and v_new go together")
+            for name, t in (("k_new", k_new), ("v_new", v_new)):
+                if t.shape != (B, Hkv, D) or t.dtype != q.dtype or t.device != q.device or not t.is_contiguous():
+                    raise ValueError(f"{name} must be a contiguous {q.dtype} [B, Hkv, D] tensor on {q.device}")
+        self.new = (k_new, v_new)
         self.scale = float(1.0 / math.sqrt(D)) if scale is None else float(scale)
         self.args = (B, Hq, Hkv, T, D)
         self.n_splits = n_splits
         self.inputs = (q, k, v, page_table, seq_lens)
         self.opt = make_options(q.dtype, page_size=page_size, max_pages=max_pages,
-                                num_pages=num_pages, path=path, fused_merge=fused_merge)
+                                num_pages=num_pages, path=path, fused_merge=fused_merge,
+                                append=self.append)
         p = fd.fd_plan_t()
         st = fd.fd_plan(B, Hq, Hkv, T, D, n_splits, self.opt, p)
         if st != fd.FD_OK:
@@ -138,7 +152,19 @@ class Decoder:
             raise FDError(st, name)
 
     def __call__(self):
-        """fd_decode: split pass and (if planned) combine pass."""
+        """fd_decode (or fd_append_decode): split pass and, if planned, the
+        combine pass."""
+        if self.append:
+            q, k, v, pt, sl = self.inputs
+            self.opt.stream = torch.cuda.current_stream(q.device).cuda_stream
+            B, Hq, Hkv, T, D = self.args
+            kn, vn = self.new
+            st = fd.fd_append_decode(_ptr(q), _ptr(kn), _ptr(vn), _ptr(k), _ptr(v), _ptr(pt),
+                                     _ptr(sl), _ptr(self.out), _ptr(self.lse), B, Hq, Hkv, T, D,
+                                     self.scale, self.n_splits, self.opt)
+            if st != fd.FD_OK:
+                raise FDError(st, "fd_append_decode")
+            return self.out, self.lse
         self._call(fd.fd_decode, "fd_decode")
         return self.out, self.lse
 
@@ -162,3 +188,13 @@ def decode(q, k, v, *, scale=None, page_table=None, seq_lens=None, T=None, n_spl
     """out [B, Hq, D] fp32 and lse [B, Hq] fp32 of single-query decode attention."""
     return Decoder(q, k, v, scale=scale, page_table=page_table, seq_lens=seq_lens, T=T,
                    n_splits=n_splits, path=path, fused_merge=fused_merge)()
+
+
+def append_decode(q, k_new, v_new, k, v, *, seq_lens, scale=None, page_table=None, T=None,
+                  n_splits=0, path=None, fused_merge=None):
+    """Store k_new, v_new [B, Hkv, D] as token seq_lens[b] of each sequence's
+    cache (k, v are updated in place), then decode over seq_lens[b] + 1
+    tokens: out [B, Hq, D] fp32 and lse [B, Hq] fp32."""
+    return Decoder(q, k, v, scale=scale, page_table=page_table, seq_lens=seq_lens, T=T,
+                   n_splits=n_splits, path=path, fused_merge=fused_merge, k_new=k_new,
+                   v_new=v_new)()

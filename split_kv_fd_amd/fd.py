@@ -19,10 +19,11 @@ FD_OK, FD_ERR_INVALID_ARG, FD_ERR_UNSUPPORTED, FD_ERR_WORKSPACE, FD_ERR_HIP = ra
 FD_PATH_AUTO, FD_PATH_VALU, FD_PATH_MFMA = -1, 0, 1
 FD_FLAG_FUSED_MERGE = 0x1
 FD_FLAG_COMBINE_KERNEL = 0x2
+FD_FLAG_APPEND = 0x4
 
 # Every function include/fd.h declares.
-EXPORTS = ("fd_options_init", "fd_plan", "fd_workspace_bytes", "fd_decode", "fd_split",
-           "fd_combine", "fd_status_string", "fd_last_error")
+EXPORTS = ("fd_options_init", "fd_plan", "fd_workspace_bytes", "fd_decode", "fd_append_decode",
+           "fd_split", "fd_combine", "fd_status_string", "fd_last_error")
 
 
 class fd_options_t(ctypes.Structure):
@@ -74,6 +75,8 @@ def load() -> ctypes.CDLL:
         for name in ("fd_decode", "fd_split"):
             getattr(lib, name).restype = _I
             getattr(lib, name).argtypes = decode_args
+        lib.fd_append_decode.restype = _I
+        lib.fd_append_decode.argtypes = [_P] * 9 + [_I] * 5 + [ctypes.c_float, _I, _OPT]
         lib.fd_combine.restype = _I
         lib.fd_combine.argtypes = [_P, _P, _P] + [_I] * 6 + [_OPT]
         lib.fd_status_string.restype = ctypes.c_char_p
@@ -100,6 +103,12 @@ def fd_decode(q, k_cache, v_cache, page_table, seq_lens, out, lse, B, Hq, Hkv, T
               n_splits, opt) -> int:
     return load().fd_decode(q, k_cache, v_cache, page_table, seq_lens, out, lse, B, Hq, Hkv, T,
                             D, scale, n_splits, ctypes.byref(opt))
+
+
+def fd_append_decode(q, k_new, v_new, k_cache, v_cache, page_table, seq_lens, out, lse, B, Hq,
+                     Hkv, T, D, scale, n_splits, opt) -> int:
+    return load().fd_append_decode(q, k_new, v_new, k_cache, v_cache, page_table, seq_lens, out,
+                                   lse, B, Hq, Hkv, T, D, scale, n_splits, ctypes.byref(opt))
 
 
 def fd_split(q, k_cache, v_cache, page_table, seq_lens, out, lse, B, Hq, Hkv, T, D, scale,

@@ -209,6 +209,14 @@ def make_case(s: Spec, device="cpu") -> Case:
     return Case(s, q, k, v)
 
 
+def make_new_token(s: Spec, step: int = 0, device="cpu"):
+    """K, V rows of one appended decode token per sequence: each [B, Hkv, D]
+    (seeded by the config seed and the step index)."""
+    k = _randn((s.B, s.Hkv, s.D), s.dtype, device, s.seed, _AUX, 5, step, 0)
+    v = _randn((s.B, s.Hkv, s.D), s.dtype, device, s.seed, _AUX, 5, step, 1)
+    return k, v
+
+
 def describe(s: Spec) -> dict:
     """The recipe of a workload as plain values (for logs and results)."""
     d = {"name": s.name, "B": s.B, "Hq": s.Hq, "Hkv": s.Hkv, "G": s.G, "D": s.D,

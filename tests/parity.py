@@ -123,3 +123,49 @@ def sampled_rows(case, rows, out, lse, what=""):
         e = compare(_Sub, go, gl, ro, rl, max_abs_v(case, b), f"{what} b={b} heads={hs}")
         worst = (max(worst[0], e[0]), max(worst[1], e[1]))
     return worst
+
+
+def run_gpu_append(case, k_new, v_new, n_splits=0, path=None, fused_merge=None, poison=False):
+    """fd_append_decode on the GPU; returns host (out, lse, k_after, v_after,
+    plan).  case.k / case.v are updated in place."""
+    dec = Decoder(case.q, case.k, case.v, scale=case.spec.scale, page_table=case.page_table,
+                  seq_lens=case.seq_lens, T=case.spec.T if case.page_table is not None else None,
+                  n_splits=n_splits, path=path, fused_merge=fused_merge, k_new=k_new, v_new=v_new)
+    if poison and dec.workspace is not None:
+        dec.workspace.fill_(0xFF)
+    announce(f"append-decode {case.spec.name} B={case.spec.B} Hq={case.spec.Hq} Hkv={case.spec.Hkv} "
+             f"T={case.spec.T} D={case.spec.D} {case.spec.dtype} seed={case.spec.seed} "
+             f"n_splits={n_splits} plan={dec.plan}")
+    out, lse = dec()
+    torch.cuda.synchronize()
+    return (out.cpu().double().numpy(), lse.cpu().double().numpy(), case.k.cpu(), case.v.cpu(),
+            dec.plan)
+
+
+def oracle_append(case_host, k_new_host, v_new_host):
+    """The oracle's append-then-decode on host copies taken before the call."""
+    c = case_host
+    return oracle_mod.default().append_decode(c.q, k_new_host, v_new_host, c.k, c.v, c.spec.scale,
+                                              c.seq_lens, page_table=c.page_table)
+
+
+def check_append(case, k_new, v_new, n_splits=0, path=None, fused_merge=None, what=""):
+    """Run fd_append_decode and compare out / lse with the oracle (tolerance
+    as decode) and the caches after the call with the oracle's, bit for
+    bit."""
+    host = case.to("cpu")
+    kn, vn = k_new.cpu(), v_new.cpu()
+    ref_out, ref_lse, ref_k, ref_v = oracle_append(host, kn, vn)
+    out, lse, k_after, v_after, plan = run_gpu_append(case, k_new, v_new, n_splits, path,
+                                                      fused_merge, poison=True)
+    if path in ("valu", "mfma"):
+        assert plan["path"] == path
+    # max |V| over the values attended to: the cached ones and the new rows
+    vmax = max(max_abs_v(host), float(vn.abs().max()))
+    err = compare(case, out, lse, ref_out, ref_lse, vmax, what or case.spec.name)
+    raw = (lambda t: t.view(torch.int16).numpy() if t.dtype == torch.bfloat16 else t.numpy())
+    ka, va = raw(k_after), raw(v_after)
+    rk = ref_k.view(np.int16) if ref_k.dtype == np.uint16 else ref_k
+    rv = ref_v.view(np.int16) if ref_v.dtype == np.uint16 else ref_v
+    assert np.array_equal(ka, rk) and np.array_equal(va, rv), f"{what}: caches after the append differ"
+    return err, plan

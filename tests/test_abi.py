@@ -115,7 +115,7 @@ def test_plan_paged_chunks_align_to_pages(lib):
     # a split stages at most 2048 page ids on chip
     st, p = plan(1, 8, 8, 65536, 128, 1, page_size=16, max_pages_per_seq=4096, num_pages=10)
     assert st == fd.FD_OK and p.chunk <= 2048 * 16 and p.n_splits >= 2
-    assert plan(1, 4, 4, 100, 128, flags=4)[0] == fd.FD_ERR_INVALID_ARG
+    assert plan(1, 4, 4, 100, 128, flags=8)[0] == fd.FD_ERR_INVALID_ARG
     assert plan(1, 4, 4, 100, 128, flags=3)[0] == fd.FD_ERR_INVALID_ARG
 
 
@@ -236,6 +236,44 @@ def test_decode_rejects_before_launch(lib):
     assert fd.fd_split(A, A, None, None, None, A, A, 1, 4, 4, 4096, 128, 0.1, 16, opts()) == fd.FD_ERR_INVALID_ARG
     assert fd.fd_combine(None, None, A, 1, 4, 4, 4096, 128, 16, opts()) == fd.FD_ERR_INVALID_ARG
     assert fd.fd_combine(None, A, A, 1, 4, 4, 4096, 128, 16, opts()) == fd.FD_ERR_WORKSPACE
+
+
+def test_append_plans_cover_one_more_token(lib):
+    for (B, Hq, Hkv, T, D) in [(1, 4, 4, 1024, 64), (2, 32, 8, 4096, 128), (1, 8, 8, 128, 128),
+                               (3, 6, 2, 1000, 64), (1, 1, 1, 1, 128)]:
+        for n in (0, 1, 4, 100000):
+            st, p = plan(B, Hq, Hkv, T, D, n, flags=fd.FD_FLAG_APPEND)
+            assert st == fd.FD_OK, fd.fd_last_error()
+            assert p.chunk * p.n_splits >= T + 1 > p.chunk * (p.n_splits - 1)
+    # paged: the stream plan does not depend on T
+    st, p = plan(4, 8, 2, 4096, 128, 0, flags=fd.FD_FLAG_APPEND, page_size=16,
+                 max_pages_per_seq=256, num_pages=10)
+    assert st == fd.FD_OK and p.stream
+
+
+def append(q=A, kn=A + 8192, vn=A + 16384, k=A, v=A, pt=None, sl=A, out=A, lse=A, shape=(1, 4, 4, 4096, 128),
+           scale=0.1, n=16, **kw):
+    return fd.fd_append_decode(q, kn, vn, k, v, pt, sl, out, lse, *shape, scale, n, opts(**kw))
+
+
+def test_append_rejects_before_launch(lib):
+    # FD_FLAG_APPEND plans are run by fd_append_decode only
+    assert decode(flags=fd.FD_FLAG_APPEND) == fd.FD_ERR_INVALID_ARG
+    assert "fd_append_decode" in fd.fd_last_error()
+    assert fd.fd_split(A, A, A, None, None, A, A, 1, 4, 4, 4096, 128, 0.1, 16,
+                       opts(flags=fd.FD_FLAG_APPEND)) == fd.FD_ERR_INVALID_ARG
+    assert fd.fd_combine(None, A, A, 1, 4, 4, 4096, 128, 16,
+                         opts(flags=fd.FD_FLAG_APPEND)) == fd.FD_ERR_INVALID_ARG
+    assert append(kn=None) == fd.FD_ERR_INVALID_ARG
+    assert append(vn=None) == fd.FD_ERR_INVALID_ARG
+    assert append(kn=MIS) == fd.FD_ERR_INVALID_ARG
+    assert append(k=A + 4096, kn=A + 4096) == fd.FD_ERR_INVALID_ARG     # k_new is the cache
+    assert append(q=None) == fd.FD_ERR_INVALID_ARG
+    assert append() == fd.FD_ERR_WORKSPACE                             # 16 splits need a workspace
+    need = fd.fd_workspace_bytes(1, 4, 4, 4096, 128, 16, opts(flags=fd.FD_FLAG_APPEND))
+    st, p = plan(1, 4, 4, 4096, 128, 16, flags=fd.FD_FLAG_APPEND)
+    assert st == fd.FD_OK and need == p.workspace_bytes > 0
+    assert append(workspace=A, workspace_bytes=need - 256) == fd.FD_ERR_WORKSPACE
 
 
 def test_status_strings(lib):
