@@ -114,6 +114,39 @@ class Oracle:
             raise ValueError(f"oracle rejected its arguments (code {rc})")
         return out, lse
 
+    def decode_multi(self, q, k, v, scale, *, causal=False, dtype=None, page_table=None,
+                     seq_lens=None, page_size=0, nthreads=0):
+        """Decode with a small batch of n_q queries per sequence, in fp64.
+
+        The dupenodi guide ("FlashDecoding and split-KV", opening section)
+        describes decode as one query, or a small batch of queries, against
+        a long KV cache.  q is [B, n_q, Hq, D]; query i of sequence b attends
+        to tokens 0 .. L - 1 of the sequence's cache with L = T_b, or, when
+        causal, L = T_b - (n_q - 1 - i) clamped at 0: the queries are the
+        sequence's last n_q tokens (already in the cache, as when a draft of
+        n_q tokens is verified), each seeing itself and the tokens before it.
+        Every query is one plain decode over its own length.
+
+        Returns out [B, n_q, Hq, D] and lse [B, n_q, Hq] (float64).
+        """
+        qa, dt = _host_array(q, dtype)
+        B, nq, Hq, D = qa.shape
+        if seq_lens is None:
+            assert page_table is None, "paged caches need seq_lens"
+            lens = np.full(B, _host_array(k, dt)[0].shape[2], np.int64)
+        else:
+            lens = np.ascontiguousarray(_to_numpy(seq_lens), dtype=np.int64)
+        out = np.zeros((B, nq, Hq, D), np.float64)
+        lse = np.zeros((B, nq, Hq), np.float64)
+        for i in range(nq):
+            li = np.maximum(lens - (nq - 1 - i), 0) if causal else lens
+            o, l = self.decode(np.ascontiguousarray(qa[:, i]), k, v, scale, dtype=dt,
+                               page_table=page_table, seq_lens=li.astype(np.int32),
+                               page_size=page_size, nthreads=nthreads)
+            out[:, i] = o
+            lse[:, i] = l
+        return out, lse
+
     def append_decode(self, q, k_new, v_new, k, v, scale, seq_lens, *, dtype=None,
                       page_table=None, page_size=0, rows=None, nthreads=0):
         """Append the step's new key and value rows to the cache, then decode

@@ -564,6 +564,104 @@ def pin_append_full_cache(orc):
 APPEND_PINS = [pin_append_to_empty, pin_append_two_tokens, pin_append_mpmath, pin_append_full_cache]
 
 
+# ---------------------------------------------------------------- several queries per sequence
+
+def pin_multi_single_query_is_decode(orc):
+    """n_q = 1 (causal or not) is the one-query decode; the library routine
+    here is the same oracle's decode, checked on its own pins above."""
+    rng = _rng(51)
+    B, Hq, Hkv, T, D = 2, 4, 2, 40, 8
+    q = rng.standard_normal((B, 1, Hq, D))
+    k = rng.standard_normal((B, Hkv, T, D))
+    v = rng.standard_normal((B, Hkv, T, D))
+    lens = np.array([40, 7], np.int32)
+    ref, ref_l = orc.decode(q[:, 0], k, v, 0.3, seq_lens=lens)
+    for causal in (False, True):
+        out, lse = orc.decode_multi(q, k, v, 0.3, causal=causal, seq_lens=lens)
+        assert np.array_equal(out[:, 0], ref) and np.array_equal(lse[:, 0], ref_l), "n_q = 1"
+
+
+def pin_multi_causal_first_query(orc):
+    """Causal with n_q = T_b: query 0 sees token 0 alone, so its out = V[0]
+    exactly and lse = its logit (integer operands); the last query sees all
+    T_b tokens (the plain decode)."""
+    rng = _rng(52)
+    B, Hq, Hkv, D, T = 1, 2, 1, 4, 6
+    q = _ints(rng, (B, T, Hq, D))
+    k = _ints(rng, (B, Hkv, T, D))
+    v = rng.standard_normal((B, Hkv, T, D))
+    out, lse = orc.decode_multi(q, k, v, 0.5, causal=True)
+    for h in range(Hq):
+        assert np.array_equal(out[0, 0, h], v[0, 0, 0]), "causal query 0 must return V[0]"
+        assert lse[0, 0, h] == 0.5 * float(np.dot(q[0, 0, h], k[0, 0, 0])), "causal query 0 lse"
+    ref, ref_l = orc.decode(q[:, T - 1], k, v, 0.5)
+    _close(out[:, T - 1], ref, 0.0, "causal last query == decode")
+    _close(lse[:, T - 1], ref_l, 0.0, "causal last query lse")
+
+
+def pin_multi_mpmath(orc):
+    """50-digit brute force of every query's softmax, causal and not, on
+    ragged contiguous and paged caches."""
+    import mpmath
+    mpmath.mp.dps = 50
+    rng = _rng(53)
+    B, nq, Hq, Hkv, T, D, P = 2, 3, 4, 2, 6, 3, 2
+    G = Hq // Hkv
+    q = rng.standard_normal((B, nq, Hq, D)) * 2
+    k = rng.standard_normal((B, Hkv, T, D)) * 2
+    v = rng.standard_normal((B, Hkv, T, D))
+    lens = np.array([5, 2], np.int32)
+    n = T // P
+    table = rng.permutation(B * n).reshape(B, n).astype(np.int32)
+    kp = np.zeros((B * n, Hkv, P, D))
+    vp = np.zeros((B * n, Hkv, P, D))
+    for b in range(B):
+        for i in range(n):
+            kp[table[b, i]] = k[b, :, i * P:(i + 1) * P]
+            vp[table[b, i]] = v[b, :, i * P:(i + 1) * P]
+    for causal in (False, True):
+        results = [orc.decode_multi(q, k, v, 0.6, causal=causal, seq_lens=lens),
+                   orc.decode_multi(q, kp, vp, 0.6, causal=causal, seq_lens=lens, page_table=table)]
+        for out, lse in results:
+            for b in range(B):
+                for i in range(nq):
+                    L = max(0, lens[b] - (nq - 1 - i)) if causal else lens[b]
+                    for h in range(Hq):
+                        j = h // G
+                        if L == 0:
+                            assert np.all(out[b, i, h] == 0) and np.isneginf(lse[b, i, h]), "empty query"
+                            continue
+                        logits = [mpmath.mpf(0.6) * mpmath.fsum(mpmath.mpf(q[b, i, h, d]) * mpmath.mpf(k[b, j, t, d])
+                                                               for d in range(D)) for t in range(L)]
+                        w = [mpmath.e ** x for x in logits]
+                        z = mpmath.fsum(w)
+                        for d in range(D):
+                            ref = float(mpmath.fsum(w[t] * mpmath.mpf(v[b, j, t, d]) for t in range(L)) / z)
+                            assert abs(out[b, i, h, d] - ref) <= 1e-14 * max(1.0, abs(ref)), "multi mpmath out"
+                        ref_l = float(mpmath.log(z))
+                        assert abs(lse[b, i, h] - ref_l) <= 1e-14 * max(1.0, abs(ref_l)), "multi mpmath lse"
+
+
+def pin_multi_query_permutation(orc):
+    """Without the causal mask the queries are independent: permuting them
+    permutes the results (and equal queries give equal results)."""
+    rng = _rng(54)
+    B, nq, Hq, Hkv, T, D = 2, 4, 2, 1, 30, 8
+    q = rng.standard_normal((B, nq, Hq, D))
+    q[:, 3] = q[:, 1]
+    k = rng.standard_normal((B, Hkv, T, D))
+    v = rng.standard_normal((B, Hkv, T, D))
+    out, lse = orc.decode_multi(q, k, v, 0.4)
+    perm = [2, 0, 3, 1]
+    out_p, lse_p = orc.decode_multi(q[:, perm], k, v, 0.4)
+    assert np.array_equal(out_p, out[:, perm]) and np.array_equal(lse_p, lse[:, perm]), "query permutation"
+    assert np.array_equal(out[:, 3], out[:, 1]), "equal queries"
+
+
+MULTI_PINS = [pin_multi_single_query_is_decode, pin_multi_causal_first_query, pin_multi_mpmath,
+              pin_multi_query_permutation]
+
+
 ALL_PINS = [
     pin_single_token, pin_constant_values, pin_uniform_weights, pin_two_tokens,
     pin_dominant_logit, pin_torch_sdpa, pin_mpmath_bruteforce, pin_f16_decoder,

@@ -104,3 +104,27 @@ def test_append_mutant_is_caught(name, old, new):
         except (AssertionError, ValueError, FloatingPointError):
             caught.append(pin.__name__)
     assert caught, f"mutant {name} passed every append pin"
+
+
+# Mistakes planted in the oracle's several-queries decode (oracle.py).
+MULTI_MUTANTS = [
+    ("multi_causal_off_by_one", "li = np.maximum(lens - (nq - 1 - i), 0) if causal else lens",
+     "li = np.maximum(lens - (nq - i), 0) if causal else lens"),
+    ("multi_causal_reversed", "li = np.maximum(lens - (nq - 1 - i), 0) if causal else lens",
+     "li = np.maximum(lens - i, 0) if causal else lens"),
+    ("multi_causal_ignored", "li = np.maximum(lens - (nq - 1 - i), 0) if causal else lens", "li = lens"),
+    ("multi_first_query_only", "o, l = self.decode(np.ascontiguousarray(qa[:, i]), k, v,",
+     "o, l = self.decode(np.ascontiguousarray(qa[:, 0]), k, v,"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MULTI_MUTANTS, ids=[m[0] for m in MULTI_MUTANTS])
+def test_multi_mutant_is_caught(name, old, new):
+    orc = _load_py_mutant(name, old, new)
+    caught = []
+    for pin in oracle_pins.MULTI_PINS:
+        try:
+            pin(orc)
+        except (AssertionError, ValueError, FloatingPointError):
+            caught.append(pin.__name__)
+    assert caught, f"mutant {name} passed every several-queries pin"

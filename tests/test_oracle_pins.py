@@ -20,6 +20,11 @@ def test_append_pin(orc, pin):
     pin(orc)
 
 
+@pytest.mark.parametrize("pin", oracle_pins.MULTI_PINS, ids=lambda f: f.__name__)
+def test_multi_pin(orc, pin):
+    pin(orc)
+
+
 def test_rejects_bad_arguments(orc):
     import numpy as np
     q = np.zeros((1, 3, 4))
