@@ -142,6 +142,10 @@ def main() -> int:
     ap.add_argument("--append", action="store_true",
                     help="time fd_append_decode: each sequence caches T_b - 1 tokens and the step "
                          "stores and attends to token T_b (same KV bytes as the plain step)")
+    ap.add_argument("--n-queries", type=int, default=1,
+                    help="queries per sequence (q [B, n_q, Hq, D]); the KV bytes stay those of one read")
+    ap.add_argument("--causal", action="store_true",
+                    help="with --n-queries: query i sees the first T_b - (n_q - 1 - i) tokens")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (for counter scaling) and exit")
     args = ap.parse_args()
@@ -182,15 +186,16 @@ def main() -> int:
         seq_lens = torch.tensor([max(0, n - 1) for n in lens], dtype=torch.int32, device="cuda")
         new_rows = inputs.make_new_token(spec, 0, device="cuda")
     copies = max(2, min(16, math.ceil((1 << 30) / kv_bytes) + 1))
+    q = case.q if args.n_queries == 1 else inputs.make_q_multi(spec, args.n_queries, device="cuda")
     decs = []
     for c in range(copies):
         k = case.k if c == 0 else case.k.clone()
         v = case.v if c == 0 else case.v.clone()
-        decs.append(Decoder(case.q, k, v, scale=spec.scale, page_table=case.page_table,
+        decs.append(Decoder(q, k, v, scale=spec.scale, page_table=case.page_table,
                             seq_lens=seq_lens, T=spec.T if case.page_table is not None else None,
                             n_splits=args.n_splits or spec.n_splits, path=args.path,
                             fused_merge={"auto": None, "fused": True, "combine": False}[args.merge],
-                            k_new=new_rows[0], v_new=new_rows[1]))
+                            k_new=new_rows[0], v_new=new_rows[1], causal=args.causal))
     plan = decs[0].plan
     print(f"[bench] plan {plan}; {copies} KV copies", file=sys.stderr, flush=True)
 
@@ -260,7 +265,8 @@ def main() -> int:
                    "kv_bytes_per_step": kv_bytes, "kv_copies_rotated": copies,
                    "n_splits": plan["n_splits"], "chunk": plan["chunk"], "path": plan["path"],
                    "fused_merge": plan["fused"], "seed": spec.seed,
-                   "step": "fd_append_decode" if args.append else "fd_decode"},
+                   "step": "fd_append_decode" if args.append else "fd_decode",
+                   "n_queries": args.n_queries, "causal": bool(args.causal)},
         "us_per_step": round(ms_per_step * 1e3, 2),
         "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,

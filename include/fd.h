@@ -29,6 +29,14 @@
  *     out must be 16-byte aligned.  out is [B, Hq, D] fp32, lse [B, Hq] fp32 (natural
  *     log; may be NULL).  A sequence with T_b = 0 yields out = 0 and
  *     lse = -inf.
+ *   - Several queries per sequence (fd_options_t.n_queries = n_q > 1; the
+ *     dupenodi guide "FlashDecoding and split-KV" has decode run one query
+ *     or a small batch of queries against the cache): q is [B, n_q, Hq, D],
+ *     out [B, n_q, Hq, D], lse [B, n_q, Hq].  Every query of a sequence
+ *     reads the same K / V once per pass; query i attends to the first T_b
+ *     tokens, or with fd_options_t.causal to the first T_b - (n_q - 1 - i)
+ *     (the queries are the sequence's last n_q cached tokens, as in
+ *     verifying a draft); a query with no token yields out = 0, lse = -inf.
  *   - Calls are stream-ordered on fd_options_t.stream and never synchronise;
  *     a fault inside a kernel surfaces at the caller's next synchronisation.
  *   - Arguments are validated on the host before any launch.  Every call
@@ -98,6 +106,10 @@ typedef struct fd_options {
     void *workspace;            /* device buffer for the split partials        */
     size_t workspace_bytes;     /* its size in bytes                          */
     void *stream;               /* hipStream_t to launch on; NULL = null stream */
+    int32_t n_queries;          /* queries per sequence, 1 .. 16 (0 means 1); */
+                                /* > 1 gives q / out an n_q axis (see below)  */
+    int32_t causal;             /* with n_queries > 1: 1 = query i sees the   */
+                                /* first T_b - (n_queries - 1 - i) tokens     */
 } fd_options_t;
 
 /* What a call with these arguments will launch (see fd_plan).  Paged calls

@@ -44,6 +44,7 @@ long env_long(const char *name, long dflt) {
 }
 
 constexpr uint32_t kOptionsV1 = sizeof(fd_options_t);
+constexpr int kMaxQueries = 16;          // queries per sequence
 
 // Compute units of the current device, cached per device id.
 fd_status_t device_cus(int *cus) {
@@ -82,6 +83,12 @@ fd_status_t read_options(const fd_options_t *opt, fd_options_t *o) {
         return fail(FD_ERR_INVALID_ARG, "unknown flags 0x%x", (unsigned)o->flags);
     if ((o->flags & FD_FLAG_FUSED_MERGE) && (o->flags & FD_FLAG_COMBINE_KERNEL))
         return fail(FD_ERR_INVALID_ARG, "FD_FLAG_FUSED_MERGE and FD_FLAG_COMBINE_KERNEL exclude each other");
+    if (o->n_queries == 0) o->n_queries = 1;
+    if (o->n_queries < 1 || o->n_queries > kMaxQueries)
+        return fail(FD_ERR_INVALID_ARG, "n_queries=%d not in [1, %d]", (int)o->n_queries, kMaxQueries);
+    if (o->causal != 0 && o->causal != 1) return fail(FD_ERR_INVALID_ARG, "causal=%d is not 0 or 1", (int)o->causal);
+    if ((o->flags & FD_FLAG_APPEND) && o->n_queries > 1)
+        return fail(FD_ERR_UNSUPPORTED, "fd_append_decode takes one query per sequence");
     return FD_OK;
 }
 
@@ -95,7 +102,7 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
     if (D != 64 && D != 128) return fail(FD_ERR_UNSUPPORTED, "D=%d (supported: 64, 128)", D);
     if (n_req < 0) return fail(FD_ERR_INVALID_ARG, "n_splits=%d < 0", n_req);
     if (B > 65535) return fail(FD_ERR_UNSUPPORTED, "B=%d > 65535", B);
-    if ((long)B * Hq > (1L << 30)) return fail(FD_ERR_UNSUPPORTED, "B*Hq too large");
+    if ((long)B * Hq * o.n_queries > (1L << 30)) return fail(FD_ERR_UNSUPPORTED, "B*n_queries*Hq too large");
     if (paged) {
         if (!is_pow2(o.page_size) || o.page_size > 65536)
             return fail(FD_ERR_INVALID_ARG, "page_size=%d is not a power of two in [1, 65536]", o.page_size);
@@ -111,6 +118,7 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
     // Path: the matrix-core kernel once a kv head's query group makes the
     // logit and value updates real small-M contractions (f16 / bf16 only).
     const int G = Hq / Hkv;
+    const int R = o.n_queries * G;       // query rows per kv head
     int path = o.path;
     if (path == FD_PATH_MFMA && o.dtype == FD_F32)
         return fail(FD_ERR_UNSUPPORTED, "the MFMA path needs f16 or bf16 inputs");
@@ -121,7 +129,7 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
         // occupancy wins at G = 4; the automatic paged plan uses the
         // balanced stream mode instead.
         const long min_g = env_long("FD_MFMA_MIN_G", (paged && n_req > 0) ? 8 : 4);
-        path = (o.dtype != FD_F32 && G >= min_g) ? FD_PATH_MFMA : FD_PATH_VALU;
+        path = (o.dtype != FD_F32 && R >= min_g) ? FD_PATH_MFMA : FD_PATH_VALU;
     }
     int hpb, tile;
     if (path == FD_PATH_MFMA) {
@@ -129,10 +137,10 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
         tile = fdk::kMfmaTile;
     } else {
         hpb = 1;
-        while (hpb < G && hpb < 8) hpb <<= 1;
+        while (hpb < R && hpb < 8) hpb <<= 1;
         tile = fdk::valu_tile(o.dtype, D, hpb);
     }
-    const int head_blocks = (int)ceil_div(G, hpb);
+    const int head_blocks = (int)ceil_div(R, hpb);
     if ((long)Hkv * head_blocks > 65535) return fail(FD_ERR_UNSUPPORTED, "Hkv*head_blocks > 65535");
     if (tile <= 0) return fail(FD_ERR_UNSUPPORTED, "no kernel instance for this shape");
 
@@ -236,10 +244,10 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
     if (o.flags & FD_FLAG_COMBINE_KERNEL) want_fused = false;
     const long env_fused = env_long("FD_FUSED", -1);
     if (env_fused == 0 || env_fused == 1) want_fused = env_fused == 1;
-    const long merge_heads = G < hpb ? G : hpb;
+    const long merge_heads = R < hpb ? R : hpb;
     p->fused = n > 1 && n * merge_heads <= fdk::kMergeMaxPairsHost && want_fused;
     if (n > 1) {
-        const size_t parts = (size_t)B * Hq * (size_t)n;
+        const size_t parts = (size_t)B * Hkv * R * (size_t)n;
         const size_t counters = (size_t)B * Hkv * head_blocks * 2 * sizeof(unsigned long long);
         p->workspace_bytes = align256(counters) + align256(parts * D * sizeof(float)) +
                              2 * align256(parts * sizeof(float));
@@ -321,7 +329,7 @@ fd_status_t prepare(const void *q, const void *k, const void *v, const int32_t *
             return fail(FD_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", c->o.workspace_bytes,
                         c->p.workspace_bytes);
         if (!aligned(c->o.workspace, 256)) return fail(FD_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-        const size_t parts = (size_t)B * Hq * (size_t)c->p.n_splits;
+        const size_t parts = (size_t)B * Hq * c->o.n_queries * (size_t)c->p.n_splits;
         char *w = static_cast<char *>(c->o.workspace);
         counters = reinterpret_cast<unsigned long long *>(w);
         w += align256((size_t)B * Hkv * c->p.head_blocks * 2 * sizeof(unsigned long long));
@@ -339,6 +347,9 @@ fd_status_t prepare(const void *q, const void *k, const void *v, const int32_t *
     s.out = out; s.lse = lse;
     s.part_o = part_o; s.part_m = part_m; s.part_l = part_l;
     s.B = B; s.Hq = Hq; s.Hkv = Hkv; s.T = T; s.D = D; s.G = Hq / Hkv;
+    s.nq = c->o.n_queries;
+    s.R = s.nq * s.G;
+    s.causal = c->o.causal;
     s.n_splits = c->p.n_splits;
     s.chunk = c->p.chunk;
     s.heads_per_block = c->p.heads_per_block;
@@ -360,7 +371,7 @@ fd_status_t prepare(const void *q, const void *k, const void *v, const int32_t *
     s.k_store = const_cast<void *>(k);
     s.v_store = const_cast<void *>(v);
     {
-        const int merge_heads = s.G < c->p.heads_per_block ? s.G : c->p.heads_per_block;
+        const int merge_heads = s.R < c->p.heads_per_block ? s.R : c->p.heads_per_block;
         s.merge_cap = (int)(fdk::kMergeMaxPairsHost / merge_heads);
     }
 
@@ -369,6 +380,7 @@ fd_status_t prepare(const void *q, const void *k, const void *v, const int32_t *
     cb.seq_lens = seq_lens;
     cb.out = out; cb.lse = lse;
     cb.B = B; cb.Hq = Hq; cb.T = T; cb.D = D;
+    cb.Hkv = Hkv; cb.G = s.G; cb.nq = s.nq; cb.R = s.R;
     cb.n_splits = c->p.n_splits;
     cb.chunk = c->p.chunk;
     cb.append = append ? 1 : 0;
@@ -455,6 +467,7 @@ void fd_options_init(fd_options_t *opt) {
     opt->struct_size = sizeof *opt;
     opt->dtype = FD_BF16;
     opt->path = FD_PATH_AUTO;
+    opt->n_queries = 1;
 }
 
 fd_status_t fd_plan(int B, int Hq, int Hkv, int T, int D, int n_splits, const fd_options_t *opt,

@@ -42,8 +42,13 @@ __global__ __launch_bounds__(256) void combine(CombineArgs a) {
     constexpr int WCH = 2048;         // split weights staged per pass
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int q = t % Q, sg = t / Q;
+    // partial row p = (b * Hkv + kv head) * R + query row; its output row is
+    // (b * nq + query) * Hq + kv head * G + head of the group
     const int bh = blockIdx.x;
-    const int b = bh / a.Hq;
+    const int b = bh / (a.Hkv * a.R);
+    const int kvh = bh / a.R - b * a.Hkv;
+    const int qr = bh - (bh / a.R) * a.R;
+    const size_t orow = ((size_t)b * a.nq + qr / a.G) * a.Hq + (size_t)kvh * a.G + qr % a.G;
 
     int Tb = a.T;
     if (a.seq_lens) {
@@ -118,15 +123,15 @@ __global__ __launch_bounds__(256) void combine(CombineArgs a) {
             r.x += v.x; r.y += v.y; r.z += v.z; r.w += v.w;
         }
         float4 o = L > 0.f ? make_float4(r.x / L, r.y / L, r.z / L, r.w / L) : make_float4(0.f, 0.f, 0.f, 0.f);
-        reinterpret_cast<float4 *>(a.out + (size_t)bh * D)[t] = o;
+        reinterpret_cast<float4 *>(a.out + orow * D)[t] = o;
     }
-    if (t == 0 && a.lse) a.lse[bh] = L > 0.f ? (M + log2f(L)) * kLn2 : kNegInf;
+    if (t == 0 && a.lse) a.lse[orow] = L > 0.f ? (M + log2f(L)) * kLn2 : kNegInf;
 }
 
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs &a, hipStream_t stream) {
-    const dim3 grid(a.B * a.Hq);
+    const dim3 grid(a.B * a.Hkv * a.R);
     switch (a.D) {
     case 64: hipLaunchKernelGGL(combine<64>, grid, dim3(256), 0, stream, a); break;
     case 128: hipLaunchKernelGGL(combine<128>, grid, dim3(256), 0, stream, a); break;

@@ -95,15 +95,23 @@ struct EpilogueLds {
     int last;
 };
 
-// A sequence with no tokens: out = 0 and lse = -inf for the block's heads.
+// Output row (index into out / lse rows) of query row r of kv head kvh of
+// sequence b: query r / G, head kvh * G + r % G.
+__device__ __forceinline__ size_t qrow(const SplitArgs &a, int b, int kvh, int r) {
+    if (a.nq == 1) return (size_t)b * a.Hq + (size_t)kvh * a.G + r;
+    const int i = r / a.G, g = r - i * a.G;
+    return ((size_t)b * a.nq + i) * a.Hq + (size_t)kvh * a.G + g;
+}
+
+// A sequence with no tokens: out = 0 and lse = -inf for the block's rows.
 // In fused mode no split of such a sequence reaches the merge, so split 0
 // writes this instead.
 template <int D>
-__device__ void write_empty_group(const SplitArgs &a, int b, int h0, int ng) {
+__device__ void write_empty_group(const SplitArgs &a, int b, int kvh, int r0, int ng) {
     for (int idx = threadIdx.x; idx < ng * D; idx += blockDim.x) {
         const int g = idx / D, d = idx - (idx / D) * D;
-        const int bh = b * a.Hq + h0 + g;
-        a.out[(size_t)bh * D + d] = 0.f;
+        const size_t bh = qrow(a, b, kvh, r0 + g);
+        a.out[bh * D + d] = 0.f;
         if (d == 0 && a.lse) a.lse[bh] = kEpNegInf;
     }
 }
@@ -164,11 +172,11 @@ struct SegOut {
     int arrivals;                  // segments of the group (its merge count)
 };
 
-__device__ __forceinline__ SegOut split_segment(const SplitArgs &a, int b, int kvh, int hb, int h0,
+__device__ __forceinline__ SegOut split_segment(const SplitArgs &a, int b, int kvh, int hb, int r0,
                                                 int split, int Tb) {
     SegOut so;
     so.final_out = a.n_splits == 1;
-    so.base = (size_t)(b * a.Hq + h0) * a.n_splits;
+    so.base = (((size_t)b * a.Hkv + kvh) * a.R + r0) * a.n_splits;
     so.gs = a.n_splits;
     so.ss = 1;
     so.s = split;
@@ -188,7 +196,7 @@ __device__ __forceinline__ SegOut split_segment(const SplitArgs &a, int b, int k
 // (deterministic).  ng * n <= kMergeMaxPairs.
 template <int WAVES, int GB, int D>
 __device__ void combine_group(const SplitArgs &a, EpilogueLds<WAVES, GB, D> &sm, const SegOut &so, int b,
-                              int h0, int ng, int n) {
+                              int kvh, int r0, int ng, int n) {
     constexpr int NT = WAVES * 64;
     constexpr int Q = D / 4;
     constexpr int PRE = 8;
@@ -217,7 +225,7 @@ __device__ void combine_group(const SplitArgs &a, EpilogueLds<WAVES, GB, D> &sm,
         const int p = p0 + t / SG, sg = t - (t / SG) * SG;
         const bool active = p < pairs;
         const int g = active ? p / Q : 0, q = active ? p - (p / Q) * Q : 0;
-        const int bh = b * a.Hq + h0 + g;
+        const size_t bh = qrow(a, b, kvh, r0 + g);
         const float *po = a.part_o + (so.base + (size_t)g * so.gs) * D + 4 * q;
         const size_t srow = (size_t)so.ss * D;
         float4 pre[PRE];
@@ -286,7 +294,7 @@ __device__ void combine_group(const SplitArgs &a, EpilogueLds<WAVES, GB, D> &sm,
             const float L = sm.gl[g];
             const float4 o = L > 0.f ? make_float4(r.x / L, r.y / L, r.z / L, r.w / L)
                                      : make_float4(0.f, 0.f, 0.f, 0.f);
-            reinterpret_cast<float4 *>(a.out + (size_t)bh * D)[q] = o;
+            reinterpret_cast<float4 *>(a.out + bh * D)[q] = o;
             if (q == 0 && a.lse) a.lse[bh] = L > 0.f ? (sm.gm[g] + log2f(L)) * kEpLn2 : kEpNegInf;
         }
         __syncthreads();
@@ -298,7 +306,7 @@ __device__ void combine_group(const SplitArgs &a, EpilogueLds<WAVES, GB, D> &sm,
 // mode, completes the group when this workgroup arrives last.
 template <int WAVES, int GB, int D>
 __device__ void finish_split(const SplitArgs &a, EpilogueLds<WAVES, GB, D> &sm, const SegOut &so, int b,
-                             int h0, int ng) {
+                             int kvh, int r0, int ng) {
     constexpr int NT = WAVES * 64;
     for (int idx = threadIdx.x; idx < ng * D; idx += NT) {
         const int g = idx / D, d = idx - (idx / D) * D;
@@ -313,10 +321,10 @@ __device__ void finish_split(const SplitArgs &a, EpilogueLds<WAVES, GB, D> &sm, 
             acc += c * sm.o[w][g][d];
             L += c * sm.l[w][g];
         }
-        const int bh = b * a.Hq + h0 + g;
+        const size_t bh = qrow(a, b, kvh, r0 + g);
         const size_t pi = so.base + (size_t)g * so.gs + (size_t)so.s * so.ss;
         if (so.final_out) {
-            a.out[(size_t)bh * D + d] = L > 0.f ? acc / L : 0.f;
+            a.out[bh * D + d] = L > 0.f ? acc / L : 0.f;
             if (d == 0 && a.lse) a.lse[bh] = L > 0.f ? (M + log2f(L)) * kEpLn2 : kEpNegInf;
         } else if (so.fused) {
             st_agent(a.part_o + pi * D + d, acc);
@@ -336,7 +344,7 @@ __device__ void finish_split(const SplitArgs &a, EpilogueLds<WAVES, GB, D> &sm, 
     if (threadIdx.x == 0) sm.last = arrive_last(so.cnt, a.epoch, a.next_epoch, so.arrivals) ? 1 : 0;
     __syncthreads();
     if (!sm.last) return;
-    combine_group<WAVES, GB, D>(a, sm, so, b, h0, ng, so.arrivals);
+    combine_group<WAVES, GB, D>(a, sm, so, b, kvh, r0, ng, so.arrivals);
 }
 
 // Stream mode.  Rows (batch, kv head, head block) are padded to
@@ -395,13 +403,14 @@ __device__ void drive_stream(const SplitArgs &a, long long *pref, int hpb, Seg &
     per = (per + align - 1) / align * align;
     if (per < align) per = align;
 
-    // sequences of length 0: out = 0, lse = -inf
+    // sequences of length 0: out = 0, lse = -inf for all their query rows
     for (int b = w; b < a.B; b += NW)
         if (real_len(b) == 0)
-            for (int idx = t; idx < a.Hq * D; idx += NT) {
+            for (int idx = t; idx < a.nq * a.Hq * D; idx += NT) {
                 const int h = idx / D, d = idx - (idx / D) * D;
-                a.out[((size_t)b * a.Hq + h) * D + d] = 0.f;
-                if (d == 0 && a.lse) a.lse[(size_t)b * a.Hq + h] = kEpNegInf;
+                const size_t row = (size_t)b * a.nq * a.Hq + h;
+                a.out[row * D + d] = 0.f;
+                if (d == 0 && a.lse) a.lse[row] = kEpNegInf;
             }
 
     const long long g0 = (long long)w * per;

@@ -40,6 +40,11 @@ struct SplitArgs {
     float *part_m;               // [B, Hq, n_splits] running max, log2 units
     float *part_l;               // [B, Hq, n_splits] running sum
     int B, Hq, Hkv, T, D, G;     // G = Hq / Hkv
+    // Query rows of one kv head: R = nq * G, row r = (query r / G, head
+    // r % G of the group).  Head blocks tile the rows; partials are indexed
+    // by row: [B, Hkv, R, n_splits].
+    int nq, R;
+    int causal;                  // query i sees the first T_b - (nq - 1 - i) tokens
     int n_splits, chunk;
     int heads_per_block, head_blocks;
     int page_size, page_shift, max_pages, num_pages;
@@ -74,6 +79,7 @@ struct CombineArgs {
     float *out;
     float *lse;
     int B, Hq, T, D;
+    int Hkv, G, nq, R;           // partial row p = (b * Hkv + kv head) * R + row
     int n_splits, chunk;
     int append;                  // sequences hold seq_lens[b] + 1 tokens
 };

@@ -129,19 +129,20 @@ __global__ __launch_bounds__(256, 2) void split_mfma(SplitArgs a) {
 
     // One segment: tokens [c0, c1) of row (b, kvh, hb) into `so`.
     auto segment = [&](int b, int kvh, int hb, int c0, int c1, const SegOut &so) {
-        const int g0 = hb * GB;
-        const int ng = min(GB, a.G - g0);
-        const int h0 = kvh * a.G + g0;
+        const int g0 = hb * GB;                 // first query row of the block
+        const int ng = min(GB, a.R - g0);
 
-        // B operand of the logit MFMAs: q pieces 4*ks + kb of head i16.
+        // B operand of the logit MFMAs: q pieces 4*ks + kb of row i16.
         uint4 qb[KS];
+        {
+            const size_t qr = i16 < ng ? qrow(a, b, kvh, g0 + i16) : 0;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            qb[ks] = make_uint4(0, 0, 0, 0);
-            if (i16 < ng)
-                qb[ks] = *reinterpret_cast<const uint4 *>(static_cast<const char *>(a.q) +
-                                                           (size_t)(b * a.Hq + h0 + i16) * ROWB +
-                                                           (4 * ks + kb) * 16);
+            for (int ks = 0; ks < KS; ++ks) {
+                qb[ks] = make_uint4(0, 0, 0, 0);
+                if (i16 < ng)
+                    qb[ks] = *reinterpret_cast<const uint4 *>(static_cast<const char *>(a.q) + qr * ROWB +
+                                                               (4 * ks + kb) * 16);
+            }
         }
 
         f32x4_v acc[PVE];
@@ -181,7 +182,9 @@ __global__ __launch_bounds__(256, 2) void split_mfma(SplitArgs a) {
             bool ok[2][4];
         };
 
-        auto consume_step = [&](const Buf &f) {
+        // lane_ok: this lane's query row attends to the step's tokens (false
+        // masks the row, for the causal tail of several queries).
+        auto consume_step = [&](const Buf &f, bool lane_ok) {
             float s[2][4];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
@@ -189,7 +192,7 @@ __global__ __launch_bounds__(256, 2) void split_mfma(SplitArgs a) {
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) c = mfma_logits<DT>(f.k[h][ks], qb[ks], c);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) s[h][r] = f.ok[h][r] ? c[r] * a.scale_log2 : kNegInf;
+                for (int r = 0; r < 4; ++r) s[h][r] = (f.ok[h][r] && lane_ok) ? c[r] * a.scale_log2 : kNegInf;
             }
             float mt = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                              fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
@@ -291,24 +294,29 @@ __global__ __launch_bounds__(256, 2) void split_mfma(SplitArgs a) {
                 load_step(base + TILE, fb);            // clamped past the end
                 asm volatile("" ::: "memory");
                 __builtin_amdgcn_sched_barrier(0);
-                consume_step(fa);
+                consume_step(fa, true);
                 if (base + TILE >= r1) break;
                 load_step(base + 2 * TILE, fa);
                 asm volatile("" ::: "memory");
                 __builtin_amdgcn_sched_barrier(0);
-                consume_step(fb);
+                consume_step(fb, true);
                 if (base + 2 * TILE >= r1) break;
             }
         };
 
-        // Appending: the segment that reaches token Tc (the new one) streams
-        // the cached tokens before it and takes the new token from k_new /
-        // v_new below.
+        // Tokens every query row attends to are streamed by the main loop:
+        // [c0, e1).  After it come the tokens some rows skip -- the causal
+        // tail of several queries, or the appended token -- one at a time.
         int e1 = c1;
-        int Tc = 0;
+        int Tc = 0, tail0 = c1;
         if (a.append) {
             Tc = cached_len(a, b);
             e1 = c1 < Tc ? c1 : Tc;
+        }
+        if (a.causal) {
+            Tc = cached_len(a, b);
+            tail0 = max(c0, Tc - (a.nq - 1));
+            e1 = min(e1, tail0);
         }
 
         if constexpr (PAGED) {
@@ -324,25 +332,58 @@ __global__ __launch_bounds__(256, 2) void split_mfma(SplitArgs a) {
             if (c0 < e1) stream_range(c0, e1);
         }
 
-        if (a.append && c1 > Tc) {
-            // The new token as token 0 of wave 0's first tile: every row of
-            // the tile reads the new rows, all but that one are masked.
-            const size_t nr = ((size_t)b * a.Hkv + kvh) * ROWB;
-            const char *kn = static_cast<const char *>(a.k_new) + nr;
-            const char *vn = static_cast<const char *>(a.v_new) + nr;
+        // A few tokens (count <= 16) as the first tile of wave 0: lane i16
+        // loads token i16's K row and lane (i16, kb) token 4*kb + r's V rows.
+        // token_at(i, ok) gives token i's row offset from kb_ / vb_ (ok =
+        // false: no such row); sees(i, row) tells whether a query row
+        // attends to token i.  The other tile and waves are masked.
+        auto fold_tokens = [&](const char *kb_, const char *vb_, int count, auto token_at, auto sees) {
             Buf f;
+            bool kok;
+            const size_t ko = token_at(i16 < count ? i16 : count - 1, kok);
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
-                    f.k[h][ks] = *reinterpret_cast<const uint4 *>(kn + (4 * ks + kb) * 16);
+                    f.k[h][ks] = *reinterpret_cast<const uint4 *>(kb_ + ko + (4 * ks + kb) * 16);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    f.v[h][r] = *reinterpret_cast<const VP *>(vn + i16 * VB);
-                    f.ok[h][r] = wave == 0 && h == 0 && kb == 0 && r == 0;
-                }
+            for (int r = 0; r < 4; ++r) {
+                const int ti = 4 * kb + r;
+                bool vok;
+                const size_t vo = token_at(ti < count ? ti : count - 1, vok);
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    f.v[h][r] = *reinterpret_cast<const VP *>(vb_ + vo + i16 * VB);
+                f.ok[0][r] = wave == 0 && ti < count && vok && sees(ti, g0 + i16);
+                f.ok[1][r] = false;
             }
-            consume_step(f);
+            consume_step(f, true);
+        };
+
+        if (a.causal && c1 > tail0) {
+            // the causal tail: query row r (query r / G) sees tokens below
+            // Tc - (nq - 1 - r / G)
+            auto tail_token = [&](int i, bool &ok) -> size_t {
+                const int t = tail0 + i;
+                ok = true;
+                if constexpr (PAGED) {
+                    const int pg = a.page_table[(size_t)b * a.max_pages + (t >> a.page_shift)];
+                    ok = (unsigned)pg < (unsigned)a.num_pages;
+                    return (((size_t)(ok ? pg : 0) * a.Hkv + kvh) * a.page_size + (t & (a.page_size - 1))) * ROWB;
+                } else {
+                    return (size_t)t * ROWB;
+                }
+            };
+            fold_tokens(kbase, vbase, c1 - tail0, tail_token,
+                        [&](int i, int r) { return tail0 + i < Tc - (a.nq - 1 - r / a.G); });
+        }
+
+        if (a.append && c1 > Tc) {
+            // the new token, read from the input rows
+            const size_t nr = ((size_t)b * a.Hkv + kvh) * ROWB;
+            fold_tokens(static_cast<const char *>(a.k_new) + nr, static_cast<const char *>(a.v_new) + nr, 1,
+                        [](int, bool &ok) -> size_t { ok = true; return 0; },
+                        [](int, int) { return true; });
             if (hb == 0) store_new_token<ROWB>(a, b, kvh, Tc);
         }
 
@@ -357,7 +398,7 @@ __global__ __launch_bounds__(256, 2) void split_mfma(SplitArgs a) {
             for (int r = 0; r < 4; ++r) sm.o[wave][i16][PVE * (4 * kb + r) + i] = acc[i][r];
         if (kb == 0) { sm.m[wave][i16] = m; sm.l[wave][i16] = l; }
         __syncthreads();
-        finish_split<WAVES, GB, D>(a, sm, so, b, h0, ng);
+        finish_split<WAVES, GB, D>(a, sm, so, b, kvh, g0, ng);
     };
 
     if constexpr (STREAM) {
@@ -371,12 +412,12 @@ __global__ __launch_bounds__(256, 2) void split_mfma(SplitArgs a) {
         const int Tb = attended_len(a, b);
         const int c0 = split * a.chunk;
         const int c1 = min(c0 + a.chunk, Tb);
-        const int h0 = kvh * a.G + hb * GB;
+        const int g0 = hb * GB;
         if (a.n_splits > 1 && c0 >= Tb) {          // empty split: never counted or read
-            if (a.fused && split == 0) write_empty_group<D>(a, b, h0, min(GB, a.G - hb * GB));
+            if (a.fused && split == 0) write_empty_group<D>(a, b, kvh, g0, min(GB, a.R - g0));
             return;
         }
-        segment(b, kvh, hb, c0, c1 > c0 ? c1 : c0, split_segment(a, b, kvh, hb, h0, split, Tb));
+        segment(b, kvh, hb, c0, c1 > c0 ? c1 : c0, split_segment(a, b, kvh, hb, g0, split, Tb));
     }
 }
 

@@ -134,22 +134,22 @@ __global__ __launch_bounds__(256) void split_valu(SplitArgs a) {
 
     // One segment: tokens [c0, c1) of row (b, kvh, hb) into `so`.
     auto segment = [&](int b, int kvh, int hb, int c0, int c1, const SegOut &so) {
-        const int g0 = hb * GB;
-        const int ng = min(GB, a.G - g0);          // valid query heads in this block
-        const int h0 = kvh * a.G + g0;
+        const int g0 = hb * GB;                     // first query row of the block
+        const int ng = min(GB, a.R - g0);          // valid query rows in this block
 
         // This lane's pieces of the query rows (raw storage words).
         uint4 qv[GB][VEC];
 #pragma unroll
-        for (int g = 0; g < GB; ++g)
+        for (int g = 0; g < GB; ++g) {
+            const size_t qr = g < ng ? qrow(a, b, kvh, g0 + g) : 0;
 #pragma unroll
             for (int v = 0; v < VEC; ++v) {
                 qv[g][v] = make_uint4(0, 0, 0, 0);
                 if (g < ng)
-                    qv[g][v] = *reinterpret_cast<const uint4 *>(static_cast<const char *>(a.q) +
-                                                                 (size_t)(b * a.Hq + h0 + g) * ROWB +
+                    qv[g][v] = *reinterpret_cast<const uint4 *>(static_cast<const char *>(a.q) + qr * ROWB +
                                                                  (v * LPR + sub) * 16);
             }
+        }
 
         float m[GB], l[GB], o[GB][EPT];
 #pragma unroll
@@ -185,7 +185,10 @@ __global__ __launch_bounds__(256) void split_valu(SplitArgs a) {
             }
         };
 
-        auto consume_step = [&](const uint4 (&kr)[U][VEC], const uint4 (&vr)[U][VEC], const bool (&ok)[U]) {
+        // rows_ok(u, g): query row g attends to this lane's token u (false
+        // masks it, for the causal tail of several queries).
+        auto consume_step = [&](const uint4 (&kr)[U][VEC], const uint4 (&vr)[U][VEC], const bool (&ok)[U],
+                                auto rows_ok) {
             float s[U][GB];
 #pragma unroll
             for (int u = 0; u < U; ++u)
@@ -195,7 +198,7 @@ __global__ __launch_bounds__(256) void split_valu(SplitArgs a) {
 #pragma unroll
                     for (int v = 0; v < VEC; ++v) acc = dot_piece<DT>(qv[g][v], kr[u][v], acc);
                     acc = row_sum<LPR>(acc) * a.scale_log2;
-                    s[u][g] = ok[u] ? acc : kNegInf;
+                    s[u][g] = (ok[u] && rows_ok(u, g)) ? acc : kNegInf;
                 }
             float vf[U][EPT];
 #pragma unroll
@@ -225,6 +228,8 @@ __global__ __launch_bounds__(256) void split_valu(SplitArgs a) {
                 m[g] = mn;
             }
         };
+
+        auto all_rows = [](int, int) { return true; };
 
         auto stream_range = [&](int r0, int r1) {
             // Byte offset of token t's row and whether the token is real.  A
@@ -268,24 +273,29 @@ __global__ __launch_bounds__(256) void split_valu(SplitArgs a) {
                 load_step(base + TILE, kb2, vb2, okb);   // clamped past the end
                 asm volatile("" ::: "memory");
                 __builtin_amdgcn_sched_barrier(0);
-                consume_step(ka, va, oka);
+                consume_step(ka, va, oka, all_rows);
                 if (base + TILE >= r1) break;
                 load_step(base + 2 * TILE, ka, va, oka);
                 asm volatile("" ::: "memory");
                 __builtin_amdgcn_sched_barrier(0);
-                consume_step(kb2, vb2, okb);
+                consume_step(kb2, vb2, okb, all_rows);
                 if (base + 2 * TILE >= r1) break;
             }
         };
 
-        // Appending: the segment that reaches token Tc (the new one) streams
-        // the cached tokens before it and takes the new token from k_new /
-        // v_new below.
+        // Tokens every query row attends to are streamed by the main loop:
+        // [c0, e1).  After it come the tokens some rows skip -- the causal
+        // tail of several queries, or the appended token -- one at a time.
         int e1 = c1;
-        int Tc = 0;
+        int Tc = 0, tail0 = c1;
         if (a.append) {
             Tc = cached_len(a, b);
             e1 = c1 < Tc ? c1 : Tc;
+        }
+        if (a.causal) {
+            Tc = cached_len(a, b);
+            tail0 = max(c0, Tc - (a.nq - 1));
+            e1 = min(e1, tail0);
         }
 
         if constexpr (PAGED) {
@@ -301,24 +311,53 @@ __global__ __launch_bounds__(256) void split_valu(SplitArgs a) {
             if (c0 < e1) stream_range(c0, e1);
         }
 
-        if (a.append && c1 > Tc) {
-            // The new token as row 0 of wave 0's first step: every row reads
-            // the new rows, all but that one are masked.
-            const size_t nr = ((size_t)b * a.Hkv + kvh) * ROWB;
-            const char *kn = static_cast<const char *>(a.k_new) + nr;
-            const char *vn = static_cast<const char *>(a.v_new) + nr;
+        // A few tokens (count <= TILE) in the slots of one step: slot i =
+        // wave * TW + u * R + row, as in the main loop.  token_at(i, ok) gives
+        // token i's row offset from kb_ / vb_ (ok = false: no such row);
+        // sees(i, row) tells whether a query row attends to token i.
+        auto fold_tokens = [&](const char *kb_, const char *vb_, int count, auto token_at, auto sees) {
             uint4 kr[U][VEC], vr[U][VEC];
             bool ok[U];
+            int ti[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
+                ti[u] = wave * TW + u * R + row;
+                bool tok;
+                const size_t off = token_at(ti[u] < count ? ti[u] : count - 1, tok);
 #pragma unroll
                 for (int v = 0; v < VEC; ++v) {
-                    kr[u][v] = *reinterpret_cast<const uint4 *>(kn + (v * LPR + sub) * 16);
-                    vr[u][v] = *reinterpret_cast<const uint4 *>(vn + (v * LPR + sub) * 16);
+                    kr[u][v] = *reinterpret_cast<const uint4 *>(kb_ + off + (v * LPR + sub) * 16);
+                    vr[u][v] = *reinterpret_cast<const uint4 *>(vb_ + off + (v * LPR + sub) * 16);
                 }
-                ok[u] = wave == 0 && u == 0 && row == 0;
+                ok[u] = ti[u] < count && tok;
             }
-            consume_step(kr, vr, ok);
+            consume_step(kr, vr, ok, [&](int u, int g) { return sees(ti[u], g0 + g); });
+        };
+
+        if (a.causal && c1 > tail0) {
+            // the causal tail: query row r (query r / G) sees tokens below
+            // Tc - (nq - 1 - r / G)
+            auto tail_token = [&](int i, bool &ok) -> size_t {
+                const int t = tail0 + i;
+                ok = true;
+                if constexpr (PAGED) {
+                    const int pg = a.page_table[(size_t)b * a.max_pages + (t >> a.page_shift)];
+                    ok = (unsigned)pg < (unsigned)a.num_pages;
+                    return (((size_t)(ok ? pg : 0) * a.Hkv + kvh) * a.page_size + (t & (a.page_size - 1))) * ROWB;
+                } else {
+                    return (size_t)t * ROWB;
+                }
+            };
+            fold_tokens(kb, vb, c1 - tail0, tail_token,
+                        [&](int i, int r) { return tail0 + i < Tc - (a.nq - 1 - r / a.G); });
+        }
+
+        if (a.append && c1 > Tc) {
+            // the new token, read from the input rows
+            const size_t nr = ((size_t)b * a.Hkv + kvh) * ROWB;
+            fold_tokens(static_cast<const char *>(a.k_new) + nr, static_cast<const char *>(a.v_new) + nr, 1,
+                        [](int, bool &ok) -> size_t { ok = true; return 0; },
+                        [](int, int) { return true; });
             if (hb == 0) store_new_token<ROWB>(a, b, kvh, Tc);
         }
 
@@ -356,7 +395,7 @@ __global__ __launch_bounds__(256) void split_valu(SplitArgs a) {
             }
         }
         __syncthreads();
-        finish_split<WAVES, GB, D>(a, sm, so, b, h0, ng);
+        finish_split<WAVES, GB, D>(a, sm, so, b, kvh, g0, ng);
     };
 
     if constexpr (STREAM) {
@@ -370,12 +409,12 @@ __global__ __launch_bounds__(256) void split_valu(SplitArgs a) {
         const int Tb = attended_len(a, b);
         const int c0 = split * a.chunk;
         const int c1 = min(c0 + a.chunk, Tb);
-        const int h0 = kvh * a.G + hb * GB;
+        const int g0 = hb * GB;
         if (a.n_splits > 1 && c0 >= Tb) {          // empty split: never counted or read
-            if (a.fused && split == 0) write_empty_group<D>(a, b, h0, min(GB, a.G - hb * GB));
+            if (a.fused && split == 0) write_empty_group<D>(a, b, kvh, g0, min(GB, a.R - g0));
             return;
         }
-        segment(b, kvh, hb, c0, c1 > c0 ? c1 : c0, split_segment(a, b, kvh, hb, h0, split, Tb));
+        segment(b, kvh, hb, c0, c1 > c0 ? c1 : c0, split_segment(a, b, kvh, hb, g0, split, Tb));
     }
 }
 

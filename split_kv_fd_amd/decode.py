@@ -29,7 +29,7 @@ def make_options(dtype: torch.dtype, *, page_size: int = 0, max_pages: int = 0,
                  num_pages: int = 0, workspace: Optional[torch.Tensor] = None,
                  stream: Optional[int] = None, num_cus: int = 0,
                  path: Optional[str] = None, fused_merge: Optional[bool] = None,
-                 append: bool = False) -> fd.fd_options_t:
+                 append: bool = False, n_queries: int = 1, causal: bool = False) -> fd.fd_options_t:
     opt = fd.fd_options_t()
     fd.fd_options_init(opt)
     opt.dtype = _DTYPE[dtype]
@@ -43,6 +43,8 @@ def make_options(dtype: torch.dtype, *, page_size: int = 0, max_pages: int = 0,
     opt.flags = {None: 0, True: fd.FD_FLAG_FUSED_MERGE, False: fd.FD_FLAG_COMBINE_KERNEL}[fused_merge]
     if append:
         opt.flags |= fd.FD_FLAG_APPEND
+    opt.n_queries = n_queries
+    opt.causal = 1 if causal else 0
     if workspace is not None:
         opt.workspace = workspace.data_ptr()
         opt.workspace_bytes = workspace.numel() * workspace.element_size()
@@ -51,12 +53,13 @@ def make_options(dtype: torch.dtype, *, page_size: int = 0, max_pages: int = 0,
 
 
 def plan(B, Hq, Hkv, T, D, n_splits=0, *, dtype=torch.bfloat16, page_size=0, max_pages=0,
-         num_pages=1, num_cus=0, path=None, fused_merge=None, append=False) -> dict:
+         num_pages=1, num_cus=0, path=None, fused_merge=None, append=False, n_queries=1,
+         causal=False) -> dict:
     """What fd_decode (fd_append_decode with append=True) would launch for
     these arguments (host only)."""
     opt = make_options(dtype, page_size=page_size, max_pages=max_pages,
                        num_pages=num_pages if page_size else 0, num_cus=num_cus, path=path,
-                       fused_merge=fused_merge, append=append)
+                       fused_merge=fused_merge, append=append, n_queries=n_queries, causal=causal)
     p = fd.fd_plan_t()
     st = fd.fd_plan(B, Hq, Hkv, T, D, n_splits, opt, p)
     if st != fd.FD_OK:
@@ -80,7 +83,7 @@ class Decoder:
     def __init__(self, q, k, v, *, scale: Optional[float] = None, page_table=None,
                  seq_lens=None, T: Optional[int] = None, n_splits: int = 0,
                  path: Optional[str] = None, fused_merge: Optional[bool] = None, out=None, lse=None,
-                 want_lse: bool = True, k_new=None, v_new=None):
+                 want_lse: bool = True, k_new=None, v_new=None, causal: bool = False):
         if q.device.type != "cuda":
             raise ValueError("q, k and v must be GPU tensors")
         if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPE:
@@ -88,9 +91,12 @@ class Decoder:
         for name, t in (("q", q), ("k", k), ("v", v)):
             if not t.is_contiguous() or t.device != q.device:
                 raise ValueError(f"{name} must be contiguous and on {q.device}")
-        if q.dim() != 3 or k.dim() != 4 or k.shape != v.shape:
-            raise ValueError("expected q [B, Hq, D] and k, v [B, Hkv, T, D] or [pages, Hkv, P, D]")
-        B, Hq, D = q.shape
+        if q.dim() not in (3, 4) or k.dim() != 4 or k.shape != v.shape:
+            raise ValueError("expected q [B, Hq, D] or [B, n_q, Hq, D] and k, v [B, Hkv, T, D] "
+                             "or [pages, Hkv, P, D]")
+        # q [B, n_q, Hq, D]: n_q queries per sequence against one cache
+        self.n_queries = q.shape[1] if q.dim() == 4 else 1
+        B, Hq, D = q.shape[0], q.shape[-2], q.shape[-1]
         Hkv = k.shape[1]
         if k.shape[3] != D:
             raise ValueError(f"head size mismatch: q has {D}, k has {k.shape[3]}")
@@ -127,7 +133,7 @@ class Decoder:
         self.inputs = (q, k, v, page_table, seq_lens)
         self.opt = make_options(q.dtype, page_size=page_size, max_pages=max_pages,
                                 num_pages=num_pages, path=path, fused_merge=fused_merge,
-                                append=self.append)
+                                append=self.append, n_queries=self.n_queries, causal=causal)
         p = fd.fd_plan_t()
         st = fd.fd_plan(B, Hq, Hkv, T, D, n_splits, self.opt, p)
         if st != fd.FD_OK:
@@ -138,9 +144,10 @@ class Decoder:
             self.workspace = torch.empty(p.workspace_bytes, dtype=torch.uint8, device=q.device)
             self.opt.workspace = self.workspace.data_ptr()
             self.opt.workspace_bytes = p.workspace_bytes
-        self.out = out if out is not None else torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+        rows = (B, self.n_queries, Hq) if q.dim() == 4 else (B, Hq)
+        self.out = out if out is not None else torch.empty(rows + (D,), dtype=torch.float32, device=q.device)
         self.lse = lse if lse is not None else (
-            torch.empty((B, Hq), dtype=torch.float32, device=q.device) if want_lse else None)
+            torch.empty(rows, dtype=torch.float32, device=q.device) if want_lse else None)
 
     def _call(self, fn, name):
         q, k, v, pt, sl = self.inputs
@@ -184,10 +191,12 @@ class Decoder:
 
 
 def decode(q, k, v, *, scale=None, page_table=None, seq_lens=None, T=None, n_splits=0,
-           path=None, fused_merge=None):
-    """out [B, Hq, D] fp32 and lse [B, Hq] fp32 of single-query decode attention."""
+           path=None, fused_merge=None, causal=False):
+    """out [B, Hq, D] fp32 and lse [B, Hq] fp32 of single-query decode
+    attention; with q [B, n_q, Hq, D] (several queries per sequence, causal
+    or not), out [B, n_q, Hq, D] and lse [B, n_q, Hq]."""
     return Decoder(q, k, v, scale=scale, page_table=page_table, seq_lens=seq_lens, T=T,
-                   n_splits=n_splits, path=path, fused_merge=fused_merge)()
+                   n_splits=n_splits, path=path, fused_merge=fused_merge, causal=causal)()
 
 
 def append_decode(q, k_new, v_new, k, v, *, seq_lens, scale=None, page_table=None, T=None,

@@ -32,7 +32,7 @@ class fd_options_t(ctypes.Structure):
                 ("num_pages", ctypes.c_int32), ("num_cus", ctypes.c_int32),
                 ("path", ctypes.c_int32), ("flags", ctypes.c_int32),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("stream", ctypes.c_void_p)]
+                ("stream", ctypes.c_void_p), ("n_queries", ctypes.c_int32), ("causal", ctypes.c_int32)]
 
 
 class fd_plan_t(ctypes.Structure):

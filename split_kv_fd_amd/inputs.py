@@ -209,6 +209,11 @@ def make_case(s: Spec, device="cpu") -> Case:
     return Case(s, q, k, v)
 
 
+def make_q_multi(s: Spec, n_queries: int, device="cpu") -> torch.Tensor:
+    """Queries of several tokens per sequence: [B, n_queries, Hq, D]."""
+    return _randn((s.B, n_queries, s.Hq, s.D), s.dtype, device, s.seed, _Q, 100 + n_queries)
+
+
 def make_new_token(s: Spec, step: int = 0, device="cpu"):
     """K, V rows of one appended decode token per sequence: each [B, Hkv, D]
     (seeded by the config seed and the step index)."""

@@ -43,6 +43,7 @@ def test_struct_sizes_match_header(lib):
     assert opt.struct_size == ctypes.sizeof(fd.fd_options_t)
     assert opt.dtype == fd.FD_BF16 and opt.path == fd.FD_PATH_AUTO
     assert opt.workspace is None and opt.stream is None and opt.page_size == 0
+    assert opt.n_queries == 1 and opt.causal == 0
 
 
 def opts(dtype=fd.FD_BF16, **kw):
@@ -249,6 +250,33 @@ def test_append_plans_cover_one_more_token(lib):
     st, p = plan(4, 8, 2, 4096, 128, 0, flags=fd.FD_FLAG_APPEND, page_size=16,
                  max_pages_per_seq=256, num_pages=10)
     assert st == fd.FD_OK and p.stream
+
+
+@pytest.mark.parametrize("nq", [1, 2, 3, 8, 16])
+def test_plan_several_queries(lib, nq):
+    # the n_q queries of a kv head's group are rows of one block of work: the
+    # matrix-core path once they make 4 rows, KV read once per head block
+    for (G, dt) in [(1, fd.FD_F16), (2, fd.FD_BF16), (4, fd.FD_BF16), (8, fd.FD_F32)]:
+        B, Hkv, T, D = 2, 2, 4096, 128
+        st, p = plan(B, G * Hkv, Hkv, T, D, 0, dtype=dt, n_queries=nq)
+        assert st == fd.FD_OK, fd.fd_last_error()
+        R = nq * G
+        want_mfma = dt != fd.FD_F32 and R >= 4
+        assert p.path == (fd.FD_PATH_MFMA if want_mfma else fd.FD_PATH_VALU)
+        assert p.heads_per_block * p.head_blocks >= R > p.heads_per_block * (p.head_blocks - 1)
+        if p.n_splits > 1:
+            assert p.workspace_bytes >= B * nq * G * Hkv * p.n_splits * (D + 2) * 4
+        st, p2 = plan(B, G * Hkv, Hkv, T, D, 0, dtype=dt, n_queries=nq, causal=1)
+        assert st == fd.FD_OK and p2.n_splits == p.n_splits
+
+
+def test_several_queries_rejects(lib):
+    assert plan(1, 4, 4, 100, 128, n_queries=17)[0] == fd.FD_ERR_INVALID_ARG
+    assert plan(1, 4, 4, 100, 128, n_queries=-1)[0] == fd.FD_ERR_INVALID_ARG
+    assert plan(1, 4, 4, 100, 128, n_queries=2, causal=2)[0] == fd.FD_ERR_INVALID_ARG
+    assert plan(1, 4, 4, 100, 128, n_queries=0)[0] == fd.FD_OK          # 0 means one query
+    st = plan(1, 4, 4, 100, 128, n_queries=2, flags=fd.FD_FLAG_APPEND)[0]
+    assert st == fd.FD_ERR_UNSUPPORTED
 
 
 def append(q=A, kn=A + 8192, vn=A + 16384, k=A, v=A, pt=None, sl=A, out=A, lse=A, shape=(1, 4, 4, 4096, 128),
