@@ -133,8 +133,9 @@ def main() -> int:
     ap.add_argument("--path", default=None, choices=[None, "auto", "valu", "mfma"])
     ap.add_argument("--merge", default="auto", choices=["auto", "fused", "combine"],
                     help="force the fused merge or the combine kernel (default: library's choice)")
-    ap.add_argument("--event-every", type=int, default=4,
-                    help="record HIP events around every N-th step's launches")
+    ap.add_argument("--event-every", type=int, default=8,
+                    help="one-launch steps: events bracket blocks of N launches; two-launch steps: "
+                         "the launches of every N-th step")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--set", action="append", default=[], metavar="KEY=VALUE",
@@ -206,36 +207,44 @@ def main() -> int:
     K = args.steps
     # fd_append_decode has no separate passes: its step is timed as a whole
     separate = plan["combine"] and not plan["fused"] and not args.append
-    # HIP events bracket the launches of every EVERY-th step (the others run
-    # without markers, which would otherwise add their own gaps).
+    # HIP events on the launch stream.  One launch per step (the split
+    # kernel with the fused merge): a pair of events brackets each block of
+    # EVERY consecutive launches, and a launch's duration is the block's
+    # time over its launch count, so the events' own cost is amortised.
+    # Two launches per step: the split and combine launches of every
+    # EVERY-th step are bracketed one by one.
     every = max(1, args.event_every)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(0, K, every)]
+    in_block = [0] * len(ev)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
         d = decs[i % copies]
-        e = ev[i // every] if i % every == 0 else None
-        if e:
-            e[0].record()
+        e = ev[i // every]
         if separate:
             # the merge is its own kernel: time the two launches apart
+            if i % every == 0:
+                e[0].record()
             d.split()
-            if e:
+            if i % every == 0:
                 e[1].record()
             d.combine()
-            if e:
+            if i % every == 0:
                 e[2].record()
+                in_block[i // every] = 1
         else:
-            # one launch per step: the split kernel (with the fused merge)
+            if i % every == 0:
+                e[0].record()
             d()
-            if e:
+            in_block[i // every] += 1
+            if i % every == every - 1 or i == K - 1:
                 e[1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
 
-    split_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    split_ms = [e[0].elapsed_time(e[1]) / n for e, n in zip(ev, in_block)]
     comb_ms = [e[1].elapsed_time(e[2]) for e in ev] if separate else [0.0]
-    step_ms = [e[0].elapsed_time(e[2 if separate else 1]) for e in ev]
+    step_ms = ([e[0].elapsed_time(e[2]) for e in ev] if separate else split_ms)
     ms_per_step = (t1 - t0) * 1e3 / K
     gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
     split_avg = statistics.mean(split_ms)
