@@ -102,12 +102,27 @@ def cpu_baseline(case, seconds: float):
         seqs += 1
         b = (b + 1) % s.B
     full_steps = seqs / s.B
+    # the same oracle on one thread, one sequence (context for the core count)
+    q = case.q[0:1].cpu()
+    one = None
+    if case.page_table is None:
+        k, v = case.k[0:1].cpu(), case.v[0:1].cpu()
+        t0 = time.perf_counter()
+        orc.decode(q, k, v, s.scale, nthreads=1)
+        one = round(2 * lens[0] * s.Hkv * s.D * ELT[s.dtype] / (time.perf_counter() - t0) / 1e9, 4)
     return {"value": round(done_bytes / total / 1e9, 4), "unit": "GB/s", "cores": orc.max_threads(),
             "kind": "oracle",
             "sample": (f"{seqs} sequence(s) of the workload ({full_steps:.2f} full steps; "
                        f"all {s.Hq} query heads each), {total:.1f} s of host time, fp64 "
                        "whole-softmax oracle, OpenMP over (batch, head)"),
-            "us_per_step": round(total / full_steps * 1e6, 1)}
+            "us_per_step": round(total / full_steps * 1e6, 1),
+            "one_core_value": one}
+
+
+def _pct(xs, p):
+    """p-th percentile (nearest rank) of a non-empty list."""
+    ys = sorted(xs)
+    return ys[min(len(ys) - 1, max(0, math.ceil(p / 100 * len(ys)) - 1))]
 
 
 def copy_calibration(gib: float = 1.0, reps: int = 5):
@@ -287,7 +302,9 @@ def main() -> int:
                        "merge": "fused into the split launch" if not separate else "combine kernel",
                        "split_median": round(statistics.median(split_ms) * 1e3, 2),
                        "combine_avg": round(statistics.mean(comb_ms) * 1e3, 2),
-                       "step_events_median": round(statistics.median(step_ms) * 1e3, 2)},
+                       "step_events_median": round(statistics.median(step_ms) * 1e3, 2),
+                       "split_p10": round(_pct(split_ms, 10) * 1e3, 2),
+                       "split_p90": round(_pct(split_ms, 90) * 1e3, 2)},
         "kernel_source_sha": kernel_source_sha(),
     }
     if not args.no_cpu_baseline:

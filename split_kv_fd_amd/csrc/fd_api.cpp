@@ -133,7 +133,9 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
     }
     int hpb, tile;
     if (path == FD_PATH_MFMA) {
-        hpb = fdk::kMfmaHeads;
+        // 16 query rows per workgroup, or 32 (two row blocks on one K / V
+        // read) when a kv head has more than 16
+        hpb = R > fdk::kMfmaHeads ? 2 * fdk::kMfmaHeads : fdk::kMfmaHeads;
         tile = fdk::kMfmaTile;
     } else {
         hpb = 1;

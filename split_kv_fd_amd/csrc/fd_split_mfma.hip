@@ -103,8 +103,12 @@ __device__ __forceinline__ uint2 load_piece<uint2>(const char *p) {
 // 16 tokens), 2 paged with one lookup per 16-token block (pages of 16+).
 // STREAM: balanced stream mode (ragged batches), else one workgroup per
 // (batch, kv head, head block, split).
-template <int DT, int D, int PG, bool STREAM>
-__global__ __launch_bounds__(256, 2) void split_mfma(SplitArgs a) {
+// NB: 16-row blocks of query rows per workgroup (1 or 2).  Both blocks use
+// the same K and V operands, so 32 query rows still read the KV once; the
+// second block's accumulators need the register file of one workgroup per
+// compute unit.
+template <int DT, int D, int PG, bool STREAM, int NB>
+__global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void split_mfma(SplitArgs a) {
     constexpr bool PAGED = PG != 0;
     constexpr int EB = 2;
     constexpr int ROWB = D * EB;
@@ -114,7 +118,7 @@ __global__ __launch_bounds__(256, 2) void split_mfma(SplitArgs a) {
     constexpr int WAVES = 4;
     constexpr int TOK = 32;             // tokens per wave step
     constexpr int TILE = WAVES * TOK;
-    constexpr int GB = kMfmaHeads;
+    constexpr int GB = kMfmaHeads * NB;
     static_assert(TILE == kMfmaTile, "host and kernel disagree on the tile");
     using VP = typename std::conditional<VB == 16, uint4, uint2>::type;
     using Off = typename std::conditional<PAGED, size_t, uint32_t>::type;
@@ -132,23 +136,31 @@ __global__ __launch_bounds__(256, 2) void split_mfma(SplitArgs a) {
         const int g0 = hb * GB;                 // first query row of the block
         const int ng = min(GB, a.R - g0);
 
-        // B operand of the logit MFMAs: q pieces 4*ks + kb of row i16.
-        uint4 qb[KS];
-        {
-            const size_t qr = i16 < ng ? qrow(a, b, kvh, g0 + i16) : 0;
+        // B operands of the logit MFMAs: q pieces 4*ks + kb of row
+        // 16*nb + i16 of the block.
+        uint4 qb[NB][KS];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int rr = 16 * nb + i16;
+            const size_t qr = rr < ng ? qrow(a, b, kvh, g0 + rr) : 0;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                qb[ks] = make_uint4(0, 0, 0, 0);
-                if (i16 < ng)
-                    qb[ks] = *reinterpret_cast<const uint4 *>(static_cast<const char *>(a.q) + qr * ROWB +
-                                                               (4 * ks + kb) * 16);
+                qb[nb][ks] = make_uint4(0, 0, 0, 0);
+                if (rr < ng)
+                    qb[nb][ks] = *reinterpret_cast<const uint4 *>(static_cast<const char *>(a.q) + qr * ROWB +
+                                                                   (4 * ks + kb) * 16);
             }
         }
 
-        f32x4_v acc[PVE];
+        f32x4_v acc[NB][PVE];
+        float m[NB], l[NB];
 #pragma unroll
-        for (int i = 0; i < PVE; ++i) acc[i] = f32x4_v{0.f, 0.f, 0.f, 0.f};
-        float m = kNegInf, l = 0.f;
+        for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+            for (int i = 0; i < PVE; ++i) acc[nb][i] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+            m[nb] = kNegInf;
+            l[nb] = 0.f;
+        }
 
         const char *kbase = static_cast<const char *>(a.k);
         const char *vbase = static_cast<const char *>(a.v);
@@ -182,35 +194,43 @@ __global__ __launch_bounds__(256, 2) void split_mfma(SplitArgs a) {
             bool ok[2][4];
         };
 
-        // lane_ok: this lane's query row attends to the step's tokens (false
-        // masks the row, for the causal tail of several queries).
-        auto consume_step = [&](const Buf &f, bool lane_ok) {
-            float s[2][4];
+        // sees(nb, t): query row 16*nb + i16 of the block attends to token
+        // t (0..31) of the wave's step (false masks it, for the causal tail
+        // of several queries).
+        auto consume_step = [&](const Buf &f, auto sees) {
+            float p[NB][2][4];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                f32x4_v c = {0.f, 0.f, 0.f, 0.f};
+            for (int nb = 0; nb < NB; ++nb) {
+                float s[2][4];
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) c = mfma_logits<DT>(f.k[h][ks], qb[ks], c);
+                for (int h = 0; h < 2; ++h) {
+                    f32x4_v c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int r = 0; r < 4; ++r) s[h][r] = (f.ok[h][r] && lane_ok) ? c[r] * a.scale_log2 : kNegInf;
+                    for (int ks = 0; ks < KS; ++ks) c = mfma_logits<DT>(f.k[h][ks], qb[nb][ks], c);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        s[h][r] = (f.ok[h][r] && sees(nb, 16 * h + 4 * kb + r)) ? c[r] * a.scale_log2 : kNegInf;
+                }
+                float mt = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                                 fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+                mt = fmaxf(mt, __shfl_xor(mt, 16));
+                mt = fmaxf(mt, __shfl_xor(mt, 32));
+                const float mn = fmaxf(m[nb], mt);
+                const float mu = mn == kNegInf ? 0.f : mn;
+                const float alpha = __builtin_amdgcn_exp2f(m[nb] - mu);
+                float ps = 0.f;
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        p[nb][h][r] = __builtin_amdgcn_exp2f(s[h][r] - mu);
+                        ps += p[nb][h][r];
+                    }
+                l[nb] = l[nb] * alpha + ps;
+                m[nb] = mn;
+#pragma unroll
+                for (int i = 0; i < PVE; ++i) acc[nb][i] *= alpha;
             }
-            float mt = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                             fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-            mt = fmaxf(mt, __shfl_xor(mt, 16));
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
-            const float mn = fmaxf(m, mt);
-            const float mu = mn == kNegInf ? 0.f : mn;
-            const float alpha = __builtin_amdgcn_exp2f(m - mu);
-            float p[2][4];
-            float ps = 0.f;
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) { p[h][r] = __builtin_amdgcn_exp2f(s[h][r] - mu); ps += p[h][r]; }
-            l = l * alpha + ps;
-            m = mn;
-#pragma unroll
-            for (int i = 0; i < PVE; ++i) acc[i] *= alpha;
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -218,10 +238,13 @@ __global__ __launch_bounds__(256, 2) void split_mfma(SplitArgs a) {
                     float vf[PVE];
                     widen<DT>(f.v[h][r], vf);
 #pragma unroll
-                    for (int i = 0; i < PVE; ++i)
-                        acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[i], p[h][r], acc[i], 0, 0, 0);
+                    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                        for (int i = 0; i < PVE; ++i)
+                            acc[nb][i] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[i], p[nb][h][r], acc[nb][i], 0, 0, 0);
                 }
         };
+        auto all_rows = [](int, int) { return true; };
 
         auto stream_range = [&](int r0, int r1) {
             auto row_offset = [&](int t, bool &ok) -> Off {
@@ -294,12 +317,12 @@ __global__ __launch_bounds__(256, 2) void split_mfma(SplitArgs a) {
                 load_step(base + TILE, fb);            // clamped past the end
                 asm volatile("" ::: "memory");
                 __builtin_amdgcn_sched_barrier(0);
-                consume_step(fa, true);
+                consume_step(fa, all_rows);
                 if (base + TILE >= r1) break;
                 load_step(base + 2 * TILE, fa);
                 asm volatile("" ::: "memory");
                 __builtin_amdgcn_sched_barrier(0);
-                consume_step(fb, true);
+                consume_step(fb, all_rows);
                 if (base + 2 * TILE >= r1) break;
             }
         };
@@ -354,10 +377,10 @@ __global__ __launch_bounds__(256, 2) void split_mfma(SplitArgs a) {
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
                     f.v[h][r] = *reinterpret_cast<const VP *>(vb_ + vo + i16 * VB);
-                f.ok[0][r] = wave == 0 && ti < count && vok && sees(ti, g0 + i16);
+                f.ok[0][r] = wave == 0 && ti < count && vok;
                 f.ok[1][r] = false;
             }
-            consume_step(f, true);
+            consume_step(f, [&](int nb, int t) { return sees(t, g0 + 16 * nb + i16); });
         };
 
         if (a.causal && c1 > tail0) {
@@ -388,15 +411,21 @@ __global__ __launch_bounds__(256, 2) void split_mfma(SplitArgs a) {
         }
 
         // The four lanes of a head share m; their sums cover different tokens.
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            l[nb] += __shfl_xor(l[nb], 16);
+            l[nb] += __shfl_xor(l[nb], 32);
+        }
 
         __syncthreads();                               // sm is free (previous segment)
 #pragma unroll
-        for (int i = 0; i < PVE; ++i)
+        for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sm.o[wave][i16][PVE * (4 * kb + r) + i] = acc[i][r];
-        if (kb == 0) { sm.m[wave][i16] = m; sm.l[wave][i16] = l; }
+            for (int i = 0; i < PVE; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sm.o[wave][16 * nb + i16][PVE * (4 * kb + r) + i] = acc[nb][i][r];
+            if (kb == 0) { sm.m[wave][16 * nb + i16] = m[nb]; sm.l[wave][16 * nb + i16] = l[nb]; }
+        }
         __syncthreads();
         finish_split<WAVES, GB, D>(a, sm, so, b, kvh, g0, ng);
     };
@@ -421,20 +450,25 @@ __global__ __launch_bounds__(256, 2) void split_mfma(SplitArgs a) {
     }
 }
 
-template <int DT, int D>
-hipError_t launch_dim(const SplitArgs &a, hipStream_t stream) {
+template <int DT, int D, int NB>
+hipError_t launch_nb(const SplitArgs &a, hipStream_t stream) {
     const dim3 grid = a.stream ? dim3(a.n_splits) : dim3(a.n_splits, a.Hkv * a.head_blocks, a.B);
     const int pg = !a.page_table ? 0 : (a.page_size >= 16 ? 2 : 1);
     if (a.stream) {
-        if (pg == 2) hipLaunchKernelGGL((split_mfma<DT, D, 2, true>), grid, dim3(256), 0, stream, a);
-        else if (pg == 1) hipLaunchKernelGGL((split_mfma<DT, D, 1, true>), grid, dim3(256), 0, stream, a);
-        else hipLaunchKernelGGL((split_mfma<DT, D, 0, true>), grid, dim3(256), 0, stream, a);
+        if (pg == 2) hipLaunchKernelGGL((split_mfma<DT, D, 2, true, NB>), grid, dim3(256), 0, stream, a);
+        else if (pg == 1) hipLaunchKernelGGL((split_mfma<DT, D, 1, true, NB>), grid, dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((split_mfma<DT, D, 0, true, NB>), grid, dim3(256), 0, stream, a);
     } else {
-        if (pg == 2) hipLaunchKernelGGL((split_mfma<DT, D, 2, false>), grid, dim3(256), 0, stream, a);
-        else if (pg == 1) hipLaunchKernelGGL((split_mfma<DT, D, 1, false>), grid, dim3(256), 0, stream, a);
-        else hipLaunchKernelGGL((split_mfma<DT, D, 0, false>), grid, dim3(256), 0, stream, a);
+        if (pg == 2) hipLaunchKernelGGL((split_mfma<DT, D, 2, false, NB>), grid, dim3(256), 0, stream, a);
+        else if (pg == 1) hipLaunchKernelGGL((split_mfma<DT, D, 1, false, NB>), grid, dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((split_mfma<DT, D, 0, false, NB>), grid, dim3(256), 0, stream, a);
     }
     return hipGetLastError();
+}
+
+template <int DT, int D>
+hipError_t launch_dim(const SplitArgs &a, hipStream_t stream) {
+    return a.heads_per_block == 2 * kMfmaHeads ? launch_nb<DT, D, 2>(a, stream) : launch_nb<DT, D, 1>(a, stream);
 }
 
 template <int DT>
@@ -449,7 +483,7 @@ hipError_t launch_dtype(const SplitArgs &a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_split_mfma(const SplitArgs &a, int dtype, hipStream_t stream) {
-    if (a.heads_per_block != kMfmaHeads) return hipErrorInvalidValue;
+    if (a.heads_per_block != kMfmaHeads && a.heads_per_block != 2 * kMfmaHeads) return hipErrorInvalidValue;
     switch (dtype) {
     case FD_F16: return launch_dtype<FD_F16>(a, stream);
     case FD_BF16: return launch_dtype<FD_BF16>(a, stream);

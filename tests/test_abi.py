@@ -156,8 +156,11 @@ def test_plan_paths(lib):
     assert plan(1, 32, 8, 4096, 128, 0, path=fd.FD_PATH_MFMA, dtype=fd.FD_F32)[0] == fd.FD_ERR_UNSUPPORTED
     st, p = plan(1, 8, 8, 4096, 128, 0, path=fd.FD_PATH_MFMA, dtype=fd.FD_F16)
     assert st == fd.FD_OK and p.path == fd.FD_PATH_MFMA and p.heads_per_block == 16
-    st, p = plan(1, 64, 2, 4096, 128, 0, path=fd.FD_PATH_MFMA)   # G = 32: two head blocks
-    assert st == fd.FD_OK and p.head_blocks == 2 and p.grid[1] == 4
+    # G = 32: one workgroup takes both 16-row blocks on a single K / V read
+    st, p = plan(1, 64, 2, 4096, 128, 0, path=fd.FD_PATH_MFMA)
+    assert st == fd.FD_OK and p.heads_per_block == 32 and p.head_blocks == 1 and p.grid[1] == 2
+    st, p = plan(1, 128, 2, 4096, 128, 0, path=fd.FD_PATH_MFMA)  # G = 64: two 32-row blocks
+    assert st == fd.FD_OK and p.heads_per_block == 32 and p.head_blocks == 2 and p.grid[1] == 4
     st, p = plan(1, 64, 8, 4096, 64, 0, path=fd.FD_PATH_VALU)     # G = 8 on the VALU path
     assert st == fd.FD_OK and p.path == fd.FD_PATH_VALU and p.heads_per_block == 8
 
@@ -264,6 +267,8 @@ def test_plan_several_queries(lib, nq):
         want_mfma = dt != fd.FD_F32 and R >= 4
         assert p.path == (fd.FD_PATH_MFMA if want_mfma else fd.FD_PATH_VALU)
         assert p.heads_per_block * p.head_blocks >= R > p.heads_per_block * (p.head_blocks - 1)
+        if want_mfma:
+            assert p.heads_per_block == (32 if R > 16 else 16)
         if p.n_splits > 1:
             assert p.workspace_bytes >= B * nq * G * Hkv * p.n_splits * (D + 2) * 4
         st, p2 = plan(B, G * Hkv, Hkv, T, D, 0, dtype=dt, n_queries=nq, causal=1)

@@ -78,12 +78,31 @@ def test_multi_merges(fused):
 
 
 def test_multi_d64_and_many_rows():
-    # 8 queries x G = 8: 64 query rows per kv head (four matrix-core blocks)
+    # 8 queries x G = 8: 64 query rows per kv head (two 32-row workgroups)
     case = contiguous("gqa128k_bf16", [900, 64, 3], Hq=16, Hkv=2, T=900, D=64)
     q = inputs.make_q_multi(case.spec, 8).to(DEV)
     for causal in (False, True):
         plan = check_multi(case, q, causal, what=f"D=64 64 rows causal={causal}")
-        assert plan["head_blocks"] == 4
+        assert plan["head_blocks"] == 2 and plan["heads_per_block"] == 32
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nq,G", [(3, 8), (4, 8), (5, 4), (8, 4)])
+def test_multi_32_row_blocks(causal, nq, G):
+    # 17..32 query rows per kv head: one workgroup, two matrix-core row
+    # blocks on one K / V read; contiguous splits and paged stream mode
+    Hkv = 2
+    case = contiguous("gqa128k_bf16", [1500, 0, 2, 700], Hq=G * Hkv, Hkv=Hkv, T=1500)
+    q = inputs.make_q_multi(case.spec, nq).to(DEV)
+    for n in (0, 1, 6):
+        plan = check_multi(case, q, causal, n_splits=n, path="mfma",
+                           what=f"32-row nq={nq} G={G} causal={causal} n={n}")
+        assert plan["heads_per_block"] == 32
+    s = inputs.spec("paged_ragged_bf16", B=4, Hq=G * Hkv, Hkv=Hkv, T=1500, len_lo=0, len_hi=1500)
+    pcase = inputs.make_case(s).to(DEV)
+    q = inputs.make_q_multi(s, nq).to(DEV)
+    plan = check_multi(pcase, q, causal, path="mfma", what=f"32-row paged nq={nq} G={G} causal={causal}")
+    assert plan["stream"] and plan["heads_per_block"] == 32
 
 
 def test_multi_query_equals_single_query_decodes():
