@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode-attention KV read GB/s (fraction of HBM peak) and µs/step, 1 MI355X"
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0        # dense bf16 / f16 matrix-core peak
 DEFAULT_WORKLOAD = "mha32k_f16"
 ELT = {"f32": 4, "f16": 2, "bf16": 2}
 
@@ -266,6 +267,25 @@ def main() -> int:
     achieved = kv_bytes / (split_avg * 1e-3) / 1e9
     kernel = "fd_split"
     traffic = read_traffic(spec.name, kernel)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "kernel": kernel,
+                "launch_us_avg": round(split_avg * 1e3, 2),
+                "bytes_per_launch": kv_bytes}
+    if plan["path"] == "prefill":
+        # the query-tiled kernel is bounded by the matrix cores: 2 flops per
+        # multiply-add for q.k and for p.v over every (query row, token seen)
+        seen = 0
+        for L in lens:
+            for i in range(args.n_queries):
+                seen += max(0, L - (args.n_queries - 1 - i)) if args.causal else L
+        flops = 4 * spec.D * spec.Hq * seen
+        tf = flops / (split_avg * 1e-3) / 1e12
+        kernel = "fd_prefill"
+        roofline = {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(tf / MFMA_PEAK_TFLOPS, 4),
+                    "traffic": read_traffic(spec.name, kernel), "kernel": kernel,
+                    "launch_us_avg": round(split_avg * 1e3, 2), "flops_per_launch": flops}
 
     if overrides:
         print(f"[bench] workload overrides {overrides}: not the reference workload",
@@ -293,11 +313,7 @@ def main() -> int:
                    "n_queries": args.n_queries, "causal": bool(args.causal)},
         "us_per_step": round(ms_per_step * 1e3, 2),
         "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": kernel,
-                     "launch_us_avg": round(split_avg * 1e3, 2),
-                     "bytes_per_launch": kv_bytes},
+        "roofline": roofline,
         "kernels_us": {"split_avg": round(split_avg * 1e3, 2),
                        "merge": "fused into the split launch" if not separate else "combine kernel",
                        "split_median": round(statistics.median(split_ms) * 1e3, 2),

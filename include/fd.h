@@ -37,6 +37,12 @@
  *     tokens, or with fd_options_t.causal to the first T_b - (n_q - 1 - i)
  *     (the queries are the sequence's last n_q cached tokens, as in
  *     verifying a draft); a query with no token yields out = 0, lse = -inf.
+ *     Up to 16 queries run on the split-KV kernels (every query row of a kv
+ *     head shares one read of K / V); more (the prefill phase: the dupenodi
+ *     guide, "Concept", has prefill attend with the whole block of prompt
+ *     queries) run on a query-tiled kernel: one workgroup per 64 query rows
+ *     of a (sequence, kv head) over the whole visible KV range, no split and
+ *     no workspace (FD_PATH_PREFILL; f16 / bf16 only).
  *   - Calls are stream-ordered on fd_options_t.stream and never synchronise;
  *     a fault inside a kernel surfaces at the caller's next synchronisation.
  *   - Arguments are validated on the host before any launch.  Every call
@@ -73,7 +79,9 @@ typedef enum {
 typedef enum {
     FD_PATH_AUTO = -1,        /* the planner chooses                          */
     FD_PATH_VALU = 0,         /* vector-ALU dot products and reductions       */
-    FD_PATH_MFMA = 1          /* matrix-core path (f16/bf16 only)             */
+    FD_PATH_MFMA = 1,         /* matrix-core path (f16/bf16 only)             */
+    FD_PATH_PREFILL = 2       /* query-tiled matrix-core kernel for many      */
+                              /* queries per sequence (f16/bf16; no split)    */
 } fd_path_t;
 
 /* fd_options_t.flags.  By default fd_decode merges the splits inside the
@@ -106,8 +114,9 @@ typedef struct fd_options {
     void *workspace;            /* device buffer for the split partials        */
     size_t workspace_bytes;     /* its size in bytes                          */
     void *stream;               /* hipStream_t to launch on; NULL = null stream */
-    int32_t n_queries;          /* queries per sequence, 1 .. 16 (0 means 1); */
-                                /* > 1 gives q / out an n_q axis (see below)  */
+    int32_t n_queries;          /* queries per sequence, 1 .. 65536 (0 = 1);  */
+                                /* > 1 gives q / out an n_q axis (see below); */
+                                /* > 16 runs the query-tiled kernel          */
     int32_t causal;             /* with n_queries > 1: 1 = query i sees the   */
                                 /* first T_b - (n_queries - 1 - i) tokens     */
 } fd_options_t;

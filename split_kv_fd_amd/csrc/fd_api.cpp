@@ -44,7 +44,8 @@ long env_long(const char *name, long dflt) {
 }
 
 constexpr uint32_t kOptionsV1 = sizeof(fd_options_t);
-constexpr int kMaxQueries = 16;          // queries per sequence
+constexpr int kMaxQueries = 65536;       // queries per sequence
+constexpr int kMaxDecodeQueries = 16;    // more take the query-tiled (prefill) kernel
 
 // Compute units of the current device, cached per device id.
 fd_status_t device_cus(int *cus) {
@@ -76,7 +77,7 @@ fd_status_t read_options(const fd_options_t *opt, fd_options_t *o) {
     std::memcpy(o, opt, kOptionsV1);
     if (o->dtype != FD_F32 && o->dtype != FD_F16 && o->dtype != FD_BF16)
         return fail(FD_ERR_INVALID_ARG, "unknown dtype %d", (int)o->dtype);
-    if (o->path != FD_PATH_AUTO && o->path != FD_PATH_VALU && o->path != FD_PATH_MFMA)
+    if (o->path != FD_PATH_AUTO && o->path != FD_PATH_VALU && o->path != FD_PATH_MFMA && o->path != FD_PATH_PREFILL)
         return fail(FD_ERR_INVALID_ARG, "unknown path %d", (int)o->path);
     if (o->num_cus < 0) return fail(FD_ERR_INVALID_ARG, "num_cus %d < 0", (int)o->num_cus);
     if (o->flags & ~(FD_FLAG_FUSED_MERGE | FD_FLAG_COMBINE_KERNEL | FD_FLAG_APPEND))
@@ -120,6 +121,30 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
     const int G = Hq / Hkv;
     const int R = o.n_queries * G;       // query rows per kv head
     int path = o.path;
+
+    // Many queries per sequence (prefill): the query-tiled kernel, one
+    // workgroup per tile of query rows over the whole KV range; no split,
+    // no workspace.
+    if (path == FD_PATH_PREFILL || (path == FD_PATH_AUTO && o.n_queries > kMaxDecodeQueries)) {
+        if (o.dtype == FD_F32) return fail(FD_ERR_UNSUPPORTED, "the query-tiled kernel needs f16 or bf16 inputs");
+        if (o.flags & FD_FLAG_APPEND) return fail(FD_ERR_UNSUPPORTED, "fd_append_decode takes one query per sequence");
+        const long tiles = ceil_div(R, fdk::kPrefillRows);
+        if (Hkv > 65535) return fail(FD_ERR_UNSUPPORTED, "Hkv=%d > 65535", Hkv);
+        std::memset(p, 0, sizeof *p);
+        p->n_splits = 1;
+        p->chunk = T;
+        p->path = FD_PATH_PREFILL;
+        p->tile = fdk::kPrefillTokens;
+        p->heads_per_block = fdk::kPrefillRows;
+        p->head_blocks = (int)tiles;
+        p->grid[0] = (int)tiles;
+        p->grid[1] = Hkv;
+        p->grid[2] = B;
+        p->block = 256;
+        return FD_OK;
+    }
+    if (o.n_queries > kMaxDecodeQueries)
+        return fail(FD_ERR_UNSUPPORTED, "more than %d queries per sequence take the query-tiled path", kMaxDecodeQueries);
     if (path == FD_PATH_MFMA && o.dtype == FD_F32)
         return fail(FD_ERR_UNSUPPORTED, "the MFMA path needs f16 or bf16 inputs");
     if (path == FD_PATH_AUTO) {
@@ -262,6 +287,7 @@ struct Call {
     fd_plan_t p;
     fdk::SplitArgs s;
     fdk::CombineArgs c;
+    fdk::PrefillArgs f;
 };
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -386,6 +412,17 @@ fd_status_t prepare(const void *q, const void *k, const void *v, const int32_t *
     cb.n_splits = c->p.n_splits;
     cb.chunk = c->p.chunk;
     cb.append = append ? 1 : 0;
+
+    fdk::PrefillArgs &f = c->f;
+    f.q = q; f.k = k; f.v = v;
+    f.page_table = page_table;
+    f.seq_lens = seq_lens;
+    f.out = out; f.lse = lse;
+    f.B = B; f.nq = s.nq; f.Hq = Hq; f.Hkv = Hkv; f.T = T; f.D = D; f.G = s.G; f.R = s.R;
+    f.row_tiles = c->p.path == FD_PATH_PREFILL ? c->p.head_blocks : 0;
+    f.causal = s.causal;
+    f.page_size = s.page_size; f.page_shift = s.page_shift; f.max_pages = s.max_pages; f.num_pages = s.num_pages;
+    f.scale_log2 = s.scale_log2;
     return FD_OK;
 }
 
@@ -438,6 +475,11 @@ struct EpochTable {
 EpochTable g_epochs;
 
 fd_status_t run_split(Call &c, bool fused) {
+    if (c.p.path == FD_PATH_PREFILL) {
+        const hipError_t e = fdk::launch_prefill(c.f, c.o.dtype, static_cast<hipStream_t>(c.o.stream));
+        if (e != hipSuccess) return hip_fail(e, "launching the query-tiled kernel");
+        return FD_OK;
+    }
     fused = fused || c.p.stream;            // stream mode always merges in the launch
     c.s.fused = fused ? 1 : 0;
     c.s.epoch = c.s.next_epoch = 0;

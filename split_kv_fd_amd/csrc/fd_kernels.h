@@ -115,4 +115,28 @@ hipError_t launch_split_mfma(const SplitArgs &a, int dtype, hipStream_t stream);
 // Launch the combine kernel.
 hipError_t launch_combine(const CombineArgs &a, hipStream_t stream);
 
+// Many queries per sequence (prefill): one workgroup per tile of
+// kPrefillRows query rows of one (batch, kv head), over the whole visible
+// KV range in tiles of kPrefillTokens tokens staged in LDS.
+constexpr int kPrefillRows = 64;
+constexpr int kPrefillTokens = 32;
+
+struct PrefillArgs {
+    const void *q;               // [B, nq, Hq, D]
+    const void *k;
+    const void *v;
+    const int32_t *page_table;   // nullptr: contiguous cache
+    const int32_t *seq_lens;     // nullptr: every sequence has length T
+    float *out;                  // [B, nq, Hq, D]
+    float *lse;                  // [B, nq, Hq], may be nullptr
+    int B, nq, Hq, Hkv, T, D, G;
+    int R;                       // query rows per kv head = nq * G
+    int row_tiles;               // ceil(R / kPrefillRows)
+    int causal;                  // query i sees the first T_b - (nq - 1 - i) tokens
+    int page_size, page_shift, max_pages, num_pages;
+    float scale_log2;
+};
+
+hipError_t launch_prefill(const PrefillArgs &a, int dtype, hipStream_t stream);
+
 }  // namespace fdk

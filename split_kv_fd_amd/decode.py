@@ -16,7 +16,7 @@ from . import fd
 
 _DTYPE = {torch.float32: fd.FD_F32, torch.float16: fd.FD_F16, torch.bfloat16: fd.FD_BF16}
 _PATH = {None: fd.FD_PATH_AUTO, "auto": fd.FD_PATH_AUTO, "valu": fd.FD_PATH_VALU,
-         "mfma": fd.FD_PATH_MFMA}
+         "mfma": fd.FD_PATH_MFMA, "prefill": fd.FD_PATH_PREFILL}
 
 
 class FDError(RuntimeError):

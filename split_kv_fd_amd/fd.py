@@ -16,7 +16,7 @@ LIB_PATH = os.environ.get("FD_LIBRARY") or os.path.join(
 
 FD_F32, FD_F16, FD_BF16 = 0, 1, 2
 FD_OK, FD_ERR_INVALID_ARG, FD_ERR_UNSUPPORTED, FD_ERR_WORKSPACE, FD_ERR_HIP = range(5)
-FD_PATH_AUTO, FD_PATH_VALU, FD_PATH_MFMA = -1, 0, 1
+FD_PATH_AUTO, FD_PATH_VALU, FD_PATH_MFMA, FD_PATH_PREFILL = -1, 0, 1, 2
 FD_FLAG_FUSED_MERGE = 0x1
 FD_FLAG_COMBINE_KERNEL = 0x2
 FD_FLAG_APPEND = 0x4
@@ -45,7 +45,7 @@ class fd_plan_t(ctypes.Structure):
 
     def as_dict(self) -> dict:
         return {"n_splits": self.n_splits, "chunk": self.chunk,
-                "path": {0: "valu", 1: "mfma"}.get(self.path, self.path), "tile": self.tile,
+                "path": {0: "valu", 1: "mfma", 2: "prefill"}.get(self.path, self.path), "tile": self.tile,
                 "heads_per_block": self.heads_per_block, "head_blocks": self.head_blocks,
                 "grid": list(self.grid), "block": self.block, "combine": bool(self.combine),
                 "fused": bool(self.fused), "stream": bool(self.stream),

@@ -276,12 +276,32 @@ def test_plan_several_queries(lib, nq):
 
 
 def test_several_queries_rejects(lib):
-    assert plan(1, 4, 4, 100, 128, n_queries=17)[0] == fd.FD_ERR_INVALID_ARG
+    assert plan(1, 4, 4, 100, 128, n_queries=65537)[0] == fd.FD_ERR_INVALID_ARG
     assert plan(1, 4, 4, 100, 128, n_queries=-1)[0] == fd.FD_ERR_INVALID_ARG
+    assert plan(1, 4, 4, 100, 128, n_queries=17, dtype=fd.FD_F32)[0] == fd.FD_ERR_UNSUPPORTED
+    assert plan(1, 4, 4, 100, 128, n_queries=17, path=fd.FD_PATH_VALU)[0] == fd.FD_ERR_UNSUPPORTED
+    assert plan(1, 4, 4, 100, 128, path=fd.FD_PATH_PREFILL, dtype=fd.FD_F32)[0] == fd.FD_ERR_UNSUPPORTED
+    assert plan(1, 4, 4, 100, 128, path=5)[0] == fd.FD_ERR_INVALID_ARG
     assert plan(1, 4, 4, 100, 128, n_queries=2, causal=2)[0] == fd.FD_ERR_INVALID_ARG
     assert plan(1, 4, 4, 100, 128, n_queries=0)[0] == fd.FD_OK          # 0 means one query
     st = plan(1, 4, 4, 100, 128, n_queries=2, flags=fd.FD_FLAG_APPEND)[0]
     assert st == fd.FD_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("nq,G", [(17, 1), (100, 4), (4096, 8), (65536, 1)])
+def test_plan_query_tiled(lib, nq, G):
+    # more than 16 queries per sequence: one workgroup per 64 query rows of
+    # each (sequence, kv head), the whole KV range, no split, no workspace
+    B, Hkv = 2, 2
+    st, p = plan(B, G * Hkv, Hkv, 8192, 128, 0, n_queries=nq, causal=1)
+    assert st == fd.FD_OK, fd.fd_last_error()
+    assert p.path == fd.FD_PATH_PREFILL and p.n_splits == 1 and p.workspace_bytes == 0
+    assert not p.fused and not p.combine and not p.stream
+    tiles = -(-(nq * G) // 64)
+    assert (p.grid[0], p.grid[1], p.grid[2]) == (tiles, Hkv, B) and p.head_blocks == tiles
+    # forced for a few queries too
+    st, p = plan(B, G * Hkv, Hkv, 8192, 128, 0, n_queries=2, path=fd.FD_PATH_PREFILL)
+    assert st == fd.FD_OK and p.path == fd.FD_PATH_PREFILL
 
 
 def append(q=A, kn=A + 8192, vn=A + 16384, k=A, v=A, pt=None, sl=A, out=A, lse=A, shape=(1, 4, 4, 4096, 128),
