@@ -40,7 +40,7 @@
  *     Up to 16 queries run on the split-KV kernels (every query row of a kv
  *     head shares one read of K / V); more (the prefill phase: the dupenodi
  *     guide, "Concept", has prefill attend with the whole block of prompt
- *     queries) run on a query-tiled kernel: one workgroup per 64 query rows
+ *     queries) run on a query-tiled kernel: one workgroup per 128 query rows
  *     of a (sequence, kv head) over the whole visible KV range, no split and
  *     no workspace (FD_PATH_PREFILL; f16 / bf16 only).
  *   - Calls are stream-ordered on fd_options_t.stream and never synchronise;

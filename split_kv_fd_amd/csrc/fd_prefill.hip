@@ -16,8 +16,11 @@
 //  * K rows as they are in memory (row stride padded by 16 bytes so the
 //    16 lanes reading 16 rows hit distinct banks);
 //  * V transposed, V^T[d][token], so that the value product can take 8
-//    consecutive tokens of one dimension per lane.
-// Per wave (16 rows) and tile (two 16-token halves):
+//    tokens of one dimension per lane in one 16-byte read: within a row the
+//    tokens are stored in the order the lanes take them (position
+//    8*((t%16)/4) + 4*(t/16) + t%4 for token t).
+// Per wave (two blocks of 16 rows, each K / V fragment read from LDS once
+// for both) and tile (two 16-token halves):
 //  * logits S^T = K Q^T with v_mfma_f32_16x16x32_{bf16,f16}: tokens on M,
 //    query rows on N (the q pieces are the B operand, loaded once), so lane
 //    (i16, kb) holds row i16's logits of tokens 4*kb .. 4*kb+3 of each half;
@@ -58,23 +61,35 @@ __device__ __forceinline__ f32x4_v mfma(const uint4 &a, const uint4 &b, f32x4_v 
                                                       __builtin_bit_cast(f16x8_v, b), c, 0, 0, 0);
 }
 
-// A finite fp32 value as the 16-bit storage type (round to nearest even),
-// and back.
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+typedef float f32x2_v __attribute__((ext_vector_type(2)));
+
+// Two finite fp32 values as packed 16-bit storage values (one instruction),
+// and back.  The rounding mode does not matter here: the low part of P is
+// taken from the exact difference p - hi.
 template <int DT>
-__device__ __forceinline__ uint32_t to16(float x) {
-    if constexpr (DT == FD_BF16) {
-        const uint32_t u = __float_as_uint(x);
-        return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-    } else {
-        return (uint32_t)__builtin_bit_cast(unsigned short, (_Float16)x);
-    }
+__device__ __forceinline__ uint32_t pack2(float x, float y) {
+    if constexpr (DT == FD_BF16)
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_v{x, y}, bf16x2_v));
+    else
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x, y));
 }
 
 template <int DT>
-__device__ __forceinline__ float from16(uint32_t h) {
-    if constexpr (DT == FD_BF16) return __uint_as_float(h << 16);
-    else return (float)__builtin_bit_cast(_Float16, (unsigned short)h);
+__device__ __forceinline__ void unpack2(uint32_t w, float &x, float &y) {
+    if constexpr (DT == FD_BF16) {
+        x = __uint_as_float(w << 16);
+        y = __uint_as_float(w & 0xffff0000u);
+    } else {
+        x = (float)__builtin_bit_cast(_Float16, (unsigned short)(w & 0xffffu));
+        y = (float)__builtin_bit_cast(_Float16, (unsigned short)(w >> 16));
+    }
 }
+
+// The running max of a row is only raised when a tile's max exceeds it by
+// more than this (log2 units): probabilities then stay below 2^kSlack,
+// exactly representable, and most tiles skip rescaling the accumulator.
+constexpr float kSlack = 8.f;
 
 template <int DT, int D, bool PAGED>
 __global__ __launch_bounds__(256, 2) void prefill(PrefillArgs a) {
@@ -85,12 +100,13 @@ __global__ __launch_bounds__(256, 2) void prefill(PrefillArgs a) {
     constexpr int NTOK = kPrefillTokens;     // tokens per KV tile
     constexpr int KSTR = ROWB + 16;          // LDS row stride of K (bytes)
     constexpr int VSTR = NTOK * 2 + 16;      // LDS row stride of V^T (bytes)
-    static_assert(NTOK == 32 && kPrefillRows == 64, "the tile maps assume 32 tokens x 64 rows");
+    constexpr int NB = 2;                    // 16-row blocks per wave
+    static_assert(NTOK == 32 && kPrefillRows == 4 * 16 * NB, "the tile maps assume 32 tokens x 4 waves x NB*16 rows");
     static_assert(PIECES * 16 <= 256, "one (token pair, piece) per thread");
 
     __shared__ __align__(16) unsigned char sK[2][NTOK * KSTR];
     __shared__ __align__(16) unsigned char sV[2][D * VSTR];
-    __shared__ int sOk[2][NTOK];
+    __shared__ uint32_t sOkBits[2];          // bit t: token t of the tile is real
 
     const int t = threadIdx.x;
     const int lane = t & 63;
@@ -106,20 +122,38 @@ __global__ __launch_bounds__(256, 2) void prefill(PrefillArgs a) {
     int Tb = a.seq_lens ? a.seq_lens[b] : a.T;
     Tb = Tb < 0 ? 0 : (Tb > a.T ? a.T : Tb);
 
-    // This lane's query row, the tokens it sees, and its q pieces.
-    const int rr = r0 + 16 * wave + i16;
-    const bool row_ok = rr < a.R;
-    const int qi = row_ok ? rr / a.G : 0;
-    int lim = 0;
-    if (row_ok) lim = a.causal ? Tb - (a.nq - 1 - qi) : Tb;
-    lim = lim < 0 ? 0 : lim;
-    const size_t qrow = ((size_t)b * a.nq + qi) * a.Hq + (size_t)kvh * a.G + (row_ok ? rr - qi * a.G : 0);
-    uint4 qb[KS];
+    // This lane's query rows (one per block), the tokens each sees, and
+    // their q pieces.
+    bool row_ok[NB];
+    int lim[NB];
+    size_t qrow[NB];
+    uint4 qb[NB][KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-        qb[ks] = row_ok ? *reinterpret_cast<const uint4 *>(static_cast<const char *>(a.q) + qrow * ROWB +
-                                                             (4 * ks + kb) * 16)
-                        : make_uint4(0, 0, 0, 0);
+    for (int nb = 0; nb < NB; ++nb) {
+        const int rr = r0 + 16 * (NB * wave + nb) + i16;
+        row_ok[nb] = rr < a.R;
+        const int qi = row_ok[nb] ? rr / a.G : 0;
+        int lm = 0;
+        if (row_ok[nb]) lm = a.causal ? Tb - (a.nq - 1 - qi) : Tb;
+        lim[nb] = lm < 0 ? 0 : lm;
+        qrow[nb] = ((size_t)b * a.nq + qi) * a.Hq + (size_t)kvh * a.G + (row_ok[nb] ? rr - qi * a.G : 0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qb[nb][ks] = row_ok[nb] ? *reinterpret_cast<const uint4 *>(static_cast<const char *>(a.q) +
+                                                                       qrow[nb] * ROWB + (4 * ks + kb) * 16)
+                                    : make_uint4(0, 0, 0, 0);
+    }
+
+    // Tokens every row of this wave sees (0 if the wave has rows past R):
+    // tiles below it need no mask.
+    int wave_lim = 0;
+    {
+        const int rw0 = r0 + 16 * NB * wave;
+        if (rw0 + 16 * NB <= a.R) {
+            wave_lim = a.causal ? Tb - (a.nq - 1 - rw0 / a.G) : Tb;
+            wave_lim = wave_lim < 0 ? 0 : wave_lim;
+        }
+    }
 
     // Tokens the workgroup's rows see at most.
     const int r_last = min(r0 + kPrefillRows, a.R) - 1;
@@ -131,8 +165,11 @@ __global__ __launch_bounds__(256, 2) void prefill(PrefillArgs a) {
     const int u = t & 15;
     const int piece = t >> 4;
     const bool loader = piece < PIECES;
-    uint4 k0 = make_uint4(0, 0, 0, 0), k1 = k0, v0 = k0, v1 = k0;
-    int ok0 = 0, ok1 = 0;
+    // One tile's worth of this thread's loads.
+    struct Regs {
+        uint4 k0, k1, v0, v1;
+        int ok0, ok1;
+    };
     // row of token tt of the sequence (a real token: Tb >= 1 here); ok =
     // false for a padding token or a page outside the pool
     auto token_row = [&](int tt, int &ok) -> size_t {
@@ -146,121 +183,194 @@ __global__ __launch_bounds__(256, 2) void prefill(PrefillArgs a) {
             return ((size_t)b * a.Hkv + kvh) * a.T + tc;
         }
     };
-    auto load_tile = [&](int j) {
-        const size_t ra = token_row(j * NTOK + 2 * u, ok0);
-        const size_t rb = token_row(j * NTOK + 2 * u + 1, ok1);
+    auto load_tile = [&](int j) -> Regs {
+        Regs g;
+        g.k0 = g.k1 = g.v0 = g.v1 = make_uint4(0, 0, 0, 0);
+        const size_t ra = token_row(j * NTOK + 2 * u, g.ok0);
+        const size_t rb = token_row(j * NTOK + 2 * u + 1, g.ok1);
         if (loader) {
             const char *kp = static_cast<const char *>(a.k) + piece * 16;
             const char *vp = static_cast<const char *>(a.v) + piece * 16;
-            k0 = *reinterpret_cast<const uint4 *>(kp + ra * ROWB);
-            k1 = *reinterpret_cast<const uint4 *>(kp + rb * ROWB);
-            v0 = *reinterpret_cast<const uint4 *>(vp + ra * ROWB);
-            v1 = *reinterpret_cast<const uint4 *>(vp + rb * ROWB);
+            g.k0 = *reinterpret_cast<const uint4 *>(kp + ra * ROWB);
+            g.k1 = *reinterpret_cast<const uint4 *>(kp + rb * ROWB);
+            g.v0 = *reinterpret_cast<const uint4 *>(vp + ra * ROWB);
+            g.v1 = *reinterpret_cast<const uint4 *>(vp + rb * ROWB);
         }
+        return g;
     };
-    auto store_tile = [&](int buf) {
+    // V^T column of token tt of a tile (see the header): tokens 2u and 2u+1
+    // stay adjacent, so one 32-bit store writes both.
+    auto vpos = [](int tt) { return 8 * ((tt & 15) >> 2) + 4 * (tt >> 4) + (tt & 3); };
+    auto store_tile = [&](int buf, const Regs g) {
+        if (wave == 0) {
+            // lanes 0..15 hold tokens 2u, 2u+1 of u = lane: interleave their flags
+            auto spread = [](uint32_t x) {
+                x = (x | (x << 8)) & 0x00FF00FFu;
+                x = (x | (x << 4)) & 0x0F0F0F0Fu;
+                x = (x | (x << 2)) & 0x33333333u;
+                return (x | (x << 1)) & 0x55555555u;
+            };
+            const uint32_t b0 = (uint32_t)__ballot(g.ok0) & 0xffffu;
+            const uint32_t b1 = (uint32_t)__ballot(g.ok1) & 0xffffu;
+            if (lane == 0) sOkBits[buf] = spread(b0) | (spread(b1) << 1);
+        }
         if (!loader) return;
-        *reinterpret_cast<uint4 *>(&sK[buf][(2 * u) * KSTR + piece * 16]) = k0;
-        *reinterpret_cast<uint4 *>(&sK[buf][(2 * u + 1) * KSTR + piece * 16]) = k1;
+        *reinterpret_cast<uint4 *>(&sK[buf][(2 * u) * KSTR + piece * 16]) = g.k0;
+        *reinterpret_cast<uint4 *>(&sK[buf][(2 * u + 1) * KSTR + piece * 16]) = g.k1;
         // V^T: dimension 8*piece + e, tokens 2u and 2u+1 packed in one word
-        const uint32_t w0[4] = {v0.x, v0.y, v0.z, v0.w};
-        const uint32_t w1[4] = {v1.x, v1.y, v1.z, v1.w};
+        const uint32_t w0[4] = {g.v0.x, g.v0.y, g.v0.z, g.v0.w};
+        const uint32_t w1[4] = {g.v1.x, g.v1.y, g.v1.z, g.v1.w};
+        const int col = 2 * vpos(2 * u);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            *reinterpret_cast<uint32_t *>(&sV[buf][(8 * piece + 2 * i) * VSTR + 4 * u]) =
+            *reinterpret_cast<uint32_t *>(&sV[buf][(8 * piece + 2 * i) * VSTR + col]) =
                 (w0[i] & 0xffffu) | (w1[i] << 16);
-            *reinterpret_cast<uint32_t *>(&sV[buf][(8 * piece + 2 * i + 1) * VSTR + 4 * u]) =
+            *reinterpret_cast<uint32_t *>(&sV[buf][(8 * piece + 2 * i + 1) * VSTR + col]) =
                 (w0[i] >> 16) | (w1[i] & 0xffff0000u);
-        }
-        if (piece == 0) {
-            sOk[buf][2 * u] = ok0;
-            sOk[buf][2 * u + 1] = ok1;
         }
     };
 
-    f32x4_v acc[DT16];
+    f32x4_v acc[NB][DT16];
+    float m[NB], l[NB];
 #pragma unroll
-    for (int dt = 0; dt < DT16; ++dt) acc[dt] = f32x4_v{0.f, 0.f, 0.f, 0.f};
-    float m = kNegInf, l = 0.f;
+    for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+        for (int dt = 0; dt < DT16; ++dt) acc[nb][dt] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+        m[nb] = kNegInf;
+        l[nb] = 0.f;
+    }
 
+    // The tile consumed from LDS buffer `buf`.
+    auto compute = [&](int j, int buf) {
+        // logits of both row blocks; each K fragment is read once, and the
+        // four accumulation chains are interleaved
+        f32x4_v c[NB][2];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) c[nb][0] = c[nb][1] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint4 kp = *reinterpret_cast<const uint4 *>(&sK[buf][(16 * h + i16) * KSTR + (4 * ks + kb) * 16]);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) c[nb][h] = mfma<DT>(kp, qb[nb][ks], c[nb][h]);
+            }
+        // Masks: tiles every row of the wave sees in full need none; else
+        // token tk counts for a row when it is real and below the row's limit.
+        const bool full = !PAGED && (j + 1) * NTOK <= wave_lim;
+        const uint32_t okbits = sOkBits[buf];
+        float s[NB][8];
+        bool need = false;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int rel = lim[nb] - j * NTOK;        // this row sees tokens [0, rel) of the tile
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int tk = 16 * (e >> 2) + 4 * kb + (e & 3);
+                const bool ok = full | ((tk < rel) & (((okbits >> tk) & 1u) != 0u));
+                s[nb][e] = ok ? c[nb][e >> 2][e & 3] * a.scale_log2 : kNegInf;
+            }
+            const float lmt = fmaxf(fmaxf(fmaxf(s[nb][0], s[nb][1]), fmaxf(s[nb][2], s[nb][3])),
+                                    fmaxf(fmaxf(s[nb][4], s[nb][5]), fmaxf(s[nb][6], s[nb][7])));
+            need = need | (lmt > m[nb] + kSlack);
+        }
+        // The running max of a row moves only when one of its logits exceeds
+        // it by more than kSlack; then (rarely, after the first tiles) the
+        // row max is formed across its four lanes and the state rescaled.
+        if (__any(need)) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                float mt = fmaxf(fmaxf(fmaxf(s[nb][0], s[nb][1]), fmaxf(s[nb][2], s[nb][3])),
+                                 fmaxf(fmaxf(s[nb][4], s[nb][5]), fmaxf(s[nb][6], s[nb][7])));
+                mt = fmaxf(mt, __shfl_xor(mt, 16));
+                mt = fmaxf(mt, __shfl_xor(mt, 32));
+                const bool grow = mt > m[nb] + kSlack;
+                const float m_new = grow ? mt : m[nb];
+                const float alpha = grow ? __builtin_amdgcn_exp2f(m[nb] - m_new) : 1.f;   // 0 when m was -inf
+                l[nb] *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < DT16; ++dt) acc[nb][dt] *= alpha;
+                m[nb] = m_new;
+            }
+        }
+        uint4 phi[NB], plo[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const float mu = m[nb] == kNegInf ? 0.f : m[nb];
+            float ps = 0.f;
+            uint32_t hi[4], lo[4];
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                const float p0 = __builtin_amdgcn_exp2f(s[nb][e] - mu);
+                const float p1 = __builtin_amdgcn_exp2f(s[nb][e + 1] - mu);
+                ps += p0 + p1;
+                hi[e / 2] = pack2<DT>(p0, p1);
+                float h0, h1;
+                unpack2<DT>(hi[e / 2], h0, h1);
+                lo[e / 2] = pack2<DT>(p0 - h0, p1 - h1);
+            }
+            l[nb] += ps;
+            // P^T as the B operand, in two 16-bit parts
+            phi[nb] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+            plo[nb] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        }
+        // values: dimension tiles in pairs, the high parts of P then the low
+        // parts, so consecutive MFMAs never wait on each other's accumulator
+#pragma unroll
+        for (int dt = 0; dt < DT16; dt += 2) {
+            uint4 va[2];
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+                va[x] = *reinterpret_cast<const uint4 *>(&sV[buf][(16 * (dt + x) + i16) * VSTR + 16 * kb]);
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) acc[nb][dt + x] = mfma<DT>(va[x], phi[nb], acc[nb][dt + x]);
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) acc[nb][dt + x] = mfma<DT>(va[x], plo[nb], acc[nb][dt + x]);
+        }
+    };
+
+    // Pipeline: tile j is consumed from LDS while tile j+1 (already in
+    // registers or arriving) waits to be stored and tile j+2 is loaded --
+    // each load has two tiles' compute to arrive.  Unrolled by two so the
+    // register sets keep fixed names.
+    Regs ga{}, gb{};
     if (nt > 0) {
-        load_tile(0);
-        store_tile(0);
+        ga = load_tile(0);
+        store_tile(0, ga);
+        if (nt > 1) gb = load_tile(1);
     }
     __syncthreads();
-    for (int j = 0; j < nt; ++j) {
-        const int buf = j & 1;
-        if (j + 1 < nt) load_tile(j + 1);            // in flight while this tile is consumed
-
-        float s[2][4];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            f32x4_v c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const uint4 kp = *reinterpret_cast<const uint4 *>(&sK[buf][(16 * h + i16) * KSTR + (4 * ks + kb) * 16]);
-                c = mfma<DT>(kp, qb[ks], c);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int tk = 16 * h + 4 * kb + r;
-                const bool ok = sOk[buf][tk] && (j * NTOK + tk < lim);
-                s[h][r] = ok ? c[r] * a.scale_log2 : kNegInf;
-            }
-        }
-        float mt = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                         fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-        mt = fmaxf(mt, __shfl_xor(mt, 16));
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const float mn = fmaxf(m, mt);
-        const float mu = mn == kNegInf ? 0.f : mn;
-        const float alpha = __builtin_amdgcn_exp2f(m - mu);
-        float p[8];
-        float ps = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            p[e] = __builtin_amdgcn_exp2f(s[e >> 2][e & 3] - mu);
-            ps += p[e];
-        }
-        l = l * alpha + ps;
-        m = mn;
-        // P^T as the B operand, in two 16-bit parts
-        uint32_t hi[8], lo[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            hi[e] = to16<DT>(p[e]);
-            lo[e] = to16<DT>(p[e] - from16<DT>(hi[e]));
-        }
-        const uint4 phi = make_uint4(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16),
-                                     hi[6] | (hi[7] << 16));
-        const uint4 plo = make_uint4(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16),
-                                     lo[6] | (lo[7] << 16));
-#pragma unroll
-        for (int dt = 0; dt < DT16; ++dt) {
-            const unsigned char *vrow = &sV[buf][(16 * dt + i16) * VSTR];
-            const uint2 v0 = *reinterpret_cast<const uint2 *>(vrow + 8 * kb);
-            const uint2 v1 = *reinterpret_cast<const uint2 *>(vrow + 32 + 8 * kb);
-            const uint4 va = make_uint4(v0.x, v0.y, v1.x, v1.y);
-            acc[dt] *= alpha;
-            acc[dt] = mfma<DT>(va, phi, acc[dt]);
-            acc[dt] = mfma<DT>(va, plo, acc[dt]);
-        }
-
-        if (j + 1 < nt) store_tile(buf ^ 1);
+    for (int j = 0; j < nt; j += 2) {
+        if (j + 2 < nt) ga = load_tile(j + 2);
+        compute(j, 0);
+        if (j + 1 < nt) store_tile(1, gb);
+        __syncthreads();
+        if (j + 1 >= nt) break;
+        if (j + 3 < nt) gb = load_tile(j + 3);
+        compute(j + 1, 1);
+        if (j + 2 < nt) store_tile(0, ga);
         __syncthreads();
     }
 
     // The four lanes of a row share m; their sums cover different tokens.
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    if (!row_ok) return;
-    const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-    for (int dt = 0; dt < DT16; ++dt) {
-        const f32x4_v o = acc[dt] * inv;
-        *reinterpret_cast<float4 *>(a.out + qrow * D + 16 * dt + 4 * kb) = make_float4(o[0], o[1], o[2], o[3]);
+    for (int nb = 0; nb < NB; ++nb) {
+        float L = l[nb];
+        L += __shfl_xor(L, 16);
+        L += __shfl_xor(L, 32);
+        if (!row_ok[nb]) continue;
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+        for (int dt = 0; dt < DT16; ++dt) {
+            const f32x4_v o = acc[nb][dt] * inv;
+            *reinterpret_cast<float4 *>(a.out + qrow[nb] * D + 16 * dt + 4 * kb) = make_float4(o[0], o[1], o[2], o[3]);
+        }
+        if (kb == 0 && a.lse) a.lse[qrow[nb]] = L > 0.f ? (m[nb] + log2f(L)) * kLn2 : kNegInf;
     }
-    if (kb == 0 && a.lse) a.lse[qrow] = l > 0.f ? (m + log2f(l)) * kLn2 : kNegInf;
 }
 
 template <int DT, int D>
