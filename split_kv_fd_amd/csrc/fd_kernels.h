@@ -118,7 +118,11 @@ hipError_t launch_combine(const CombineArgs &a, hipStream_t stream);
 // Many queries per sequence (prefill): one workgroup per tile of
 // kPrefillRows query rows of one (batch, kv head), over the whole visible
 // KV range in tiles of kPrefillTokens tokens staged in LDS.
-constexpr int kPrefillRows = 128;
+#ifndef FD_PREFILL_NB
+#define FD_PREFILL_NB 2
+#endif
+constexpr int kPrefillNB = FD_PREFILL_NB;          // 16-row blocks per wave
+constexpr int kPrefillRows = 64 * kPrefillNB;
 constexpr int kPrefillTokens = 32;
 
 struct PrefillArgs {

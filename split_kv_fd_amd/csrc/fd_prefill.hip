@@ -92,7 +92,7 @@ __device__ __forceinline__ void unpack2(uint32_t w, float &x, float &y) {
 constexpr float kSlack = 8.f;
 
 template <int DT, int D, bool PAGED>
-__global__ __launch_bounds__(256, 2) void prefill(PrefillArgs a) {
+__global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillArgs a) {
     constexpr int ROWB = D * 2;              // bytes per K / V row
     constexpr int KS = D / 32;               // 32-wide k chunks of the logit product
     constexpr int DT16 = D / 16;             // 16-wide dimension tiles of the value product
@@ -100,7 +100,7 @@ __global__ __launch_bounds__(256, 2) void prefill(PrefillArgs a) {
     constexpr int NTOK = kPrefillTokens;     // tokens per KV tile
     constexpr int KSTR = ROWB + 16;          // LDS row stride of K (bytes)
     constexpr int VSTR = NTOK * 2 + 16;      // LDS row stride of V^T (bytes)
-    constexpr int NB = 2;                    // 16-row blocks per wave
+    constexpr int NB = kPrefillNB;           // 16-row blocks per wave
     static_assert(NTOK == 32 && kPrefillRows == 4 * 16 * NB, "the tile maps assume 32 tokens x 4 waves x NB*16 rows");
     static_assert(PIECES * 16 <= 256, "one (token pair, piece) per thread");
 
