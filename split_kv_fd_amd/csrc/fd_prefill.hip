@@ -104,9 +104,10 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
     static_assert(NTOK == 32 && kPrefillRows == 4 * 16 * NB, "the tile maps assume 32 tokens x 4 waves x NB*16 rows");
     static_assert(PIECES * 16 <= 256, "one (token pair, piece) per thread");
 
-    __shared__ __align__(16) unsigned char sK[2][NTOK * KSTR];
-    __shared__ __align__(16) unsigned char sV[2][D * VSTR];
-    __shared__ uint32_t sOkBits[2];          // bit t: token t of the tile is real
+    constexpr int NBUF = 3;                  // tiles j and j+1 in use, j+2 being stored
+    __shared__ __align__(16) unsigned char sK[NBUF][NTOK * KSTR];
+    __shared__ __align__(16) unsigned char sV[NBUF][D * VSTR];
+    __shared__ uint32_t sOkBits[NBUF];       // bit t: token t of the tile is real
 
     const int t = threadIdx.x;
     const int lane = t & 63;
@@ -240,11 +241,9 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
         l[nb] = 0.f;
     }
 
-    // The tile consumed from LDS buffer `buf`.
-    auto compute = [&](int j, int buf) {
-        // logits of both row blocks; each K fragment is read once, and the
-        // four accumulation chains are interleaved
-        f32x4_v c[NB][2];
+    // Logits of the tile in LDS buffer `buf` for both row blocks; each K
+    // fragment is read once, and the four accumulation chains interleave.
+    auto qk = [&](int buf, f32x4_v (&c)[NB][2]) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) c[nb][0] = c[nb][1] = f32x4_v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -255,24 +254,50 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) c[nb][h] = mfma<DT>(kp, qb[nb][ks], c[nb][h]);
             }
+    };
+
+    // Softmax of tile j's logits and its value product (V from buffer `buf`).
+    auto softmax_pv = [&](int j, int buf, const f32x4_v (&c)[NB][2]) {
         // Masks: tiles every row of the wave sees in full need none; else
         // token tk counts for a row when it is real and below the row's limit.
+        // On full tiles the raw logits are kept and the scale is applied
+        // inside the exponent (p = 2^(x * mult - m)); masked tiles hold scaled
+        // logits with -inf for masked tokens (mult = 1).
         const bool full = !PAGED && (j + 1) * NTOK <= wave_lim;
-        const uint32_t okbits = sOkBits[buf];
-        float s[NB][8];
+        const float mult = full ? a.scale_log2 : 1.f;
+        float x[NB][8];
+        if (full) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[nb][e] = c[nb][e >> 2][e & 3];
+        } else {
+            const uint32_t okbits = sOkBits[buf];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const int rel = lim[nb] - j * NTOK;    // this row sees tokens [0, rel) of the tile
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int tk = 16 * (e >> 2) + 4 * kb + (e & 3);
+                    const bool ok = (tk < rel) & (((okbits >> tk) & 1u) != 0u);
+                    x[nb][e] = ok ? c[nb][e >> 2][e & 3] * a.scale_log2 : kNegInf;
+                }
+            }
+        }
+        // this lane's largest scaled logit of each row
+        float lmt[NB];
         bool need = false;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            const int rel = lim[nb] - j * NTOK;        // this row sees tokens [0, rel) of the tile
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int tk = 16 * (e >> 2) + 4 * kb + (e & 3);
-                const bool ok = full | ((tk < rel) & (((okbits >> tk) & 1u) != 0u));
-                s[nb][e] = ok ? c[nb][e >> 2][e & 3] * a.scale_log2 : kNegInf;
-            }
-            const float lmt = fmaxf(fmaxf(fmaxf(s[nb][0], s[nb][1]), fmaxf(s[nb][2], s[nb][3])),
-                                    fmaxf(fmaxf(s[nb][4], s[nb][5]), fmaxf(s[nb][6], s[nb][7])));
-            need = need | (lmt > m[nb] + kSlack);
+            float ext;
+            if (mult >= 0.f)
+                ext = fmaxf(fmaxf(fmaxf(x[nb][0], x[nb][1]), fmaxf(x[nb][2], x[nb][3])),
+                            fmaxf(fmaxf(x[nb][4], x[nb][5]), fmaxf(x[nb][6], x[nb][7])));
+            else
+                ext = fminf(fminf(fminf(x[nb][0], x[nb][1]), fminf(x[nb][2], x[nb][3])),
+                            fminf(fminf(x[nb][4], x[nb][5]), fminf(x[nb][6], x[nb][7])));
+            lmt[nb] = ext * mult;
+            need = need | (lmt[nb] > m[nb] + kSlack);
         }
         // The running max of a row moves only when one of its logits exceeds
         // it by more than kSlack; then (rarely, after the first tiles) the
@@ -280,8 +305,7 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
         if (__any(need)) {
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                float mt = fmaxf(fmaxf(fmaxf(s[nb][0], s[nb][1]), fmaxf(s[nb][2], s[nb][3])),
-                                 fmaxf(fmaxf(s[nb][4], s[nb][5]), fmaxf(s[nb][6], s[nb][7])));
+                float mt = lmt[nb];
                 mt = fmaxf(mt, __shfl_xor(mt, 16));
                 mt = fmaxf(mt, __shfl_xor(mt, 32));
                 const bool grow = mt > m[nb] + kSlack;
@@ -296,13 +320,13 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
         uint4 phi[NB], plo[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            const float mu = m[nb] == kNegInf ? 0.f : m[nb];
+            const float nmu = m[nb] == kNegInf ? 0.f : -m[nb];
             float ps = 0.f;
             uint32_t hi[4], lo[4];
 #pragma unroll
             for (int e = 0; e < 8; e += 2) {
-                const float p0 = __builtin_amdgcn_exp2f(s[nb][e] - mu);
-                const float p1 = __builtin_amdgcn_exp2f(s[nb][e + 1] - mu);
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(x[nb][e], mult, nmu));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(x[nb][e + 1], mult, nmu));
                 ps += p0 + p1;
                 hi[e / 2] = pack2<DT>(p0, p1);
                 float h0, h1;
@@ -333,26 +357,30 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
         }
     };
 
-    // Pipeline: tile j is consumed from LDS while tile j+1 (already in
-    // registers or arriving) waits to be stored and tile j+2 is loaded --
-    // each load has two tiles' compute to arrive.  Unrolled by two so the
-    // register sets keep fixed names.
-    Regs ga{}, gb{};
-    if (nt > 0) {
-        ga = load_tile(0);
-        store_tile(0, ga);
-        if (nt > 1) gb = load_tile(1);
-    }
+    // Pipeline over three LDS buffers: at step j, tile j's values and tile
+    // j+1's keys are read while tile j+2 (loaded during step j-1) is stored
+    // and tile j+3 is loaded.  The logits of tile j+1 are formed before the
+    // softmax of tile j, so their matrix-core work overlaps the vector work
+    // of the softmax within the wave.
+    Regs g{};
+    f32x4_v c_cur[NB][2], c_next[NB][2];
+    if (nt > 0) store_tile(0, load_tile(0));
+    if (nt > 1) store_tile(1, load_tile(1));
+    if (nt > 2) g = load_tile(2);
     __syncthreads();
-    for (int j = 0; j < nt; j += 2) {
-        if (j + 2 < nt) ga = load_tile(j + 2);
-        compute(j, 0);
-        if (j + 1 < nt) store_tile(1, gb);
-        __syncthreads();
-        if (j + 1 >= nt) break;
-        if (j + 3 < nt) gb = load_tile(j + 3);
-        compute(j + 1, 1);
-        if (j + 2 < nt) store_tile(0, ga);
+    if (nt > 0) qk(0, c_cur);
+    for (int j = 0; j < nt; ++j) {
+        if (j + 2 < nt) {
+            store_tile((j + 2) % NBUF, g);          // its buffer held tile j-1, finished
+            if (j + 3 < nt) g = load_tile(j + 3);
+        }
+        if (j + 1 < nt) qk((j + 1) % NBUF, c_next);
+        softmax_pv(j, j % NBUF, c_cur);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            c_cur[nb][0] = c_next[nb][0];
+            c_cur[nb][1] = c_next[nb][1];
+        }
         __syncthreads();
     }
 

@@ -88,3 +88,22 @@ def test_prefill_full_size_sampled():
             lerr = float(np.max(np.abs(lse[b, i].cpu().double().numpy() - ref_l[0])))
             parity.announce(f"prefill b={b} query={i}: err {err:.2e} lse {lerr:.2e}")
             assert err <= parity.OUT_TOL["bf16"] and lerr <= parity.LSE_TOL["bf16"]
+
+
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 0.35])
+def test_prefill_scale_sign(scale):
+    # the scale enters the exponent on unmasked tiles: negative and zero
+    # scales must give the oracle's softmax too
+    case = contiguous("gqa128k_bf16", [300, 129], Hq=8, Hkv=2, T=300)
+    q = inputs.make_q_multi(case.spec, 40).to(DEV)
+    host = case.to("cpu")
+    for causal in (False, True):
+        ref_out, ref_lse = oracle_mod.default().decode_multi(q.cpu(), host.k, host.v, scale, causal=causal,
+                                                             seq_lens=host.seq_lens)
+        dec = Decoder(q, case.k, case.v, scale=scale, seq_lens=case.seq_lens, causal=causal)
+        assert dec.plan["path"] == "prefill"
+        parity.announce(f"prefill scale={scale} causal={causal}")
+        out, lse = dec()
+        torch.cuda.synchronize()
+        parity.compare(case, out.cpu().double().numpy(), lse.cpu().double().numpy(), ref_out, ref_lse,
+                       parity.max_abs_v(host), f"prefill scale={scale} causal={causal}")
