@@ -11,8 +11,9 @@
 // kPrefillTokens tokens with an online softmax (the same running max / sum
 // / unnormalised accumulator as the split pass), then divides once.
 //
-// Per KV tile, staged in LDS by the whole workgroup (two buffers, the next
-// tile's loads in flight while the current one is consumed):
+// Per KV tile, staged in LDS by the whole workgroup (three buffers: tile j
+// being consumed, tile j+1 being read for its logits, tile j+2 being
+// stored; global loads run one more tile ahead):
 //  * K rows as they are in memory (row stride padded by 16 bytes so the
 //    16 lanes reading 16 rows hit distinct banks);
 //  * V transposed, V^T[d][token], so that the value product can take 8
@@ -24,14 +25,15 @@
 //  * logits S^T = K Q^T with v_mfma_f32_16x16x32_{bf16,f16}: tokens on M,
 //    query rows on N (the q pieces are the B operand, loaded once), so lane
 //    (i16, kb) holds row i16's logits of tokens 4*kb .. 4*kb+3 of each half;
+//    the logits of tile j+1 are formed while tile j's softmax runs;
 //  * online softmax in base 2 per row: max over the lane's 8 logits, then
-//    across the four lanes of the row (xor 16, xor 32);
+//    (only when the running max must move) across the four lanes of the row;
 //  * values O^T += V^T P^T with the same MFMA: V^T rows from LDS as the A
 //    operand, P^T from the lane's own probabilities as the B operand (k slot
 //    8*kb + e is token 4*kb + e of the first half for e < 4, of the second
-//    half for e >= 4, on both operands).  P goes in as a high and a low
-//    16-bit part (P = hi + lo, two MFMAs), so its rounding stays near fp32:
-//    a single bf16 P would spend the whole output tolerance.
+//    half for e >= 4, on both operands).  For bf16, P goes in as a high and
+//    a low part (P = hi + lo, two MFMAs), so its rounding stays near fp32; an
+//    f16 P (11 significant bits, rounded to nearest) goes in once.
 //    The accumulator leaves lane (i16, kb) holding row i16's dimensions
 //    16*dt + 4*kb .. +3, written out as one 16-byte store per tile of 16.
 // Causal rows (query i sees the first T_b - (nq - 1 - i) tokens) are masked
@@ -40,6 +42,7 @@
 #include <type_traits>
 
 #include "fd_kernels.h"
+
 
 namespace fdk {
 namespace {
@@ -62,33 +65,34 @@ __device__ __forceinline__ f32x4_v mfma(const uint4 &a, const uint4 &b, f32x4_v 
 }
 
 typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_v __attribute__((ext_vector_type(2)));
 typedef float f32x2_v __attribute__((ext_vector_type(2)));
 
-// Two finite fp32 values as packed 16-bit storage values (one instruction),
-// and back.  The rounding mode does not matter here: the low part of P is
-// taken from the exact difference p - hi.
+// Two finite fp32 values as packed 16-bit storage values, rounded to
+// nearest (one instruction each way on gfx950).
 template <int DT>
 __device__ __forceinline__ uint32_t pack2(float x, float y) {
     if constexpr (DT == FD_BF16)
         return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_v{x, y}, bf16x2_v));
     else
-        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x, y));
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_v{x, y}, f16x2_v));
 }
 
-template <int DT>
-__device__ __forceinline__ void unpack2(uint32_t w, float &x, float &y) {
-    if constexpr (DT == FD_BF16) {
-        x = __uint_as_float(w << 16);
-        y = __uint_as_float(w & 0xffff0000u);
-    } else {
-        x = (float)__builtin_bit_cast(_Float16, (unsigned short)(w & 0xffffu));
-        y = (float)__builtin_bit_cast(_Float16, (unsigned short)(w >> 16));
-    }
+// The two bf16 halves of a packed word as fp32 (exact).
+__device__ __forceinline__ void unpack2_bf16(uint32_t w, float &x, float &y) {
+    x = __uint_as_float(w << 16);
+    y = __uint_as_float(w & 0xffff0000u);
+}
+
+// max(a, b, c) with NaN propagation: one v_maximum3_f32, no canonicalising
+// moves in front of it.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+    return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
 }
 
 // The running max of a row is only raised when a tile's max exceeds it by
-// more than this (log2 units): probabilities then stay below 2^kSlack,
-// exactly representable, and most tiles skip rescaling the accumulator.
+// more than this (log2 units): probabilities then stay below 2^kSlack and
+// most tiles skip rescaling the accumulator.
 constexpr float kSlack = 8.f;
 
 template <int DT, int D, bool PAGED>
@@ -101,13 +105,20 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
     constexpr int KSTR = ROWB + 16;          // LDS row stride of K (bytes)
     constexpr int VSTR = NTOK * 2 + 16;      // LDS row stride of V^T (bytes)
     constexpr int NB = kPrefillNB;           // 16-row blocks per wave
+    // bf16 keeps 8 significant bits: a single bf16 P would spend the whole
+    // output tolerance, so P goes in as a high and a low part.  f16 keeps 11:
+    // one product is enough (weights off by at most 2^-11 relative).
+    constexpr bool SPLIT_P = DT == FD_BF16;
+    // f16 probabilities are formed as 2^(x - m + kPBias), in [0, 2^14]: far
+    // above the f16 subnormal range for every weight that matters and below
+    // its largest finite value.  The bias cancels in the division by the sum.
+    constexpr float kPBias = SPLIT_P ? 0.f : 6.f;
     static_assert(NTOK == 32 && kPrefillRows == 4 * 16 * NB, "the tile maps assume 32 tokens x 4 waves x NB*16 rows");
-    static_assert(PIECES * 16 <= 256, "one (token pair, piece) per thread");
+    static_assert(PIECES * 16 <= 256 && 256 % (PIECES * 16) == 0, "loader threads cover the pieces evenly");
 
     constexpr int NBUF = 3;                  // tiles j and j+1 in use, j+2 being stored
     __shared__ __align__(16) unsigned char sK[NBUF][NTOK * KSTR];
     __shared__ __align__(16) unsigned char sV[NBUF][D * VSTR];
-    __shared__ uint32_t sOkBits[NBUF];       // bit t: token t of the tile is real
 
     const int t = threadIdx.x;
     const int lane = t & 63;
@@ -122,6 +133,13 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
 
     int Tb = a.seq_lens ? a.seq_lens[b] : a.T;
     Tb = Tb < 0 ? 0 : (Tb > a.T ? a.T : Tb);
+
+    // A negative scale is folded into q: flipping the sign of every element
+    // is exact, and the exponent's multiplier is then never negative, so a
+    // row's largest scaled logit is its largest logit times the multiplier.
+    const bool neg = a.scale_log2 < 0.f;
+    const float sl2 = neg ? -a.scale_log2 : a.scale_log2;
+    const uint32_t qflip = neg ? 0x80008000u : 0u;
 
     // This lane's query rows (one per block), the tokens each sees, and
     // their q pieces.
@@ -139,10 +157,13 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
         lim[nb] = lm < 0 ? 0 : lm;
         qrow[nb] = ((size_t)b * a.nq + qi) * a.Hq + (size_t)kvh * a.G + (row_ok[nb] ? rr - qi * a.G : 0);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            qb[nb][ks] = row_ok[nb] ? *reinterpret_cast<const uint4 *>(static_cast<const char *>(a.q) +
-                                                                       qrow[nb] * ROWB + (4 * ks + kb) * 16)
-                                    : make_uint4(0, 0, 0, 0);
+        for (int ks = 0; ks < KS; ++ks) {
+            uint4 w = row_ok[nb] ? *reinterpret_cast<const uint4 *>(static_cast<const char *>(a.q) +
+                                                                   qrow[nb] * ROWB + (4 * ks + kb) * 16)
+                                 : make_uint4(0, 0, 0, 0);
+            w.x ^= qflip; w.y ^= qflip; w.z ^= qflip; w.w ^= qflip;
+            qb[nb][ks] = w;
+        }
     }
 
     // Tokens every row of this wave sees (0 if the wave has rows past R):
@@ -162,17 +183,18 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
     seen = seen < 0 ? 0 : seen;
     const int nt = (seen + NTOK - 1) / NTOK;
 
-    // Loader: thread t moves tokens 2u, 2u+1 of the tile, piece p of each.
+    // Loader: thread t moves tokens 2u, 2u+1 of the tile, piece p of each
+    // (with D = 64 two threads share a piece and store the same bytes).
     const int u = t & 15;
-    const int piece = t >> 4;
-    const bool loader = piece < PIECES;
+    const int piece = (t >> 4) % PIECES;
     // One tile's worth of this thread's loads.
     struct Regs {
         uint4 k0, k1, v0, v1;
         int ok0, ok1;
     };
-    // row of token tt of the sequence (a real token: Tb >= 1 here); ok =
-    // false for a padding token or a page outside the pool
+    // Row of token tt of the sequence, clamped to the last real token (Tb >=
+    // 1 wherever it is called), so every load is in bounds; ok = false for a
+    // token past the end or on a page outside the pool.
     auto token_row = [&](int tt, int &ok) -> size_t {
         const int tc = tt < Tb ? tt : Tb - 1;
         ok = tt < Tb;
@@ -186,36 +208,34 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
     };
     auto load_tile = [&](int j) -> Regs {
         Regs g;
-        g.k0 = g.k1 = g.v0 = g.v1 = make_uint4(0, 0, 0, 0);
         const size_t ra = token_row(j * NTOK + 2 * u, g.ok0);
         const size_t rb = token_row(j * NTOK + 2 * u + 1, g.ok1);
-        if (loader) {
-            const char *kp = static_cast<const char *>(a.k) + piece * 16;
-            const char *vp = static_cast<const char *>(a.v) + piece * 16;
-            g.k0 = *reinterpret_cast<const uint4 *>(kp + ra * ROWB);
-            g.k1 = *reinterpret_cast<const uint4 *>(kp + rb * ROWB);
-            g.v0 = *reinterpret_cast<const uint4 *>(vp + ra * ROWB);
-            g.v1 = *reinterpret_cast<const uint4 *>(vp + rb * ROWB);
-        }
+        const char *kp = static_cast<const char *>(a.k) + piece * 16;
+        const char *vp = static_cast<const char *>(a.v) + piece * 16;
+        g.k0 = *reinterpret_cast<const uint4 *>(kp + ra * ROWB);
+        g.k1 = *reinterpret_cast<const uint4 *>(kp + rb * ROWB);
+        g.v0 = *reinterpret_cast<const uint4 *>(vp + ra * ROWB);
+        g.v1 = *reinterpret_cast<const uint4 *>(vp + rb * ROWB);
         return g;
+    };
+    // Paged tiles: bit t is set when token t of the tile is real and its
+    // page lies in the pool.  Lanes 0..15 of every wave hold tokens 2u, 2u+1
+    // of u = lane, so each wave forms the word itself, in scalar registers.
+    auto tile_bits = [](const Regs g) -> uint32_t {
+        auto spread = [](uint32_t x) {
+            x = (x | (x << 8)) & 0x00FF00FFu;
+            x = (x | (x << 4)) & 0x0F0F0F0Fu;
+            x = (x | (x << 2)) & 0x33333333u;
+            return (x | (x << 1)) & 0x55555555u;
+        };
+        const uint32_t b0 = (uint32_t)__ballot(g.ok0) & 0xffffu;
+        const uint32_t b1 = (uint32_t)__ballot(g.ok1) & 0xffffu;
+        return spread(b0) | (spread(b1) << 1);
     };
     // V^T column of token tt of a tile (see the header): tokens 2u and 2u+1
     // stay adjacent, so one 32-bit store writes both.
     auto vpos = [](int tt) { return 8 * ((tt & 15) >> 2) + 4 * (tt >> 4) + (tt & 3); };
     auto store_tile = [&](int buf, const Regs g) {
-        if (wave == 0) {
-            // lanes 0..15 hold tokens 2u, 2u+1 of u = lane: interleave their flags
-            auto spread = [](uint32_t x) {
-                x = (x | (x << 8)) & 0x00FF00FFu;
-                x = (x | (x << 4)) & 0x0F0F0F0Fu;
-                x = (x | (x << 2)) & 0x33333333u;
-                return (x | (x << 1)) & 0x55555555u;
-            };
-            const uint32_t b0 = (uint32_t)__ballot(g.ok0) & 0xffffu;
-            const uint32_t b1 = (uint32_t)__ballot(g.ok1) & 0xffffu;
-            if (lane == 0) sOkBits[buf] = spread(b0) | (spread(b1) << 1);
-        }
-        if (!loader) return;
         *reinterpret_cast<uint4 *>(&sK[buf][(2 * u) * KSTR + piece * 16]) = g.k0;
         *reinterpret_cast<uint4 *>(&sK[buf][(2 * u + 1) * KSTR + piece * 16]) = g.k1;
         // V^T: dimension 8*piece + e, tokens 2u and 2u+1 packed in one word
@@ -231,18 +251,21 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
         }
     };
 
+    // Per row: the running max m (log2 units), m + kSlack, the exponent
+    // offset kPBias - m (kPBias while m = -inf), the sum and the accumulator.
     f32x4_v acc[NB][DT16];
-    float m[NB], l[NB];
+    float m[NB], mth[NB], nm[NB], l[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
         for (int dt = 0; dt < DT16; ++dt) acc[nb][dt] = f32x4_v{0.f, 0.f, 0.f, 0.f};
-        m[nb] = kNegInf;
+        m[nb] = mth[nb] = kNegInf;
+        nm[nb] = kPBias;
         l[nb] = 0.f;
     }
 
-    // Logits of the tile in LDS buffer `buf` for both row blocks; each K
-    // fragment is read once, and the four accumulation chains interleave.
+    // Logits of the tile in LDS buffer `buf` for all row blocks; each K
+    // fragment is read once.
     auto qk = [&](int buf, f32x4_v (&c)[NB][2]) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) c[nb][0] = c[nb][1] = f32x4_v{0.f, 0.f, 0.f, 0.f};
@@ -256,132 +279,150 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
             }
     };
 
-    // Softmax of tile j's logits and its value product (V from buffer `buf`).
-    auto softmax_pv = [&](int j, int buf, const f32x4_v (&c)[NB][2]) {
-        // Masks: tiles every row of the wave sees in full need none; else
-        // token tk counts for a row when it is real and below the row's limit.
-        // On full tiles the raw logits are kept and the scale is applied
-        // inside the exponent (p = 2^(x * mult - m)); masked tiles hold scaled
-        // logits with -inf for masked tokens (mult = 1).
+    Regs g{};
+    uint32_t ok_cur = 0, ok_next = 0;       // paged mask words of tiles j, j+1
+
+    // One tile: step j consumes the logits cc of tile j (formed one step
+    // earlier) and forms cn, those of tile j+1.
+    //  1. masks, row maxima and (rarely) the rescale -- the only branches;
+    //  2. one straight-line block: tile j+2 (loaded one step earlier) into
+    //     its LDS buffer, tile j+3 from memory, logits of tile j+1, and the
+    //     probabilities and value product of tile j.  Past the last tile the
+    //     loads read clamped rows and the logits go unused, so nothing there
+    //     needs a branch, and the matrix-core work of the logits can be
+    //     interleaved with the vector work of the probabilities.
+    auto step = [&](const int j, const f32x4_v (&cc)[NB][2], f32x4_v (&cn)[NB][2]) {
+        const int bj = j % NBUF;
+        // Masks: tiles every row of the wave sees in full need none; there
+        // the raw logits are kept and the scale goes into the exponent
+        // (p = 2^(x * mult + nm)).  Masked tiles hold scaled logits with -inf
+        // for masked tokens (mult = 1).
         const bool full = !PAGED && (j + 1) * NTOK <= wave_lim;
-        const float mult = full ? a.scale_log2 : 1.f;
+        const float mult = full ? sl2 : 1.f;
         float x[NB][8];
         if (full) {
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) x[nb][e] = c[nb][e >> 2][e & 3];
+                for (int e = 0; e < 8; ++e) x[nb][e] = cc[nb][e >> 2][e & 3];
         } else {
-            const uint32_t okbits = sOkBits[buf];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
                 const int rel = lim[nb] - j * NTOK;    // this row sees tokens [0, rel) of the tile
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int tk = 16 * (e >> 2) + 4 * kb + (e & 3);
-                    const bool ok = (tk < rel) & (((okbits >> tk) & 1u) != 0u);
-                    x[nb][e] = ok ? c[nb][e >> 2][e & 3] * a.scale_log2 : kNegInf;
+                    bool ok = tk < rel;
+                    if constexpr (PAGED) ok = ok & (((ok_cur >> tk) & 1u) != 0u);
+                    x[nb][e] = ok ? cc[nb][e >> 2][e & 3] * sl2 : kNegInf;
                 }
             }
-        }
-        // this lane's largest scaled logit of each row
-        float lmt[NB];
-        bool need = false;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            float ext;
-            if (mult >= 0.f)
-                ext = fmaxf(fmaxf(fmaxf(x[nb][0], x[nb][1]), fmaxf(x[nb][2], x[nb][3])),
-                            fmaxf(fmaxf(x[nb][4], x[nb][5]), fmaxf(x[nb][6], x[nb][7])));
-            else
-                ext = fminf(fminf(fminf(x[nb][0], x[nb][1]), fminf(x[nb][2], x[nb][3])),
-                            fminf(fminf(x[nb][4], x[nb][5]), fminf(x[nb][6], x[nb][7])));
-            lmt[nb] = ext * mult;
-            need = need | (lmt[nb] > m[nb] + kSlack);
         }
         // The running max of a row moves only when one of its logits exceeds
         // it by more than kSlack; then (rarely, after the first tiles) the
         // row max is formed across its four lanes and the state rescaled.
+        float lmt[NB];
+        bool need = false;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            lmt[nb] = __builtin_elementwise_maximum(max3(x[nb][0], x[nb][1], x[nb][2]),
+                                                    max3(max3(x[nb][3], x[nb][4], x[nb][5]), x[nb][6], x[nb][7])) *
+                      mult;
+            need = need | (lmt[nb] > mth[nb]);
+        }
         if (__any(need)) {
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
                 float mt = lmt[nb];
                 mt = fmaxf(mt, __shfl_xor(mt, 16));
                 mt = fmaxf(mt, __shfl_xor(mt, 32));
-                const bool grow = mt > m[nb] + kSlack;
+                const bool grow = mt > mth[nb];
                 const float m_new = grow ? mt : m[nb];
                 const float alpha = grow ? __builtin_amdgcn_exp2f(m[nb] - m_new) : 1.f;   // 0 when m was -inf
                 l[nb] *= alpha;
 #pragma unroll
                 for (int dt = 0; dt < DT16; ++dt) acc[nb][dt] *= alpha;
                 m[nb] = m_new;
+                mth[nb] = m_new + kSlack;
+                nm[nb] = m_new == kNegInf ? kPBias : kPBias - m_new;
             }
         }
+
+        // ---- straight-line block ----
+        if constexpr (PAGED) {
+            const uint32_t ok_new = tile_bits(g);
+            ok_cur = ok_next;
+            ok_next = ok_new;
+        }
+        qk((j + 1) % NBUF, cn);
         uint4 phi[NB], plo[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            const float nmu = m[nb] == kNegInf ? 0.f : -m[nb];
-            float ps = 0.f;
+            float p[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(x[nb][e], mult, nm[nb]));
+            l[nb] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
             uint32_t hi[4], lo[4];
 #pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-                const float p0 = __builtin_amdgcn_exp2f(fmaf(x[nb][e], mult, nmu));
-                const float p1 = __builtin_amdgcn_exp2f(fmaf(x[nb][e + 1], mult, nmu));
-                ps += p0 + p1;
-                hi[e / 2] = pack2<DT>(p0, p1);
-                float h0, h1;
-                unpack2<DT>(hi[e / 2], h0, h1);
-                lo[e / 2] = pack2<DT>(p0 - h0, p1 - h1);
+            for (int e = 0; e < 4; ++e) {
+                hi[e] = pack2<DT>(p[2 * e], p[2 * e + 1]);
+                if constexpr (SPLIT_P) {
+                    float h0, h1;
+                    unpack2_bf16(hi[e], h0, h1);
+                    lo[e] = pack2<DT>(p[2 * e] - h0, p[2 * e + 1] - h1);   // exact differences
+                }
             }
-            l[nb] += ps;
-            // P^T as the B operand, in two 16-bit parts
+            // P^T as the B operand (in two 16-bit parts for bf16)
             phi[nb] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-            plo[nb] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+            if constexpr (SPLIT_P) plo[nb] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
         }
-        // values: dimension tiles in pairs, the high parts of P then the low
-        // parts, so consecutive MFMAs never wait on each other's accumulator
+        // values: dimension tiles in pairs (the high parts of P, then the
+        // low parts), so consecutive MFMAs never wait on each other; the
+        // staging of tile j+2 and the loads of tile j+3 fill the gaps
 #pragma unroll
         for (int dt = 0; dt < DT16; dt += 2) {
             uint4 va[2];
 #pragma unroll
-            for (int x = 0; x < 2; ++x)
-                va[x] = *reinterpret_cast<const uint4 *>(&sV[buf][(16 * (dt + x) + i16) * VSTR + 16 * kb]);
+            for (int y = 0; y < 2; ++y)
+                va[y] = *reinterpret_cast<const uint4 *>(&sV[bj][(16 * (dt + y) + i16) * VSTR + 16 * kb]);
 #pragma unroll
-            for (int x = 0; x < 2; ++x)
+            for (int y = 0; y < 2; ++y)
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) acc[nb][dt + x] = mfma<DT>(va[x], phi[nb], acc[nb][dt + x]);
+                for (int nb = 0; nb < NB; ++nb) acc[nb][dt + y] = mfma<DT>(va[y], phi[nb], acc[nb][dt + y]);
+            if constexpr (SPLIT_P) {
 #pragma unroll
-            for (int x = 0; x < 2; ++x)
+                for (int y = 0; y < 2; ++y)
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) acc[nb][dt + x] = mfma<DT>(va[x], plo[nb], acc[nb][dt + x]);
+                    for (int nb = 0; nb < NB; ++nb) acc[nb][dt + y] = mfma<DT>(va[y], plo[nb], acc[nb][dt + y]);
+            }
         }
+        store_tile((j + 2) % NBUF, g);          // its buffer held tile j-1, finished
+        g = load_tile(j + 3);
+        __syncthreads();
     };
 
-    // Pipeline over three LDS buffers: at step j, tile j's values and tile
-    // j+1's keys are read while tile j+2 (loaded during step j-1) is stored
-    // and tile j+3 is loaded.  The logits of tile j+1 are formed before the
-    // softmax of tile j, so their matrix-core work overlaps the vector work
-    // of the softmax within the wave.
-    Regs g{};
-    f32x4_v c_cur[NB][2], c_next[NB][2];
-    if (nt > 0) store_tile(0, load_tile(0));
-    if (nt > 1) store_tile(1, load_tile(1));
-    if (nt > 2) g = load_tile(2);
-    __syncthreads();
-    if (nt > 0) qk(0, c_cur);
-    for (int j = 0; j < nt; ++j) {
-        if (j + 2 < nt) {
-            store_tile((j + 2) % NBUF, g);          // its buffer held tile j-1, finished
-            if (j + 3 < nt) g = load_tile(j + 3);
+    f32x4_v cA[NB][2], cB[NB][2];
+    if (nt > 0) {
+        if constexpr (PAGED) {
+            Regs g0 = load_tile(0);
+            ok_cur = tile_bits(g0);
+            store_tile(0, g0);
+            Regs g1 = load_tile(1);
+            ok_next = tile_bits(g1);
+            store_tile(1, g1);
+        } else {
+            store_tile(0, load_tile(0));
+            store_tile(1, load_tile(1));
         }
-        if (j + 1 < nt) qk((j + 1) % NBUF, c_next);
-        softmax_pv(j, j % NBUF, c_cur);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            c_cur[nb][0] = c_next[nb][0];
-            c_cur[nb][1] = c_next[nb][1];
-        }
+        g = load_tile(2);
         __syncthreads();
+        qk(0, cA);
+        int j = 0;
+        for (; j + 2 <= nt; j += 2) {
+            step(j, cA, cB);
+            step(j + 1, cB, cA);
+        }
+        if (j < nt) step(j, cA, cB);
     }
 
     // The four lanes of a row share m; their sums cover different tokens.
@@ -397,7 +438,7 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
             const f32x4_v o = acc[nb][dt] * inv;
             *reinterpret_cast<float4 *>(a.out + qrow[nb] * D + 16 * dt + 4 * kb) = make_float4(o[0], o[1], o[2], o[3]);
         }
-        if (kb == 0 && a.lse) a.lse[qrow[nb]] = L > 0.f ? (m[nb] + log2f(L)) * kLn2 : kNegInf;
+        if (kb == 0 && a.lse) a.lse[qrow[nb]] = L > 0.f ? (m[nb] + log2f(L) - kPBias) * kLn2 : kNegInf;
     }
 }
 

@@ -107,3 +107,50 @@ def test_prefill_scale_sign(scale):
         torch.cuda.synchronize()
         parity.compare(case, out.cpu().double().numpy(), lse.cpu().double().numpy(), ref_out, ref_lse,
                        parity.max_abs_v(host), f"prefill scale={scale} causal={causal}")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("scale", [0.5, 2.0])
+def test_prefill_sharp_softmax(dtype, scale):
+    # large scales spread the logits over tens of log2 units: most
+    # probabilities are tiny (an f16 P formed without headroom would fall
+    # into the subnormal range) and the running max moves often
+    case = contiguous("gqa128k_bf16", [640, 333], Hq=8, Hkv=2, T=640, dtype=dtype)
+    q = inputs.make_q_multi(case.spec, 64).to(DEV)
+    host = case.to("cpu")
+    for causal in (False, True):
+        ref_out, ref_lse = oracle_mod.default().decode_multi(q.cpu(), host.k, host.v, scale, causal=causal,
+                                                             seq_lens=host.seq_lens)
+        dec = Decoder(q, case.k, case.v, scale=scale, seq_lens=case.seq_lens, causal=causal)
+        assert dec.plan["path"] == "prefill"
+        parity.announce(f"prefill sharp dtype={dtype} scale={scale} causal={causal}")
+        out, lse = dec()
+        torch.cuda.synchronize()
+        parity.compare(case, out.cpu().double().numpy(), lse.cpu().double().numpy(), ref_out, ref_lse,
+                       parity.max_abs_v(host), f"prefill sharp dtype={dtype} scale={scale} causal={causal}")
+
+
+def test_prefill_full_size_sampled_f16():
+    # MHA 32 heads, f16 (one P product per tile): a 4096-token causal prompt,
+    # sampled query rows against the oracle one query at a time
+    s = inputs.spec("mha32k_f16", B=1, T=4096)
+    case = inputs.make_case(s, device=DEV)
+    nq = 4096
+    q = inputs.make_q_multi(s, nq, device=DEV)
+    dec = Decoder(q, case.k, case.v, scale=s.scale, causal=True)
+    assert dec.plan["path"] == "prefill"
+    parity.announce(f"prefill f16 full size nq={nq} plan={dec.plan}")
+    out, lse = dec()
+    torch.cuda.synchronize()
+    orc = oracle_mod.default()
+    k_h, v_h = case.k.cpu(), case.v.cpu()
+    vmax = float(v_h.abs().max())
+    g = torch.Generator().manual_seed(11)
+    for i in [0, 1, nq // 2, nq - 1] + torch.randint(0, nq, (3,), generator=g).tolist():
+        L = s.T - (nq - 1 - i)
+        ref, ref_l = orc.decode(q[:, i].cpu(), k_h, v_h, s.scale, seq_lens=np.array([L], np.int32))
+        got = out[0, i].cpu().double().numpy()
+        err = float(np.max(np.abs(got - ref[0]))) / vmax
+        lerr = float(np.max(np.abs(lse[0, i].cpu().double().numpy() - ref_l[0])))
+        parity.announce(f"prefill f16 query={i}: err {err:.2e} lse {lerr:.2e}")
+        assert err <= parity.OUT_TOL["f16"] and lerr <= parity.LSE_TOL["f16"]
