@@ -14,12 +14,14 @@
 // Per KV tile, staged in LDS by the whole workgroup (three buffers: tile j
 // being consumed, tile j+1 being read for its logits, tile j+2 being
 // stored; global loads run one more tile ahead):
-//  * K rows as they are in memory (row stride padded by 16 bytes so the
-//    16 lanes reading 16 rows hit distinct banks);
-//  * V transposed, V^T[d][token], so that the value product can take 8
-//    tokens of one dimension per lane in one 16-byte read: within a row the
-//    tokens are stored in the order the lanes take them (position
-//    8*((t%16)/4) + 4*(t/16) + t%4 for token t).
+//  * K rows as they are in memory and V transposed, V^T[d][token], so that
+//    the value product can take 8 tokens of one dimension per lane in one
+//    16-byte read: within a row the tokens are stored in the order the
+//    lanes take them (position 8*((t%16)/4) + 4*(t/16) + t%4 for token t).
+//    Both row strides are padded by 32 bytes: gfx950 serves a 16-byte LDS
+//    read 32 lanes at a time over 128 banks, and rows 8 dwords apart (mod
+//    128) keep the 16 rows x 2 chunks of such a read on distinct banks,
+//    where a 16-byte pad (4 dwords) measured 2-way conflicts.
 // Per wave (two blocks of 16 rows, each K / V fragment read from LDS once
 // for both) and tile (two 16-token halves):
 //  * logits S^T = K Q^T with v_mfma_f32_16x16x32_{bf16,f16}: tokens on M,
@@ -42,6 +44,7 @@
 #include <type_traits>
 
 #include "fd_kernels.h"
+
 
 
 namespace fdk {
@@ -102,8 +105,11 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
     constexpr int DT16 = D / 16;             // 16-wide dimension tiles of the value product
     constexpr int PIECES = ROWB / 16;        // 16-byte pieces per row
     constexpr int NTOK = kPrefillTokens;     // tokens per KV tile
-    constexpr int KSTR = ROWB + 16;          // LDS row stride of K (bytes)
-    constexpr int VSTR = NTOK * 2 + 16;      // LDS row stride of V^T (bytes)
+    // LDS row strides: 16-byte reads of 16 rows x 2 lanes hit distinct banks
+    // when consecutive rows start 8 dwords apart modulo 128 dwords (rows of
+    // ROWB + 16 bytes, 4 apart, conflict in pairs on gfx950).
+    constexpr int KSTR = ROWB + 32;          // K (bytes)
+    constexpr int VSTR = NTOK * 2 + 32;      // V^T (bytes)
     constexpr int NB = kPrefillNB;           // 16-row blocks per wave
     // bf16 keeps 8 significant bits: a single bf16 P would spend the whole
     // output tolerance, so P goes in as a high and a low part.  f16 keeps 11:
@@ -143,23 +149,28 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
 
     // This lane's query rows (one per block), the tokens each sees, and
     // their q pieces.
-    bool row_ok[NB];
+    // Output row of a lane's query row (recomputed after the loop rather than
+    // kept live through it).
+    auto row_of = [&](int nb, bool &ok) -> size_t {
+        const int rr = r0 + 16 * (NB * wave + nb) + i16;
+        ok = rr < a.R;
+        const int qi = ok ? rr / a.G : 0;
+        return ((size_t)b * a.nq + qi) * a.Hq + (size_t)kvh * a.G + (ok ? rr - qi * a.G : 0);
+    };
     int lim[NB];
-    size_t qrow[NB];
     uint4 qb[NB][KS];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-        const int rr = r0 + 16 * (NB * wave + nb) + i16;
-        row_ok[nb] = rr < a.R;
-        const int qi = row_ok[nb] ? rr / a.G : 0;
+        bool ok;
+        const size_t qrow = row_of(nb, ok);
+        const int qi = ok ? (r0 + 16 * (NB * wave + nb) + i16) / a.G : 0;
         int lm = 0;
-        if (row_ok[nb]) lm = a.causal ? Tb - (a.nq - 1 - qi) : Tb;
+        if (ok) lm = a.causal ? Tb - (a.nq - 1 - qi) : Tb;
         lim[nb] = lm < 0 ? 0 : lm;
-        qrow[nb] = ((size_t)b * a.nq + qi) * a.Hq + (size_t)kvh * a.G + (row_ok[nb] ? rr - qi * a.G : 0);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            uint4 w = row_ok[nb] ? *reinterpret_cast<const uint4 *>(static_cast<const char *>(a.q) +
-                                                                   qrow[nb] * ROWB + (4 * ks + kb) * 16)
+            uint4 w = ok ? *reinterpret_cast<const uint4 *>(static_cast<const char *>(a.q) +
+                                                           qrow * ROWB + (4 * ks + kb) * 16)
                                  : make_uint4(0, 0, 0, 0);
             w.x ^= qflip; w.y ^= qflip; w.z ^= qflip; w.w ^= qflip;
             qb[nb][ks] = w;
@@ -184,9 +195,13 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
     const int nt = (seen + NTOK - 1) / NTOK;
 
     // Loader: thread t moves tokens 2u, 2u+1 of the tile, piece p of each
-    // (with D = 64 two threads share a piece and store the same bytes).
+    // (with D = 64 two threads share a piece and store the same bytes).  V
+    // takes u = t % 16, so the 16 lanes of a store write 16 columns of one
+    // V^T row; K takes the piece from t % PIECES, so they write one K row.
     const int u = t & 15;
     const int piece = (t >> 4) % PIECES;
+    const int ku = (t / PIECES) % 16;
+    const int kpiece = t % PIECES;
     // One tile's worth of this thread's loads.
     struct Regs {
         uint4 k0, k1, v0, v1;
@@ -206,14 +221,45 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
             return ((size_t)b * a.Hkv + kvh) * a.T + tc;
         }
     };
+    // Contiguous caches: the (batch, kv head) slices of K and V as buffer
+    // resources sized to the real tokens.  Rows past the end read as zeros
+    // (and are masked), so no clamp is needed, and each load takes one
+    // 32-bit offset: the tile's (uniform) plus the lane's (constant).  The
+    // offsets wrap modulo 2^32 like the hardware's; a wrapped one lands
+    // inside the slice (the host keeps each slice below 4 GiB).
+    const size_t slice = PAGED ? 0 : ((size_t)b * a.Hkv + kvh) * (size_t)a.T * ROWB;
+    const int n_bytes = PAGED ? 0 : Tb * ROWB;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char *>(static_cast<const char *>(a.k)) + slice, 0, n_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char *>(static_cast<const char *>(a.v)) + slice, 0, n_bytes, 0x00020000);
+    const uint32_t kofs = (uint32_t)(2 * ku * ROWB + kpiece * 16);
+    const uint32_t vofs = (uint32_t)(2 * u * ROWB + piece * 16);
+    auto bload = [](__amdgpu_buffer_rsrc_t r, uint32_t off) -> uint4 {
+        typedef unsigned u32x4_v __attribute__((ext_vector_type(4)));
+        const u32x4_v x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+        return make_uint4(x[0], x[1], x[2], x[3]);
+    };
     auto load_tile = [&](int j) -> Regs {
         Regs g;
+        if constexpr (!PAGED) {
+            const uint32_t base = (uint32_t)j * (uint32_t)(NTOK * ROWB);
+            g.k0 = bload(rk, base + kofs);
+            g.k1 = bload(rk, base + kofs + ROWB);
+            g.v0 = bload(rv, base + vofs);
+            g.v1 = bload(rv, base + vofs + ROWB);
+            g.ok0 = g.ok1 = 1;                   // unused: the row limits mask the tail
+            return g;
+        }
         const size_t ra = token_row(j * NTOK + 2 * u, g.ok0);
         const size_t rb = token_row(j * NTOK + 2 * u + 1, g.ok1);
-        const char *kp = static_cast<const char *>(a.k) + piece * 16;
+        int dummy;
+        const size_t ka = token_row(j * NTOK + 2 * ku, dummy);
+        const size_t kb2 = token_row(j * NTOK + 2 * ku + 1, dummy);
+        const char *kp = static_cast<const char *>(a.k) + kpiece * 16;
         const char *vp = static_cast<const char *>(a.v) + piece * 16;
-        g.k0 = *reinterpret_cast<const uint4 *>(kp + ra * ROWB);
-        g.k1 = *reinterpret_cast<const uint4 *>(kp + rb * ROWB);
+        g.k0 = *reinterpret_cast<const uint4 *>(kp + ka * ROWB);
+        g.k1 = *reinterpret_cast<const uint4 *>(kp + kb2 * ROWB);
         g.v0 = *reinterpret_cast<const uint4 *>(vp + ra * ROWB);
         g.v1 = *reinterpret_cast<const uint4 *>(vp + rb * ROWB);
         return g;
@@ -236,8 +282,8 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
     // stay adjacent, so one 32-bit store writes both.
     auto vpos = [](int tt) { return 8 * ((tt & 15) >> 2) + 4 * (tt >> 4) + (tt & 3); };
     auto store_tile = [&](int buf, const Regs g) {
-        *reinterpret_cast<uint4 *>(&sK[buf][(2 * u) * KSTR + piece * 16]) = g.k0;
-        *reinterpret_cast<uint4 *>(&sK[buf][(2 * u + 1) * KSTR + piece * 16]) = g.k1;
+        *reinterpret_cast<uint4 *>(&sK[buf][(2 * ku) * KSTR + kpiece * 16]) = g.k0;
+        *reinterpret_cast<uint4 *>(&sK[buf][(2 * ku + 1) * KSTR + kpiece * 16]) = g.k1;
         // V^T: dimension 8*piece + e, tokens 2u and 2u+1 packed in one word
         const uint32_t w0[4] = {g.v0.x, g.v0.y, g.v0.z, g.v0.w};
         const uint32_t w1[4] = {g.v1.x, g.v1.y, g.v1.z, g.v1.w};
@@ -291,8 +337,8 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
     //     loads read clamped rows and the logits go unused, so nothing there
     //     needs a branch, and the matrix-core work of the logits can be
     //     interleaved with the vector work of the probabilities.
-    auto step = [&](const int j, const f32x4_v (&cc)[NB][2], f32x4_v (&cn)[NB][2]) {
-        const int bj = j % NBUF;
+    auto step = [&](auto bjc, const int j, const f32x4_v (&cc)[NB][2], f32x4_v (&cn)[NB][2]) {
+        constexpr int bj = decltype(bjc)::value;   // j % NBUF, known at compile time
         // Masks: tiles every row of the wave sees in full need none; there
         // the raw logits are kept and the scale goes into the exponent
         // (p = 2^(x * mult + nm)).  Masked tiles hold scaled logits with -inf
@@ -354,7 +400,7 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
             ok_cur = ok_next;
             ok_next = ok_new;
         }
-        qk((j + 1) % NBUF, cn);
+        qk((bj + 1) % NBUF, cn);
         uint4 phi[NB], plo[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
@@ -396,12 +442,18 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
                     for (int nb = 0; nb < NB; ++nb) acc[nb][dt + y] = mfma<DT>(va[y], plo[nb], acc[nb][dt + y]);
             }
         }
-        store_tile((j + 2) % NBUF, g);          // its buffer held tile j-1, finished
+        store_tile((bj + 2) % NBUF, g);         // its buffer held tile j-1, finished
         g = load_tile(j + 3);
         __syncthreads();
     };
 
-    f32x4_v cA[NB][2], cB[NB][2];
+    // The loop runs three tiles per trip, so every LDS buffer index is a
+    // compile-time constant (addresses become instruction offsets); the
+    // logits rotate through three register sets, two live at a time.
+    f32x4_v cA[NB][2], cB[NB][2], cC[NB][2];
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    using B2 = std::integral_constant<int, 2>;
     if (nt > 0) {
         if constexpr (PAGED) {
             Regs g0 = load_tile(0);
@@ -418,11 +470,13 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
         __syncthreads();
         qk(0, cA);
         int j = 0;
-        for (; j + 2 <= nt; j += 2) {
-            step(j, cA, cB);
-            step(j + 1, cB, cA);
+        for (; j + 3 <= nt; j += 3) {
+            step(B0{}, j, cA, cB);
+            step(B1{}, j + 1, cB, cC);
+            step(B2{}, j + 2, cC, cA);
         }
-        if (j < nt) step(j, cA, cB);
+        if (j < nt) step(B0{}, j, cA, cB);
+        if (j + 1 < nt) step(B1{}, j + 1, cB, cC);
     }
 
     // The four lanes of a row share m; their sums cover different tokens.
@@ -431,14 +485,16 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
         float L = l[nb];
         L += __shfl_xor(L, 16);
         L += __shfl_xor(L, 32);
-        if (!row_ok[nb]) continue;
+        bool ok;
+        const size_t qrow = row_of(nb, ok);
+        if (!ok) continue;
         const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
         for (int dt = 0; dt < DT16; ++dt) {
             const f32x4_v o = acc[nb][dt] * inv;
-            *reinterpret_cast<float4 *>(a.out + qrow[nb] * D + 16 * dt + 4 * kb) = make_float4(o[0], o[1], o[2], o[3]);
+            *reinterpret_cast<float4 *>(a.out + qrow * D + 16 * dt + 4 * kb) = make_float4(o[0], o[1], o[2], o[3]);
         }
-        if (kb == 0 && a.lse) a.lse[qrow[nb]] = L > 0.f ? (m[nb] + log2f(L) - kPBias) * kLn2 : kNegInf;
+        if (kb == 0 && a.lse) a.lse[qrow] = L > 0.f ? (m[nb] + log2f(L) - kPBias) * kLn2 : kNegInf;
     }
 }
 
