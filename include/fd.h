@@ -41,8 +41,13 @@
  *     head shares one read of K / V); more (the prefill phase: the dupenodi
  *     guide, "Concept", has prefill attend with the whole block of prompt
  *     queries) run on a query-tiled kernel: one workgroup per 128 query rows
- *     of a (sequence, kv head) over the whole visible KV range, no split and
- *     no workspace (FD_PATH_PREFILL; f16 / bf16 only).
+ *     of a (sequence, kv head) over the whole visible KV range, no split
+ *     (FD_PATH_PREFILL; f16 / bf16 only).  f16 needs no workspace; bf16
+ *     takes one of fd_plan_t.workspace_bytes (about the size of the V
+ *     slices): two passes ahead of the kernel write V there as f16 under a
+ *     power-of-two scale per (sequence, kv head), exact for every value
+ *     above 2^-28 of the slice's largest |V|, so the value product runs on
+ *     f16 with one probability product.
  *   - Calls are stream-ordered on fd_options_t.stream and never synchronise;
  *     a fault inside a kernel surfaces at the caller's next synchronisation.
  *   - Arguments are validated on the host before any launch.  Every call
@@ -145,7 +150,8 @@ typedef struct fd_plan {
                                 /* is 0 and n_splits = grid[0]; the merge is  */
                                 /* always inside the split launch             */
     int32_t reserved;
-    size_t workspace_bytes;     /* workspace this call needs (0 if n_splits=1) */
+    size_t workspace_bytes;     /* workspace this call needs (0 for one split,  */
+                                /* except bf16 query-tiled plans)               */
 } fd_plan_t;
 
 /* Fill *opt with defaults: dtype bf16, contiguous cache, automatic path,

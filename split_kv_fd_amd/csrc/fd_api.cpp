@@ -123,8 +123,10 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
     int path = o.path;
 
     // Many queries per sequence (prefill): the query-tiled kernel, one
-    // workgroup per tile of query rows over the whole KV range; no split,
-    // no workspace.
+    // workgroup per tile of query rows over the whole KV range; no split.
+    // bf16 inputs take a workspace for V converted to f16 (two passes ahead
+    // of the kernel; FD_PREFILL_VT=0 keeps V as given, a slower value
+    // product in two bf16 parts).
     if (path == FD_PATH_PREFILL || (path == FD_PATH_AUTO && o.n_queries > kMaxDecodeQueries)) {
         if (o.dtype == FD_F32) return fail(FD_ERR_UNSUPPORTED, "the query-tiled kernel needs f16 or bf16 inputs");
         if (o.flags & FD_FLAG_APPEND) return fail(FD_ERR_UNSUPPORTED, "fd_append_decode takes one query per sequence");
@@ -141,6 +143,8 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
         p->grid[1] = Hkv;
         p->grid[2] = B;
         p->block = 256;
+        if (o.dtype == FD_BF16 && env_long("FD_PREFILL_VT", 1) == 1)
+            p->workspace_bytes = fdk::prefill_vt_bytes(B, Hkv, T, D);
         return FD_OK;
     }
     if (o.n_queries > kMaxDecodeQueries)
@@ -423,6 +427,25 @@ fd_status_t prepare(const void *q, const void *k, const void *v, const int32_t *
     f.causal = s.causal;
     f.page_size = s.page_size; f.page_shift = s.page_shift; f.max_pages = s.max_pages; f.num_pages = s.num_pages;
     f.scale_log2 = s.scale_log2;
+    f.vt = nullptr; f.vmax = nullptr; f.vexp = nullptr;
+    f.vt_tiles = (int)ceil_div(T, fdk::kPrefillTokens);
+    f.vmax_chunks = (int)ceil_div(T, fdk::kVconvChunk);
+    if (c->p.path == FD_PATH_PREFILL && c->p.workspace_bytes > 0) {
+        if (!c->o.workspace)
+            return fail(FD_ERR_WORKSPACE, "query-tiled bf16 plan: a workspace of %zu bytes is required",
+                        c->p.workspace_bytes);
+        if (c->o.workspace_bytes < c->p.workspace_bytes)
+            return fail(FD_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", c->o.workspace_bytes,
+                        c->p.workspace_bytes);
+        if (!aligned(c->o.workspace, 256)) return fail(FD_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+        const size_t sl = (size_t)B * Hkv;
+        char *w = static_cast<char *>(c->o.workspace);
+        f.vexp = reinterpret_cast<int32_t *>(w);
+        w += align256(sl * 4);
+        f.vmax = reinterpret_cast<uint32_t *>(w);
+        w += align256(sl * f.vmax_chunks * 4);
+        f.vt = reinterpret_cast<uint16_t *>(w);
+    }
     return FD_OK;
 }
 

@@ -139,7 +139,25 @@ struct PrefillArgs {
     int causal;                  // query i sees the first T_b - (nq - 1 - i) tokens
     int page_size, page_shift, max_pages, num_pages;
     float scale_log2;
+    // bf16 inputs: V converted to f16 under a per-(batch, kv head) power-of-
+    // two scale 2^k, transposed in tile order (nullptr: V read as given).
+    uint16_t *vt;                // [B, Hkv, vt_tiles, D, kPrefillTokens]
+    uint32_t *vmax;              // [B, Hkv, vmax_chunks]: largest |V| (bf16 bits) per chunk
+    int32_t *vexp;               // [B, Hkv]: k
+    int vt_tiles;                // ceil(T / kPrefillTokens)
+    int vmax_chunks;             // ceil(T / kVconvChunk)
 };
+constexpr int kVconvChunk = 256;                  // tokens per workgroup of the conversion passes
+
+// Workspace of a query-tiled call with converted V (bf16), 256-byte aligned
+// pieces: vexp, vmax, vt.
+inline size_t prefill_vt_bytes(int B, int Hkv, int T, int D) {
+    auto a256 = [](size_t x) { return (x + 255) / 256 * 256; };
+    const size_t sl = (size_t)B * Hkv;
+    const size_t tiles = ((size_t)T + kPrefillTokens - 1) / kPrefillTokens;
+    const size_t chunks = ((size_t)T + kVconvChunk - 1) / kVconvChunk;
+    return a256(sl * 4) + a256(sl * chunks * 4) + a256(sl * tiles * D * kPrefillTokens * 2);
+}
 
 hipError_t launch_prefill(const PrefillArgs &a, int dtype, hipStream_t stream);
 

@@ -98,7 +98,10 @@ __device__ __forceinline__ float max3(float a, float b, float c) {
 // most tiles skip rescaling the accumulator.
 constexpr float kSlack = 8.f;
 
-template <int DT, int D, bool PAGED>
+// VT: bf16 inputs whose V was converted by the passes below to f16 under a
+// per-(batch, kv head) power-of-two scale, transposed in tile order; the
+// value product then runs on f16 with one P product, as for f16 inputs.
+template <int DT, int D, bool PAGED, bool VT>
 __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillArgs a) {
     constexpr int ROWB = D * 2;              // bytes per K / V row
     constexpr int KS = D / 32;               // 32-wide k chunks of the logit product
@@ -114,7 +117,9 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
     // bf16 keeps 8 significant bits: a single bf16 P would spend the whole
     // output tolerance, so P goes in as a high and a low part.  f16 keeps 11:
     // one product is enough (weights off by at most 2^-11 relative).
-    constexpr bool SPLIT_P = DT == FD_BF16;
+    constexpr bool SPLIT_P = DT == FD_BF16 && !VT;
+    constexpr int PVT = VT ? FD_F16 : DT;    // operand type of the value product
+    static_assert(!VT || DT == FD_BF16, "only bf16 V is converted");
     // f16 probabilities are formed as 2^(x - m + kPBias), in [0, 2^14]: far
     // above the f16 subnormal range for every weight that matters and below
     // its largest finite value.  The bias cancels in the division by the sum.
@@ -235,6 +240,18 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
         const_cast<char *>(static_cast<const char *>(a.v)) + slice, 0, n_bytes, 0x00020000);
     const uint32_t kofs = (uint32_t)(2 * ku * ROWB + kpiece * 16);
     const uint32_t vofs = (uint32_t)(2 * u * ROWB + piece * 16);
+    // Converted V: tile j of the slice is D rows of 32 f16 (64 bytes, tokens
+    // in the order the lanes take them); thread t moves 32 bytes of row
+    // (t / 2) % D, half t % 2.  Tiles past the sequence read as zeros.
+    const int vtrow = (t >> 1) % D, vthalf = t & 1;
+    [[maybe_unused]] int vexp = 0;               // V was scaled by 2^vexp
+    [[maybe_unused]] __amdgpu_buffer_rsrc_t rvt = rv;
+    if constexpr (VT) {
+        const size_t sl = (size_t)b * a.Hkv + kvh;
+        const int vt_bytes = ((Tb + NTOK - 1) / NTOK) * D * 64;
+        rvt = __builtin_amdgcn_make_buffer_rsrc(a.vt + sl * (size_t)a.vt_tiles * D * 32, 0, vt_bytes, 0x00020000);
+        vexp = a.vexp[sl];
+    }
     auto bload = [](__amdgpu_buffer_rsrc_t r, uint32_t off) -> uint4 {
         typedef unsigned u32x4_v __attribute__((ext_vector_type(4)));
         const u32x4_v x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
@@ -246,8 +263,14 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
             const uint32_t base = (uint32_t)j * (uint32_t)(NTOK * ROWB);
             g.k0 = bload(rk, base + kofs);
             g.k1 = bload(rk, base + kofs + ROWB);
-            g.v0 = bload(rv, base + vofs);
-            g.v1 = bload(rv, base + vofs + ROWB);
+            if constexpr (VT) {
+                const uint32_t vb = (uint32_t)j * (uint32_t)(D * 64) + (uint32_t)(vtrow * 64 + vthalf * 32);
+                g.v0 = bload(rvt, vb);
+                g.v1 = bload(rvt, vb + 16);
+            } else {
+                g.v0 = bload(rv, base + vofs);
+                g.v1 = bload(rv, base + vofs + ROWB);
+            }
             g.ok0 = g.ok1 = 1;                   // unused: the row limits mask the tail
             return g;
         }
@@ -257,11 +280,17 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
         const size_t ka = token_row(j * NTOK + 2 * ku, dummy);
         const size_t kb2 = token_row(j * NTOK + 2 * ku + 1, dummy);
         const char *kp = static_cast<const char *>(a.k) + kpiece * 16;
-        const char *vp = static_cast<const char *>(a.v) + piece * 16;
+        [[maybe_unused]] const char *vp = static_cast<const char *>(a.v) + piece * 16;
         g.k0 = *reinterpret_cast<const uint4 *>(kp + ka * ROWB);
         g.k1 = *reinterpret_cast<const uint4 *>(kp + kb2 * ROWB);
-        g.v0 = *reinterpret_cast<const uint4 *>(vp + ra * ROWB);
-        g.v1 = *reinterpret_cast<const uint4 *>(vp + rb * ROWB);
+        if constexpr (VT) {
+            const uint32_t vb = (uint32_t)j * (uint32_t)(D * 64) + (uint32_t)(vtrow * 64 + vthalf * 32);
+            g.v0 = bload(rvt, vb);
+            g.v1 = bload(rvt, vb + 16);
+        } else {
+            g.v0 = *reinterpret_cast<const uint4 *>(vp + ra * ROWB);
+            g.v1 = *reinterpret_cast<const uint4 *>(vp + rb * ROWB);
+        }
         return g;
     };
     // Paged tiles: bit t is set when token t of the tile is real and its
@@ -284,6 +313,12 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
     auto store_tile = [&](int buf, const Regs g) {
         *reinterpret_cast<uint4 *>(&sK[buf][(2 * ku) * KSTR + kpiece * 16]) = g.k0;
         *reinterpret_cast<uint4 *>(&sK[buf][(2 * ku + 1) * KSTR + kpiece * 16]) = g.k1;
+        if constexpr (VT) {
+            // already transposed and in lane order: a plain copy
+            *reinterpret_cast<uint4 *>(&sV[buf][vtrow * VSTR + vthalf * 32]) = g.v0;
+            *reinterpret_cast<uint4 *>(&sV[buf][vtrow * VSTR + vthalf * 32 + 16]) = g.v1;
+            return;
+        }
         // V^T: dimension 8*piece + e, tokens 2u and 2u+1 packed in one word
         const uint32_t w0[4] = {g.v0.x, g.v0.y, g.v0.z, g.v0.w};
         const uint32_t w1[4] = {g.v1.x, g.v1.y, g.v1.z, g.v1.w};
@@ -411,7 +446,7 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
             uint32_t hi[4], lo[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                hi[e] = pack2<DT>(p[2 * e], p[2 * e + 1]);
+                hi[e] = pack2<PVT>(p[2 * e], p[2 * e + 1]);
                 if constexpr (SPLIT_P) {
                     float h0, h1;
                     unpack2_bf16(hi[e], h0, h1);
@@ -434,7 +469,7 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
 #pragma unroll
             for (int y = 0; y < 2; ++y)
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) acc[nb][dt + y] = mfma<DT>(va[y], phi[nb], acc[nb][dt + y]);
+                for (int nb = 0; nb < NB; ++nb) acc[nb][dt + y] = mfma<PVT>(va[y], phi[nb], acc[nb][dt + y]);
             if constexpr (SPLIT_P) {
 #pragma unroll
                 for (int y = 0; y < 2; ++y)
@@ -491,18 +526,146 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
         const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
         for (int dt = 0; dt < DT16; ++dt) {
-            const f32x4_v o = acc[nb][dt] * inv;
+            f32x4_v o = acc[nb][dt] * inv;
+            if constexpr (VT) {
+                // undo the conversion scale exactly (one rounding, also for
+                // results in the fp32 subnormal range)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = __builtin_amdgcn_ldexpf(o[e], -vexp);
+            }
             *reinterpret_cast<float4 *>(a.out + qrow * D + 16 * dt + 4 * kb) = make_float4(o[0], o[1], o[2], o[3]);
         }
         if (kb == 0 && a.lse) a.lse[qrow] = L > 0.f ? (m[nb] + log2f(L) - kPBias) * kLn2 : kNegInf;
     }
 }
 
+// ---- bf16 V converted for the value product ----
+// A bf16 value v becomes the f16 value v * 2^k, with k chosen per (batch,
+// kv head) so that the sequence's largest |v| lands in [2^14, 2^15).  bf16
+// keeps 8 significant bits and f16 11, so every value down to 2^-28 of that
+// maximum converts exactly (f16 normal range); smaller ones, rounded to the
+// f16 subnormal grid, are off by at most 2^-39 of the maximum.  Rounding is
+// to nearest; infinities and NaNs stay what they are.
+
+// Pass 1: the largest |V| (bf16 bits, sign cleared) of each chunk of
+// kVconvChunk tokens of each (batch, kv head) slice.
+template <int D, bool PAGED>
+__global__ __launch_bounds__(256) void vmax_pass(PrefillArgs a) {
+    constexpr int ROWB = D * 2, PIECES = ROWB / 16, RPI = 256 / PIECES;   // rows per sweep
+    const int t = threadIdx.x, chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    int Tb = a.seq_lens ? a.seq_lens[b] : a.T;
+    Tb = Tb < 0 ? 0 : (Tb > a.T ? a.T : Tb);
+    const int t0 = chunk * kVconvChunk, t1 = min(t0 + kVconvChunk, Tb);
+    const int piece = t % PIECES;
+    uint32_t mx = 0;
+#pragma unroll 4
+    for (int tt = t0 + t / PIECES; tt < t1; tt += RPI) {
+        size_t row;
+        bool ok = true;
+        if constexpr (PAGED) {
+            const int pg = a.page_table[(size_t)b * a.max_pages + (tt >> a.page_shift)];
+            ok = (unsigned)pg < (unsigned)a.num_pages;
+            row = ((size_t)(ok ? pg : 0) * a.Hkv + kvh) * a.page_size + (tt & (a.page_size - 1));
+        } else {
+            row = ((size_t)b * a.Hkv + kvh) * a.T + tt;
+        }
+        const uint4 w = *reinterpret_cast<const uint4 *>(static_cast<const char *>(a.v) + row * ROWB + piece * 16);
+        const uint32_t m4 = max(max(w.x & 0x7fff7fffu, w.y & 0x7fff7fffu), max(w.z & 0x7fff7fffu, w.w & 0x7fff7fffu));
+        const uint32_t m2 = ok ? max(m4 & 0xffffu, m4 >> 16) : 0u;
+        mx = max(mx, m2);
+    }
+    __shared__ uint32_t red[4];
+    for (int off = 32; off > 0; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
+    if ((t & 63) == 0) red[t >> 6] = mx;
+    __syncthreads();
+    if (t == 0)
+        a.vmax[((size_t)b * a.Hkv + kvh) * a.vmax_chunks + chunk] = max(max(red[0], red[1]), max(red[2], red[3]));
+}
+
+// Pass 2: the slice's scale exponent k from the chunk maxima, and the
+// chunk's tiles converted: tile j is D rows of kPrefillTokens f16, tokens
+// in the order the query-tiled kernel's lanes take them; tokens past the
+// sequence (or on pages outside the pool) are zeros.
+template <int D, bool PAGED>
+__global__ __launch_bounds__(256) void vconv_pass(PrefillArgs a) {
+    constexpr int ROWB = D * 2, PIECES = ROWB / 16, NTOK = kPrefillTokens;
+    const int t = threadIdx.x, chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    const size_t sl = (size_t)b * a.Hkv + kvh;
+    int Tb = a.seq_lens ? a.seq_lens[b] : a.T;
+    Tb = Tb < 0 ? 0 : (Tb > a.T ? a.T : Tb);
+
+    uint32_t mx = 0;
+    for (int c = t; c < a.vmax_chunks; c += 256) mx = max(mx, a.vmax[sl * a.vmax_chunks + c]);
+    __shared__ uint32_t red[4];
+    for (int off = 32; off > 0; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
+    if ((t & 63) == 0) red[t >> 6] = mx;
+    __syncthreads();
+    mx = max(max(red[0], red[1]), max(red[2], red[3]));
+    // floor(log2 of the largest |v|): from the exponent field, or for a
+    // subnormal from the top mantissa bit (value = mantissa * 2^-133)
+    const int E = (int)(mx >> 7);
+    const int lg = E > 0 ? E - 127 : -133 + (31 - __builtin_clz(mx | 1u));
+    const int k = mx == 0 ? 0 : 14 - lg;
+    if (chunk == 0 && t == 0) a.vexp[sl] = k;
+
+    const int u = t & 15, piece = (t >> 4) % PIECES;   // D = 64: two threads per piece, same values
+    const int pos = 8 * ((2 * u & 15) >> 2) + 4 * (2 * u >> 4) + (2 * u & 3);   // lane order of token 2u
+    const int nt = (Tb + NTOK - 1) / NTOK;
+    const int j0 = chunk * (kVconvChunk / NTOK);
+    const int j1 = min(j0 + kVconvChunk / NTOK, nt);
+    auto load = [&](int tt) -> uint4 {
+        if (tt >= Tb) return make_uint4(0, 0, 0, 0);
+        size_t row;
+        if constexpr (PAGED) {
+            const int pg = a.page_table[(size_t)b * a.max_pages + (tt >> a.page_shift)];
+            if ((unsigned)pg >= (unsigned)a.num_pages) return make_uint4(0, 0, 0, 0);
+            row = ((size_t)pg * a.Hkv + kvh) * a.page_size + (tt & (a.page_size - 1));
+        } else {
+            row = ((size_t)b * a.Hkv + kvh) * a.T + tt;
+        }
+        return *reinterpret_cast<const uint4 *>(static_cast<const char *>(a.v) + row * ROWB + piece * 16);
+    };
+    auto cvt = [k](float x, float y) -> uint32_t {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(
+                                                f32x2_v{__builtin_amdgcn_ldexpf(x, k), __builtin_amdgcn_ldexpf(y, k)},
+                                                f16x2_v));
+    };
+    for (int j = j0; j < j1; ++j) {
+        const uint4 v0 = load(j * NTOK + 2 * u), v1 = load(j * NTOK + 2 * u + 1);
+        const uint32_t w0[4] = {v0.x, v0.y, v0.z, v0.w};
+        const uint32_t w1[4] = {v1.x, v1.y, v1.z, v1.w};
+        uint32_t *tile = reinterpret_cast<uint32_t *>(a.vt + (sl * a.vt_tiles + j) * (size_t)D * NTOK);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int d = 8 * piece + 2 * i;
+            tile[(size_t)d * (NTOK / 2) + pos / 2] =
+                cvt(__uint_as_float(w0[i] << 16), __uint_as_float(w1[i] << 16));
+            tile[(size_t)(d + 1) * (NTOK / 2) + pos / 2] =
+                cvt(__uint_as_float(w0[i] & 0xffff0000u), __uint_as_float(w1[i] & 0xffff0000u));
+        }
+    }
+}
+
 template <int DT, int D>
 hipError_t launch_dim(const PrefillArgs &a, hipStream_t stream) {
     const dim3 grid(a.row_tiles, a.Hkv, a.B);
-    if (a.page_table) hipLaunchKernelGGL((prefill<DT, D, true>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((prefill<DT, D, false>), grid, dim3(256), 0, stream, a);
+    if constexpr (DT == FD_BF16) {
+        if (a.vt) {
+            const dim3 pgrid(a.vmax_chunks, a.Hkv, a.B);
+            if (a.page_table) {
+                hipLaunchKernelGGL((vmax_pass<D, true>), pgrid, dim3(256), 0, stream, a);
+                hipLaunchKernelGGL((vconv_pass<D, true>), pgrid, dim3(256), 0, stream, a);
+            } else {
+                hipLaunchKernelGGL((vmax_pass<D, false>), pgrid, dim3(256), 0, stream, a);
+                hipLaunchKernelGGL((vconv_pass<D, false>), pgrid, dim3(256), 0, stream, a);
+            }
+            if (a.page_table) hipLaunchKernelGGL((prefill<DT, D, true, true>), grid, dim3(256), 0, stream, a);
+            else hipLaunchKernelGGL((prefill<DT, D, false, true>), grid, dim3(256), 0, stream, a);
+            return hipGetLastError();
+        }
+    }
+    if (a.page_table) hipLaunchKernelGGL((prefill<DT, D, true, false>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((prefill<DT, D, false, false>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -291,11 +291,19 @@ def test_several_queries_rejects(lib):
 @pytest.mark.parametrize("nq,G", [(17, 1), (100, 4), (4096, 8), (65536, 1)])
 def test_plan_query_tiled(lib, nq, G):
     # more than 16 queries per sequence: one workgroup per 128 query rows of
-    # each (sequence, kv head), the whole KV range, no split, no workspace
+    # each (sequence, kv head), the whole KV range, no split; f16 takes no
+    # workspace, bf16 one for V converted to f16 (scale exponents, chunk
+    # maxima, transposed tiles; 256-byte aligned pieces)
     B, Hkv = 2, 2
-    st, p = plan(B, G * Hkv, Hkv, 8192, 128, 0, n_queries=nq, causal=1)
+    st, p = plan(B, G * Hkv, Hkv, 8192, 128, 0, n_queries=nq, causal=1, dtype=fd.FD_F16)
     assert st == fd.FD_OK, fd.fd_last_error()
     assert p.path == fd.FD_PATH_PREFILL and p.n_splits == 1 and p.workspace_bytes == 0
+    st, p = plan(B, G * Hkv, Hkv, 8192, 128, 0, n_queries=nq, causal=1)
+    assert st == fd.FD_OK, fd.fd_last_error()
+    a256 = lambda x: -(-x // 256) * 256
+    sl = B * Hkv
+    assert p.path == fd.FD_PATH_PREFILL and p.n_splits == 1
+    assert p.workspace_bytes == a256(sl * 4) + a256(sl * (8192 // 256) * 4) + a256(sl * 8192 * 128 * 2)
     assert not p.fused and not p.combine and not p.stream
     tiles = -(-(nq * G) // 128)
     assert (p.grid[0], p.grid[1], p.grid[2]) == (tiles, Hkv, B) and p.head_blocks == tiles

@@ -59,7 +59,12 @@ def test_prefill_kernel_for_few_queries(nq):
     d = Decoder(q, case.k, case.v, scale=case.spec.scale, seq_lens=case.seq_lens, causal=True)
     out_d, lse_d = d()
     torch.cuda.synchronize()
-    assert torch.allclose(out_a, out_d, rtol=0, atol=1e-4) and torch.allclose(lse_a, lse_d, rtol=0, atol=1e-4)
+    # the query-tiled kernel rounds P to f16 (weights within 2^-11), the
+    # split kernels keep it in fp32: outputs agree within 1e-3 of max|V|,
+    # the lse (summed in fp32 on both) within 1e-4
+    vmax = float(case.v.float().abs().max())
+    assert torch.allclose(out_a, out_d, rtol=0, atol=1e-3 * vmax)
+    assert torch.allclose(lse_a, lse_d, rtol=0, atol=1e-4)
 
 
 def test_prefill_full_size_sampled():
@@ -154,3 +159,24 @@ def test_prefill_full_size_sampled_f16():
         lerr = float(np.max(np.abs(lse[0, i].cpu().double().numpy() - ref_l[0])))
         parity.announce(f"prefill f16 query={i}: err {err:.2e} lse {lerr:.2e}")
         assert err <= parity.OUT_TOL["f16"] and lerr <= parity.LSE_TOL["f16"]
+
+
+@pytest.mark.parametrize("vmul", [2.0 ** 20, 2.0 ** -20, 2.0 ** -130, 0.0])
+def test_prefill_bf16_value_range(vmul):
+    # bf16 V far from 1 in magnitude -- large, small, in the bf16 subnormal
+    # range, all zero: the per-(sequence, kv head) scale of the f16
+    # conversion keeps the value product within the tolerance of max|V|
+    case = contiguous("gqa128k_bf16", [300, 129], Hq=8, Hkv=2, T=300)
+    case.v = (case.v.float() * vmul).to(torch.bfloat16)
+    q = inputs.make_q_multi(case.spec, 40).to(DEV)
+    host = case.to("cpu")
+    for causal in (False, True):
+        ref_out, ref_lse = oracle_mod.default().decode_multi(q.cpu(), host.k, host.v, case.spec.scale,
+                                                             causal=causal, seq_lens=host.seq_lens)
+        dec = Decoder(q, case.k, case.v, scale=case.spec.scale, seq_lens=case.seq_lens, causal=causal)
+        assert dec.plan["path"] == "prefill" and dec.plan["workspace_bytes"] > 0
+        parity.announce(f"prefill bf16 V x {vmul:g} causal={causal}")
+        out, lse = dec()
+        torch.cuda.synchronize()
+        parity.compare(case, out.cpu().double().numpy(), lse.cpu().double().numpy(), ref_out, ref_lse,
+                       parity.max_abs_v(host), f"prefill bf16 V x {vmul:g} causal={causal}")
