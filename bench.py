@@ -288,6 +288,9 @@ def main() -> int:
                     "unit": "TFLOP/s", "frac": round(tf / MFMA_PEAK_TFLOPS, 4),
                     "traffic": read_traffic(spec.name, kernel), "kernel": kernel,
                     "launch_us_avg": round(split_avg * 1e3, 2), "flops_per_launch": flops}
+        if plan["workspace_bytes"]:
+            # bf16: the two V conversion passes run inside the timed call
+            roofline["launch_includes"] = "V conversion passes + query-tiled kernel"
 
     if overrides:
         print(f"[bench] workload overrides {overrides}: not the reference workload",
