@@ -428,6 +428,7 @@ fd_status_t prepare(const void *q, const void *k, const void *v, const int32_t *
     f.page_size = s.page_size; f.page_shift = s.page_shift; f.max_pages = s.max_pages; f.num_pages = s.num_pages;
     f.scale_log2 = s.scale_log2;
     f.vt = nullptr; f.vmax = nullptr; f.vexp = nullptr;
+    f.xcd_map = env_long("FD_PREFILL_XCD", 1) == 1 ? 1 : 0;
     f.vt_tiles = (int)ceil_div(T, fdk::kPrefillTokens);
     f.vmax_chunks = (int)ceil_div(T, fdk::kVconvChunk);
     if (c->p.path == FD_PATH_PREFILL && c->p.workspace_bytes > 0) {

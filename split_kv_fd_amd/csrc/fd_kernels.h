@@ -146,6 +146,7 @@ struct PrefillArgs {
     int32_t *vexp;               // [B, Hkv]: k
     int vt_tiles;                // ceil(T / kPrefillTokens)
     int vmax_chunks;             // ceil(T / kVconvChunk)
+    int xcd_map;                 // 1: each XCD walks a contiguous run of work items
 };
 constexpr int kVconvChunk = 256;                  // tokens per workgroup of the conversion passes
 

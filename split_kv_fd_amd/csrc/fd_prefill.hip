@@ -137,9 +137,20 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
     const int i16 = lane & 15;
     const int kb = lane >> 4;
 
-    const int tile = a.causal ? a.row_tiles - 1 - (int)blockIdx.x : (int)blockIdx.x;   // longest first
-    const int kvh = blockIdx.y;
-    const int b = blockIdx.z;
+    // Work item of this workgroup.  Workgroups are dealt to the 8 XCDs
+    // round-robin by linear id; with xcd_map each XCD instead walks one
+    // contiguous run of (batch, kv head, row tile) items, so the workgroups
+    // it runs at once share a K/V slice that its own L2 holds.  Within a
+    // slice causal tiles run longest first.
+    const int n_wg = (int)(gridDim.x * gridDim.y * gridDim.z);
+    const int lin = (int)(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
+    const int per_xcd = n_wg / 8;
+    const int item = (a.xcd_map && lin < 8 * per_xcd) ? (lin % 8) * per_xcd + lin / 8 : lin;
+    const int tile_i = item % a.row_tiles;
+    const int slc = item / a.row_tiles;
+    const int tile = a.causal ? a.row_tiles - 1 - tile_i : tile_i;
+    const int kvh = slc % a.Hkv;
+    const int b = slc / a.Hkv;
     const int r0 = tile * kPrefillRows;
 
     int Tb = a.seq_lens ? a.seq_lens[b] : a.T;
