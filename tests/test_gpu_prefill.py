@@ -180,3 +180,39 @@ def test_prefill_bf16_value_range(vmul):
         torch.cuda.synchronize()
         parity.compare(case, out.cpu().double().numpy(), lse.cpu().double().numpy(), ref_out, ref_lse,
                        parity.max_abs_v(host), f"prefill bf16 V x {vmul:g} causal={causal}")
+
+
+@pytest.fixture
+def env_switch(monkeypatch):
+    # the library reads its FD_* switches when a call is prepared
+    return monkeypatch
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_prefill_bf16_split_p_form(env_switch, causal):
+    # FD_PREFILL_VT=0: bf16 V read as given, P in a high and a low bf16 part
+    # (no workspace) -- the same oracle bar, contiguous and paged
+    env_switch.setenv("FD_PREFILL_VT", "0")
+    case = contiguous("gqa128k_bf16", [300, 100, 0], Hq=8, Hkv=2, T=300)
+    q = inputs.make_q_multi(case.spec, 48).to(DEV)
+    plan = check_multi(case, q, causal, what=f"prefill bf16 split P causal={causal}")
+    assert plan["path"] == "prefill" and plan["workspace_bytes"] == 0
+    s = inputs.spec("paged_ragged_bf16", B=3, Hq=8, Hkv=2, T=900, page_size=16, len_lo=50, len_hi=900)
+    pc = inputs.make_case(s).to(DEV)
+    check_multi(pc, inputs.make_q_multi(s, 40).to(DEV), causal, what=f"prefill bf16 split P paged causal={causal}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_prefill_work_order_does_not_change_results(env_switch, dtype):
+    # the XCD-aware work order only permutes which workgroup takes which
+    # (sequence, kv head, row tile): outputs are bit-identical
+    case = contiguous("gqa128k_bf16", [700, 333, 512], Hq=8, Hkv=2, T=700, dtype=dtype)
+    q = inputs.make_q_multi(case.spec, 300).to(DEV)
+    res = []
+    for x in ("1", "0"):
+        env_switch.setenv("FD_PREFILL_XCD", x)
+        dec = Decoder(q, case.k, case.v, scale=case.spec.scale, seq_lens=case.seq_lens, causal=True)
+        out, lse = dec()
+        torch.cuda.synchronize()
+        res.append((out.clone(), lse.clone()))
+    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
