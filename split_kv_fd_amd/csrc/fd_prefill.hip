@@ -33,9 +33,12 @@
 //  * values O^T += V^T P^T with the same MFMA: V^T rows from LDS as the A
 //    operand, P^T from the lane's own probabilities as the B operand (k slot
 //    8*kb + e is token 4*kb + e of the first half for e < 4, of the second
-//    half for e >= 4, on both operands).  For bf16, P goes in as a high and
-//    a low part (P = hi + lo, two MFMAs), so its rounding stays near fp32; an
-//    f16 P (11 significant bits, rounded to nearest) goes in once.
+//    half for e >= 4, on both operands).  P goes in once, rounded to f16
+//    (11 significant bits, to nearest).  bf16 V is first converted to f16 by
+//    two passes (the end of this file) under a per-(batch, kv head) power of
+//    two, exact for every value that matters; without that conversion a bf16
+//    P would be needed, and it goes in as a high and a low part (P = hi + lo,
+//    two MFMAs) so that its rounding stays near fp32.
 //    The accumulator leaves lane (i16, kb) holding row i16's dimensions
 //    16*dt + 4*kb .. +3, written out as one 16-byte store per tile of 16.
 // Causal rows (query i sees the first T_b - (nq - 1 - i) tokens) are masked
@@ -108,15 +111,17 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
     constexpr int DT16 = D / 16;             // 16-wide dimension tiles of the value product
     constexpr int PIECES = ROWB / 16;        // 16-byte pieces per row
     constexpr int NTOK = kPrefillTokens;     // tokens per KV tile
-    // LDS row strides: 16-byte reads of 16 rows x 2 lanes hit distinct banks
-    // when consecutive rows start 8 dwords apart modulo 128 dwords (rows of
-    // ROWB + 16 bytes, 4 apart, conflict in pairs on gfx950).
+    // LDS row strides: gfx950 serves a 16-byte read 32 lanes at a time over
+    // 128 banks; 16 rows x 2 chunks land on distinct banks when consecutive
+    // rows start 8 dwords apart (mod 128).  A 16-byte pad (4 dwords) measured
+    // 2-way conflicts.
     constexpr int KSTR = ROWB + 32;          // K (bytes)
     constexpr int VSTR = NTOK * 2 + 32;      // V^T (bytes)
     constexpr int NB = kPrefillNB;           // 16-row blocks per wave
-    // bf16 keeps 8 significant bits: a single bf16 P would spend the whole
-    // output tolerance, so P goes in as a high and a low part.  f16 keeps 11:
-    // one product is enough (weights off by at most 2^-11 relative).
+    // The value product takes P rounded to f16 (11 significant bits: weights
+    // off by at most 2^-11 relative) -- for f16 inputs, and for bf16 inputs
+    // whose V was converted (VT).  Otherwise bf16 P, with 8 bits, would spend
+    // the whole output tolerance: it goes in as a high and a low part.
     constexpr bool SPLIT_P = DT == FD_BF16 && !VT;
     constexpr int PVT = VT ? FD_F16 : DT;    // operand type of the value product
     static_assert(!VT || DT == FD_BF16, "only bf16 V is converted");
@@ -163,16 +168,16 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
     const float sl2 = neg ? -a.scale_log2 : a.scale_log2;
     const uint32_t qflip = neg ? 0x80008000u : 0u;
 
-    // This lane's query rows (one per block), the tokens each sees, and
-    // their q pieces.
-    // Output row of a lane's query row (recomputed after the loop rather than
-    // kept live through it).
+    // Output row of a lane's query row in block nb (recomputed after the
+    // loop rather than kept live through it).
     auto row_of = [&](int nb, bool &ok) -> size_t {
         const int rr = r0 + 16 * (NB * wave + nb) + i16;
         ok = rr < a.R;
         const int qi = ok ? rr / a.G : 0;
         return ((size_t)b * a.nq + qi) * a.Hq + (size_t)kvh * a.G + (ok ? rr - qi * a.G : 0);
     };
+    // This lane's query rows (one per block): the tokens each sees and its
+    // q pieces.
     int lim[NB];
     uint4 qb[NB][KS];
 #pragma unroll
@@ -240,15 +245,16 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
     // Contiguous caches: the (batch, kv head) slices of K and V as buffer
     // resources sized to the real tokens.  Rows past the end read as zeros
     // (and are masked), so no clamp is needed, and each load takes one
-    // 32-bit offset: the tile's (uniform) plus the lane's (constant).  The
-    // offsets wrap modulo 2^32 like the hardware's; a wrapped one lands
-    // inside the slice (the host keeps each slice below 4 GiB).
+    // 32-bit offset: the tile's (uniform) plus the lane's (constant).  Sizes
+    // and offsets are unsigned 32-bit (the host keeps each slice below 4
+    // GiB); an offset that wraps past 2^32 lands inside the slice or past its
+    // end (zeros), never outside the resource.
     const size_t slice = PAGED ? 0 : ((size_t)b * a.Hkv + kvh) * (size_t)a.T * ROWB;
-    const int n_bytes = PAGED ? 0 : Tb * ROWB;
+    const uint32_t n_bytes = PAGED ? 0u : (uint32_t)Tb * (uint32_t)ROWB;
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char *>(static_cast<const char *>(a.k)) + slice, 0, n_bytes, 0x00020000);
+        const_cast<char *>(static_cast<const char *>(a.k)) + slice, 0, (int)n_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char *>(static_cast<const char *>(a.v)) + slice, 0, n_bytes, 0x00020000);
+        const_cast<char *>(static_cast<const char *>(a.v)) + slice, 0, (int)n_bytes, 0x00020000);
     const uint32_t kofs = (uint32_t)(2 * ku * ROWB + kpiece * 16);
     const uint32_t vofs = (uint32_t)(2 * u * ROWB + piece * 16);
     // Converted V: tile j of the slice is D rows of 32 f16 (64 bytes, tokens
@@ -259,8 +265,9 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
     [[maybe_unused]] __amdgpu_buffer_rsrc_t rvt = rv;
     if constexpr (VT) {
         const size_t sl = (size_t)b * a.Hkv + kvh;
-        const int vt_bytes = ((Tb + NTOK - 1) / NTOK) * D * 64;
-        rvt = __builtin_amdgcn_make_buffer_rsrc(a.vt + sl * (size_t)a.vt_tiles * D * 32, 0, vt_bytes, 0x00020000);
+        const uint32_t vt_bytes = (uint32_t)((Tb + NTOK - 1) / NTOK) * (uint32_t)(D * 64);
+        rvt = __builtin_amdgcn_make_buffer_rsrc(a.vt + sl * (size_t)a.vt_tiles * D * 32, 0, (int)vt_bytes,
+                                                0x00020000);
         vexp = a.vexp[sl];
     }
     auto bload = [](__amdgpu_buffer_rsrc_t r, uint32_t off) -> uint4 {
@@ -287,9 +294,9 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
         }
         const size_t ra = token_row(j * NTOK + 2 * u, g.ok0);
         const size_t rb = token_row(j * NTOK + 2 * u + 1, g.ok1);
-        int dummy;
-        const size_t ka = token_row(j * NTOK + 2 * ku, dummy);
-        const size_t kb2 = token_row(j * NTOK + 2 * ku + 1, dummy);
+        int unused_ok;                           // the mask bits come from the V rows
+        const size_t ka = token_row(j * NTOK + 2 * ku, unused_ok);
+        const size_t kb2 = token_row(j * NTOK + 2 * ku + 1, unused_ok);
         const char *kp = static_cast<const char *>(a.k) + kpiece * 16;
         [[maybe_unused]] const char *vp = static_cast<const char *>(a.v) + piece * 16;
         g.k0 = *reinterpret_cast<const uint4 *>(kp + ka * ROWB);
@@ -380,7 +387,7 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
     //  2. one straight-line block: tile j+2 (loaded one step earlier) into
     //     its LDS buffer, tile j+3 from memory, logits of tile j+1, and the
     //     probabilities and value product of tile j.  Past the last tile the
-    //     loads read clamped rows and the logits go unused, so nothing there
+    //     loads read clamped rows (or zeros) and the logits go unused, so nothing there
     //     needs a branch, and the matrix-core work of the logits can be
     //     interleaved with the vector work of the probabilities.
     auto step = [&](auto bjc, const int j, const f32x4_v (&cc)[NB][2], f32x4_v (&cn)[NB][2]) {
