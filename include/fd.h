@@ -48,6 +48,10 @@
  *     power-of-two scale per (sequence, kv head), exact for every value
  *     above 2^-28 of the slice's largest |V|, so the value product runs on
  *     f16 with one probability product.
+ *   - A few FD_* environment variables, read when a call is planned, switch
+ *     planner and kernel choices for measurement; every setting computes the
+ *     same attention (within the tolerances above) and the defaults are the
+ *     measured choices.
  *   - Calls are stream-ordered on fd_options_t.stream and never synchronise;
  *     a fault inside a kernel surfaces at the caller's next synchronisation.
  *   - Arguments are validated on the host before any launch.  Every call
