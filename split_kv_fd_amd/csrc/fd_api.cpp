@@ -132,6 +132,11 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
         if (o.flags & FD_FLAG_APPEND) return fail(FD_ERR_UNSUPPORTED, "fd_append_decode takes one query per sequence");
         const long tiles = ceil_div(R, fdk::kPrefillRows);
         if (Hkv > 65535) return fail(FD_ERR_UNSUPPORTED, "Hkv=%d > 65535", Hkv);
+        const bool vt = o.dtype == FD_BF16 && env_long("FD_PREFILL_VT", 1) == 1;
+        // the converted V of one (batch, kv head) is addressed with 32-bit
+        // offsets, as contiguous slices are
+        if (vt && ceil_div(T, fdk::kPrefillTokens) * fdk::kPrefillTokens * D * 2 >= (1L << 32))
+            return fail(FD_ERR_UNSUPPORTED, "T=%d: the converted V of one (batch, kv head) must be < 4 GiB", T);
         std::memset(p, 0, sizeof *p);
         p->n_splits = 1;
         p->chunk = T;
@@ -143,8 +148,7 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
         p->grid[1] = Hkv;
         p->grid[2] = B;
         p->block = 256;
-        if (o.dtype == FD_BF16 && env_long("FD_PREFILL_VT", 1) == 1)
-            p->workspace_bytes = fdk::prefill_vt_bytes(B, Hkv, T, D);
+        if (vt) p->workspace_bytes = fdk::prefill_vt_bytes(B, Hkv, T, D);
         return FD_OK;
     }
     if (o.n_queries > kMaxDecodeQueries)

@@ -351,3 +351,16 @@ def test_no_device_reports_hip_error(lib):
     st = decode(num_cus=0, workspace=A, workspace_bytes=need)
     assert st == fd.FD_ERR_HIP
     assert "hip" in fd.fd_last_error().lower()
+
+
+def test_plan_query_tiled_size_limits(lib):
+    # bf16 query-tiled plans address each (batch, kv head) of converted V with
+    # 32-bit offsets: a paged T whose converted slice reaches 4 GiB is refused
+    T = (1 << 24)                                   # 2^24 tokens x 128 x 2 B = 4 GiB
+    kw = dict(n_queries=64, page_size=16, max_pages_per_seq=T // 16, num_pages=1)
+    st, _ = plan(1, 8, 2, T, 128, 0, **kw)
+    assert st == fd.FD_ERR_UNSUPPORTED and "4 GiB" in fd.fd_last_error()
+    st, _ = plan(1, 8, 2, T - 64, 128, 0, **kw)
+    assert st == fd.FD_OK, fd.fd_last_error()
+    st, p = plan(1, 8, 2, T, 128, 0, dtype=fd.FD_F16, **kw)   # f16 needs no conversion
+    assert st == fd.FD_OK and p.workspace_bytes == 0
