@@ -242,6 +242,25 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
             return ((size_t)b * a.Hkv + kvh) * a.T + tc;
         }
     };
+    // Paged rows of tokens tt and tt+1 (tt even), clamped like token_row.
+    // With pages of two or more tokens the pair never straddles a page, so
+    // one page-table read serves both.
+    auto pair_rows = [&](int tt, size_t &r0_, size_t &r1_, int &ok0_, int &ok1_) {
+        if (a.page_shift == 0) {
+            r0_ = token_row(tt, ok0_);
+            r1_ = token_row(tt + 1, ok1_);
+            return;
+        }
+        const int t0 = tt < Tb ? tt : Tb - 1;
+        const int t1 = tt + 1 < Tb ? tt + 1 : Tb - 1;
+        int pg = a.page_table[(size_t)b * a.max_pages + (t0 >> a.page_shift)];
+        const bool valid = (unsigned)pg < (unsigned)a.num_pages;
+        if (!valid) pg = 0;
+        r0_ = ((size_t)pg * a.Hkv + kvh) * a.page_size + (t0 & (a.page_size - 1));
+        r1_ = r0_ + (size_t)(t1 - t0);
+        ok0_ = (tt < Tb) & valid;
+        ok1_ = (tt + 1 < Tb) & valid;
+    };
     // Contiguous caches: the (batch, kv head) slices of K and V as buffer
     // resources sized to the real tokens.  Rows past the end read as zeros
     // (and are masked), so no clamp is needed, and each load takes one
@@ -292,11 +311,10 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
             g.ok0 = g.ok1 = 1;                   // unused: the row limits mask the tail
             return g;
         }
-        const size_t ra = token_row(j * NTOK + 2 * u, g.ok0);
-        const size_t rb = token_row(j * NTOK + 2 * u + 1, g.ok1);
+        size_t ra, rb, ka, kb2;
         int unused_ok;                           // the mask bits come from the V rows
-        const size_t ka = token_row(j * NTOK + 2 * ku, unused_ok);
-        const size_t kb2 = token_row(j * NTOK + 2 * ku + 1, unused_ok);
+        pair_rows(j * NTOK + 2 * u, ra, rb, g.ok0, g.ok1);
+        pair_rows(j * NTOK + 2 * ku, ka, kb2, unused_ok, unused_ok);
         const char *kp = static_cast<const char *>(a.k) + kpiece * 16;
         [[maybe_unused]] const char *vp = static_cast<const char *>(a.v) + piece * 16;
         g.k0 = *reinterpret_cast<const uint4 *>(kp + ka * ROWB);
@@ -396,7 +414,8 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
         // the raw logits are kept and the scale goes into the exponent
         // (p = 2^(x * mult + nm)).  Masked tiles hold scaled logits with -inf
         // for masked tokens (mult = 1).
-        const bool full = !PAGED && (j + 1) * NTOK <= wave_lim;
+        // (paged tiles also need every page in the pool)
+        const bool full = (j + 1) * NTOK <= wave_lim && (!PAGED || ok_cur == 0xffffffffu);
         const float mult = full ? sl2 : 1.f;
         float x[NB][8];
         if (full) {
