@@ -41,13 +41,19 @@
  *     head shares one read of K / V); more (the prefill phase: the dupenodi
  *     guide, "Concept", has prefill attend with the whole block of prompt
  *     queries) run on a query-tiled kernel: one workgroup per 128 query rows
- *     of a (sequence, kv head) over the whole visible KV range, no split
- *     (FD_PATH_PREFILL; f16 / bf16 only).  f16 needs no workspace; bf16
- *     takes one of fd_plan_t.workspace_bytes (about the size of the V
- *     slices): two passes ahead of the kernel write V there as f16 under a
- *     power-of-two scale per (sequence, kv head), exact for every value
- *     above 2^-28 of the slice's largest |V|, so the value product runs on
- *     f16 with one probability product.
+ *     of a (sequence, kv head) and KV split (FD_PATH_PREFILL; f16 / bf16
+ *     only).  The planner splits the KV axis only when the row tiles alone
+ *     leave the device short of workgroups (few queries over a long cache,
+ *     or a ragged batch, planned for its longest sequence T); the splits'
+ *     partials are then merged by the combine kernel, as in decode, and
+ *     n_splits > 0 asks for that many splits.  The workspace
+ *     (fd_plan_t.workspace_bytes) holds, for bf16, V converted by two passes
+ *     ahead of the kernel to f16 under a power-of-two scale per (sequence,
+ *     kv head) -- exact for every value above 2^-28 of the slice's largest
+ *     |V|, so the value product runs on f16 with one probability product;
+ *     about the size of the V slices -- followed, with several splits, by
+ *     the partials [B, Hkv, n_q * G, n_splits, D] and two
+ *     [B, Hkv, n_q * G, n_splits] rows.  One-split f16 calls need none.
  *   - A few FD_* environment variables, read when a call is planned, switch
  *     planner and kernel choices for measurement; every setting computes the
  *     same attention (within the tolerances above) and the defaults are the

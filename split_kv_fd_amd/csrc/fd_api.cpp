@@ -123,7 +123,10 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
     int path = o.path;
 
     // Many queries per sequence (prefill): the query-tiled kernel, one
-    // workgroup per tile of query rows over the whole KV range; no split.
+    // workgroup per tile of query rows and split of the KV axis.  The KV
+    // axis is split only when the row tiles alone give the device too few
+    // workgroups (few queries over a long cache; a ragged batch, whose
+    // lengths the host does not see, is planned for its longest sequence).
     // bf16 inputs take a workspace for V converted to f16 (two passes ahead
     // of the kernel; FD_PREFILL_VT=0 keeps V as given, a slower value
     // product in two bf16 parts).
@@ -137,18 +140,46 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
         // offsets, as contiguous slices are
         if (vt && ceil_div(T, fdk::kPrefillTokens) * fdk::kPrefillTokens * D * 2 >= (1L << 32))
             return fail(FD_ERR_UNSUPPORTED, "T=%d: the converted V of one (batch, kv head) must be < 4 GiB", T);
+        const long ntiles = ceil_div(T, fdk::kPrefillTokens);   // KV tiles of the longest sequence
+        long n = 1;
+        if (n_req > 0) {
+            n = n_req < ntiles ? n_req : ntiles;
+        } else {
+            int cus = o.num_cus;
+            if (cus == 0) {
+                fd_status_t st = device_cus(&cus);
+                if (st != FD_OK) return st;
+            }
+            // Enough workgroups for about four rounds at two per compute
+            // unit, so that ragged lengths and causal triangles even out;
+            // no split shorter than min_chunk tokens (its pipeline fill and
+            // partial write stay small against its matrix-core work).
+            const long units = (long)B * Hkv * tiles;
+            const long target = std::max(1L, env_long("FD_PREFILL_WGS", 8L * cus));
+            const long min_chunk = std::max((long)fdk::kPrefillTokens, env_long("FD_PREFILL_CHUNK_MIN", 1024));
+            if (units < target) {
+                n = ceil_div(target, units);
+                const long cap = std::max(1L, (long)T / min_chunk);
+                if (n > cap) n = cap;
+            }
+        }
+        const long chunk = ceil_div(ceil_div(T, n), fdk::kPrefillTokens) * fdk::kPrefillTokens;
+        n = ceil_div(T, chunk);
+        if (tiles * n * Hkv * B > 0x7fffffffL) return fail(FD_ERR_UNSUPPORTED, "too many query-tiled workgroups");
         std::memset(p, 0, sizeof *p);
-        p->n_splits = 1;
-        p->chunk = T;
+        p->n_splits = (int)n;
+        p->chunk = (int)(n > 1 ? chunk : T);
         p->path = FD_PATH_PREFILL;
         p->tile = fdk::kPrefillTokens;
         p->heads_per_block = fdk::kPrefillRows;
         p->head_blocks = (int)tiles;
-        p->grid[0] = (int)tiles;
+        p->grid[0] = (int)(tiles * n);
         p->grid[1] = Hkv;
         p->grid[2] = B;
         p->block = 256;
+        p->combine = n > 1;
         if (vt) p->workspace_bytes = fdk::prefill_vt_bytes(B, Hkv, T, D);
+        p->workspace_bytes += fdk::prefill_part_bytes(B, Hkv, R, D, (int)n);
         return FD_OK;
     }
     if (o.n_queries > kMaxDecodeQueries)
@@ -357,7 +388,7 @@ fd_status_t prepare(const void *q, const void *k, const void *v, const int32_t *
         part_m = reinterpret_cast<float *>(w);
         w += align256(slots * sizeof(float));
         part_l = reinterpret_cast<float *>(w);
-    } else if (c->p.n_splits > 1) {
+    } else if (c->p.n_splits > 1 && c->p.path != FD_PATH_PREFILL) {
         if (!c->o.workspace)
             return fail(FD_ERR_WORKSPACE, "plan has %d splits: a workspace of %zu bytes is required",
                         c->p.n_splits, c->p.workspace_bytes);
@@ -420,6 +451,9 @@ fd_status_t prepare(const void *q, const void *k, const void *v, const int32_t *
     cb.n_splits = c->p.n_splits;
     cb.chunk = c->p.chunk;
     cb.append = append ? 1 : 0;
+    cb.causal = s.causal;
+    // the query-tiled kernel's partials: many rows, few splits
+    cb.per_wave = c->p.path == FD_PATH_PREFILL && env_long("FD_COMBINE_ROWS", 1) == 1 ? 1 : 0;
 
     fdk::PrefillArgs &f = c->f;
     f.q = q; f.k = k; f.v = v;
@@ -435,21 +469,38 @@ fd_status_t prepare(const void *q, const void *k, const void *v, const int32_t *
     f.xcd_map = env_long("FD_PREFILL_XCD", 1) == 1 ? 1 : 0;
     f.vt_tiles = (int)ceil_div(T, fdk::kPrefillTokens);
     f.vmax_chunks = (int)ceil_div(T, fdk::kVconvChunk);
+    f.n_splits = c->p.path == FD_PATH_PREFILL ? c->p.n_splits : 1;
+    f.chunk = c->p.chunk;
+    f.part_o = f.part_m = f.part_l = nullptr;
     if (c->p.path == FD_PATH_PREFILL && c->p.workspace_bytes > 0) {
         if (!c->o.workspace)
-            return fail(FD_ERR_WORKSPACE, "query-tiled bf16 plan: a workspace of %zu bytes is required",
+            return fail(FD_ERR_WORKSPACE, "query-tiled plan: a workspace of %zu bytes is required",
                         c->p.workspace_bytes);
         if (c->o.workspace_bytes < c->p.workspace_bytes)
             return fail(FD_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", c->o.workspace_bytes,
                         c->p.workspace_bytes);
         if (!aligned(c->o.workspace, 256)) return fail(FD_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-        const size_t sl = (size_t)B * Hkv;
+        // converted V (bf16), then the split partials
+        const size_t vt_bytes = c->p.workspace_bytes - fdk::prefill_part_bytes(B, Hkv, s.R, D, c->p.n_splits);
         char *w = static_cast<char *>(c->o.workspace);
-        f.vexp = reinterpret_cast<int32_t *>(w);
-        w += align256(sl * 4);
-        f.vmax = reinterpret_cast<uint32_t *>(w);
-        w += align256(sl * f.vmax_chunks * 4);
-        f.vt = reinterpret_cast<uint16_t *>(w);
+        if (vt_bytes > 0) {
+            const size_t sl = (size_t)B * Hkv;
+            f.vexp = reinterpret_cast<int32_t *>(w);
+            f.vmax = reinterpret_cast<uint32_t *>(w + align256(sl * 4));
+            f.vt = reinterpret_cast<uint16_t *>(w + align256(sl * 4) + align256(sl * f.vmax_chunks * 4));
+        }
+        if (c->p.n_splits > 1) {
+            const size_t parts = (size_t)B * Hkv * s.R * (size_t)c->p.n_splits;
+            w += vt_bytes;
+            f.part_o = reinterpret_cast<float *>(w);
+            w += align256(parts * D * sizeof(float));
+            f.part_m = reinterpret_cast<float *>(w);
+            w += align256(parts * sizeof(float));
+            f.part_l = reinterpret_cast<float *>(w);
+            cb.part_o = f.part_o;
+            cb.part_m = f.part_m;
+            cb.part_l = f.part_l;
+        }
     }
     return FD_OK;
 }

@@ -11,8 +11,9 @@
 // splits costs one memory round trip; the global max and normaliser are
 // workgroup reductions, and the SG partial sums of each quad are added in
 // split-group order (deterministic).  Split maxima are in base-2 units (the
-// split kernel folds log2(e) into the scale).  Splits that start past a
-// sequence's length were never written and are not read.
+// split kernel folds log2(e) into the scale).  Splits that start past the
+// tokens a row sees (the sequence's length; for causal queries fewer) may
+// not have been written and are not read.
 #include "fd_kernels.h"
 
 namespace fdk {
@@ -56,7 +57,11 @@ __global__ __launch_bounds__(256) void combine(CombineArgs a) {
         Tb = Tb < 0 ? 0 : (Tb > a.T ? a.T : Tb);
     }
     Tb += a.append;                          // the appended token
-    int n = (Tb + a.chunk - 1) / a.chunk;   // splits that hold tokens
+    if (a.causal) {                          // this row's query sees fewer
+        Tb -= a.nq - 1 - qr / a.G;
+        Tb = Tb < 0 ? 0 : Tb;
+    }
+    int n = (Tb + a.chunk - 1) / a.chunk;   // splits that hold its tokens
     n = n < a.n_splits ? n : a.n_splits;
 
     const float *pm = a.part_m + (size_t)bh * a.n_splits;
@@ -128,10 +133,88 @@ __global__ __launch_bounds__(256) void combine(CombineArgs a) {
     if (t == 0 && a.lse) a.lse[orow] = L > 0.f ? (M + log2f(L)) * kLn2 : kNegInf;
 }
 
+// The same merge with one wave per partial row, four rows per workgroup:
+// for calls with many rows and few splits (the query-tiled kernel's), where
+// a workgroup per row would idle most of its lanes and pay a workgroup's
+// latency per row.  Lane i owns elements D/64 * i .. of the row; the first
+// PRE partial rows are loaded together with the split maxima (lane s holds
+// split s's max and sum), so up to PRE splits cost one memory round trip.
+// Each lane adds its splits in order, the sums are xor-shuffle reductions:
+// results are deterministic.
+template <int D>
+__global__ __launch_bounds__(256) void combine_rows(CombineArgs a) {
+    constexpr int EPL = D / 64;       // elements per lane
+    constexpr int PRE = 16;
+    typedef float vec_t __attribute__((ext_vector_type(EPL)));
+    const int lane = threadIdx.x & 63;
+    const long rows = (long)a.B * a.Hkv * a.R;
+    const long bh = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (bh >= rows) return;
+    const int b = (int)(bh / ((long)a.Hkv * a.R));
+    const int kvh = (int)(bh / a.R - (long)b * a.Hkv);
+    const int qr = (int)(bh - (bh / a.R) * a.R);
+    const size_t orow = ((size_t)b * a.nq + qr / a.G) * a.Hq + (size_t)kvh * a.G + qr % a.G;
+
+    int Tb = a.T;
+    if (a.seq_lens) {
+        Tb = a.seq_lens[b];
+        Tb = Tb < 0 ? 0 : (Tb > a.T ? a.T : Tb);
+    }
+    Tb += a.append;
+    if (a.causal) {
+        Tb -= a.nq - 1 - qr / a.G;
+        Tb = Tb < 0 ? 0 : Tb;
+    }
+    int n = (Tb + a.chunk - 1) / a.chunk;
+    n = n < a.n_splits ? n : a.n_splits;
+
+    const float *pm = a.part_m + (size_t)bh * a.n_splits;
+    const float *pl = a.part_l + (size_t)bh * a.n_splits;
+    const vec_t *po = reinterpret_cast<const vec_t *>(a.part_o + (size_t)bh * a.n_splits * D) + lane;
+
+    vec_t pre[PRE];
+#pragma unroll
+    for (int j = 0; j < PRE; ++j) pre[j] = j < n ? po[(size_t)j * (D / EPL)] : vec_t{};
+    float M = kNegInf;
+    for (int s = lane; s < n; s += 64) M = fmaxf(M, pm[s]);
+    M = wave_max(M);
+    const float mu = M == kNegInf ? 0.f : M;
+
+    float L = 0.f;
+    vec_t acc{};
+    for (int s0 = 0; s0 < n; s0 += 64) {
+        const int s = s0 + lane;
+        const float w = s < n ? __builtin_amdgcn_exp2f(pm[s] - mu) : 0.f;
+        L += s < n ? w * pl[s] : 0.f;
+        const int cnt = n - s0 < 64 ? n - s0 : 64;
+        int j = 0;
+        if (s0 == 0) {
+#pragma unroll
+            for (; j < PRE; ++j)
+                if (j < cnt) acc += __shfl(w, j) * pre[j];
+        }
+        for (; j < cnt; ++j) acc += __shfl(w, j) * po[(size_t)(s0 + j) * (D / EPL)];
+    }
+    L = wave_sum(L);
+    const vec_t o = L > 0.f ? acc / L : vec_t{};
+    reinterpret_cast<vec_t *>(a.out + orow * D)[lane] = o;
+    if (lane == 0 && a.lse) a.lse[orow] = L > 0.f ? (M + log2f(L)) * kLn2 : kNegInf;
+}
+
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs &a, hipStream_t stream) {
-    const dim3 grid(a.B * a.Hkv * a.R);
+    const long rows = (long)a.B * a.Hkv * a.R;
+    if (a.per_wave) {
+        const dim3 grid((unsigned)((rows + 3) / 4));
+        switch (a.D) {
+        case 64: hipLaunchKernelGGL(combine_rows<64>, grid, dim3(256), 0, stream, a); break;
+        case 128: hipLaunchKernelGGL(combine_rows<128>, grid, dim3(256), 0, stream, a); break;
+        default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
+    const dim3 grid((unsigned)rows);
     switch (a.D) {
     case 64: hipLaunchKernelGGL(combine<64>, grid, dim3(256), 0, stream, a); break;
     case 128: hipLaunchKernelGGL(combine<128>, grid, dim3(256), 0, stream, a); break;

@@ -82,6 +82,9 @@ struct CombineArgs {
     int Hkv, G, nq, R;           // partial row p = (b * Hkv + kv head) * R + row
     int n_splits, chunk;
     int append;                  // sequences hold seq_lens[b] + 1 tokens
+    int causal;                  // query r / G sees T_b - (nq - 1 - r / G) tokens:
+                                 // only splits that start below that are read
+    int per_wave;                // 1: one wave per row (many rows, few splits)
 };
 
 // Shape constants of the vector-ALU split kernel.  Each 64-lane wavefront
@@ -116,8 +119,10 @@ hipError_t launch_split_mfma(const SplitArgs &a, int dtype, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t stream);
 
 // Many queries per sequence (prefill): one workgroup per tile of
-// kPrefillRows query rows of one (batch, kv head), over the whole visible
-// KV range in tiles of kPrefillTokens tokens staged in LDS.
+// kPrefillRows query rows of one (batch, kv head) and split of the KV axis,
+// over the split's visible tokens in tiles of kPrefillTokens tokens staged
+// in LDS.  With one split the workgroup normalises and writes out / lse;
+// with several it leaves partials in the combine kernel's layout.
 #ifndef FD_PREFILL_NB
 #define FD_PREFILL_NB 2
 #endif
@@ -137,6 +142,15 @@ struct PrefillArgs {
     int R;                       // query rows per kv head = nq * G
     int row_tiles;               // ceil(R / kPrefillRows)
     int causal;                  // query i sees the first T_b - (nq - 1 - i) tokens
+    // KV splits: split s covers tokens [s * chunk, (s + 1) * chunk), chunk a
+    // multiple of kPrefillTokens.  n_splits > 1 writes unnormalised partials
+    // (row p = (b * Hkv + kv head) * R + query row, slot p * n_splits + s);
+    // a split a row tile sees nothing of is skipped (the combine reads a
+    // row's splits only up to its visible length).
+    int n_splits, chunk;
+    float *part_o;               // [B, Hkv, R, n_splits, D]
+    float *part_m;               // [B, Hkv, R, n_splits], log2 units
+    float *part_l;               // [B, Hkv, R, n_splits]
     int page_size, page_shift, max_pages, num_pages;
     float scale_log2;
     // bf16 inputs: V converted to f16 under a per-(batch, kv head) power-of-
@@ -158,6 +172,15 @@ inline size_t prefill_vt_bytes(int B, int Hkv, int T, int D) {
     const size_t tiles = ((size_t)T + kPrefillTokens - 1) / kPrefillTokens;
     const size_t chunks = ((size_t)T + kVconvChunk - 1) / kVconvChunk;
     return a256(sl * 4) + a256(sl * chunks * 4) + a256(sl * tiles * D * kPrefillTokens * 2);
+}
+
+// Partials of a query-tiled call with n_splits > 1 (after the converted V
+// pieces, if any): part_o, part_m, part_l, 256-byte aligned.
+inline size_t prefill_part_bytes(int B, int Hkv, int R, int D, int n_splits) {
+    if (n_splits <= 1) return 0;
+    auto a256 = [](size_t x) { return (x + 255) / 256 * 256; };
+    const size_t parts = (size_t)B * Hkv * R * (size_t)n_splits;
+    return a256(parts * D * 4) + 2 * a256(parts * 4);
 }
 
 hipError_t launch_prefill(const PrefillArgs &a, int dtype, hipStream_t stream);

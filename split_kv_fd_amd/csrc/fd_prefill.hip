@@ -10,6 +10,12 @@
 // reads the same K and V -- and walks the visible KV range in tiles of
 // kPrefillTokens tokens with an online softmax (the same running max / sum
 // / unnormalised accumulator as the split pass), then divides once.
+// Where row tiles alone leave the device short of work (few queries over a
+// long cache, or a ragged batch whose longest sequence would set the time),
+// the KV axis is split as in decode: a workgroup then covers one split and
+// leaves the unnormalised partial with its max and sum, and the combine
+// kernel merges a row's splits (tinyvolt "Kernel visualization: Flash
+// Decoding", "Combine kernel").
 //
 // Per KV tile, staged in LDS by the whole workgroup (three buffers: tile j
 // being consumed, tile j+1 being read for its logits, tile j+2 being
@@ -142,17 +148,28 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
     const int i16 = lane & 15;
     const int kb = lane >> 4;
 
-    // Work item of this workgroup.  Workgroups are dealt to the 8 XCDs
-    // round-robin by linear id; with xcd_map each XCD instead walks one
-    // contiguous run of (batch, kv head, row tile) items, so the workgroups
-    // it runs at once share a K/V slice that its own L2 holds.  Within a
-    // slice causal tiles run longest first.
-    const int n_wg = (int)(gridDim.x * gridDim.y * gridDim.z);
+    // Work item of this workgroup: a K/V range -- (batch, kv head, KV split),
+    // numbered split-major -- and a row tile.  Workgroups are dealt to the 8
+    // XCDs round-robin by linear id.  With xcd_map, XCD x instead runs the
+    // ranges x, x + 8, x + 16, ... in turn, all row tiles of one range
+    // back to back: the workgroups it runs at once share a K/V range that
+    // its own L2 holds, and the ranges of every sequence and split spread
+    // evenly over the XCDs (consecutive kv heads of one split land on
+    // different XCDs), however ragged the lengths.  Ranges past the last
+    // multiple of 8 keep the plain order.  Within a range causal tiles run
+    // longest first.
     const int lin = (int)(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
-    const int per_xcd = n_wg / 8;
-    const int item = (a.xcd_map && lin < 8 * per_xcd) ? (lin % 8) * per_xcd + lin / 8 : lin;
+    const int n_rng = a.B * a.Hkv * a.n_splits;
+    const int mapped = (n_rng / 8) * 8 * a.row_tiles;
+    int item = lin;
+    if (a.xcd_map && lin < mapped) {
+        const int g = lin / 8;
+        item = ((lin % 8) + 8 * (g / a.row_tiles)) * a.row_tiles + g % a.row_tiles;
+    }
     const int tile_i = item % a.row_tiles;
-    const int slc = item / a.row_tiles;
+    const int rng = item / a.row_tiles;
+    const int split = rng / (a.B * a.Hkv);
+    const int slc = rng - split * (a.B * a.Hkv);
     const int tile = a.causal ? a.row_tiles - 1 - tile_i : tile_i;
     const int kvh = slc % a.Hkv;
     const int b = slc / a.Hkv;
@@ -209,11 +226,19 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
         }
     }
 
-    // Tokens the workgroup's rows see at most.
+    // Tokens the workgroup's rows see at most, and its tiles [j0, j1) of
+    // them: the split's.
     const int r_last = min(r0 + kPrefillRows, a.R) - 1;
     int seen = a.causal ? Tb - (a.nq - 1 - r_last / a.G) : Tb;
     seen = seen < 0 ? 0 : seen;
-    const int nt = (seen + NTOK - 1) / NTOK;
+    const bool parts = a.n_splits > 1;
+    const int j0 = parts ? split * (a.chunk / NTOK) : 0;
+    int j1 = (seen + NTOK - 1) / NTOK;
+    if (parts) {
+        j1 = min(j1, j0 + a.chunk / NTOK);
+        if (j1 <= j0) return;    // no row of the tile sees this split: never read
+    }
+    const int nt = j1 - j0;
 
     // Loader: thread t moves tokens 2u, 2u+1 of the tile, piece p of each
     // (with D = 64 two threads share a piece and store the same bytes).  V
@@ -526,29 +551,31 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
     using B0 = std::integral_constant<int, 0>;
     using B1 = std::integral_constant<int, 1>;
     using B2 = std::integral_constant<int, 2>;
+    // Tiles are numbered from the sequence start (masks and loads use that
+    // index); LDS buffers count from the split's first tile.
     if (nt > 0) {
         if constexpr (PAGED) {
-            Regs g0 = load_tile(0);
+            Regs g0 = load_tile(j0);
             ok_cur = tile_bits(g0);
             store_tile(0, g0);
-            Regs g1 = load_tile(1);
+            Regs g1 = load_tile(j0 + 1);
             ok_next = tile_bits(g1);
             store_tile(1, g1);
         } else {
-            store_tile(0, load_tile(0));
-            store_tile(1, load_tile(1));
+            store_tile(0, load_tile(j0));
+            store_tile(1, load_tile(j0 + 1));
         }
-        g = load_tile(2);
+        g = load_tile(j0 + 2);
         __syncthreads();
         qk(0, cA);
         int j = 0;
         for (; j + 3 <= nt; j += 3) {
-            step(B0{}, j, cA, cB);
-            step(B1{}, j + 1, cB, cC);
-            step(B2{}, j + 2, cC, cA);
+            step(B0{}, j0 + j, cA, cB);
+            step(B1{}, j0 + j + 1, cB, cC);
+            step(B2{}, j0 + j + 2, cC, cA);
         }
-        if (j < nt) step(B0{}, j, cA, cB);
-        if (j + 1 < nt) step(B1{}, j + 1, cB, cC);
+        if (j < nt) step(B0{}, j0 + j, cA, cB);
+        if (j + 1 < nt) step(B1{}, j0 + j + 1, cB, cC);
     }
 
     // The four lanes of a row share m; their sums cover different tokens.
@@ -560,6 +587,25 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
         bool ok;
         const size_t qrow = row_of(nb, ok);
         if (!ok) continue;
+        if (parts) {
+            // unnormalised partial of this split, in the units of V; with the
+            // bias moved into the max, l = sum 2^(s - m) and o = sum 2^(s - m) v
+            const size_t pr = ((size_t)slc * a.R + (r0 + 16 * (NB * wave + nb) + i16)) * a.n_splits + split;
+#pragma unroll
+            for (int dt = 0; dt < DT16; ++dt) {
+                f32x4_v o = acc[nb][dt];
+                if constexpr (VT) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[e] = __builtin_amdgcn_ldexpf(o[e], -vexp);
+                }
+                *reinterpret_cast<float4 *>(a.part_o + pr * D + 16 * dt + 4 * kb) = make_float4(o[0], o[1], o[2], o[3]);
+            }
+            if (kb == 0) {
+                a.part_m[pr] = m[nb] == kNegInf ? kNegInf : m[nb] - kPBias;
+                a.part_l[pr] = L;
+            }
+            continue;
+        }
         const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
         for (int dt = 0; dt < DT16; ++dt) {
@@ -685,7 +731,7 @@ __global__ __launch_bounds__(256) void vconv_pass(PrefillArgs a) {
 
 template <int DT, int D>
 hipError_t launch_dim(const PrefillArgs &a, hipStream_t stream) {
-    const dim3 grid(a.row_tiles, a.Hkv, a.B);
+    const dim3 grid(a.row_tiles * a.n_splits, a.Hkv, a.B);
     if constexpr (DT == FD_BF16) {
         if (a.vt) {
             const dim3 pgrid(a.vmax_chunks, a.Hkv, a.B);

@@ -288,28 +288,63 @@ def test_several_queries_rejects(lib):
     assert st == fd.FD_ERR_UNSUPPORTED
 
 
+def _query_tiled_splits(units, T, cus=256, n_req=0):
+    """The planner's KV split rule for the query-tiled kernel, restated:
+    about 8 * cus workgroups (four rounds at two per compute unit), no split
+    below 1024 tokens; chunks are whole 32-token tiles."""
+    if n_req > 0:
+        n = min(n_req, -(-T // 32))
+    else:
+        target = 8 * cus
+        n = 1 if units >= target else min(-(-target // units), max(1, T // 1024))
+    chunk = -(-(-(-T // n)) // 32) * 32
+    return -(-T // chunk), chunk
+
+
 @pytest.mark.parametrize("nq,G", [(17, 1), (100, 4), (4096, 8), (65536, 1)])
 def test_plan_query_tiled(lib, nq, G):
     # more than 16 queries per sequence: one workgroup per 128 query rows of
-    # each (sequence, kv head), the whole KV range, no split; f16 takes no
-    # workspace, bf16 one for V converted to f16 (scale exponents, chunk
-    # maxima, transposed tiles; 256-byte aligned pieces)
-    B, Hkv = 2, 2
-    st, p = plan(B, G * Hkv, Hkv, 8192, 128, 0, n_queries=nq, causal=1, dtype=fd.FD_F16)
-    assert st == fd.FD_OK, fd.fd_last_error()
-    assert p.path == fd.FD_PATH_PREFILL and p.n_splits == 1 and p.workspace_bytes == 0
-    st, p = plan(B, G * Hkv, Hkv, 8192, 128, 0, n_queries=nq, causal=1)
-    assert st == fd.FD_OK, fd.fd_last_error()
+    # each (sequence, kv head) and KV split; the KV axis is split only while
+    # the row tiles leave the device short of workgroups.  bf16 takes a
+    # workspace for V converted to f16 (scale exponents, chunk maxima,
+    # transposed tiles; 256-byte aligned pieces), and with several splits
+    # the partials follow it
+    B, Hkv, T, D = 2, 2, 8192, 128
     a256 = lambda x: -(-x // 256) * 256
     sl = B * Hkv
-    assert p.path == fd.FD_PATH_PREFILL and p.n_splits == 1
-    assert p.workspace_bytes == a256(sl * 4) + a256(sl * (8192 // 256) * 4) + a256(sl * 8192 * 128 * 2)
-    assert not p.fused and not p.combine and not p.stream
-    tiles = -(-(nq * G) // 128)
-    assert (p.grid[0], p.grid[1], p.grid[2]) == (tiles, Hkv, B) and p.head_blocks == tiles
+    R = nq * G
+    tiles = -(-R // 128)
+    n, chunk = _query_tiled_splits(B * Hkv * tiles, T)
+    parts = sl * R * n
+    part_bytes = (a256(parts * D * 4) + 2 * a256(parts * 4)) if n > 1 else 0
+    st, p = plan(B, G * Hkv, Hkv, T, D, 0, n_queries=nq, causal=1, dtype=fd.FD_F16)
+    assert st == fd.FD_OK, fd.fd_last_error()
+    assert p.path == fd.FD_PATH_PREFILL and p.n_splits == n and p.workspace_bytes == part_bytes
+    st, p = plan(B, G * Hkv, Hkv, T, D, 0, n_queries=nq, causal=1)
+    assert st == fd.FD_OK, fd.fd_last_error()
+    assert p.path == fd.FD_PATH_PREFILL and p.n_splits == n
+    assert p.workspace_bytes == a256(sl * 4) + a256(sl * (T // 256) * 4) + a256(sl * T * D * 2) + part_bytes
+    assert not p.fused and not p.stream and p.combine == (n > 1)
+    assert (p.grid[0], p.grid[1], p.grid[2]) == (tiles * n, Hkv, B) and p.head_blocks == tiles
+    if n > 1:
+        assert p.chunk == chunk and p.chunk % 32 == 0 and (n - 1) * chunk < T
     # forced for a few queries too
-    st, p = plan(B, G * Hkv, Hkv, 8192, 128, 0, n_queries=2, path=fd.FD_PATH_PREFILL)
+    st, p = plan(B, G * Hkv, Hkv, T, D, 0, n_queries=2, path=fd.FD_PATH_PREFILL)
     assert st == fd.FD_OK and p.path == fd.FD_PATH_PREFILL
+
+
+@pytest.mark.parametrize("n_req", [1, 2, 5, 7, 300, 100000])
+def test_plan_query_tiled_explicit_splits(lib, n_req):
+    # an explicit split count is taken as asked, capped at one 32-token tile
+    # per split; the effective count covers T with no empty split
+    B, Hkv, G, T, D, nq = 1, 8, 4, 4000, 128, 512
+    n, chunk = _query_tiled_splits(0, T, n_req=n_req)
+    st, p = plan(B, G * Hkv, Hkv, T, D, n_req, n_queries=nq, causal=1)
+    assert st == fd.FD_OK, fd.fd_last_error()
+    assert p.path == fd.FD_PATH_PREFILL and p.n_splits == n and p.combine == (n > 1)
+    if n > 1:
+        assert p.chunk == chunk and (n - 1) * chunk < T <= n * chunk
+    assert p.grid[0] == 16 * n
 
 
 def append(q=A, kn=A + 8192, vn=A + 16384, k=A, v=A, pt=None, sl=A, out=A, lse=A, shape=(1, 4, 4, 4096, 128),
@@ -362,5 +397,7 @@ def test_plan_query_tiled_size_limits(lib):
     assert st == fd.FD_ERR_UNSUPPORTED and "4 GiB" in fd.fd_last_error()
     st, _ = plan(1, 8, 2, T - 64, 128, 0, **kw)
     assert st == fd.FD_OK, fd.fd_last_error()
-    st, p = plan(1, 8, 2, T, 128, 0, dtype=fd.FD_F16, **kw)   # f16 needs no conversion
-    assert st == fd.FD_OK and p.workspace_bytes == 0
+    st, p = plan(1, 8, 2, T, 128, 1, dtype=fd.FD_F16, **kw)   # f16 needs no conversion
+    assert st == fd.FD_OK and p.n_splits == 1 and p.workspace_bytes == 0
+    st, p = plan(1, 8, 2, T, 128, 0, dtype=fd.FD_F16, **kw)   # two row tiles: the KV axis is split
+    assert st == fd.FD_OK and p.n_splits == 512 and p.workspace_bytes > 0

@@ -216,3 +216,126 @@ def test_prefill_work_order_does_not_change_results(env_switch, dtype):
         torch.cuda.synchronize()
         res.append((out.clone(), lse.clone()))
     assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+
+
+# ------------------------------------------------------------------ KV splits of the query-tiled kernel
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f16", 128), ("bf16", 64), ("f16", 64)])
+@pytest.mark.parametrize("n", [2, 3, 7, 64])
+def test_prefill_kv_splits(causal, dtype, D, n):
+    # the KV axis split n ways (chunks of whole 32-token tiles; the last
+    # split short, some splits past a short sequence's end or past what a
+    # causal row tile sees), partials merged by the combine kernel; an empty
+    # sequence and one shorter than the query count.  The workspace starts
+    # as 0xFF bytes (NaN partials): a merge that read an unwritten split
+    # would show
+    case = contiguous("gqa128k_bf16", [1500, 37, 0, 777, 1200], Hq=8, Hkv=2, T=1500, D=D, dtype=dtype)
+    q = inputs.make_q_multi(case.spec, 150).to(DEV)
+    plan = check_multi(case, q, causal, n_splits=n, what=f"prefill splits n={n} {dtype} D={D} causal={causal}")
+    chunk = -(-(-(-1500 // n)) // 32) * 32          # whole tiles: 64 asked gives 47 splits of 32 tokens
+    assert plan["path"] == "prefill" and plan["n_splits"] == -(-1500 // chunk) and plan["combine"]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_prefill_kv_splits_paged(causal):
+    for P in (1, 16, 256):
+        s = inputs.spec("paged_ragged_bf16", B=3, Hq=8, Hkv=2, T=2000, page_size=P, len_lo=50, len_hi=2000)
+        case = inputs.make_case(s).to(DEV)
+        q = inputs.make_q_multi(s, 48).to(DEV)
+        for n in (2, 5):
+            plan = check_multi(case, q, causal, n_splits=n, what=f"prefill splits paged P={P} n={n} causal={causal}")
+            assert plan["path"] == "prefill" and plan["n_splits"] == n
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_prefill_kv_splits_split_p_form(env_switch, causal):
+    # bf16 V read as given (P in two bf16 parts, no conversion): the
+    # partials carry no conversion scale and no probability bias
+    env_switch.setenv("FD_PREFILL_VT", "0")
+    case = contiguous("gqa128k_bf16", [1000, 300, 0], Hq=8, Hkv=2, T=1000)
+    q = inputs.make_q_multi(case.spec, 64).to(DEV)
+    plan = check_multi(case, q, causal, n_splits=4, what=f"prefill splits bf16 split P causal={causal}")
+    assert plan["path"] == "prefill" and plan["n_splits"] == 4
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_prefill_auto_splits_few_queries_long_cache(dtype):
+    # 64 queries after an 8k-token prefix: one row tile per kv head, so the
+    # planner splits the KV axis (a chunked-prefill step)
+    case = contiguous("gqa128k_bf16", [8192, 5000], Hq=8, Hkv=2, T=8192, dtype=dtype)
+    q = inputs.make_q_multi(case.spec, 64).to(DEV)
+    for causal in (False, True):
+        plan = check_multi(case, q, causal, what=f"prefill auto splits {dtype} causal={causal}")
+        assert plan["path"] == "prefill" and plan["n_splits"] > 1
+
+
+@pytest.mark.parametrize("scale", [-0.3, 2.0])
+def test_prefill_kv_splits_scale(scale):
+    # negative scales (folded into q) and sharp softmaxes, whose running
+    # maxima differ much between splits, through the merge
+    case = contiguous("gqa128k_bf16", [1100, 400], Hq=8, Hkv=2, T=1100)
+    q = inputs.make_q_multi(case.spec, 40).to(DEV)
+    host = case.to("cpu")
+    for causal in (False, True):
+        ref_out, ref_lse = oracle_mod.default().decode_multi(q.cpu(), host.k, host.v, scale, causal=causal,
+                                                             seq_lens=host.seq_lens)
+        dec = Decoder(q, case.k, case.v, scale=scale, seq_lens=case.seq_lens, causal=causal, n_splits=6)
+        assert dec.plan["path"] == "prefill" and dec.plan["n_splits"] == 6
+        parity.announce(f"prefill splits scale={scale} causal={causal}")
+        out, lse = dec()
+        torch.cuda.synchronize()
+        parity.compare(case, out.cpu().double().numpy(), lse.cpu().double().numpy(), ref_out, ref_lse,
+                       parity.max_abs_v(host), f"prefill splits scale={scale} causal={causal}")
+
+
+def test_prefill_kv_splits_separate_entry_points():
+    # fd_split then fd_combine give fd_decode's result bit for bit, and the
+    # same plan run twice gives identical bits
+    case = contiguous("gqa128k_bf16", [900, 450], Hq=8, Hkv=2, T=900)
+    q = inputs.make_q_multi(case.spec, 80).to(DEV)
+    dec = Decoder(q, case.k, case.v, scale=case.spec.scale, seq_lens=case.seq_lens, causal=True, n_splits=3)
+    out_a, lse_a = (x.clone() for x in dec())
+    dec.out.fill_(float("nan"))
+    dec.lse.fill_(float("nan"))
+    dec.split()
+    dec.combine()
+    torch.cuda.synchronize()
+    assert torch.equal(out_a, dec.out) and torch.equal(lse_a, dec.lse)
+    out_c, lse_c = dec()
+    torch.cuda.synchronize()
+    assert torch.equal(out_a, out_c) and torch.equal(lse_a, lse_c)
+
+
+def test_prefill_ragged_full_size_sampled():
+    # the paged ragged workload's shape (16-token pages, lengths from 1k to
+    # 64k) with 512 causal queries per sequence, B=4: the automatic plan
+    # splits the KV axis; sampled (sequence, query) rows against the oracle
+    s = inputs.spec("paged_ragged_bf16", B=4)
+    case = inputs.make_case(s, device=DEV)
+    nq = 512
+    q = inputs.make_q_multi(s, nq, device=DEV)
+    dec = Decoder(q, case.k, case.v, scale=s.scale, page_table=case.page_table, seq_lens=case.seq_lens,
+                  T=s.T, causal=True)
+    assert dec.plan["path"] == "prefill" and dec.plan["n_splits"] > 1
+    parity.announce(f"prefill ragged full size nq={nq} plan={dec.plan}")
+    out, lse = dec()
+    torch.cuda.synchronize()
+    orc = oracle_mod.default()
+    lens = case.lengths()
+    g = torch.Generator().manual_seed(13)
+    for b in range(s.B):
+        n = -(-lens[b] // s.page_size)
+        pages = case.page_table[b, :n].long()
+        k_h, v_h = case.k[pages].cpu(), case.v[pages].cpu()
+        table = torch.arange(n, dtype=torch.int32)[None]
+        vmax = float(v_h.abs().max())
+        for i in [0, nq - 1] + torch.randint(0, nq, (2,), generator=g).tolist():
+            L = lens[b] - (nq - 1 - i)
+            ref, ref_l = orc.decode(q[b:b + 1, i].cpu(), k_h, v_h, s.scale, page_table=table,
+                                    seq_lens=np.array([L], np.int32))
+            got = out[b, i].cpu().double().numpy()
+            err = float(np.max(np.abs(got - ref[0]))) / vmax
+            lerr = float(np.max(np.abs(lse[b, i].cpu().double().numpy() - ref_l[0])))
+            parity.announce(f"prefill ragged b={b} T_b={lens[b]} query={i}: err {err:.2e} lse {lerr:.2e}")
+            assert err <= parity.OUT_TOL["bf16"] and lerr <= parity.LSE_TOL["bf16"]
