@@ -148,7 +148,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default=DEFAULT_WORKLOAD)
     ap.add_argument("--n-splits", type=int, default=0, help="0 = the planner's choice")
-    ap.add_argument("--path", default=None, choices=[None, "auto", "valu", "mfma"])
+    ap.add_argument("--path", default=None, choices=[None, "auto", "valu", "mfma", "prefill"])
     ap.add_argument("--merge", default="auto", choices=["auto", "fused", "combine"],
                     help="force the fused merge or the combine kernel (default: library's choice)")
     ap.add_argument("--event-every", type=int, default=8,

@@ -38,20 +38,24 @@
  *     (the queries are the sequence's last n_q cached tokens, as in
  *     verifying a draft); a query with no token yields out = 0, lse = -inf.
  *     Up to 16 queries run on the split-KV kernels (every query row of a kv
- *     head shares one read of K / V); more (the prefill phase: the dupenodi
- *     guide, "Concept", has prefill attend with the whole block of prompt
- *     queries) run on a query-tiled kernel: one workgroup per 128 query rows
- *     of a (sequence, kv head) and KV split (FD_PATH_PREFILL; f16 / bf16
- *     only).  The planner splits the KV axis only when the row tiles alone
- *     leave the device short of workgroups (few queries over a long cache,
- *     or a ragged batch, planned for its longest sequence T); the splits'
+ *     head shares one read of K / V), as long as a kv head has at most 32
+ *     query rows (n_q * G) or the inputs are fp32; more queries (the
+ *     prefill phase: the dupenodi guide, "Concept", has prefill attend with
+ *     the whole block of prompt queries), or more rows, run on a query-tiled
+ *     kernel: one workgroup per 128 query rows of a (sequence, kv head) and
+ *     KV split (FD_PATH_PREFILL; f16 / bf16 only).  The planner splits the
+ *     KV axis only when the row tiles alone leave the device short of
+ *     workgroups (few queries over a long cache, or a ragged batch, planned
+ *     for its longest sequence T); the splits'
  *     partials are then merged by the combine kernel, as in decode, and
  *     n_splits > 0 asks for that many splits.  The workspace
- *     (fd_plan_t.workspace_bytes) holds, for bf16, V converted by two passes
- *     ahead of the kernel to f16 under a power-of-two scale per (sequence,
- *     kv head) -- exact for every value above 2^-28 of the slice's largest
- *     |V|, so the value product runs on f16 with one probability product;
- *     about the size of the V slices -- followed, with several splits, by
+ *     (fd_plan_t.workspace_bytes) holds, for bf16 with at least 1024 query
+ *     rows per kv head, V converted by two passes ahead of the kernel to f16
+ *     under a power-of-two scale per (sequence, kv head) -- exact for every
+ *     value above 2^-28 of the slice's largest |V|, so the value product
+ *     runs on f16 with one probability product; about the size of the V
+ *     slices (fewer rows keep bf16 V and split the probabilities into two
+ *     bf16 parts instead) -- followed, with several splits, by
  *     the partials [B, Hkv, n_q * G, n_splits, D] and two
  *     [B, Hkv, n_q * G, n_splits] rows.  One-split f16 calls need none.
  *   - A few FD_* environment variables, read when a call is planned, switch
@@ -131,7 +135,8 @@ typedef struct fd_options {
     void *stream;               /* hipStream_t to launch on; NULL = null stream */
     int32_t n_queries;          /* queries per sequence, 1 .. 65536 (0 = 1);  */
                                 /* > 1 gives q / out an n_q axis (see below); */
-                                /* > 16 runs the query-tiled kernel          */
+                                /* > 16 (or > 32 query rows per kv head,     */
+                                /* f16 / bf16) runs the query-tiled kernel   */
     int32_t causal;             /* with n_queries > 1: 1 = query i sees the   */
                                 /* first T_b - (n_queries - 1 - i) tokens     */
 } fd_options_t;
@@ -161,7 +166,7 @@ typedef struct fd_plan {
                                 /* always inside the split launch             */
     int32_t reserved;
     size_t workspace_bytes;     /* workspace this call needs (0 for one split,  */
-                                /* except bf16 query-tiled plans)               */
+                                /* except bf16 query-tiled plans that convert V) */
 } fd_plan_t;
 
 /* Fill *opt with defaults: dtype bf16, contiguous cache, automatic path,

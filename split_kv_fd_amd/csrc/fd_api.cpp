@@ -46,6 +46,15 @@ long env_long(const char *name, long dflt) {
 constexpr uint32_t kOptionsV1 = sizeof(fd_options_t);
 constexpr int kMaxQueries = 65536;       // queries per sequence
 constexpr int kMaxDecodeQueries = 16;    // more take the query-tiled (prefill) kernel
+// More query rows per kv head than the matrix-core split kernel covers in
+// one K/V read (two 16-row blocks) take the query-tiled kernel too
+// (f16 / bf16): it reads K/V once for 128 rows.
+constexpr int kMaxSplitRows = 32;
+// bf16 V is converted to f16 for the query-tiled kernel's value product
+// from this many query rows per kv head: the conversion reads V twice and
+// writes it once, which the cheaper product repays only when many rows
+// share each V tile (measured crossover near 1024 rows).
+constexpr int kConvertRows = 1024;
 
 // Compute units of the current device, cached per device id.
 fd_status_t device_cus(int *cus) {
@@ -122,20 +131,24 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
     const int R = o.n_queries * G;       // query rows per kv head
     int path = o.path;
 
-    // Many queries per sequence (prefill): the query-tiled kernel, one
-    // workgroup per tile of query rows and split of the KV axis.  The KV
-    // axis is split only when the row tiles alone give the device too few
-    // workgroups (few queries over a long cache; a ragged batch, whose
+    // Many queries per sequence (prefill), or more query rows per kv head
+    // than one matrix-core split workgroup holds: the query-tiled kernel,
+    // one workgroup per tile of query rows and split of the KV axis.  The
+    // KV axis is split only when the row tiles alone give the device too
+    // few workgroups (few queries over a long cache; a ragged batch, whose
     // lengths the host does not see, is planned for its longest sequence).
-    // bf16 inputs take a workspace for V converted to f16 (two passes ahead
-    // of the kernel; FD_PREFILL_VT=0 keeps V as given, a slower value
-    // product in two bf16 parts).
-    if (path == FD_PATH_PREFILL || (path == FD_PATH_AUTO && o.n_queries > kMaxDecodeQueries)) {
+    // bf16 inputs with many rows take a workspace for V converted to f16
+    // (two passes ahead of the kernel); with fewer, V is read as given and
+    // P enters the value product in two bf16 parts.  FD_PREFILL_VT=0 / 1
+    // forces either form.
+    const bool many_rows = o.dtype != FD_F32 && R > kMaxSplitRows && !(o.flags & FD_FLAG_APPEND);
+    if (path == FD_PATH_PREFILL ||
+        (path == FD_PATH_AUTO && (o.n_queries > kMaxDecodeQueries || many_rows))) {
         if (o.dtype == FD_F32) return fail(FD_ERR_UNSUPPORTED, "the query-tiled kernel needs f16 or bf16 inputs");
         if (o.flags & FD_FLAG_APPEND) return fail(FD_ERR_UNSUPPORTED, "fd_append_decode takes one query per sequence");
         const long tiles = ceil_div(R, fdk::kPrefillRows);
         if (Hkv > 65535) return fail(FD_ERR_UNSUPPORTED, "Hkv=%d > 65535", Hkv);
-        const bool vt = o.dtype == FD_BF16 && env_long("FD_PREFILL_VT", 1) == 1;
+        const bool vt = o.dtype == FD_BF16 && env_long("FD_PREFILL_VT", R >= kConvertRows ? 1 : 0) == 1;
         // the converted V of one (batch, kv head) is addressed with 32-bit
         // offsets, as contiguous slices are
         if (vt && ceil_div(T, fdk::kPrefillTokens) * fdk::kPrefillTokens * D * 2 >= (1L << 32))
@@ -150,12 +163,17 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
                 fd_status_t st = device_cus(&cus);
                 if (st != FD_OK) return st;
             }
-            // Enough workgroups for about four rounds at two per compute
-            // unit, so that ragged lengths and causal triangles even out;
-            // no split shorter than min_chunk tokens (its pipeline fill and
-            // partial write stay small against its matrix-core work).
+            // Several row tiles per kv head (bound by the matrix cores), or
+            // a paged (ragged) batch: enough workgroups for about four
+            // rounds at two per compute unit, so that ragged lengths and
+            // causal triangles even out.  One row tile of a contiguous cache
+            // (a few queries: bound by K/V reads): about two rounds, as
+            // longer splits stream more efficiently.  No split shorter than
+            // min_chunk tokens (its pipeline fill and partial write stay
+            // small against its work).
             const long units = (long)B * Hkv * tiles;
-            const long target = std::max(1L, env_long("FD_PREFILL_WGS", 8L * cus));
+            const long dflt = (tiles > 1 || paged ? 8L : 4L) * cus;
+            const long target = std::max(1L, env_long("FD_PREFILL_WGS", dflt));
             const long min_chunk = std::max((long)fdk::kPrefillTokens, env_long("FD_PREFILL_CHUNK_MIN", 1024));
             if (units < target) {
                 n = ceil_div(target, units);

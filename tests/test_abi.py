@@ -264,6 +264,9 @@ def test_plan_several_queries(lib, nq):
         st, p = plan(B, G * Hkv, Hkv, T, D, 0, dtype=dt, n_queries=nq)
         assert st == fd.FD_OK, fd.fd_last_error()
         R = nq * G
+        if dt != fd.FD_F32 and R > 32:      # past one matrix-core workgroup's rows
+            assert p.path == fd.FD_PATH_PREFILL
+            continue
         want_mfma = dt != fd.FD_F32 and R >= 4
         assert p.path == (fd.FD_PATH_MFMA if want_mfma else fd.FD_PATH_VALU)
         assert p.heads_per_block * p.head_blocks >= R > p.heads_per_block * (p.head_blocks - 1)
@@ -288,14 +291,15 @@ def test_several_queries_rejects(lib):
     assert st == fd.FD_ERR_UNSUPPORTED
 
 
-def _query_tiled_splits(units, T, cus=256, n_req=0):
+def _query_tiled_splits(units, T, cus=256, n_req=0, tiles=2):
     """The planner's KV split rule for the query-tiled kernel, restated:
-    about 8 * cus workgroups (four rounds at two per compute unit), no split
-    below 1024 tokens; chunks are whole 32-token tiles."""
+    about 8 * cus workgroups (four rounds at two per compute unit; 4 * cus
+    with one row tile per kv head of a contiguous cache), no split below
+    1024 tokens; chunks are whole 32-token tiles."""
     if n_req > 0:
         n = min(n_req, -(-T // 32))
     else:
-        target = 8 * cus
+        target = (8 if tiles > 1 else 4) * cus
         n = 1 if units >= target else min(-(-target // units), max(1, T // 1024))
     chunk = -(-(-(-T // n)) // 32) * 32
     return -(-T // chunk), chunk
@@ -314,7 +318,7 @@ def test_plan_query_tiled(lib, nq, G):
     sl = B * Hkv
     R = nq * G
     tiles = -(-R // 128)
-    n, chunk = _query_tiled_splits(B * Hkv * tiles, T)
+    n, chunk = _query_tiled_splits(B * Hkv * tiles, T, tiles=tiles)
     parts = sl * R * n
     part_bytes = (a256(parts * D * 4) + 2 * a256(parts * 4)) if n > 1 else 0
     st, p = plan(B, G * Hkv, Hkv, T, D, 0, n_queries=nq, causal=1, dtype=fd.FD_F16)
@@ -323,7 +327,9 @@ def test_plan_query_tiled(lib, nq, G):
     st, p = plan(B, G * Hkv, Hkv, T, D, 0, n_queries=nq, causal=1)
     assert st == fd.FD_OK, fd.fd_last_error()
     assert p.path == fd.FD_PATH_PREFILL and p.n_splits == n
-    assert p.workspace_bytes == a256(sl * 4) + a256(sl * (T // 256) * 4) + a256(sl * T * D * 2) + part_bytes
+    # bf16 V is converted from 1024 query rows per kv head
+    vt_bytes = a256(sl * 4) + a256(sl * (T // 256) * 4) + a256(sl * T * D * 2) if R >= 1024 else 0
+    assert p.workspace_bytes == vt_bytes + part_bytes
     assert not p.fused and not p.stream and p.combine == (n > 1)
     assert (p.grid[0], p.grid[1], p.grid[2]) == (tiles * n, Hkv, B) and p.head_blocks == tiles
     if n > 1:
@@ -338,7 +344,7 @@ def test_plan_query_tiled_explicit_splits(lib, n_req):
     # an explicit split count is taken as asked, capped at one 32-token tile
     # per split; the effective count covers T with no empty split
     B, Hkv, G, T, D, nq = 1, 8, 4, 4000, 128, 512
-    n, chunk = _query_tiled_splits(0, T, n_req=n_req)
+    n, chunk = _query_tiled_splits(0, T, n_req=n_req, tiles=16)
     st, p = plan(B, G * Hkv, Hkv, T, D, n_req, n_queries=nq, causal=1)
     assert st == fd.FD_OK, fd.fd_last_error()
     assert p.path == fd.FD_PATH_PREFILL and p.n_splits == n and p.combine == (n > 1)
@@ -392,12 +398,47 @@ def test_plan_query_tiled_size_limits(lib):
     # bf16 query-tiled plans address each (batch, kv head) of converted V with
     # 32-bit offsets: a paged T whose converted slice reaches 4 GiB is refused
     T = (1 << 24)                                   # 2^24 tokens x 128 x 2 B = 4 GiB
-    kw = dict(n_queries=64, page_size=16, max_pages_per_seq=T // 16, num_pages=1)
+    kw = dict(n_queries=256, page_size=16, max_pages_per_seq=T // 16, num_pages=1)   # 1024 rows: V converted
     st, _ = plan(1, 8, 2, T, 128, 0, **kw)
     assert st == fd.FD_ERR_UNSUPPORTED and "4 GiB" in fd.fd_last_error()
     st, _ = plan(1, 8, 2, T - 64, 128, 0, **kw)
     assert st == fd.FD_OK, fd.fd_last_error()
     st, p = plan(1, 8, 2, T, 128, 1, dtype=fd.FD_F16, **kw)   # f16 needs no conversion
     assert st == fd.FD_OK and p.n_splits == 1 and p.workspace_bytes == 0
-    st, p = plan(1, 8, 2, T, 128, 0, dtype=fd.FD_F16, **kw)   # two row tiles: the KV axis is split
-    assert st == fd.FD_OK and p.n_splits == 512 and p.workspace_bytes > 0
+    st, p = plan(1, 8, 2, T, 128, 0, dtype=fd.FD_F16, **kw)   # eight row tiles: the KV axis is split
+    assert st == fd.FD_OK and p.n_splits == 128 and p.workspace_bytes > 0
+
+
+@pytest.mark.parametrize("nq,G,dtype,want", [
+    (1, 32, fd.FD_BF16, fd.FD_PATH_MFMA),       # 32 rows: one matrix-core split workgroup
+    (1, 64, fd.FD_BF16, fd.FD_PATH_PREFILL),    # 64 rows of one query: query-tiled
+    (8, 4, fd.FD_BF16, fd.FD_PATH_MFMA),
+    (9, 4, fd.FD_F16, fd.FD_PATH_PREFILL),      # 36 rows
+    (16, 8, fd.FD_BF16, fd.FD_PATH_PREFILL),
+    (16, 8, fd.FD_F32, fd.FD_PATH_VALU),        # fp32 stays on the vector kernel
+    (17, 1, fd.FD_F16, fd.FD_PATH_PREFILL),     # more than 16 queries
+])
+def test_plan_rows_route(lib, nq, G, dtype, want):
+    # query rows per kv head (n_q * G) beyond what one matrix-core split
+    # workgroup holds take the query-tiled kernel, which reads K/V once for
+    # 128 rows; one-query calls with an appended token stay on the split
+    # kernels
+    st, p = plan(2, G * 2, 2, 4096, 128, 0, n_queries=nq, causal=1 if nq > 1 else 0, dtype=dtype)
+    assert st == fd.FD_OK, fd.fd_last_error()
+    assert p.path == want
+    if want == fd.FD_PATH_PREFILL and dtype == fd.FD_BF16:
+        assert p.workspace_bytes == (0 if p.n_splits == 1 else p.workspace_bytes)
+    st, p = plan(2, 64 * 2, 2, 4096, 128, 0, flags=fd.FD_FLAG_APPEND)
+    assert st == fd.FD_OK and p.path == fd.FD_PATH_MFMA
+
+
+def test_plan_query_tiled_paged_splits(lib):
+    # a paged (ragged) batch with one row tile per kv head is planned for
+    # four rounds of workgroups, a contiguous one for two
+    B, Hq, Hkv, T = 16, 32, 8, 65536
+    kw = dict(n_queries=16, causal=1)
+    st, p = plan(B, Hq, Hkv, T, 128, 0, page_size=16, max_pages_per_seq=T // 16, num_pages=10, **kw)
+    assert st == fd.FD_OK and p.path == fd.FD_PATH_PREFILL
+    assert p.n_splits == _query_tiled_splits(B * Hkv, T, tiles=2)[0] == 16
+    st, p = plan(B, Hq, Hkv, T, 128, 0, **kw)
+    assert st == fd.FD_OK and p.n_splits == _query_tiled_splits(B * Hkv, T, tiles=1)[0] == 8

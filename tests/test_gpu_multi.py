@@ -78,12 +78,16 @@ def test_multi_merges(fused):
 
 
 def test_multi_d64_and_many_rows():
-    # 8 queries x G = 8: 64 query rows per kv head (two 32-row workgroups)
+    # 8 queries x G = 8: 64 query rows per kv head -- two 32-row workgroups
+    # on the matrix-core split kernel when forced, the query-tiled kernel
+    # (one K/V read for all 64 rows) by default
     case = contiguous("gqa128k_bf16", [900, 64, 3], Hq=16, Hkv=2, T=900, D=64)
     q = inputs.make_q_multi(case.spec, 8).to(DEV)
     for causal in (False, True):
-        plan = check_multi(case, q, causal, what=f"D=64 64 rows causal={causal}")
+        plan = check_multi(case, q, causal, path="mfma", what=f"D=64 64 rows mfma causal={causal}")
         assert plan["head_blocks"] == 2 and plan["heads_per_block"] == 32
+        plan = check_multi(case, q, causal, what=f"D=64 64 rows causal={causal}")
+        assert plan["path"] == "prefill"
 
 
 @pytest.mark.parametrize("causal", [False, True])

@@ -161,11 +161,15 @@ def test_prefill_full_size_sampled_f16():
         assert err <= parity.OUT_TOL["f16"] and lerr <= parity.LSE_TOL["f16"]
 
 
+@pytest.mark.parametrize("vt", ["1", "0"])
 @pytest.mark.parametrize("vmul", [2.0 ** 20, 2.0 ** -20, 2.0 ** -130, 0.0])
-def test_prefill_bf16_value_range(vmul):
+def test_prefill_bf16_value_range(env_switch, vt, vmul):
     # bf16 V far from 1 in magnitude -- large, small, in the bf16 subnormal
     # range, all zero: the per-(sequence, kv head) scale of the f16
-    # conversion keeps the value product within the tolerance of max|V|
+    # conversion (vt = 1; forced, as 160 query rows would not convert) keeps
+    # the value product within the tolerance of max|V|, and so does the
+    # two-part bf16 probability product (vt = 0)
+    env_switch.setenv("FD_PREFILL_VT", vt)
     case = contiguous("gqa128k_bf16", [300, 129], Hq=8, Hkv=2, T=300)
     case.v = (case.v.float() * vmul).to(torch.bfloat16)
     q = inputs.make_q_multi(case.spec, 40).to(DEV)
@@ -174,8 +178,8 @@ def test_prefill_bf16_value_range(vmul):
         ref_out, ref_lse = oracle_mod.default().decode_multi(q.cpu(), host.k, host.v, case.spec.scale,
                                                              causal=causal, seq_lens=host.seq_lens)
         dec = Decoder(q, case.k, case.v, scale=case.spec.scale, seq_lens=case.seq_lens, causal=causal)
-        assert dec.plan["path"] == "prefill" and dec.plan["workspace_bytes"] > 0
-        parity.announce(f"prefill bf16 V x {vmul:g} causal={causal}")
+        assert dec.plan["path"] == "prefill" and (dec.plan["workspace_bytes"] > 0) == (vt == "1")
+        parity.announce(f"prefill bf16 V x {vmul:g} vt={vt} causal={causal}")
         out, lse = dec()
         torch.cuda.synchronize()
         parity.compare(case, out.cpu().double().numpy(), lse.cpu().double().numpy(), ref_out, ref_lse,
@@ -235,6 +239,32 @@ def test_prefill_kv_splits(causal, dtype, D, n):
     plan = check_multi(case, q, causal, n_splits=n, what=f"prefill splits n={n} {dtype} D={D} causal={causal}")
     chunk = -(-(-(-1500 // n)) // 32) * 32          # whole tiles: 64 asked gives 47 splits of 32 tokens
     assert plan["path"] == "prefill" and plan["n_splits"] == -(-1500 // chunk) and plan["combine"]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n", [3, 7])
+def test_prefill_kv_splits_converted_v(env_switch, causal, n):
+    # bf16 V converted to f16 (forced: 600 query rows would not convert):
+    # each split's partial undoes the conversion scale before the merge
+    env_switch.setenv("FD_PREFILL_VT", "1")
+    case = contiguous("gqa128k_bf16", [1500, 37, 0, 777, 1200], Hq=8, Hkv=2, T=1500)
+    q = inputs.make_q_multi(case.spec, 150).to(DEV)
+    plan = check_multi(case, q, causal, n_splits=n, what=f"prefill splits converted V n={n} causal={causal}")
+    assert plan["path"] == "prefill" and plan["n_splits"] == n and plan["workspace_bytes"] > 0
+
+
+@pytest.mark.parametrize("nq,G,dtype", [(1, 64, "bf16"), (2, 20, "f16"), (9, 4, "bf16"), (16, 8, "bf16")])
+def test_many_rows_take_query_tiled_kernel(nq, G, dtype):
+    # more than 32 query rows per kv head (n_q * G) go to the query-tiled
+    # kernel, which reads K/V once for 128 rows (bf16 V unconverted at these
+    # row counts); ragged lengths, one empty sequence, both masks
+    case = contiguous("gqa128k_bf16", [3000, 1500, 0], Hq=G * 2, Hkv=2, T=3000, dtype=dtype)
+    q = inputs.make_q_multi(case.spec, nq).to(DEV)
+    for causal in ((False, True) if nq > 1 else (False,)):
+        plan = check_multi(case, q, causal, what=f"many rows nq={nq} G={G} {dtype} causal={causal}")
+        assert plan["path"] == "prefill" and plan["workspace_bytes"] >= 0
+        if dtype == "bf16" and plan["n_splits"] == 1:
+            assert plan["workspace_bytes"] == 0
 
 
 @pytest.mark.parametrize("causal", [False, True])
