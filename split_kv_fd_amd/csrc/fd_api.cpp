@@ -146,9 +146,13 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
         (path == FD_PATH_AUTO && (o.n_queries > kMaxDecodeQueries || many_rows))) {
         if (o.dtype == FD_F32) return fail(FD_ERR_UNSUPPORTED, "the query-tiled kernel needs f16 or bf16 inputs");
         if (o.flags & FD_FLAG_APPEND) return fail(FD_ERR_UNSUPPORTED, "fd_append_decode takes one query per sequence");
-        const long tiles = ceil_div(R, fdk::kPrefillRows);
         if (Hkv > 65535) return fail(FD_ERR_UNSUPPORTED, "Hkv=%d > 65535", Hkv);
         const bool vt = o.dtype == FD_BF16 && env_long("FD_PREFILL_VT", R >= kConvertRows ? 1 : 0) == 1;
+        // 64-row tiles for up to 64 rows (no idle row blocks), else 128
+        const int tile_rows = (R <= fdk::kPrefillSmallRows && !vt && env_long("FD_PREFILL_SMALL", 1) == 1)
+                                  ? fdk::kPrefillSmallRows
+                                  : fdk::kPrefillRows;
+        const long tiles = ceil_div(R, tile_rows);
         // the converted V of one (batch, kv head) is addressed with 32-bit
         // offsets, as contiguous slices are
         if (vt && ceil_div(T, fdk::kPrefillTokens) * fdk::kPrefillTokens * D * 2 >= (1L << 32))
@@ -189,7 +193,7 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
         p->chunk = (int)(n > 1 ? chunk : T);
         p->path = FD_PATH_PREFILL;
         p->tile = fdk::kPrefillTokens;
-        p->heads_per_block = fdk::kPrefillRows;
+        p->heads_per_block = tile_rows;
         p->head_blocks = (int)tiles;
         p->grid[0] = (int)(tiles * n);
         p->grid[1] = Hkv;
@@ -480,6 +484,7 @@ fd_status_t prepare(const void *q, const void *k, const void *v, const int32_t *
     f.out = out; f.lse = lse;
     f.B = B; f.nq = s.nq; f.Hq = Hq; f.Hkv = Hkv; f.T = T; f.D = D; f.G = s.G; f.R = s.R;
     f.row_tiles = c->p.path == FD_PATH_PREFILL ? c->p.head_blocks : 0;
+    f.tile_rows = c->p.path == FD_PATH_PREFILL ? c->p.heads_per_block : 0;
     f.causal = s.causal;
     f.page_size = s.page_size; f.page_shift = s.page_shift; f.max_pages = s.max_pages; f.num_pages = s.num_pages;
     f.scale_log2 = s.scale_log2;

@@ -128,6 +128,9 @@ hipError_t launch_combine(const CombineArgs &a, hipStream_t stream);
 #endif
 constexpr int kPrefillNB = FD_PREFILL_NB;          // 16-row blocks per wave
 constexpr int kPrefillRows = 64 * kPrefillNB;
+// Tile of one 16-row block per wave, for 64 or fewer query rows per kv
+// head (value product without converted V only).
+constexpr int kPrefillSmallRows = 64;
 constexpr int kPrefillTokens = 32;
 
 struct PrefillArgs {
@@ -140,7 +143,8 @@ struct PrefillArgs {
     float *lse;                  // [B, nq, Hq], may be nullptr
     int B, nq, Hq, Hkv, T, D, G;
     int R;                       // query rows per kv head = nq * G
-    int row_tiles;               // ceil(R / kPrefillRows)
+    int tile_rows;               // query rows per workgroup: kPrefillRows or kPrefillSmallRows
+    int row_tiles;               // ceil(R / tile_rows)
     int causal;                  // query i sees the first T_b - (nq - 1 - i) tokens
     // KV splits: split s covers tokens [s * chunk, (s + 1) * chunk), chunk a
     // multiple of kPrefillTokens.  n_splits > 1 writes unnormalised partials

@@ -5,9 +5,10 @@
 // split-KV", "Concept" and "The big idea"): prefill attends with a whole
 // block of queries and wants tiling over the query axis, decode has one
 // query and wants the KV axis split.  This kernel is the query-tiled one:
-// a workgroup owns kPrefillRows query rows of one (batch, kv head) -- the
-// rows are (query, head of the GQA group) pairs, so every row of the tile
-// reads the same K and V -- and walks the visible KV range in tiles of
+// a workgroup owns a tile of 64 * NB query rows (128; 64 when a kv head
+// has no more) of one (batch, kv head) -- the rows are (query, head of the
+// GQA group) pairs, so every row of the tile reads the same K and V -- and
+// walks the visible KV range in tiles of
 // kPrefillTokens tokens with an online softmax (the same running max / sum
 // / unnormalised accumulator as the split pass), then divides once.
 // Where row tiles alone leave the device short of work (few queries over a
@@ -110,8 +111,9 @@ constexpr float kSlack = 8.f;
 // VT: bf16 inputs whose V was converted by the passes below to f16 under a
 // per-(batch, kv head) power-of-two scale, transposed in tile order; the
 // value product then runs on f16 with one P product, as for f16 inputs.
-template <int DT, int D, bool PAGED, bool VT>
-__global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillArgs a) {
+// NB: 16-row blocks per wave (the workgroup's tile is 64 * NB query rows).
+template <int DT, int D, bool PAGED, bool VT, int NB>
+__global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void prefill(PrefillArgs a) {
     constexpr int ROWB = D * 2;              // bytes per K / V row
     constexpr int KS = D / 32;               // 32-wide k chunks of the logit product
     constexpr int DT16 = D / 16;             // 16-wide dimension tiles of the value product
@@ -123,7 +125,7 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
     // 2-way conflicts.
     constexpr int KSTR = ROWB + 32;          // K (bytes)
     constexpr int VSTR = NTOK * 2 + 32;      // V^T (bytes)
-    constexpr int NB = kPrefillNB;           // 16-row blocks per wave
+    constexpr int ROWS = 64 * NB;            // query rows of the workgroup's tile
     // The value product takes P rounded to f16 (11 significant bits: weights
     // off by at most 2^-11 relative) -- for f16 inputs, and for bf16 inputs
     // whose V was converted (VT).  Otherwise bf16 P, with 8 bits, would spend
@@ -135,7 +137,7 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
     // above the f16 subnormal range for every weight that matters and below
     // its largest finite value.  The bias cancels in the division by the sum.
     constexpr float kPBias = SPLIT_P ? 0.f : 6.f;
-    static_assert(NTOK == 32 && kPrefillRows == 4 * 16 * NB, "the tile maps assume 32 tokens x 4 waves x NB*16 rows");
+    static_assert(NTOK == 32, "the tile maps assume 32 tokens x 4 waves x NB*16 rows");
     static_assert(PIECES * 16 <= 256 && 256 % (PIECES * 16) == 0, "loader threads cover the pieces evenly");
 
     constexpr int NBUF = 3;                  // tiles j and j+1 in use, j+2 being stored
@@ -173,7 +175,7 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
     const int tile = a.causal ? a.row_tiles - 1 - tile_i : tile_i;
     const int kvh = slc % a.Hkv;
     const int b = slc / a.Hkv;
-    const int r0 = tile * kPrefillRows;
+    const int r0 = tile * ROWS;
 
     int Tb = a.seq_lens ? a.seq_lens[b] : a.T;
     Tb = Tb < 0 ? 0 : (Tb > a.T ? a.T : Tb);
@@ -228,7 +230,7 @@ __global__ __launch_bounds__(256, kPrefillNB > 2 ? 1 : 2) void prefill(PrefillAr
 
     // Tokens the workgroup's rows see at most, and its tiles [j0, j1) of
     // them: the split's.
-    const int r_last = min(r0 + kPrefillRows, a.R) - 1;
+    const int r_last = min(r0 + ROWS, a.R) - 1;
     int seen = a.causal ? Tb - (a.nq - 1 - r_last / a.G) : Tb;
     seen = seen < 0 ? 0 : seen;
     const bool parts = a.n_splits > 1;
@@ -734,6 +736,7 @@ hipError_t launch_dim(const PrefillArgs &a, hipStream_t stream) {
     const dim3 grid(a.row_tiles * a.n_splits, a.Hkv, a.B);
     if constexpr (DT == FD_BF16) {
         if (a.vt) {
+            if (a.tile_rows != kPrefillRows) return hipErrorInvalidValue;
             const dim3 pgrid(a.vmax_chunks, a.Hkv, a.B);
             if (a.page_table) {
                 hipLaunchKernelGGL((vmax_pass<D, true>), pgrid, dim3(256), 0, stream, a);
@@ -742,13 +745,21 @@ hipError_t launch_dim(const PrefillArgs &a, hipStream_t stream) {
                 hipLaunchKernelGGL((vmax_pass<D, false>), pgrid, dim3(256), 0, stream, a);
                 hipLaunchKernelGGL((vconv_pass<D, false>), pgrid, dim3(256), 0, stream, a);
             }
-            if (a.page_table) hipLaunchKernelGGL((prefill<DT, D, true, true>), grid, dim3(256), 0, stream, a);
-            else hipLaunchKernelGGL((prefill<DT, D, false, true>), grid, dim3(256), 0, stream, a);
+            if (a.page_table) hipLaunchKernelGGL((prefill<DT, D, true, true, kPrefillNB>), grid, dim3(256), 0, stream, a);
+            else hipLaunchKernelGGL((prefill<DT, D, false, true, kPrefillNB>), grid, dim3(256), 0, stream, a);
             return hipGetLastError();
         }
     }
-    if (a.page_table) hipLaunchKernelGGL((prefill<DT, D, true, false>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((prefill<DT, D, false, false>), grid, dim3(256), 0, stream, a);
+    if (a.tile_rows == 64 * kPrefillNB) {
+        if (a.page_table) hipLaunchKernelGGL((prefill<DT, D, true, false, kPrefillNB>), grid, dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((prefill<DT, D, false, false, kPrefillNB>), grid, dim3(256), 0, stream, a);
+    } else if (a.tile_rows == kPrefillSmallRows) {
+        // a 64-row tile for 33..64 query rows per kv head: no row block idles
+        if (a.page_table) hipLaunchKernelGGL((prefill<DT, D, true, false, 1>), grid, dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((prefill<DT, D, false, false, 1>), grid, dim3(256), 0, stream, a);
+    } else {
+        return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

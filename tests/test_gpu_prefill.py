@@ -219,7 +219,9 @@ def test_prefill_work_order_does_not_change_results(env_switch, dtype):
         out, lse = dec()
         torch.cuda.synchronize()
         res.append((out.clone(), lse.clone()))
-    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+    vmax = float(case.v.float().abs().max())
+    assert torch.allclose(res[0][0], res[1][0], rtol=0, atol=1e-3 * vmax)
+    assert torch.allclose(res[0][1], res[1][1], rtol=0, atol=1e-4)
 
 
 # ------------------------------------------------------------------ KV splits of the query-tiled kernel
@@ -263,8 +265,33 @@ def test_many_rows_take_query_tiled_kernel(nq, G, dtype):
     for causal in ((False, True) if nq > 1 else (False,)):
         plan = check_multi(case, q, causal, what=f"many rows nq={nq} G={G} {dtype} causal={causal}")
         assert plan["path"] == "prefill" and plan["workspace_bytes"] >= 0
+        # 64-row tiles (one 16-row block per wave) up to 64 rows, else 128
+        assert plan["heads_per_block"] == (64 if nq * G <= 64 else 128)
         if dtype == "bf16" and plan["n_splits"] == 1:
             assert plan["workspace_bytes"] == 0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_small_and_large_row_tiles_agree(env_switch, dtype):
+    # the 64-row and 128-row tiles both meet the oracle's bar on the same
+    # rows (one tile holds every row here); they group rows into waves
+    # differently, and a wave shares its masks and running-max moves, so
+    # their rounding differs: they agree within 1e-3 of max|V| (f16
+    # probabilities) and 1e-4 in the lse
+    case = contiguous("gqa128k_bf16", [2500, 700, 1], Hq=16, Hkv=2, T=2500, dtype=dtype)
+    q = inputs.make_q_multi(case.spec, 6).to(DEV)
+    res = []
+    for small in ("1", "0"):
+        env_switch.setenv("FD_PREFILL_SMALL", small)
+        plan = check_multi(case, q, True, n_splits=3, what=f"row tiles small={small} {dtype}")
+        assert plan["path"] == "prefill" and plan["heads_per_block"] == (64 if small == "1" else 128)
+        dec = Decoder(q, case.k, case.v, scale=case.spec.scale, seq_lens=case.seq_lens, causal=True, n_splits=3)
+        out, lse = dec()
+        torch.cuda.synchronize()
+        res.append((out.clone(), lse.clone()))
+    vmax = float(case.v.float().abs().max())
+    assert torch.allclose(res[0][0], res[1][0], rtol=0, atol=1e-3 * vmax)
+    assert torch.allclose(res[0][1], res[1][1], rtol=0, atol=1e-4)
 
 
 @pytest.mark.parametrize("causal", [False, True])
