@@ -38,8 +38,9 @@
  *     (the queries are the sequence's last n_q cached tokens, as in
  *     verifying a draft); a query with no token yields out = 0, lse = -inf.
  *     Up to 16 queries run on the split-KV kernels (every query row of a kv
- *     head shares one read of K / V), as long as a kv head has at most 32
- *     query rows (n_q * G) or the inputs are fp32; more queries (the
+ *     head shares one read of K / V), as long as a kv head has at most 16
+ *     query rows (n_q * G; 32 for paged caches) or the inputs are fp32;
+ *     more queries (the
  *     prefill phase: the dupenodi guide, "Concept", has prefill attend with
  *     the whole block of prompt queries), or more rows, run on a query-tiled
  *     kernel: one workgroup per 128 query rows of a (sequence, kv head) and
@@ -135,8 +136,9 @@ typedef struct fd_options {
     void *stream;               /* hipStream_t to launch on; NULL = null stream */
     int32_t n_queries;          /* queries per sequence, 1 .. 65536 (0 = 1);  */
                                 /* > 1 gives q / out an n_q axis (see below); */
-                                /* > 16 (or > 32 query rows per kv head,     */
-                                /* f16 / bf16) runs the query-tiled kernel   */
+                                /* > 16 (or > 16 query rows per kv head,     */
+                                /* 32 paged; f16 / bf16) runs the query-     */
+                                /* tiled kernel                              */
     int32_t causal;             /* with n_queries > 1: 1 = query i sees the   */
                                 /* first T_b - (n_queries - 1 - i) tokens     */
 } fd_options_t;

@@ -264,7 +264,7 @@ def test_plan_several_queries(lib, nq):
         st, p = plan(B, G * Hkv, Hkv, T, D, 0, dtype=dt, n_queries=nq)
         assert st == fd.FD_OK, fd.fd_last_error()
         R = nq * G
-        if dt != fd.FD_F32 and R > 32:      # past one matrix-core workgroup's rows
+        if dt != fd.FD_F32 and R > 16:      # contiguous: the query-tiled kernel from 17 rows
             assert p.path == fd.FD_PATH_PREFILL
             continue
         want_mfma = dt != fd.FD_F32 and R >= 4
@@ -409,25 +409,29 @@ def test_plan_query_tiled_size_limits(lib):
     assert st == fd.FD_OK and p.n_splits == 128 and p.workspace_bytes > 0
 
 
-@pytest.mark.parametrize("nq,G,dtype,want", [
-    (1, 32, fd.FD_BF16, fd.FD_PATH_MFMA),       # 32 rows: one matrix-core split workgroup
-    (1, 64, fd.FD_BF16, fd.FD_PATH_PREFILL),    # 64 rows of one query: query-tiled
-    (8, 4, fd.FD_BF16, fd.FD_PATH_MFMA),
-    (9, 4, fd.FD_F16, fd.FD_PATH_PREFILL),      # 36 rows
-    (16, 8, fd.FD_BF16, fd.FD_PATH_PREFILL),
-    (16, 8, fd.FD_F32, fd.FD_PATH_VALU),        # fp32 stays on the vector kernel
-    (17, 1, fd.FD_F16, fd.FD_PATH_PREFILL),     # more than 16 queries
+@pytest.mark.parametrize("nq,G,dtype,want,want_paged", [
+    (1, 16, fd.FD_BF16, fd.FD_PATH_MFMA, fd.FD_PATH_MFMA),        # 16 rows: split kernels
+    (1, 32, fd.FD_BF16, fd.FD_PATH_PREFILL, fd.FD_PATH_MFMA),     # 32 rows: paged keeps stream mode
+    (1, 64, fd.FD_BF16, fd.FD_PATH_PREFILL, fd.FD_PATH_PREFILL),  # 64 rows of one query
+    (4, 4, fd.FD_F16, fd.FD_PATH_MFMA, fd.FD_PATH_MFMA),
+    (5, 4, fd.FD_BF16, fd.FD_PATH_PREFILL, fd.FD_PATH_MFMA),      # 20 rows
+    (9, 4, fd.FD_F16, fd.FD_PATH_PREFILL, fd.FD_PATH_PREFILL),    # 36 rows
+    (16, 8, fd.FD_BF16, fd.FD_PATH_PREFILL, fd.FD_PATH_PREFILL),
+    (16, 8, fd.FD_F32, fd.FD_PATH_VALU, fd.FD_PATH_VALU),         # fp32 stays on the vector kernel
+    (17, 1, fd.FD_F16, fd.FD_PATH_PREFILL, fd.FD_PATH_PREFILL),   # more than 16 queries
 ])
-def test_plan_rows_route(lib, nq, G, dtype, want):
-    # query rows per kv head (n_q * G) beyond what one matrix-core split
-    # workgroup holds take the query-tiled kernel, which reads K/V once for
-    # 128 rows; one-query calls with an appended token stay on the split
-    # kernels
+def test_plan_rows_route(lib, nq, G, dtype, want, want_paged):
+    # query rows per kv head (n_q * G) past 16 (contiguous) or 32 (paged,
+    # where the split kernels' stream mode balances ragged lengths) take
+    # the query-tiled kernel, which reads K/V once for a 64- or 128-row
+    # tile; one-query calls with an appended token stay on the split kernels
     st, p = plan(2, G * 2, 2, 4096, 128, 0, n_queries=nq, causal=1 if nq > 1 else 0, dtype=dtype)
     assert st == fd.FD_OK, fd.fd_last_error()
     assert p.path == want
-    if want == fd.FD_PATH_PREFILL and dtype == fd.FD_BF16:
-        assert p.workspace_bytes == (0 if p.n_splits == 1 else p.workspace_bytes)
+    st, p = plan(2, G * 2, 2, 4096, 128, 0, n_queries=nq, causal=1 if nq > 1 else 0, dtype=dtype,
+                 page_size=16, max_pages_per_seq=256, num_pages=10)
+    assert st == fd.FD_OK, fd.fd_last_error()
+    assert p.path == want_paged
     st, p = plan(2, 64 * 2, 2, 4096, 128, 0, flags=fd.FD_FLAG_APPEND)
     assert st == fd.FD_OK and p.path == fd.FD_PATH_MFMA
 
