@@ -293,11 +293,14 @@ def test_several_queries_rejects(lib):
 
 def _query_tiled_splits(units, T, cus=256, n_req=0, tiles=2):
     """The planner's KV split rule for the query-tiled kernel, restated:
-    about 8 * cus workgroups (four rounds at two per compute unit; 4 * cus
-    with one row tile per kv head of a contiguous cache), no split below
-    1024 tokens; chunks are whole 32-token tiles."""
+    about 8 * cus workgroups (four rounds at two per compute unit); with one
+    row tile per kv head of a contiguous cache 4 * cus, or none once the
+    tiles alone give 2 * cus; no split below 1024 tokens; chunks are whole
+    32-token tiles."""
     if n_req > 0:
         n = min(n_req, -(-T // 32))
+    elif tiles == 1 and units >= 2 * cus:
+        n = 1
     else:
         target = (8 if tiles > 1 else 4) * cus
         n = 1 if units >= target else min(-(-target // units), max(1, T // 1024))
@@ -446,3 +449,8 @@ def test_plan_query_tiled_paged_splits(lib):
     assert p.n_splits == _query_tiled_splits(B * Hkv, T, tiles=2)[0] == 16
     st, p = plan(B, Hq, Hkv, T, 128, 0, **kw)
     assert st == fd.FD_OK and p.n_splits == _query_tiled_splits(B * Hkv, T, tiles=1)[0] == 8
+    # one row tile per kv head that already gives two workgroups per CU: no split
+    st, p = plan(64, 64, 8, 32768, 128, 0, n_queries=8, causal=1)
+    assert st == fd.FD_OK and p.path == fd.FD_PATH_PREFILL and p.n_splits == 1 and p.workspace_bytes == 0
+    st, p = plan(32, 64, 8, 32768, 128, 0, n_queries=8, causal=1)
+    assert st == fd.FD_OK and p.n_splits == _query_tiled_splits(32 * 8, 32768, tiles=1)[0] == 4
