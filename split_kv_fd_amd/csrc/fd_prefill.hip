@@ -255,38 +255,47 @@ __global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void prefill(PrefillArgs a) {
         uint4 k0, k1, v0, v1;
         int ok0, ok1;
     };
-    // Row of token tt of the sequence, clamped to the last real token (Tb >=
-    // 1 wherever it is called), so every load is in bounds; ok = false for a
-    // token past the end or on a page outside the pool.
-    auto token_row = [&](int tt, int &ok) -> size_t {
-        const int tc = tt < Tb ? tt : Tb - 1;
-        ok = tt < Tb;
-        if constexpr (PAGED) {
-            int pg = a.page_table[(size_t)b * a.max_pages + (tc >> a.page_shift)];
-            if ((unsigned)pg >= (unsigned)a.num_pages) { ok = 0; pg = 0; }
-            return ((size_t)pg * a.Hkv + kvh) * a.page_size + (tc & (a.page_size - 1));
-        } else {
-            return ((size_t)b * a.Hkv + kvh) * a.T + tc;
-        }
+    // Paged caches: the page ids this thread needs for tile j -- of its V
+    // token pair 2u, 2u+1 and its K token pair 2ku, 2ku+1 (with pages of two
+    // or more tokens a pair never straddles a page, so one id serves both).
+    // Without converted V they are read one step before the tile's K/V
+    // loads, which then do not wait on a dependent page-table read (calls
+    // with few rows are bound by those reads).  With converted V (many rows,
+    // bound by the matrix cores), and in the f16 128-row instance, they are
+    // read just before: there the four registers would spill.  Tokens past
+    // the end are clamped to the last real one (Tb >= 1 wherever a tile is
+    // loaded), so every read is in bounds.
+    constexpr bool PREFETCH_PAGES = PAGED && !VT && (NB == 1 || DT == FD_BF16);
+    struct Pages {
+        int v0, v1, k0, k1;
     };
-    // Paged rows of tokens tt and tt+1 (tt even), clamped like token_row.
-    // With pages of two or more tokens the pair never straddles a page, so
-    // one page-table read serves both.
-    auto pair_rows = [&](int tt, size_t &r0_, size_t &r1_, int &ok0_, int &ok1_) {
-        if (a.page_shift == 0) {
-            r0_ = token_row(tt, ok0_);
-            r1_ = token_row(tt + 1, ok1_);
-            return;
+    auto fetch_pages = [&](int j) -> Pages {
+        Pages pp{0, 0, 0, 0};
+        if constexpr (PAGED) {
+            auto pid = [&](int tt) {
+                const int tc = tt < Tb ? tt : Tb - 1;
+                return a.page_table[(size_t)b * a.max_pages + (tc >> a.page_shift)];
+            };
+            const int tv = j * NTOK + 2 * u, tk = j * NTOK + 2 * ku;
+            pp.v0 = pid(tv);
+            pp.k0 = pid(tk);
+            if (a.page_shift == 0) {
+                pp.v1 = pid(tv + 1);
+                pp.k1 = pid(tk + 1);
+            } else {
+                pp.v1 = pp.v0;
+                pp.k1 = pp.k0;
+            }
         }
-        const int t0 = tt < Tb ? tt : Tb - 1;
-        const int t1 = tt + 1 < Tb ? tt + 1 : Tb - 1;
-        int pg = a.page_table[(size_t)b * a.max_pages + (t0 >> a.page_shift)];
+        return pp;
+    };
+    // Row of token tt on page pg, clamped as above; ok = false for a token
+    // past the end or on a page outside the pool (read from page 0).
+    auto page_row = [&](int pg, int tt, int &ok) -> size_t {
+        const int tc = tt < Tb ? tt : Tb - 1;
         const bool valid = (unsigned)pg < (unsigned)a.num_pages;
-        if (!valid) pg = 0;
-        r0_ = ((size_t)pg * a.Hkv + kvh) * a.page_size + (t0 & (a.page_size - 1));
-        r1_ = r0_ + (size_t)(t1 - t0);
-        ok0_ = (tt < Tb) & valid;
-        ok1_ = (tt + 1 < Tb) & valid;
+        ok = (tt < Tb) & valid;
+        return ((size_t)(valid ? pg : 0) * a.Hkv + kvh) * a.page_size + (tc & (a.page_size - 1));
     };
     // Contiguous caches: the (batch, kv head) slices of K and V as buffer
     // resources sized to the real tokens.  Rows past the end read as zeros
@@ -321,7 +330,7 @@ __global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void prefill(PrefillArgs a) {
         const u32x4_v x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
         return make_uint4(x[0], x[1], x[2], x[3]);
     };
-    auto load_tile = [&](int j) -> Regs {
+    auto load_tile = [&](int j, [[maybe_unused]] const Pages &pp) -> Regs {
         Regs g;
         if constexpr (!PAGED) {
             const uint32_t base = (uint32_t)j * (uint32_t)(NTOK * ROWB);
@@ -338,10 +347,12 @@ __global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void prefill(PrefillArgs a) {
             g.ok0 = g.ok1 = 1;                   // unused: the row limits mask the tail
             return g;
         }
-        size_t ra, rb, ka, kb2;
         int unused_ok;                           // the mask bits come from the V rows
-        pair_rows(j * NTOK + 2 * u, ra, rb, g.ok0, g.ok1);
-        pair_rows(j * NTOK + 2 * ku, ka, kb2, unused_ok, unused_ok);
+        const int tv = j * NTOK + 2 * u, tk = j * NTOK + 2 * ku;
+        [[maybe_unused]] const size_t ra = page_row(pp.v0, tv, g.ok0);
+        [[maybe_unused]] const size_t rb = page_row(pp.v1, tv + 1, g.ok1);
+        const size_t ka = page_row(pp.k0, tk, unused_ok);
+        const size_t kb2 = page_row(pp.k1, tk + 1, unused_ok);
         const char *kp = static_cast<const char *>(a.k) + kpiece * 16;
         [[maybe_unused]] const char *vp = static_cast<const char *>(a.v) + piece * 16;
         g.k0 = *reinterpret_cast<const uint4 *>(kp + ka * ROWB);
@@ -425,6 +436,7 @@ __global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void prefill(PrefillArgs a) {
 
     Regs g{};
     uint32_t ok_cur = 0, ok_next = 0;       // paged mask words of tiles j, j+1
+    Pages pnext{0, 0, 0, 0};                // paged, prefetching: page ids of the next tile to load
 
     // One tile: step j consumes the logits cc of tile j (formed one step
     // earlier) and forms cn, those of tile j+1.
@@ -542,7 +554,12 @@ __global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void prefill(PrefillArgs a) {
             }
         }
         store_tile((bj + 2) % NBUF, g);         // its buffer held tile j-1, finished
-        g = load_tile(j + 3);
+        if constexpr (PREFETCH_PAGES) {
+            g = load_tile(j + 3, pnext);
+            pnext = fetch_pages(j + 4);
+        } else {
+            g = load_tile(j + 3, fetch_pages(j + 3));
+        }
         __syncthreads();
     };
 
@@ -557,17 +574,20 @@ __global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void prefill(PrefillArgs a) {
     // index); LDS buffers count from the split's first tile.
     if (nt > 0) {
         if constexpr (PAGED) {
-            Regs g0 = load_tile(j0);
+            const Pages p0 = fetch_pages(j0), p1 = fetch_pages(j0 + 1), p2 = fetch_pages(j0 + 2);
+            if constexpr (PREFETCH_PAGES) pnext = fetch_pages(j0 + 3);
+            Regs g0 = load_tile(j0, p0);
             ok_cur = tile_bits(g0);
             store_tile(0, g0);
-            Regs g1 = load_tile(j0 + 1);
+            Regs g1 = load_tile(j0 + 1, p1);
             ok_next = tile_bits(g1);
             store_tile(1, g1);
+            g = load_tile(j0 + 2, p2);
         } else {
-            store_tile(0, load_tile(j0));
-            store_tile(1, load_tile(j0 + 1));
+            store_tile(0, load_tile(j0, pnext));
+            store_tile(1, load_tile(j0 + 1, pnext));
+            g = load_tile(j0 + 2, pnext);
         }
-        g = load_tile(j0 + 2);
         __syncthreads();
         qk(0, cA);
         int j = 0;
