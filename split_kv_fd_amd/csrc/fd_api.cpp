@@ -175,7 +175,10 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
             // Several row tiles per kv head (bound by the matrix cores), or
             // a paged (ragged) batch: enough workgroups for about four
             // rounds at two per compute unit, so that ragged lengths and
-            // causal triangles even out.  One row tile of a contiguous cache
+            // causal triangles even out -- unless the row tiles alone give
+            // two such rounds (measured: splitting 1024 workgroups of MHA
+            // 4096-query prefill in two added 40% for the merge).  One row
+            // tile of a contiguous cache
             // (a few queries: bound by K/V reads): about two rounds, as
             // longer splits stream more efficiently, and no split at all
             // once the row tiles give two workgroups per compute unit (the
@@ -185,7 +188,7 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
             const long units = (long)B * Hkv * tiles;
             const bool streaming = tiles == 1 && !paged;
             long dflt = (streaming ? 4L : 8L) * cus;
-            if (streaming && units >= 2L * cus) dflt = units;
+            if (units >= (streaming ? 2L : 4L) * cus) dflt = units;
             const long target = std::max(1L, env_long("FD_PREFILL_WGS", dflt));
             const long min_chunk = std::max((long)fdk::kPrefillTokens, env_long("FD_PREFILL_CHUNK_MIN", 1024));
             if (units < target) {

@@ -133,26 +133,31 @@ __global__ __launch_bounds__(256) void combine(CombineArgs a) {
     if (t == 0 && a.lse) a.lse[orow] = L > 0.f ? (M + log2f(L)) * kLn2 : kNegInf;
 }
 
-// The same merge with one wave per partial row, four rows per workgroup:
-// for calls with many rows and few splits (the query-tiled kernel's), where
-// a workgroup per row would idle most of its lanes and pay a workgroup's
-// latency per row.  Lane i owns elements D/64 * i .. of the row; the first
-// PRE partial rows are loaded together with the split maxima (lane s holds
-// split s's max and sum), so up to PRE splits cost one memory round trip.
-// Each lane adds its splits in order, the sums are xor-shuffle reductions:
-// results are deterministic.
+// The same merge with half a wave per partial row, eight rows per
+// workgroup: for calls with many rows and few splits (the query-tiled
+// kernel's), where a workgroup per row would idle most of its lanes and pay
+// a workgroup's latency per row.  Lane i of a half owns elements D/32 * i ..
+// of its row (one 16-byte load per split at D = 128); lane s of a half
+// holds split s's max and sum.  The first PRE partial rows are loaded
+// together with the maxima, so up to PRE splits cost one memory round
+// trip.  Each lane adds its splits in order and the sums are xor-shuffle
+// reductions within the half: results are deterministic.
 template <int D>
 __global__ __launch_bounds__(256) void combine_rows(CombineArgs a) {
-    constexpr int EPL = D / 64;       // elements per lane
+    constexpr int LPR = 32;           // lanes per row
+    constexpr int EPL = D / LPR;      // elements per lane
     constexpr int PRE = 16;
     typedef float vec_t __attribute__((ext_vector_type(EPL)));
     const int lane = threadIdx.x & 63;
+    const int li = lane & (LPR - 1);
+    const int base = lane & LPR;      // first lane of this half
     const long rows = (long)a.B * a.Hkv * a.R;
-    const long bh = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (bh >= rows) return;
-    const int b = (int)(bh / ((long)a.Hkv * a.R));
-    const int kvh = (int)(bh / a.R - (long)b * a.Hkv);
-    const int qr = (int)(bh - (bh / a.R) * a.R);
+    const long bh = ((long)blockIdx.x * 4 + (threadIdx.x >> 6)) * 2 + (lane >> 5);
+    const bool live = bh < rows;      // a half past the last row idles (shuffles stay wave-wide)
+    const long bq = live ? bh : 0;
+    const int b = (int)(bq / ((long)a.Hkv * a.R));
+    const int kvh = (int)(bq / a.R - (long)b * a.Hkv);
+    const int qr = (int)(bq - (bq / a.R) * a.R);
     const size_t orow = ((size_t)b * a.nq + qr / a.G) * a.Hq + (size_t)kvh * a.G + qr % a.G;
 
     int Tb = a.T;
@@ -167,38 +172,42 @@ __global__ __launch_bounds__(256) void combine_rows(CombineArgs a) {
     }
     int n = (Tb + a.chunk - 1) / a.chunk;
     n = n < a.n_splits ? n : a.n_splits;
+    if (!live) n = 0;
 
-    const float *pm = a.part_m + (size_t)bh * a.n_splits;
-    const float *pl = a.part_l + (size_t)bh * a.n_splits;
-    const vec_t *po = reinterpret_cast<const vec_t *>(a.part_o + (size_t)bh * a.n_splits * D) + lane;
+    const float *pm = a.part_m + (size_t)bq * a.n_splits;
+    const float *pl = a.part_l + (size_t)bq * a.n_splits;
+    const vec_t *po = reinterpret_cast<const vec_t *>(a.part_o + (size_t)bq * a.n_splits * D) + li;
 
     vec_t pre[PRE];
 #pragma unroll
-    for (int j = 0; j < PRE; ++j) pre[j] = j < n ? po[(size_t)j * (D / EPL)] : vec_t{};
+    for (int j = 0; j < PRE; ++j) pre[j] = j < n ? po[(size_t)j * LPR] : vec_t{};
     float M = kNegInf;
-    for (int s = lane; s < n; s += 64) M = fmaxf(M, pm[s]);
-    M = wave_max(M);
+    for (int s = li; s < n; s += LPR) M = fmaxf(M, pm[s]);
+#pragma unroll
+    for (int off = 1; off < LPR; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
     const float mu = M == kNegInf ? 0.f : M;
 
     float L = 0.f;
     vec_t acc{};
-    for (int s0 = 0; s0 < n; s0 += 64) {
-        const int s = s0 + lane;
+    for (int s0 = 0; s0 < n; s0 += LPR) {
+        const int s = s0 + li;
         const float w = s < n ? __builtin_amdgcn_exp2f(pm[s] - mu) : 0.f;
         L += s < n ? w * pl[s] : 0.f;
-        const int cnt = n - s0 < 64 ? n - s0 : 64;
+        const int cnt = n - s0 < LPR ? n - s0 : LPR;
         int j = 0;
         if (s0 == 0) {
 #pragma unroll
             for (; j < PRE; ++j)
-                if (j < cnt) acc += __shfl(w, j) * pre[j];
+                if (j < cnt) acc += __shfl(w, base + j) * pre[j];
         }
-        for (; j < cnt; ++j) acc += __shfl(w, j) * po[(size_t)(s0 + j) * (D / EPL)];
+        for (; j < cnt; ++j) acc += __shfl(w, base + j) * po[(size_t)(s0 + j) * LPR];
     }
-    L = wave_sum(L);
+#pragma unroll
+    for (int off = 1; off < LPR; off <<= 1) L += __shfl_xor(L, off);
+    if (!live) return;
     const vec_t o = L > 0.f ? acc / L : vec_t{};
-    reinterpret_cast<vec_t *>(a.out + orow * D)[lane] = o;
-    if (lane == 0 && a.lse) a.lse[orow] = L > 0.f ? (M + log2f(L)) * kLn2 : kNegInf;
+    reinterpret_cast<vec_t *>(a.out + orow * D)[li] = o;
+    if (li == 0 && a.lse) a.lse[orow] = L > 0.f ? (M + log2f(L)) * kLn2 : kNegInf;
 }
 
 }  // namespace
@@ -206,7 +215,7 @@ __global__ __launch_bounds__(256) void combine_rows(CombineArgs a) {
 hipError_t launch_combine(const CombineArgs &a, hipStream_t stream) {
     const long rows = (long)a.B * a.Hkv * a.R;
     if (a.per_wave) {
-        const dim3 grid((unsigned)((rows + 3) / 4));
+        const dim3 grid((unsigned)((rows + 7) / 8));
         switch (a.D) {
         case 64: hipLaunchKernelGGL(combine_rows<64>, grid, dim3(256), 0, stream, a); break;
         case 128: hipLaunchKernelGGL(combine_rows<128>, grid, dim3(256), 0, stream, a); break;

@@ -84,7 +84,7 @@ struct CombineArgs {
     int append;                  // sequences hold seq_lens[b] + 1 tokens
     int causal;                  // query r / G sees T_b - (nq - 1 - r / G) tokens:
                                  // only splits that start below that are read
-    int per_wave;                // 1: one wave per row (many rows, few splits)
+    int per_wave;                // 1: half a wave per row (many rows, few splits)
 };
 
 // Shape constants of the vector-ALU split kernel.  Each 64-lane wavefront

@@ -293,13 +293,13 @@ def test_several_queries_rejects(lib):
 
 def _query_tiled_splits(units, T, cus=256, n_req=0, tiles=2):
     """The planner's KV split rule for the query-tiled kernel, restated:
-    about 8 * cus workgroups (four rounds at two per compute unit); with one
-    row tile per kv head of a contiguous cache 4 * cus, or none once the
-    tiles alone give 2 * cus; no split below 1024 tokens; chunks are whole
-    32-token tiles."""
+    about 8 * cus workgroups (four rounds at two per compute unit), none
+    once the row tiles alone give 4 * cus; with one row tile per kv head of
+    a contiguous cache 4 * cus, none from 2 * cus; no split below 1024
+    tokens; chunks are whole 32-token tiles."""
     if n_req > 0:
         n = min(n_req, -(-T // 32))
-    elif tiles == 1 and units >= 2 * cus:
+    elif units >= (2 if tiles == 1 else 4) * cus:
         n = 1
     else:
         target = (8 if tiles > 1 else 4) * cus
