@@ -39,7 +39,7 @@
  *     verifying a draft); a query with no token yields out = 0, lse = -inf.
  *     Up to 16 queries run on the split-KV kernels (every query row of a kv
  *     head shares one read of K / V), as long as a kv head has at most 16
- *     query rows (n_q * G; 32 for paged caches) or the inputs are fp32;
+ *     query rows (n_q * G) or the inputs are fp32;
  *     more queries (the
  *     prefill phase: the dupenodi guide, "Concept", has prefill attend with
  *     the whole block of prompt queries), or more rows, run on a query-tiled
@@ -137,8 +137,7 @@ typedef struct fd_options {
     int32_t n_queries;          /* queries per sequence, 1 .. 65536 (0 = 1);  */
                                 /* > 1 gives q / out an n_q axis (see below); */
                                 /* > 16 (or > 16 query rows per kv head,     */
-                                /* 32 paged; f16 / bf16) runs the query-     */
-                                /* tiled kernel                              */
+                                /* f16 / bf16) runs the query-tiled kernel   */
     int32_t causal;             /* with n_queries > 1: 1 = query i sees the   */
                                 /* first T_b - (n_queries - 1 - i) tokens     */
 } fd_options_t;

@@ -46,14 +46,12 @@ long env_long(const char *name, long dflt) {
 constexpr uint32_t kOptionsV1 = sizeof(fd_options_t);
 constexpr int kMaxQueries = 65536;       // queries per sequence
 constexpr int kMaxDecodeQueries = 16;    // more take the query-tiled (prefill) kernel
-// More query rows per kv head than these take the query-tiled kernel too
+// More query rows per kv head than this take the query-tiled kernel too
 // (f16 / bf16), which reads K/V once for a tile of 64 or 128 rows.  The
 // matrix-core split kernel holds 32 rows in one K/V read (two 16-row
-// blocks), but from 17 rows on the query-tiled kernel is faster on
-// contiguous caches (measured); paged (ragged) batches keep the split
-// kernel's balanced stream mode up to 32.
+// blocks), but from 17 rows on the query-tiled kernel is faster (measured,
+// contiguous and paged caches).
 constexpr int kMaxSplitRows = 16;
-constexpr int kMaxSplitRowsPaged = 32;
 // bf16 V is converted to f16 for the query-tiled kernel's value product
 // from this many query rows per kv head: the conversion reads V twice and
 // writes it once, which the cheaper product repays only when many rows
@@ -145,8 +143,7 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
     // (two passes ahead of the kernel); with fewer, V is read as given and
     // P enters the value product in two bf16 parts.  FD_PREFILL_VT=0 / 1
     // forces either form.
-    const bool many_rows = o.dtype != FD_F32 && R > (paged ? kMaxSplitRowsPaged : kMaxSplitRows) &&
-                           !(o.flags & FD_FLAG_APPEND);
+    const bool many_rows = o.dtype != FD_F32 && R > kMaxSplitRows && !(o.flags & FD_FLAG_APPEND);
     if (path == FD_PATH_PREFILL ||
         (path == FD_PATH_AUTO && (o.n_queries > kMaxDecodeQueries || many_rows))) {
         if (o.dtype == FD_F32) return fail(FD_ERR_UNSUPPORTED, "the query-tiled kernel needs f16 or bf16 inputs");

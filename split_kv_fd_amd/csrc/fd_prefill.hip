@@ -447,6 +447,19 @@ __global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void prefill(PrefillArgs a) {
     //     loads read clamped rows (or zeros) and the logits go unused, so nothing there
     //     needs a branch, and the matrix-core work of the logits can be
     //     interleaved with the vector work of the probabilities.
+    // End of a tile step: tile j+2 (loaded one step earlier) into its LDS
+    // buffer, whose previous tile j-1 is finished; tile j+3 from memory.
+    auto stage_next = [&](auto bjc, const int j) {
+        constexpr int bj = decltype(bjc)::value;
+        store_tile((bj + 2) % NBUF, g);
+        if constexpr (PREFETCH_PAGES) {
+            g = load_tile(j + 3, pnext);
+            pnext = fetch_pages(j + 4);
+        } else {
+            g = load_tile(j + 3, fetch_pages(j + 3));
+        }
+        __syncthreads();
+    };
     auto step = [&](auto bjc, const int j, const f32x4_v (&cc)[NB][2], f32x4_v (&cn)[NB][2]) {
         constexpr int bj = decltype(bjc)::value;   // j % NBUF, known at compile time
         // Masks: tiles every row of the wave sees in full need none; there
@@ -553,14 +566,7 @@ __global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void prefill(PrefillArgs a) {
                     for (int nb = 0; nb < NB; ++nb) acc[nb][dt + y] = mfma<DT>(va[y], plo[nb], acc[nb][dt + y]);
             }
         }
-        store_tile((bj + 2) % NBUF, g);         // its buffer held tile j-1, finished
-        if constexpr (PREFETCH_PAGES) {
-            g = load_tile(j + 3, pnext);
-            pnext = fetch_pages(j + 4);
-        } else {
-            g = load_tile(j + 3, fetch_pages(j + 3));
-        }
-        __syncthreads();
+        stage_next(bjc, j);
     };
 
     // The loop runs three tiles per trip, so every LDS buffer index is a
@@ -589,15 +595,31 @@ __global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void prefill(PrefillArgs a) {
             g = load_tile(j0 + 2, pnext);
         }
         __syncthreads();
-        qk(0, cA);
         int j = 0;
-        for (; j + 3 <= nt; j += 3) {
-            step(B0{}, j0 + j, cA, cB);
-            step(B1{}, j0 + j + 1, cB, cC);
-            step(B2{}, j0 + j + 2, cC, cA);
+        if (NB == 1 && r0 + 16 * NB * wave >= a.R) {
+            // every row block of this wave is past the last row: it computes
+            // nothing and only helps stage the tiles, through the same
+            // barriers (the wave index is uniform, so is the branch).  Only
+            // the 64-row tiles of few-row calls take this form (in 128-row
+            // tiles it would make the paged instance spill, and a tile there
+            // idles waves only when it is a kv head's last)
+            for (; j + 3 <= nt; j += 3) {
+                stage_next(B0{}, j0 + j);
+                stage_next(B1{}, j0 + j + 1);
+                stage_next(B2{}, j0 + j + 2);
+            }
+            if (j < nt) stage_next(B0{}, j0 + j);
+            if (j + 1 < nt) stage_next(B1{}, j0 + j + 1);
+        } else {
+            qk(0, cA);
+            for (; j + 3 <= nt; j += 3) {
+                step(B0{}, j0 + j, cA, cB);
+                step(B1{}, j0 + j + 1, cB, cC);
+                step(B2{}, j0 + j + 2, cC, cA);
+            }
+            if (j < nt) step(B0{}, j0 + j, cA, cB);
+            if (j + 1 < nt) step(B1{}, j0 + j + 1, cB, cC);
         }
-        if (j < nt) step(B0{}, j0 + j, cA, cB);
-        if (j + 1 < nt) step(B1{}, j0 + j + 1, cB, cC);
     }
 
     // The four lanes of a row share m; their sums cover different tokens.

@@ -120,13 +120,17 @@ def test_plan_paged_chunks_align_to_pages(lib):
     assert plan(1, 4, 4, 100, 128, flags=3)[0] == fd.FD_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("G,dtype", [(4, fd.FD_BF16), (1, fd.FD_F16), (8, fd.FD_F32), (32, fd.FD_BF16)])
-def test_plan_paged_stream_mode(lib, G, dtype):
-    # automatic plans of paged (ragged) batches use the balanced stream mode:
-    # one workgroup per stream range, two per compute unit, merged in-launch
+@pytest.mark.parametrize("G,dtype,path", [(4, fd.FD_BF16, fd.FD_PATH_AUTO), (1, fd.FD_F16, fd.FD_PATH_AUTO),
+                                          (8, fd.FD_F32, fd.FD_PATH_AUTO), (16, fd.FD_BF16, fd.FD_PATH_AUTO),
+                                          (32, fd.FD_BF16, fd.FD_PATH_MFMA)])
+def test_plan_paged_stream_mode(lib, G, dtype, path):
+    # automatic plans of paged (ragged) batches on the split kernels use the
+    # balanced stream mode: one workgroup per stream range, two per compute
+    # unit, merged in-launch (32 query rows per kv head would take the
+    # query-tiled kernel unless the matrix-core path is asked for)
     B, Hkv, D = 16, 2, 128
     st, p = plan(B, G * Hkv, Hkv, 65536, D, 0, dtype=dtype, page_size=16,
-                 max_pages_per_seq=4096, num_pages=10, num_cus=100)
+                 max_pages_per_seq=4096, num_pages=10, num_cus=100, path=path)
     assert st == fd.FD_OK, fd.fd_last_error()
     assert p.stream and p.fused and p.combine and p.chunk == 0
     assert (p.n_splits, p.grid[0], p.grid[1], p.grid[2]) == (200, 200, 1, 1)
@@ -136,7 +140,7 @@ def test_plan_paged_stream_mode(lib, G, dtype):
     assert p.tile > 0 and p.tile % 16 == 0
     # too many sequences for the on-chip prefix scan: the split grid
     st, p = plan(4096, G * Hkv, Hkv, 1024, D, 0, dtype=dtype, page_size=16,
-                 max_pages_per_seq=64, num_pages=10)
+                 max_pages_per_seq=64, num_pages=10, path=path)
     assert st == fd.FD_OK and not p.stream and p.chunk > 0
 
 
@@ -412,29 +416,28 @@ def test_plan_query_tiled_size_limits(lib):
     assert st == fd.FD_OK and p.n_splits == 128 and p.workspace_bytes > 0
 
 
-@pytest.mark.parametrize("nq,G,dtype,want,want_paged", [
-    (1, 16, fd.FD_BF16, fd.FD_PATH_MFMA, fd.FD_PATH_MFMA),        # 16 rows: split kernels
-    (1, 32, fd.FD_BF16, fd.FD_PATH_PREFILL, fd.FD_PATH_MFMA),     # 32 rows: paged keeps stream mode
-    (1, 64, fd.FD_BF16, fd.FD_PATH_PREFILL, fd.FD_PATH_PREFILL),  # 64 rows of one query
-    (4, 4, fd.FD_F16, fd.FD_PATH_MFMA, fd.FD_PATH_MFMA),
-    (5, 4, fd.FD_BF16, fd.FD_PATH_PREFILL, fd.FD_PATH_MFMA),      # 20 rows
-    (9, 4, fd.FD_F16, fd.FD_PATH_PREFILL, fd.FD_PATH_PREFILL),    # 36 rows
-    (16, 8, fd.FD_BF16, fd.FD_PATH_PREFILL, fd.FD_PATH_PREFILL),
-    (16, 8, fd.FD_F32, fd.FD_PATH_VALU, fd.FD_PATH_VALU),         # fp32 stays on the vector kernel
-    (17, 1, fd.FD_F16, fd.FD_PATH_PREFILL, fd.FD_PATH_PREFILL),   # more than 16 queries
+@pytest.mark.parametrize("nq,G,dtype,want", [
+    (1, 16, fd.FD_BF16, fd.FD_PATH_MFMA),        # 16 rows: split kernels
+    (1, 32, fd.FD_BF16, fd.FD_PATH_PREFILL),     # 32 rows
+    (1, 64, fd.FD_BF16, fd.FD_PATH_PREFILL),     # 64 rows of one query
+    (4, 4, fd.FD_F16, fd.FD_PATH_MFMA),
+    (5, 4, fd.FD_BF16, fd.FD_PATH_PREFILL),      # 20 rows
+    (9, 4, fd.FD_F16, fd.FD_PATH_PREFILL),       # 36 rows
+    (16, 8, fd.FD_BF16, fd.FD_PATH_PREFILL),
+    (16, 8, fd.FD_F32, fd.FD_PATH_VALU),         # fp32 stays on the vector kernel
+    (17, 1, fd.FD_F16, fd.FD_PATH_PREFILL),      # more than 16 queries
 ])
-def test_plan_rows_route(lib, nq, G, dtype, want, want_paged):
-    # query rows per kv head (n_q * G) past 16 (contiguous) or 32 (paged,
-    # where the split kernels' stream mode balances ragged lengths) take
-    # the query-tiled kernel, which reads K/V once for a 64- or 128-row
-    # tile; one-query calls with an appended token stay on the split kernels
+def test_plan_rows_route(lib, nq, G, dtype, want):
+    # query rows per kv head (n_q * G) past 16 take the query-tiled kernel,
+    # which reads K/V once for a 64- or 128-row tile, contiguous or paged;
+    # one-query calls with an appended token stay on the split kernels
     st, p = plan(2, G * 2, 2, 4096, 128, 0, n_queries=nq, causal=1 if nq > 1 else 0, dtype=dtype)
     assert st == fd.FD_OK, fd.fd_last_error()
     assert p.path == want
     st, p = plan(2, G * 2, 2, 4096, 128, 0, n_queries=nq, causal=1 if nq > 1 else 0, dtype=dtype,
                  page_size=16, max_pages_per_seq=256, num_pages=10)
     assert st == fd.FD_OK, fd.fd_last_error()
-    assert p.path == want_paged
+    assert p.path == want
     st, p = plan(2, 64 * 2, 2, 4096, 128, 0, flags=fd.FD_FLAG_APPEND)
     assert st == fd.FD_OK and p.path == fd.FD_PATH_MFMA
 
