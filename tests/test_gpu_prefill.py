@@ -400,20 +400,21 @@ def test_prefill_ragged_full_size_sampled():
             assert err <= parity.OUT_TOL["bf16"] and lerr <= parity.LSE_TOL["bf16"]
 
 
+@pytest.mark.parametrize("D", [128, 64])
 @pytest.mark.parametrize("P", [1, 16, 64])
 @pytest.mark.parametrize("nq,G,dtype", [(16, 4, "bf16"), (9, 4, "f16"), (40, 4, "f16"), (40, 4, "bf16")])
-def test_query_tiled_paged_page_ids(P, nq, G, dtype):
+def test_query_tiled_paged_page_ids(P, nq, G, dtype, D):
     # paged caches through the query-tiled kernel in each page-id form: read
     # one tile ahead (64-row tiles; bf16 128-row tiles with V unconverted)
     # or just before (f16 128-row tiles); one-token pages take a page id
     # per token.  Ragged lengths, a page shuffle, KV splits, both masks
     s = inputs.spec("paged_ragged_bf16", B=3, Hq=G * 2, Hkv=2, T=1800, page_size=P, len_lo=40, len_hi=1800,
-                    dtype=dtype)
+                    dtype=dtype, D=D)
     case = inputs.make_case(s).to(DEV)
     q = inputs.make_q_multi(s, nq).to(DEV)
     for causal in (False, True):
         for n in (0, 3):
             plan = check_multi(case, q, causal, n_splits=n,
-                               what=f"paged page ids P={P} nq={nq} G={G} {dtype} n={n} causal={causal}")
+                               what=f"paged page ids D={D} P={P} nq={nq} G={G} {dtype} n={n} causal={causal}")
             assert plan["path"] == "prefill"
             assert plan["heads_per_block"] == (64 if nq * G <= 64 else 128)
