@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 import torch
 
+from oracle import oracle as oracle_mod
 from split_kv_fd_amd import inputs
 from split_kv_fd_amd.decode import Decoder
 from tests import parity
@@ -351,3 +352,41 @@ def test_full_gqa_b64_bf16_hot_heads():
     qn = case.q.float().norm(dim=-1)                     # [B, Hq]
     hot = [int(b * s.Hq + int(qn[b].argmax())) for b in (0, 31, 63)]
     parity.sampled_rows(case, _full_rows(case, extra=hot), out, lse, "b64 gqa")
+
+
+def test_largest_contiguous_slice():
+    # one (batch, kv head) slice just under 4 GiB -- the largest the kernels'
+    # 32-bit offsets address (2^24 - 32 tokens x 128 x 2 bytes) -- through
+    # the vector and matrix-core split kernels and, with 8 causal queries
+    # (32 rows per kv head), the query-tiled kernel with its KV splits;
+    # sampled against the oracle
+    T = (1 << 24) - 32
+    s = inputs.spec("gqa128k_bf16", B=1, Hq=4, Hkv=1, T=T)
+    case = inputs.make_case(s, device=DEV)
+    parity.announce(f"largest slice T={T}: host copies for the oracle")
+    k_h, v_h = case.k.cpu(), case.v.cpu()
+    vmax = float(v_h.abs().max())
+    orc = oracle_mod.default()
+    ref, ref_l = orc.decode(case.q.cpu(), k_h, v_h, s.scale)
+    for path in ("valu", "mfma"):
+        out, lse, plan = parity.run_gpu(case, 0, path=path)
+        assert plan["path"] == path
+        err = float(np.max(np.abs(out - ref))) / vmax
+        lerr = float(np.max(np.abs(lse - ref_l)))
+        parity.announce(f"largest slice {path}: err {err:.2e} lse {lerr:.2e}")
+        assert err <= parity.OUT_TOL["bf16"] and lerr <= parity.LSE_TOL["bf16"]
+    nq = 8
+    q = inputs.make_q_multi(s, nq, device=DEV)
+    dec = Decoder(q, case.k, case.v, scale=s.scale, causal=True)
+    assert dec.plan["path"] == "prefill" and dec.plan["n_splits"] > 1
+    parity.announce(f"largest slice query-tiled plan={dec.plan}")
+    out, lse = dec()
+    torch.cuda.synchronize()
+    for i in (0, nq - 1):
+        r, rl = orc.decode(q[:, i].cpu(), k_h, v_h, s.scale, seq_lens=np.array([T - (nq - 1 - i)], np.int32))
+        err = float(np.max(np.abs(out[0, i].cpu().double().numpy() - r[0]))) / vmax
+        lerr = float(np.max(np.abs(lse[0, i].cpu().double().numpy() - rl[0])))
+        parity.announce(f"largest slice query-tiled query={i}: err {err:.2e} lse {lerr:.2e}")
+        assert err <= parity.OUT_TOL["bf16"] and lerr <= parity.LSE_TOL["bf16"]
+    del dec, out, lse, q, case, k_h, v_h
+    torch.cuda.empty_cache()
