@@ -390,3 +390,29 @@ def test_largest_contiguous_slice():
         assert err <= parity.OUT_TOL["bf16"] and lerr <= parity.LSE_TOL["bf16"]
     del dec, out, lse, q, case, k_h, v_h
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("B,layout", [(2048, "paged"), (2049, "paged"), (65535, "contiguous")])
+def test_many_sequences(B, layout):
+    # batch-size edges: stream mode scans at most 2048 sequences on chip
+    # (one more falls back to the split grid), and B = 65535 is the largest
+    # grid the split kernels take; short ragged sequences, some empty
+    if layout == "paged":
+        s = inputs.spec("paged_ragged_bf16", B=B, Hq=8, Hkv=2, D=64, T=48, page_size=16, len_lo=0, len_hi=48)
+    else:
+        s = inputs.spec("gqa128k_bf16", B=B, Hq=4, Hkv=1, D=64, T=8)
+    case = inputs.make_case(s).to(DEV)
+    (_, _), plan = parity.check_full(case, what=f"B={B} {layout}")
+    if layout == "paged":
+        assert plan["stream"] == (B <= 2048)
+
+
+def test_many_sequences_query_tiled():
+    # the query-tiled kernel's grid at a large batch (z = B), with KV splits
+    s = inputs.spec("gqa128k_bf16", B=3000, Hq=4, Hkv=1, D=64, T=40)
+    case = inputs.make_case(s).to(DEV)
+    from tests.test_gpu_multi import check_multi
+    q = inputs.make_q_multi(s, 20).to(DEV)
+    for n in (0, 2):
+        plan = check_multi(case, q, True, n_splits=n, what=f"query-tiled B=3000 n={n}")
+        assert plan["path"] == "prefill"
