@@ -275,8 +275,11 @@ def main() -> int:
                 "launch_us_avg": round(split_avg * 1e3, 2),
                 "bytes_per_launch": kv_bytes}
     if plan["path"] == "prefill":
-        # the query-tiled kernel is bounded by the matrix cores: 2 flops per
-        # multiply-add for q.k and for p.v over every (query row, token seen)
+        # the query-tiled kernel: 2 flops per multiply-add for q.k and for
+        # p.v over every (query row, token seen).  Its bound follows the
+        # call's arithmetic intensity: below the ridge point (peak flops over
+        # peak bytes) K/V reads bound it (a few queries per sequence), above
+        # it the matrix cores (prefill).
         seen = 0
         for L in lens:
             for i in range(args.n_queries):
@@ -284,12 +287,24 @@ def main() -> int:
         flops = 4 * spec.D * spec.Hq * seen
         tf = flops / (split_avg * 1e-3) / 1e12
         kernel = "fd_prefill"
-        roofline = {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(tf / MFMA_PEAK_TFLOPS, 4),
-                    "traffic": read_traffic(spec.name, kernel), "kernel": kernel,
-                    "launch_us_avg": round(split_avg * 1e3, 2), "flops_per_launch": flops}
-        if plan["workspace_bytes"]:
-            # bf16: the two V conversion passes run inside the timed call
+        ridge = MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+        if flops / kv_bytes >= ridge:
+            roofline = {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(tf / MFMA_PEAK_TFLOPS, 4)}
+        else:
+            roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                        "bytes_per_launch": kv_bytes, "tflops": round(tf, 2)}
+        roofline.update({"traffic": read_traffic(spec.name, kernel), "kernel": kernel,
+                         "launch_us_avg": round(split_avg * 1e3, 2), "flops_per_launch": flops,
+                         "flops_per_kv_byte": round(flops / kv_bytes, 1), "ridge_flops_per_byte": round(ridge, 1)})
+        # the workspace holds the split partials and, when V is converted,
+        # the converted V: then the two conversion passes run inside the
+        # timed launch
+        a256 = lambda x: -(-x // 256) * 256
+        parts = spec.B * spec.Hkv * args.n_queries * spec.G * plan["n_splits"]
+        part_bytes = a256(parts * spec.D * 4) + 2 * a256(parts * 4) if plan["n_splits"] > 1 else 0
+        if plan["workspace_bytes"] > part_bytes:
             roofline["launch_includes"] = "V conversion passes + query-tiled kernel"
 
     if overrides:
