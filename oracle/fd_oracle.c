@@ -35,7 +35,7 @@
  * order), the oracle does NOT split, tile or rescale online: subtracting m
  * is only the textbook stable form of one softmax over all T_b logits.
  *
- * Readings taken where the pages are silent (each listed in the design doc):
+ * Readings taken where the pages are silent:
  *   - GQA: query head h reads kv head h / (Hq/Hkv) (consecutive groups).
  *   - Paged layout: pool [num_pages, Hkv, P, D]; token t of sequence b lives
  *     in page page_table[b*max_pages + t/P] at in-page row t % P.
