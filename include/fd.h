@@ -152,9 +152,12 @@ typedef struct fd_plan {
     int32_t path;               /* fd_path_t that runs                        */
     int32_t tile;               /* tokens one workgroup consumes per step     */
     int32_t heads_per_block;    /* query heads of one kv group per workgroup  */
+                                /* (query-tiled plans: rows per row tile)     */
     int32_t head_blocks;        /* workgroups across one kv head's group      */
+                                /* (query-tiled plans: row tiles)             */
     int32_t grid[3];            /* split-kernel grid (x: split, y: kv head *  */
-                                /* head_blocks, z: batch)                     */
+                                /* head_blocks, z: batch; query-tiled plans:  */
+                                /* x: row tiles * splits, y: kv head, z: batch) */
     int32_t block;              /* threads per split workgroup                */
     int32_t combine;            /* 1 if the splits are merged (n_splits > 1)   */
     int32_t fused;              /* 1 if fd_decode merges them inside the split */
