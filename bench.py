@@ -8,10 +8,14 @@ To keep the 256 MiB last-level cache from serving KV bytes, each step reads
 a different one of several identical copies of the KV cache (together at
 least 1 GiB).
 
-Prints ONE JSON line: KV read throughput (GB/s, algorithmic bytes over wall
-time), us per step, the split kernel's roofline fraction from HIP events
-recorded around it in the timed loop, and the fp64 CPU oracle's throughput
-on a bounded sample of the same workload as a host baseline.
+Prints ONE JSON line for the headline workload (by default the largest:
+B=64 GQA 64/8 heads over 32768 bf16 tokens, 8.6 GB of KV per step): KV read
+throughput (GB/s, algorithmic bytes over wall time), us per step, the split
+kernel's roofline fraction from HIP events recorded around it in the timed
+loop, and the fp64 CPU oracle's throughput on a bounded sample of the same
+workload as a host baseline.  The default run then times the other
+long-context workloads (MHA 32k f16, GQA 128k bf16, the paged ragged
+batch) the same way in the same process and nests them under "configs".
 
     python bench.py [--steps K] [--warmup W] [--config NAME] [--n-splits N]
 """
@@ -32,7 +36,9 @@ sys.path.insert(0, ROOT)
 METRIC = "decode-attention KV read GB/s (fraction of HBM peak) and µs/step, 1 MI355X"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = 2500.0        # dense bf16 / f16 matrix-core peak
-DEFAULT_WORKLOAD = "mha32k_f16"
+DEFAULT_WORKLOAD = "gqa_b64_bf16"
+# timed after the headline workload in the default run
+OTHER_WORKLOADS = ("mha32k_f16", "gqa128k_bf16", "paged_ragged_bf16")
 ELT = {"f32": 4, "f16": 2, "bf16": 2}
 
 
@@ -159,61 +165,15 @@ def copy_calibration(gib: float = 1.0, reps: int = 5):
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "reps": reps}), flush=True)
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--config", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--n-splits", type=int, default=0, help="0 = the planner's choice")
-    ap.add_argument("--path", default=None, choices=[None, "auto", "valu", "mfma", "prefill"])
-    ap.add_argument("--merge", default="auto", choices=["auto", "fused", "combine"],
-                    help="force the fused merge or the combine kernel (default: library's choice)")
-    ap.add_argument("--event-every", type=int, default=8,
-                    help="one-launch steps: events bracket blocks of N launches; two-launch steps: "
-                         "the launches of every N-th step")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--set", action="append", default=[], metavar="KEY=VALUE",
-                    help="override a workload field (experiments; e.g. T=65536)")
-    ap.add_argument("--append", action="store_true",
-                    help="time fd_append_decode: each sequence caches T_b - 1 tokens and the step "
-                         "stores and attends to token T_b (same KV bytes as the plain step)")
-    ap.add_argument("--n-queries", type=int, default=1,
-                    help="queries per sequence (q [B, n_q, Hq, D]); the KV bytes stay those of one read")
-    ap.add_argument("--causal", action="store_true",
-                    help="with --n-queries: query i sees the first T_b - (n_q - 1 - i) tokens")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run a 1 GiB device copy (for counter scaling) and exit")
-    args = ap.parse_args()
-
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: the decode runs on a single MI355X and there is no "
-              "multi-GPU path to time. Run it with --gpus 1.", file=sys.stderr)
-        return 2
-
+def measure(spec, case, args, overrides=None):
+    """Time K steps of one workload (after W warm-up steps) with its inputs
+    resident in HBM, rotating over KV copies of at least 1 GiB together.
+    Returns the measured figures (wall time per step, KV bytes, the split
+    launch's event-timed duration, the roofline of its kernel, the plan)."""
     import torch
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        return 1
-    if args.copy_calibration:
-        copy_calibration()
-        return 0
-
-    from split_kv_fd_amd import fd, inputs
+    from split_kv_fd_amd import inputs
     from split_kv_fd_amd.decode import Decoder
-    fd.load()   # fails loudly if the HIP library is not built
 
-    overrides = {}
-    for kv in args.set:
-        key, _, val = kv.partition("=")
-        cur = getattr(inputs.SPECS[args.config], key)
-        overrides[key] = type(cur)(float(val)) if not isinstance(cur, (str, bool)) else (
-            val if isinstance(cur, str) else val.lower() in ("1", "true", "yes"))
-    spec = inputs.spec(args.config, **overrides)
-    print(f"[bench] generating {spec.name} on the GPU", file=sys.stderr, flush=True)
-    case = inputs.make_case(spec, device="cuda")
     lens = case.lengths()
     kv_bytes = kv_bytes_of(spec, lens)
     new_rows = (None, None)
@@ -234,7 +194,7 @@ def main() -> int:
                             fused_merge={"auto": None, "fused": True, "combine": False}[args.merge],
                             k_new=new_rows[0], v_new=new_rows[1], causal=args.causal))
     plan = decs[0].plan
-    print(f"[bench] plan {plan}; {copies} KV copies", file=sys.stderr, flush=True)
+    print(f"[bench] {spec.name}: plan {plan}; {copies} KV copies", file=sys.stderr, flush=True)
 
     for i in range(args.warmup):
         decs[i % copies]()
@@ -286,7 +246,7 @@ def main() -> int:
     split_avg = statistics.mean(split_ms)
     achieved = kv_bytes / (split_avg * 1e-3) / 1e9
     kernel = "fd_split"
-    traffic = read_traffic(spec.name, kernel)
+    traffic = None if overrides else read_traffic(spec.name, kernel)
     roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "kernel": kernel,
@@ -305,8 +265,8 @@ def main() -> int:
         flops = 4 * spec.D * spec.Hq * seen
         kernel = "fd_prefill"
         roofline = query_tiled_roofline(flops, kv_bytes, split_avg)
-        roofline.update({"traffic": read_traffic(spec.name, kernel), "kernel": kernel,
-                         "launch_us_avg": round(split_avg * 1e3, 2)})
+        roofline.update({"traffic": None if overrides else read_traffic(spec.name, kernel),
+                         "kernel": kernel, "launch_us_avg": round(split_avg * 1e3, 2)})
         # the workspace holds the split partials and, when V is converted,
         # the converted V: then the two conversion passes run inside the
         # timed launch
@@ -315,18 +275,99 @@ def main() -> int:
         part_bytes = a256(parts * spec.D * 4) + 2 * a256(parts * 4) if plan["n_splits"] > 1 else 0
         if plan["workspace_bytes"] > part_bytes:
             roofline["launch_includes"] = "V conversion passes + query-tiled kernel"
+    del decs
+    torch.cuda.synchronize()
+    return {"ms_per_step": ms_per_step, "gbs": gbs, "kv_bytes": kv_bytes, "copies": copies,
+            "plan": plan, "roofline": roofline, "separate": separate,
+            "split_ms": split_ms, "comb_ms": comb_ms, "step_ms": step_ms, "split_avg": split_avg}
 
+
+def kernels_us(m) -> dict:
+    return {"split_avg": round(m["split_avg"] * 1e3, 2),
+            "merge": "fused into the split launch" if not m["separate"] else "combine kernel",
+            "split_median": round(statistics.median(m["split_ms"]) * 1e3, 2),
+            "combine_avg": round(statistics.mean(m["comb_ms"]) * 1e3, 2),
+            "step_events_median": round(statistics.median(m["step_ms"]) * 1e3, 2),
+            "split_p10": round(_pct(m["split_ms"], 10) * 1e3, 2),
+            "split_p90": round(_pct(m["split_ms"], 90) * 1e3, 2)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--config", default=None,
+                    help=f"workload to time (default {DEFAULT_WORKLOAD}, with the other long-context "
+                         "workloads timed after it under 'configs')")
+    ap.add_argument("--n-splits", type=int, default=0, help="0 = the planner's choice")
+    ap.add_argument("--path", default=None, choices=[None, "auto", "valu", "mfma", "prefill"])
+    ap.add_argument("--merge", default="auto", choices=["auto", "fused", "combine"],
+                    help="force the fused merge or the combine kernel (default: library's choice)")
+    ap.add_argument("--event-every", type=int, default=8,
+                    help="one-launch steps: events bracket blocks of N launches; two-launch steps: "
+                         "the launches of every N-th step")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="time only the headline workload (skip the other long-context workloads)")
+    ap.add_argument("--set", action="append", default=[], metavar="KEY=VALUE",
+                    help="override a workload field (experiments; e.g. T=65536)")
+    ap.add_argument("--append", action="store_true",
+                    help="time fd_append_decode: each sequence caches T_b - 1 tokens and the step "
+                         "stores and attends to token T_b (same KV bytes as the plain step)")
+    ap.add_argument("--n-queries", type=int, default=1,
+                    help="queries per sequence (q [B, n_q, Hq, D]); the KV bytes stay those of one read")
+    ap.add_argument("--causal", action="store_true",
+                    help="with --n-queries: query i sees the first T_b - (n_q - 1 - i) tokens")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (for counter scaling) and exit")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the decode runs on a single MI355X and there is no "
+              "multi-GPU path to time. Run it with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    if args.copy_calibration:
+        copy_calibration()
+        return 0
+
+    from split_kv_fd_amd import fd, inputs
+    fd.load()   # fails loudly if the HIP library is not built
+
+    name = args.config or DEFAULT_WORKLOAD
+    overrides = {}
+    for kv in args.set:
+        key, _, val = kv.partition("=")
+        cur = getattr(inputs.SPECS[name], key)
+        overrides[key] = type(cur)(float(val)) if not isinstance(cur, (str, bool)) else (
+            val if isinstance(cur, str) else val.lower() in ("1", "true", "yes"))
+    spec = inputs.spec(name, **overrides)
+    print(f"[bench] generating {spec.name} on the GPU", file=sys.stderr, flush=True)
+    case = inputs.make_case(spec, device="cuda")
+    m = measure(spec, case, args, overrides)
+    print(f"[bench] {spec.name}: {m['ms_per_step'] * 1e3:.2f} us/step, {m['gbs']:.1f} GB/s", file=sys.stderr,
+          flush=True)
+    K = args.steps
+    plan = m["plan"]
+    kv_bytes = m["kv_bytes"]
     if overrides:
         print(f"[bench] workload overrides {overrides}: not the reference workload",
               file=sys.stderr, flush=True)
     result = {
         "metric": METRIC,
-        "value": round(gbs, 2),
+        "value": round(m["gbs"], 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": round(m["ms_per_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -335,21 +376,15 @@ def main() -> int:
         "config": {"workload": spec.name + ("" if not overrides else f" (overrides {overrides})"),
                    "B": spec.B, "Hq": spec.Hq, "Hkv": spec.Hkv, "G": spec.G,
                    "D": spec.D, "T": spec.T, "kv_dtype": spec.dtype, "accumulate": "f32",
-                   "kv_bytes_per_step": kv_bytes, "kv_copies_rotated": copies,
+                   "kv_bytes_per_step": kv_bytes, "kv_copies_rotated": m["copies"],
                    "n_splits": plan["n_splits"], "chunk": plan["chunk"], "path": plan["path"],
-                   "fused_merge": plan["fused"], "seed": spec.seed,
+                   "fused_merge": plan["fused"], "stream_mode": plan["stream"], "seed": spec.seed,
                    "step": "fd_append_decode" if args.append else "fd_decode",
                    "n_queries": args.n_queries, "causal": bool(args.causal)},
-        "us_per_step": round(ms_per_step * 1e3, 2),
-        "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-        "roofline": roofline,
-        "kernels_us": {"split_avg": round(split_avg * 1e3, 2),
-                       "merge": "fused into the split launch" if not separate else "combine kernel",
-                       "split_median": round(statistics.median(split_ms) * 1e3, 2),
-                       "combine_avg": round(statistics.mean(comb_ms) * 1e3, 2),
-                       "step_events_median": round(statistics.median(step_ms) * 1e3, 2),
-                       "split_p10": round(_pct(split_ms, 10) * 1e3, 2),
-                       "split_p90": round(_pct(split_ms, 90) * 1e3, 2)},
+        "us_per_step": round(m["ms_per_step"] * 1e3, 2),
+        "frac_of_hbm_peak": round(m["gbs"] / HBM_PEAK_GBS, 4),
+        "roofline": m["roofline"],
+        "kernels_us": kernels_us(m),
         "kernel_source_sha": kernel_source_sha(),
     }
     if not args.no_cpu_baseline:
@@ -357,6 +392,36 @@ def main() -> int:
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     else:
         result["cpu_baseline"] = None
+    del case
+    torch.cuda.empty_cache()
+
+    # The other long-context workloads, timed the same way in this process
+    # (the headline line above is the largest one).
+    if args.config is None and not overrides and not args.no_configs:
+        result["configs"] = {}
+        for other in OTHER_WORKLOADS:
+            s2 = inputs.spec(other)
+            print(f"[bench] generating {other} on the GPU", file=sys.stderr, flush=True)
+            c2 = inputs.make_case(s2, device="cuda")
+            m2 = measure(s2, c2, args)
+            del c2
+            torch.cuda.empty_cache()
+            print(f"[bench] {other}: {m2['ms_per_step'] * 1e3:.2f} us/step, {m2['gbs']:.1f} GB/s",
+                  file=sys.stderr, flush=True)
+            p2 = m2["plan"]
+            result["configs"][other] = {
+                "us_per_step": round(m2["ms_per_step"] * 1e3, 2),
+                "kv_gbs": round(m2["gbs"], 2),
+                "frac_of_hbm_peak": round(m2["gbs"] / HBM_PEAK_GBS, 4),
+                "kv_bytes_per_step": m2["kv_bytes"],
+                "split_launch_us_avg": m2["roofline"]["launch_us_avg"],
+                "split_launch_frac": m2["roofline"]["frac"],
+                "traffic": m2["roofline"]["traffic"],
+                "kernels_us": kernels_us(m2),
+                "kv_copies_rotated": m2["copies"],
+                "plan": {"path": p2["path"], "n_splits": p2["n_splits"], "chunk": p2["chunk"],
+                         "fused_merge": p2["fused"], "stream_mode": p2["stream"], "grid": p2["grid"]},
+            }
     print(json.dumps(result), flush=True)
     return 0
 

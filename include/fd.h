@@ -217,7 +217,14 @@ size_t fd_workspace_bytes(int B, int Hq, int Hkv, int T, int D, int n_splits,
  * any other call are ignored (a fused call leaves its counters tagged for
  * the next call on the same workspace, which then counts arrivals with one
  * atomic add each; anything else is counted once through a slower exchange
- * loop).  Calls that share a workspace must not overlap in time.
+ * loop).  The completing workgroup of each group resets both counter words,
+ * so a call captured into a HIP graph (detected with hipStreamIsCapturing)
+ * counts correctly on every replay.  Calls that share a workspace must not
+ * overlap in time.
+ *
+ * FD_LOG=1 in the environment prints one line per planned call on stderr:
+ * the entry point, the shape, and the plan that runs (kernel path, split
+ * count and chunk, grid, merge form, stream mode, workspace bytes).
  */
 fd_status_t fd_decode(const void *q, const void *k_cache, const void *v_cache,
                       const int32_t *page_table, const int32_t *seq_lens,

@@ -352,6 +352,37 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
     return FD_OK;
 }
 
+// FD_LOG=1: one line per planned call on stderr naming the kernel path and
+// the plan that runs (the backend that ran is then on record).
+bool log_enabled() {
+    const char *e = std::getenv("FD_LOG");
+    return e && e[0] == '1' && e[1] == '\0';
+}
+
+const char *path_name(int path) {
+    switch (path) {
+    case FD_PATH_VALU: return "valu";
+    case FD_PATH_MFMA: return "mfma";
+    case FD_PATH_PREFILL: return "query-tiled";
+    default: return "?";
+    }
+}
+
+void log_plan(const char *entry, int B, int Hq, int Hkv, int T, int D, int n_req, const fd_options_t &o,
+              const fd_plan_t &p) {
+    if (!log_enabled()) return;
+    static const char *const dt[] = {"f32", "f16", "bf16"};
+    const char *merge = p.n_splits <= 1 ? "none" : (p.stream || p.fused) ? "fused" : "combine-kernel";
+    std::fprintf(stderr,
+                 "[fd] %s B=%d Hq=%d Hkv=%d T=%d D=%d dtype=%s n_queries=%d causal=%d paged=%d page_size=%d "
+                 "n_splits_req=%d -> path=%s n_splits=%d chunk=%d grid=%dx%dx%d rows_per_wg=%d head_blocks=%d "
+                 "merge=%s stream=%d workspace=%zu\n",
+                 entry, B, Hq, Hkv, T, D, (o.dtype >= 0 && o.dtype <= 2) ? dt[o.dtype] : "?", (int)o.n_queries,
+                 (int)o.causal, o.page_size > 0 ? 1 : 0, o.page_size > 0 ? (int)o.page_size : 0, n_req,
+                 path_name(p.path), p.n_splits, p.chunk, p.grid[0], p.grid[1], p.grid[2], p.heads_per_block,
+                 p.head_blocks, merge, p.stream, p.workspace_bytes);
+}
+
 struct Call {
     fd_options_t o;
     fd_plan_t p;
@@ -575,6 +606,24 @@ struct EpochTable {
         victim = (victim + 1) % kSlots;
     }
 
+    // A launch captured into a graph: it runs later, once per replay, with
+    // the arguments fixed now.  It gets one fresh epoch as both its own and
+    // the one it leaves, so each replay leaves the counters tagged for the
+    // next replay (the first replay counts through the slow word).  Eager
+    // calls after the replays find the tag here.
+    void take_captured(const void *w, unsigned *cur, unsigned *next) {
+        std::lock_guard<std::mutex> g(mu);
+        *cur = *next = fresh_epoch();
+        for (int i = 0; i < kSlots; ++i)
+            if (ws[i] == w) {
+                left[i] = *cur;
+                return;
+            }
+        ws[victim] = w;
+        left[victim] = *cur;
+        victim = (victim + 1) % kSlots;
+    }
+
     // the launch failed: the counters were not touched
     void forget(const void *w) {
         std::lock_guard<std::mutex> g(mu);
@@ -594,8 +643,16 @@ fd_status_t run_split(Call &c, bool fused) {
     fused = fused || c.p.stream;            // stream mode always merges in the launch
     c.s.fused = fused ? 1 : 0;
     c.s.epoch = c.s.next_epoch = 0;
-    if (fused) g_epochs.take(c.s.counters, &c.s.epoch, &c.s.next_epoch);
     const hipStream_t stream = static_cast<hipStream_t>(c.o.stream);
+    if (fused) {
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        const hipError_t ce = hipStreamIsCapturing(stream, &cap);
+        if (ce != hipSuccess) return hip_fail(ce, "hipStreamIsCapturing");
+        if (cap == hipStreamCaptureStatusActive)
+            g_epochs.take_captured(c.s.counters, &c.s.epoch, &c.s.next_epoch);
+        else
+            g_epochs.take(c.s.counters, &c.s.epoch, &c.s.next_epoch);
+    }
     const hipError_t e = c.p.path == FD_PATH_MFMA ? fdk::launch_split_mfma(c.s, c.o.dtype, stream)
                                                   : fdk::launch_split_valu(c.s, c.o.dtype, stream);
     if (e != hipSuccess) {
@@ -631,7 +688,9 @@ fd_status_t fd_plan(int B, int Hq, int Hkv, int T, int D, int n_splits, const fd
     fd_options_t o;
     fd_status_t st = read_options(opt, &o);
     if (st != FD_OK) return st;
-    return make_plan(B, Hq, Hkv, T, D, n_splits, o, o.page_size > 0, plan);
+    st = make_plan(B, Hq, Hkv, T, D, n_splits, o, o.page_size > 0, plan);
+    if (st == FD_OK) log_plan("fd_plan", B, Hq, Hkv, T, D, n_splits, o, *plan);
+    return st;
 }
 
 size_t fd_workspace_bytes(int B, int Hq, int Hkv, int T, int D, int n_splits, const fd_options_t *opt) {
@@ -647,6 +706,7 @@ fd_status_t fd_decode(const void *q, const void *k_cache, const void *v_cache, c
     fd_status_t st = prepare(q, k_cache, v_cache, page_table, seq_lens, out, lse, B, Hq, Hkv, T, D, scale,
                              n_splits, opt, true, nullptr, nullptr, &c);
     if (st != FD_OK) return st;
+    log_plan("fd_decode", B, Hq, Hkv, T, D, n_splits, c.o, c.p);
     const bool fused = c.p.fused != 0;
     st = run_split(c, fused);
     if (st != FD_OK || fused) return st;
@@ -661,6 +721,7 @@ fd_status_t fd_append_decode(const void *q, const void *k_new, const void *v_new
     fd_status_t st = prepare(q, k_cache, v_cache, page_table, seq_lens, out, lse, B, Hq, Hkv, T, D, scale,
                              n_splits, opt, true, k_new, v_new, &c);
     if (st != FD_OK) return st;
+    log_plan("fd_append_decode", B, Hq, Hkv, T, D, n_splits, c.o, c.p);
     const bool fused = c.p.fused != 0;
     st = run_split(c, fused);
     if (st != FD_OK || fused) return st;
@@ -674,6 +735,7 @@ fd_status_t fd_split(const void *q, const void *k_cache, const void *v_cache, co
     fd_status_t st = prepare(q, k_cache, v_cache, page_table, seq_lens, out, lse, B, Hq, Hkv, T, D, scale,
                              n_splits, opt, true, nullptr, nullptr, &c);
     if (st != FD_OK) return st;
+    log_plan("fd_split", B, Hq, Hkv, T, D, n_splits, c.o, c.p);
     return run_split(c, false);
 }
 
@@ -683,6 +745,7 @@ fd_status_t fd_combine(const int32_t *seq_lens, float *out, float *lse, int B, i
     fd_status_t st = prepare(nullptr, nullptr, nullptr, nullptr, seq_lens, out, lse, B, Hq, Hkv, T, D, 1.0f,
                              n_splits, opt, false, nullptr, nullptr, &c);
     if (st != FD_OK) return st;
+    log_plan("fd_combine", B, Hq, Hkv, T, D, n_splits, c.o, c.p);
     return run_combine(c);
 }
 

@@ -32,19 +32,39 @@ __device__ __forceinline__ float ep_exp2(float x) { return __builtin_amdgcn_exp2
 // changes it, after every fetch-add), so they all take the same path.  The
 // loop ends: every failed exchange means another workgroup's succeeded.
 //
-// Ordering.  A device-scope release here would write back the whole L2 of
-// the XCD for every workgroup (about 1.7 us each, serialised), which costs
-// more than the separate combine launch it replaces.  Instead the partials
-// are written and read only with device-coherent (sc1) accesses, which go to
-// the coherent level instead of a per-XCD L2 copy; every thread waits for
-// its stores to complete (vmcnt 0) before the barrier, so all partials of
-// the workgroup are at the coherent level before the count is issued, and
-// the last workgroup issues its coherent loads only after the count that
-// completed the group has returned.
+// The completing workgroup leaves both words in a state that depends on
+// this call's arguments only: the first at (next_epoch << 32 | 0), the
+// second at 0 (epoch 0, which no call uses).  A launch repeated with the
+// same arguments -- a captured graph replayed, whose host passes
+// epoch == next_epoch -- therefore counts from zero every time: through the
+// fast word once the first replay has tagged it, through the cleared slow
+// word before that.
+//
+// Ordering (LLVM AMDGPUUsage, memory model code sequences for GFX942, which
+// gfx950 follows).  Every arriving workgroup publishes its partials with
+// agent-scope atomic stores; all its threads wait for them (vmcnt 0) and
+// meet at a barrier; its counting RMW is an agent-scope release.  The
+// workgroup whose RMW completes the group then issues an agent-scope
+// acquire fence: its RMW read a value in the release sequence of every
+// earlier arrival (all are RMWs on one word), so each of those releases
+// synchronises with the fence (C++ [atomics.fences], which the AMDGPU model
+// follows), and the completing workgroup's other threads take that ordering
+// over through a barrier before they load the partials with agent-scope
+// atomic loads.  In the GFX942 sequences an agent-scope release is a
+// write-back of the L2's dirty lines plus vmcnt(0), and an acquire fence is
+// vmcnt(0) plus an invalidate of the L2's non-local lines: issued once per
+// arriving workgroup and once per group respectively.  FD_MERGE_RELEASE=0
+// builds the relaxed form (measurement only), which relies on the
+// coherent sc1 stores and loads alone.
+#ifndef FD_MERGE_RELEASE
+#define FD_MERGE_RELEASE 1
+#endif
+constexpr int kArriveOrder = FD_MERGE_RELEASE ? __ATOMIC_RELEASE : __ATOMIC_RELAXED;
+
 __device__ __forceinline__ bool arrive_last(unsigned long long *cnt, unsigned epoch, unsigned next_epoch,
                                             int n_active) {
     const unsigned long long old =
-        __hip_atomic_fetch_add(cnt, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(cnt, 1ull, kArriveOrder, __HIP_MEMORY_SCOPE_AGENT);
     bool last;
     if ((unsigned)(old >> 32) == epoch) {
         last = (unsigned)(old & 0xffffffffull) + 1u == (unsigned)n_active;
@@ -55,15 +75,20 @@ __device__ __forceinline__ bool arrive_last(unsigned long long *cnt, unsigned ep
         for (;;) {
             next = ((unsigned)(prev >> 32) == epoch) ? prev + 1ull
                                                       : (((unsigned long long)epoch << 32) | 1ull);
-            if (__hip_atomic_compare_exchange_strong(slow, &prev, next, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+            if (__hip_atomic_compare_exchange_strong(slow, &prev, next, kArriveOrder, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT))
                 break;
         }
         last = (unsigned)(next & 0xffffffffull) == (unsigned)n_active;
     }
-    if (last)   // every arrival of the group has counted: hand the word to the next call
+    if (last) {
+        // every arrival of the group has counted: make their partials
+        // visible here, then hand the words to the next call
+        if (FD_MERGE_RELEASE) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        __hip_atomic_store(cnt + 1, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(cnt, (unsigned long long)next_epoch << 32, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
+    }
     return last;
 }
 

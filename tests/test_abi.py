@@ -457,3 +457,47 @@ def test_plan_query_tiled_paged_splits(lib):
     assert st == fd.FD_OK and p.path == fd.FD_PATH_PREFILL and p.n_splits == 1 and p.workspace_bytes == 0
     st, p = plan(32, 64, 8, 32768, 128, 0, n_queries=8, causal=1)
     assert st == fd.FD_OK and p.n_splits == _query_tiled_splits(32 * 8, 32768, tiles=1)[0] == 4
+
+
+_LOG_SCRIPT = r"""
+import sys
+sys.path.insert(0, sys.argv[1])
+from split_kv_fd_amd import fd
+o = fd.fd_options_t(); fd.fd_options_init(o); o.num_cus = 256
+p = fd.fd_plan_t()
+assert fd.fd_plan(4, 32, 8, 131072, 128, 0, o, p) == fd.FD_OK
+print("PLAN", p.path, p.n_splits, p.chunk, p.fused, p.stream, flush=True)
+o.page_size, o.max_pages_per_seq, o.num_pages = 16, 4096, 100
+assert fd.fd_plan(16, 32, 8, 65536, 128, 0, o, p) == fd.FD_OK
+print("PLAN", p.path, p.n_splits, p.chunk, p.fused, p.stream, flush=True)
+o.page_size = 0
+# fails validation: nothing is planned, nothing logged
+assert fd.fd_decode(None, 1 << 20, 1 << 20, None, None, 1 << 20, None, 1, 4, 4, 4096, 128, 0.1, 0, o) != fd.FD_OK
+"""
+
+
+@pytest.mark.parametrize("flag", ["1", None])
+def test_fd_log_prints_each_plan(lib, flag):
+    # FD_LOG=1: one stderr line per planned call naming the path and the plan
+    import subprocess
+    import sys
+    env = dict(os.environ)
+    env.pop("FD_LOG", None)
+    if flag:
+        env["FD_LOG"] = flag
+    r = subprocess.run([sys.executable, "-c", _LOG_SCRIPT, ROOT], capture_output=True, text=True,
+                       env=env, timeout=120)
+    assert r.returncode == 0, r.stderr
+    plans = [ln.split()[1:] for ln in r.stdout.splitlines() if ln.startswith("PLAN")]
+    logs = [ln for ln in r.stderr.splitlines() if ln.startswith("[fd] ")]
+    if not flag:
+        assert logs == []
+        return
+    assert len(logs) == 2 and all(ln.startswith("[fd] fd_plan ") for ln in logs)
+    names = {0: "valu", 1: "mfma", 2: "query-tiled"}
+    for ln, (path, n, chunk, fused, stream) in zip(logs, plans):
+        kv = dict(t.split("=", 1) for t in ln.split() if "=" in t)
+        assert kv["path"] == names[int(path)] and kv["n_splits"] == n and kv["chunk"] == chunk
+        assert kv["stream"] == stream
+        assert kv["merge"] == ("none" if int(n) == 1 else "fused" if (int(fused) or int(stream)) else "combine-kernel")
+    assert "paged=1" in logs[1] and "stream=1" in logs[1] and "B=16" in logs[1]

@@ -1,0 +1,90 @@
+"""Decode calls captured into a HIP graph and replayed: the in-launch merge's
+arrival counters are left in a state that only depends on the launch's own
+arguments, so every replay of a captured fused or stream-mode call counts its
+workgroups from zero and merges.  Each replay gets a new q (copied in by
+eager work between replays) and is compared with the fp64 oracle; the
+workspace starts full of foreign bytes.  An eager call after the replays
+must find the counters usable too."""
+from dataclasses import replace
+
+import pytest
+import torch
+
+from split_kv_fd_amd import inputs
+from split_kv_fd_amd.decode import Decoder
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _case(kind):
+    if kind == "fused":
+        s = inputs.spec("mha32k_f16", Hq=16, Hkv=16, T=9000)
+    elif kind == "fused_gqa":
+        s = inputs.spec("gqa128k_bf16", B=2, T=7000)
+    else:
+        s = inputs.spec("paged_ragged_bf16", B=6, Hq=8, Hkv=2, T=6000, len_lo=0, len_hi=6000)
+    case = inputs.make_case(s, device="cpu")
+    if kind == "stream":
+        case.seq_lens[2] = 0
+    return case
+
+
+def _decoder(kind, case):
+    c = case.to(DEV)
+    if kind == "stream":
+        return Decoder(c.q, c.k, c.v, scale=case.spec.scale, page_table=c.page_table,
+                       seq_lens=c.seq_lens, T=case.spec.T)
+    n = 8 if kind == "fused" else 12
+    return Decoder(c.q, c.k, c.v, scale=case.spec.scale, n_splits=n, fused_merge=True)
+
+
+def _check(kind, case, dec, q_host, what):
+    from oracle import oracle as oracle_mod
+    c = case.to("cpu")
+    ref_out, ref_lse = oracle_mod.default().decode(q_host, c.k, c.v, case.spec.scale,
+                                                   page_table=c.page_table, seq_lens=c.seq_lens)
+    parity.compare(case, dec.out.cpu().double().numpy(), dec.lse.cpu().double().numpy(),
+                   ref_out, ref_lse, parity.max_abs_v(case), what)
+
+
+@pytest.mark.parametrize("kind", ["fused", "fused_gqa", "stream"])
+def test_graph_replays_of_fused_calls(kind):
+    case = _case(kind)
+    dec = _decoder(kind, case)
+    assert dec.plan["fused"] and dec.plan["n_splits"] > 1
+    assert dec.plan["stream"] == (kind == "stream")
+    q_dev = dec.inputs[0]
+    parity.announce(f"graph {kind}: plan={dec.plan}")
+    dec.workspace.fill_(0xFF)                  # foreign counters and NaN partials
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dec()
+    torch.cuda.synchronize()
+    for rep in range(5):
+        q_host = inputs.make_q(replace(case.spec, seed=case.spec.seed + 11 * rep + 1))
+        q_dev.copy_(q_host.to(DEV))
+        dec.out.fill_(float("nan"))            # a replay that skipped its merge would leave NaN
+        torch.cuda.synchronize()
+        parity.announce(f"graph {kind}: replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        _check(kind, case, dec, q_host, f"graph {kind} replay {rep}")
+    # eager calls on the same workspace after the replays, then one more replay
+    for rep in range(2):
+        q_host = inputs.make_q(replace(case.spec, seed=case.spec.seed + 97 + rep))
+        q_dev.copy_(q_host.to(DEV))
+        dec.out.fill_(float("nan"))
+        parity.announce(f"graph {kind}: eager call {rep} after the replays")
+        dec()
+        torch.cuda.synchronize()
+        _check(kind, case, dec, q_host, f"graph {kind} eager {rep}")
+    dec.out.fill_(float("nan"))
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    _check(kind, case, dec, q_host, f"graph {kind} replay after eager calls")
+    del g
