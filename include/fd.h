@@ -19,7 +19,8 @@
  * Conventions shared by every entry point:
  *   - All tensor arguments are DEVICE pointers on the current HIP device,
  *     contiguous, row-major.  The caller allocates and owns every buffer,
- *     including the workspace; the library keeps no pointer after a call
+ *     including the workspace (fd_decode_noalloc uses a static scratch of
+ *     the library instead); the library keeps no pointer after a call
  *     returns and allocates no device memory.
  *   - q: [B, Hq, D]; contiguous caches: [B, Hkv, T, D]; paged pools:
  *     [num_pages, Hkv, page_size, D] with page_table [B, max_pages_per_seq]
@@ -284,6 +285,32 @@ fd_status_t fd_split(const void *q, const void *k_cache, const void *v_cache,
 fd_status_t fd_combine(const int32_t *seq_lens, float *out, float *lse,
                        int B, int Hq, int Hkv, int T, int D, int n_splits,
                        const fd_options_t *opt);
+
+/*
+ * fd_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same call, whose workspace is a static device array of the library
+ * (FD_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends) instead of
+ * a caller-owned buffer.  Allocates nothing (no hipMalloc, no allocating
+ * library routine); the caller still passes inputs and outputs.
+ *   opt->workspace must be NULL and opt->workspace_bytes 0 (else
+ *   FD_ERR_INVALID_ARG).  A call whose plan needs more workspace than the
+ *   scratch holds (fd_workspace_bytes > FD_NOALLOC_SCRATCH_BYTES) fails with
+ *   FD_ERR_WORKSPACE before any device work; fd_decode with a caller-owned
+ *   workspace serves it.
+ *   The scratch keeps the last call's contents; nothing in it must start at
+ *   zero (counters carry per-call tags).  Every call on one GPU uses that
+ *   GPU's one array, so calls that overlap in time on one GPU (other
+ *   streams, other threads) race and give wrong results: order them.
+ * Results are those of fd_decode with the same arguments.
+ */
+#define FD_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+fd_status_t fd_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                              const int32_t *page_table, const int32_t *seq_lens,
+                              float *out, float *lse,
+                              int B, int Hq, int Hkv, int T, int D, float scale,
+                              int n_splits, const fd_options_t *opt);
 
 /* Static text for a status code. */
 const char *fd_status_string(fd_status_t status);

@@ -18,7 +18,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfd.so")
-SOURCES = ["fd_api.cpp", "fd_split_valu.hip", "fd_split_mfma.hip", "fd_combine.hip", "fd_prefill.hip"]
+SOURCES = ["fd_api.cpp", "fd_split_valu.hip", "fd_split_mfma.hip", "fd_combine.hip", "fd_prefill.hip",
+           "fd_noalloc.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

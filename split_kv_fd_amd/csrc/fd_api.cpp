@@ -671,6 +671,61 @@ fd_status_t run_combine(const Call &c) {
 
 }  // namespace
 
+namespace fdk {
+
+fd_status_t scratch_plan(const void *q, const void *k_cache, const void *v_cache, const int32_t *page_table,
+                         const int32_t *seq_lens, float *out, float *lse, int B, int Hq, int Hkv, int T, int D,
+                         float scale, int n_splits, const fd_options_t *opt, size_t scratch_bytes) {
+    fd_options_t o;
+    fd_status_t st = read_options(opt, &o);
+    if (st != FD_OK) return st;
+    if (o.workspace || o.workspace_bytes)
+        return fail(FD_ERR_INVALID_ARG,
+                    "fd_decode_noalloc uses the library's own scratch: opt->workspace must be NULL and "
+                    "opt->workspace_bytes 0");
+    fd_plan_t p;
+    st = make_plan(B, Hq, Hkv, T, D, n_splits, o, o.page_size > 0, &p);
+    if (st != FD_OK) return st;
+    if (p.workspace_bytes > scratch_bytes)
+        return fail(FD_ERR_WORKSPACE,
+                    "this call needs %zu bytes of scratch, more than the %zu-byte static scratch of "
+                    "fd_decode_noalloc holds; call fd_decode with a caller-owned workspace instead",
+                    p.workspace_bytes, scratch_bytes);
+    // every other check of fd_decode, with a stand-in workspace address (the
+    // host never dereferences it)
+    o.workspace = reinterpret_cast<void *>(uintptr_t(256));
+    o.workspace_bytes = scratch_bytes;
+    Call c;
+    return prepare(q, k_cache, v_cache, page_table, seq_lens, out, lse, B, Hq, Hkv, T, D, scale, n_splits, &o, true,
+                   nullptr, nullptr, &c);
+}
+
+fd_status_t decode_with_scratch(const void *q, const void *k_cache, const void *v_cache,
+                                const int32_t *page_table, const int32_t *seq_lens, float *out, float *lse,
+                                int B, int Hq, int Hkv, int T, int D, float scale, int n_splits,
+                                const fd_options_t *opt, void *scratch, size_t scratch_bytes) {
+    fd_options_t o;
+    fd_status_t st = read_options(opt, &o);
+    if (st != FD_OK) return st;
+    o.workspace = scratch;
+    o.workspace_bytes = scratch_bytes;
+    Call c;
+    st = prepare(q, k_cache, v_cache, page_table, seq_lens, out, lse, B, Hq, Hkv, T, D, scale, n_splits, &o, true,
+                 nullptr, nullptr, &c);
+    if (st != FD_OK) return st;
+    log_plan("fd_decode_noalloc", B, Hq, Hkv, T, D, n_splits, c.o, c.p);
+    const bool fused = c.p.fused != 0;
+    st = run_split(c, fused);
+    if (st != FD_OK || fused) return st;
+    return run_combine(c);
+}
+
+fd_status_t hip_error(hipError_t e, const char *what) { return hip_fail(e, what); }
+
+fd_status_t error(fd_status_t st, const char *msg) { return fail(st, "%s", msg); }
+
+}  // namespace fdk
+
 extern "C" {
 
 void fd_options_init(fd_options_t *opt) {

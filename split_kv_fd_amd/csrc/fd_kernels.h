@@ -189,4 +189,19 @@ inline size_t prefill_part_bytes(int B, int Hkv, int R, int D, int n_splits) {
 
 hipError_t launch_prefill(const PrefillArgs &a, int dtype, hipStream_t stream);
 
+// Host side of fd_decode_noalloc (fd_api.cpp).  scratch_plan makes every
+// check fd_decode makes, plus no caller workspace and a plan that fits the
+// static scratch, without touching the device unless num_cus is 0;
+// decode_with_scratch then runs fd_decode with the scratch as workspace.
+fd_status_t scratch_plan(const void *q, const void *k_cache, const void *v_cache, const int32_t *page_table,
+                         const int32_t *seq_lens, float *out, float *lse, int B, int Hq, int Hkv, int T, int D,
+                         float scale, int n_splits, const fd_options_t *opt, size_t scratch_bytes);
+fd_status_t decode_with_scratch(const void *q, const void *k_cache, const void *v_cache,
+                                const int32_t *page_table, const int32_t *seq_lens, float *out, float *lse,
+                                int B, int Hq, int Hkv, int T, int D, float scale, int n_splits,
+                                const fd_options_t *opt, void *scratch, size_t scratch_bytes);
+// Record a failure in fd_last_error and return its status.
+fd_status_t hip_error(hipError_t e, const char *what);
+fd_status_t error(fd_status_t st, const char *msg);
+
 }  // namespace fdk

@@ -23,7 +23,9 @@ FD_FLAG_APPEND = 0x4
 
 # Every function include/fd.h declares.
 EXPORTS = ("fd_options_init", "fd_plan", "fd_workspace_bytes", "fd_decode", "fd_append_decode",
-           "fd_split", "fd_combine", "fd_status_string", "fd_last_error")
+           "fd_split", "fd_combine", "fd_decode_noalloc", "fd_status_string", "fd_last_error")
+# Bytes of the static device scratch fd_decode_noalloc uses (per GPU).
+FD_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class fd_options_t(ctypes.Structure):
@@ -72,7 +74,7 @@ def load() -> ctypes.CDLL:
         lib.fd_workspace_bytes.restype = ctypes.c_size_t
         lib.fd_workspace_bytes.argtypes = [_I] * 6 + [_OPT]
         decode_args = [_P, _P, _P, _P, _P, _P, _P] + [_I] * 5 + [ctypes.c_float, _I, _OPT]
-        for name in ("fd_decode", "fd_split"):
+        for name in ("fd_decode", "fd_split", "fd_decode_noalloc"):
             getattr(lib, name).restype = _I
             getattr(lib, name).argtypes = decode_args
         lib.fd_append_decode.restype = _I
@@ -103,6 +105,12 @@ def fd_decode(q, k_cache, v_cache, page_table, seq_lens, out, lse, B, Hq, Hkv, T
               n_splits, opt) -> int:
     return load().fd_decode(q, k_cache, v_cache, page_table, seq_lens, out, lse, B, Hq, Hkv, T,
                             D, scale, n_splits, ctypes.byref(opt))
+
+
+def fd_decode_noalloc(q, k_cache, v_cache, page_table, seq_lens, out, lse, B, Hq, Hkv, T, D, scale,
+                      n_splits, opt) -> int:
+    return load().fd_decode_noalloc(q, k_cache, v_cache, page_table, seq_lens, out, lse, B, Hq, Hkv,
+                                    T, D, scale, n_splits, ctypes.byref(opt))
 
 
 def fd_append_decode(q, k_new, v_new, k_cache, v_cache, page_table, seq_lens, out, lse, B, Hq,

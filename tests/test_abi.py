@@ -501,3 +501,48 @@ def test_fd_log_prints_each_plan(lib, flag):
         assert kv["stream"] == stream
         assert kv["merge"] == ("none" if int(n) == 1 else "fused" if (int(fused) or int(stream)) else "combine-kernel")
     assert "paged=1" in logs[1] and "stream=1" in logs[1] and "B=16" in logs[1]
+
+
+def noalloc(q=A, k=A, v=A, pt=None, sl=None, out=A, lse=A, shape=(1, 4, 4, 4096, 128), scale=0.1,
+            n=16, **kw):
+    return fd.fd_decode_noalloc(q, k, v, pt, sl, out, lse, *shape, scale, n, opts(**kw))
+
+
+def test_noalloc_rejects_before_device_work(lib):
+    # the static scratch replaces the caller's workspace: passing one is an error
+    assert noalloc(workspace=A, workspace_bytes=1 << 20) == fd.FD_ERR_INVALID_ARG
+    assert "workspace must be NULL" in fd.fd_last_error()
+    # argument checks as fd_decode, all before the device is touched
+    assert noalloc(q=None) == fd.FD_ERR_INVALID_ARG
+    assert noalloc(k=MIS) == fd.FD_ERR_INVALID_ARG
+    assert noalloc(out=A + 4) == fd.FD_ERR_INVALID_ARG
+    assert noalloc(scale=float("nan")) == fd.FD_ERR_INVALID_ARG
+    assert noalloc(pt=A) == fd.FD_ERR_INVALID_ARG
+    assert noalloc(shape=(1, 4, 4, 4096, 80)) == fd.FD_ERR_UNSUPPORTED
+    # a plan needing more than the scratch holds is refused with the sizes
+    kw = dict(page_size=16, max_pages_per_seq=4096, num_pages=100)
+    st, p = plan(2048, 32, 8, 65536, 128, 0, **kw)
+    assert st == fd.FD_OK and p.workspace_bytes > fd.FD_NOALLOC_SCRATCH_BYTES
+    assert noalloc(shape=(2048, 32, 8, 65536, 128), pt=A, sl=A, n=0, **kw) == fd.FD_ERR_WORKSPACE
+    msg = fd.fd_last_error()
+    assert str(p.workspace_bytes) in msg and str(fd.FD_NOALLOC_SCRATCH_BYTES) in msg
+    # bf16 prefill that converts V needs about V's size: refused too
+    st, p = plan(4, 32, 8, 4096, 128, 0, n_queries=4096)
+    assert st == fd.FD_OK and p.workspace_bytes > fd.FD_NOALLOC_SCRATCH_BYTES
+    assert noalloc(shape=(4, 32, 8, 4096, 128), n=0, n_queries=4096) == fd.FD_ERR_WORKSPACE
+
+
+def test_noalloc_scratch_fits_the_decode_workloads(lib):
+    # every decode workload's automatic plan fits the static scratch
+    for name in ("tiny_f32", "mha32k_f16", "gqa128k_bf16", "paged_ragged_bf16", "gqa_b64_bf16"):
+        s = SPECS[name]
+        dt = {"f32": fd.FD_F32, "f16": fd.FD_F16, "bf16": fd.FD_BF16}[s.dtype]
+        kw = dict(page_size=16, max_pages_per_seq=4096, num_pages=100) if s.paged else {}
+        st, p = plan(s.B, s.Hq, s.Hkv, s.T, s.D, s.n_splits, dtype=dt, **kw)
+        assert st == fd.FD_OK and p.workspace_bytes <= fd.FD_NOALLOC_SCRATCH_BYTES, (name, p.workspace_bytes)
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
+def test_noalloc_without_device_reports_hip_error(lib):
+    # a valid call that fits reaches the device lookup, which fails cleanly here
+    assert noalloc(n=0) == fd.FD_ERR_HIP
