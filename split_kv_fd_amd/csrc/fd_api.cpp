@@ -274,6 +274,7 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
         const size_t slots = (size_t)(rows + nw) * hpb;
         p->workspace_bytes = align256(rows * 2 * sizeof(unsigned long long)) + align256(slots * D * sizeof(float)) +
                              2 * align256(slots * sizeof(float));
+        if (FD_WG_TIMING) p->workspace_bytes += align256((size_t)nw * fdk::kWgClockSlots * 8);
         return FD_OK;
     }
 
@@ -433,6 +434,7 @@ fd_status_t prepare(const void *q, const void *k, const void *v, const int32_t *
 
     float *part_o = nullptr, *part_m = nullptr, *part_l = nullptr;
     unsigned long long *counters = nullptr;
+    c->s.wg_clock = nullptr;
     if (c->p.stream) {
         if (!c->o.workspace)
             return fail(FD_ERR_WORKSPACE, "stream plan: a workspace of %zu bytes is required", c->p.workspace_bytes);
@@ -450,6 +452,10 @@ fd_status_t prepare(const void *q, const void *k, const void *v, const int32_t *
         part_m = reinterpret_cast<float *>(w);
         w += align256(slots * sizeof(float));
         part_l = reinterpret_cast<float *>(w);
+        if (FD_WG_TIMING) {
+            w += align256(slots * sizeof(float));
+            c->s.wg_clock = reinterpret_cast<unsigned long long *>(w);
+        }
     } else if (c->p.n_splits > 1 && c->p.path != FD_PATH_PREFILL) {
         if (!c->o.workspace)
             return fail(FD_ERR_WORKSPACE, "plan has %d splits: a workspace of %zu bytes is required",

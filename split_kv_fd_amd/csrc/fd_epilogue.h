@@ -43,28 +43,33 @@ __device__ __forceinline__ float ep_exp2(float x) { return __builtin_amdgcn_exp2
 // Ordering (LLVM AMDGPUUsage, memory model code sequences for GFX942, which
 // gfx950 follows).  Every arriving workgroup publishes its partials with
 // agent-scope atomic stores; all its threads wait for them (vmcnt 0) and
-// meet at a barrier; its counting RMW is an agent-scope release.  The
-// workgroup whose RMW completes the group then issues an agent-scope
-// acquire fence: its RMW read a value in the release sequence of every
-// earlier arrival (all are RMWs on one word), so each of those releases
-// synchronises with the fence (C++ [atomics.fences], which the AMDGPU model
-// follows), and the completing workgroup's other threads take that ordering
-// over through a barrier before they load the partials with agent-scope
-// atomic loads.  In the GFX942 sequences an agent-scope release is a
-// write-back of the L2's dirty lines plus vmcnt(0), and an acquire fence is
-// vmcnt(0) plus an invalidate of the L2's non-local lines: issued once per
-// arriving workgroup and once per group respectively.  FD_MERGE_RELEASE=0
-// builds the relaxed form (measurement only), which relies on the
-// coherent sc1 stores and loads alone.
+// meet at a barrier; then one thread issues an agent-scope release fence
+// and counts the arrival with a relaxed RMW.  The workgroup whose RMW
+// completes the group issues an agent-scope acquire fence: its RMW read a
+// value in the release sequence every earlier arrival's RMW would head
+// (all are RMWs on one word), so each earlier release fence synchronises
+// with this acquire fence (the C++ fence rules, which the AMDGPU model
+// follows), and the completing workgroup's other threads take that
+// ordering over through a barrier before they load the partials with
+// agent-scope atomic loads.  In the GFX942 sequences an agent-scope release
+// fence is a write-back of the L2's dirty lines plus vmcnt(0), and an
+// acquire fence vmcnt(0) plus an invalidate of the L2's non-local lines:
+// one of each per arriving workgroup and per group (a stream-mode
+// workgroup issues one release for all of its arrivals, at its end).
+// FD_MERGE_RELEASE=0 builds the fence-free form (measurement only), which
+// relies on the coherent sc1 stores and loads alone.
 #ifndef FD_MERGE_RELEASE
 #define FD_MERGE_RELEASE 1
 #endif
-constexpr int kArriveOrder = FD_MERGE_RELEASE ? __ATOMIC_RELEASE : __ATOMIC_RELAXED;
+
+__device__ __forceinline__ void release_fence() {
+    if (FD_MERGE_RELEASE) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+}
 
 __device__ __forceinline__ bool arrive_last(unsigned long long *cnt, unsigned epoch, unsigned next_epoch,
                                             int n_active) {
     const unsigned long long old =
-        __hip_atomic_fetch_add(cnt, 1ull, kArriveOrder, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(cnt, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     bool last;
     if ((unsigned)(old >> 32) == epoch) {
         last = (unsigned)(old & 0xffffffffull) + 1u == (unsigned)n_active;
@@ -75,7 +80,7 @@ __device__ __forceinline__ bool arrive_last(unsigned long long *cnt, unsigned ep
         for (;;) {
             next = ((unsigned)(prev >> 32) == epoch) ? prev + 1ull
                                                       : (((unsigned long long)epoch << 32) | 1ull);
-            if (__hip_atomic_compare_exchange_strong(slow, &prev, next, kArriveOrder, __ATOMIC_RELAXED,
+            if (__hip_atomic_compare_exchange_strong(slow, &prev, next, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT))
                 break;
         }
@@ -195,6 +200,8 @@ struct SegOut {
     int fused;                     // the last arriving segment merges the group
     unsigned long long *cnt;       // the group's two arrival counter words
     int arrivals;                  // segments of the group (its merge count)
+    int defer;                     // publish only: the caller counts the arrival later
+    int ord;                       // stream mode: the segment's ordinal in its workgroup (clock marks)
 };
 
 __device__ __forceinline__ SegOut split_segment(const SplitArgs &a, int b, int kvh, int hb, int r0,
@@ -208,6 +215,8 @@ __device__ __forceinline__ SegOut split_segment(const SplitArgs &a, int b, int k
     so.fused = a.fused;
     so.cnt = a.counters + 2 * (((size_t)b * a.Hkv + kvh) * a.head_blocks + hb);
     so.arrivals = active_splits(a, Tb);
+    so.defer = 0;
+    so.ord = 3;
     return so;
 }
 
@@ -326,9 +335,30 @@ __device__ void combine_group(const SplitArgs &a, EpilogueLds<WAVES, GB, D> &sm,
     }
 }
 
+// Count a published segment's arrival and, in the workgroup that
+// completes its group, merge the group.  Called by every thread; `fence`
+// issues the release fence first (once per workgroup covers every arrival
+// counted after it).
+template <int WAVES, int GB, int D>
+__device__ void arrive_and_merge(const SplitArgs &a, EpilogueLds<WAVES, GB, D> &sm, const SegOut &so, int b,
+                                 int kvh, int r0, int ng, bool fence) {
+    // every thread's coherent partial stores complete (vmcnt 0), the barrier
+    // gathers the workgroup, one thread counts the arrival
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        if (fence) release_fence();
+        sm.last = arrive_last(so.cnt, a.epoch, a.next_epoch, so.arrivals) ? 1 : 0;
+    }
+    __syncthreads();
+    if (!sm.last) return;
+    combine_group<WAVES, GB, D>(a, sm, so, b, kvh, r0, ng, so.arrivals);
+}
+
 // Called by every thread after sm.o / sm.m / sm.l hold each wave's state
 // (the caller has synchronised).  Writes this segment's result and, in fused
-// mode, completes the group when this workgroup arrives last.
+// mode, completes the group when this workgroup arrives last (unless
+// so.defer: then the caller counts the arrival later).
 template <int WAVES, int GB, int D>
 __device__ void finish_split(const SplitArgs &a, EpilogueLds<WAVES, GB, D> &sm, const SegOut &so, int b,
                              int kvh, int r0, int ng) {
@@ -359,17 +389,8 @@ __device__ void finish_split(const SplitArgs &a, EpilogueLds<WAVES, GB, D> &sm, 
             if (d == 0) { a.part_m[pi] = M; a.part_l[pi] = L; }
         }
     }
-    if (so.final_out || !so.fused) return;
-
-    // Fused combine: every thread's coherent partial stores complete
-    // (vmcnt 0), the barrier gathers the workgroup, one exchange counts the
-    // arrival, and the workgroup that completes the group merges its splits.
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (threadIdx.x == 0) sm.last = arrive_last(so.cnt, a.epoch, a.next_epoch, so.arrivals) ? 1 : 0;
-    __syncthreads();
-    if (!sm.last) return;
-    combine_group<WAVES, GB, D>(a, sm, so, b, kvh, r0, ng, so.arrivals);
+    if (so.final_out || !so.fused || so.defer) return;
+    arrive_and_merge<WAVES, GB, D>(a, sm, so, b, kvh, r0, ng, true);
 }
 
 // Stream mode.  Rows (batch, kv head, head block) are padded to
@@ -381,10 +402,15 @@ __device__ void finish_split(const SplitArgs &a, EpilogueLds<WAVES, GB, D> &sm, 
 // workgroups, and consecutive within a row); a row's last arriving segment
 // merges it, and a row covered by one segment writes out directly.
 // `seg(b, kvh, hb, c0, c1, so)` runs one segment (tokens [c0, c1) of the
-// row; c0 == c1 for a range that only covers padding).  Sequences of
-// length 0 have no segments: their outputs are written here.
-template <int NT, int D, typename Seg>
-__device__ void drive_stream(const SplitArgs &a, long long *pref, int hpb, Seg &&seg) {
+// row; c0 == c1 for a range that only covers padding).  A range cuts at
+// most two rows (its first and its last); their segments only publish
+// their partials, and after its last segment the workgroup counts both
+// arrivals behind one release fence, `arrive(b, kvh, hb, so, fence)`
+// merging a row it completes.  Sequences of length 0 have no segments:
+// their outputs are written here.
+template <int NT, int D, typename Seg, typename Arrive>
+__device__ void drive_stream(const SplitArgs &a, long long *pref, int hpb, Seg &&seg, Arrive &&arrive) {
+    FD_MARK(a, 0);
     const int t = threadIdx.x;
     const int RB = a.Hkv * a.head_blocks;             // rows per sequence
     const int align = a.stream_align;
@@ -447,14 +473,19 @@ __device__ void drive_stream(const SplitArgs &a, long long *pref, int hpb, Seg &
         const int mid = (lo + hi + 1) / 2;
         if (pref[mid] <= g0) lo = mid; else hi = mid - 1;
     }
-    for (int b = lo; b < a.B && pref[b] < g1; ++b) {
+    FD_MARK(a, 1);
+    // cut rows whose arrival is counted at the end (uniform across the workgroup)
+    SegOut pend[2];
+    int pb[2], pk[2], npend = 0, nseg = 0;
+    bool done = false;
+    for (int b = lo; b < a.B && pref[b] < g1 && !done; ++b) {
         const long long lb = pad_len(b);
         if (lb == 0) continue;
         const int Tb = real_len(b);
         long long k = g0 > pref[b] ? (g0 - pref[b]) / lb : 0;
         for (; k < RB; ++k) {
             const long long rs = pref[b] + k * lb;     // row start in the stream
-            if (rs >= g1) return;
+            if (rs >= g1) { done = true; break; }
             const long long c0 = g0 > rs ? g0 - rs : 0;
             const long long c1p = g1 - rs < lb ? g1 - rs : lb;
             const int c1 = (int)(c1p < Tb ? c1p : Tb);
@@ -470,10 +501,28 @@ __device__ void drive_stream(const SplitArgs &a, long long *pref, int hpb, Seg &
             so.fused = 1;
             so.cnt = a.counters + 2 * (size_t)r;
             so.arrivals = (int)(wl - wf + 1);
+            so.defer = !so.final_out && npend < 2;
+            so.ord = nseg < 3 ? nseg : 3;
+            ++nseg;
             __syncthreads();                       // LDS of the previous segment is free
+            FD_MARK(a, 2 + 4 * so.ord);
             seg(b, kvh, hb, (int)c0, c1 > (int)c0 ? c1 : (int)c0, so);
+            FD_MARK(a, 5 + 4 * so.ord);
+            if (so.defer) {
+                pend[npend] = so;
+                pb[npend] = b;
+                pk[npend] = (int)k;
+                ++npend;
+            }
         }
     }
+    FD_MARK(a, 14);
+    for (int i = 0; i < npend; ++i) {
+        const int kvh = pk[i] / a.head_blocks, hb = pk[i] - kvh * a.head_blocks;
+        __syncthreads();                           // LDS of the previous segment or merge is free
+        arrive(pb[i], kvh, hb, pend[i], i == 0);
+    }
+    FD_MARK(a, 15);
 }
 
 }  // namespace fdk

@@ -66,7 +66,31 @@ struct SplitArgs {
     const void *v_new;
     void *k_store;               // the caches again, writable
     void *v_store;
+    // Measurement builds (FD_WG_TIMING=1) only: kWgClockSlots real-time
+    // clock marks per stream-mode workgroup; nullptr otherwise.
+    unsigned long long *wg_clock;
 };
+
+#ifndef FD_WG_TIMING
+#define FD_WG_TIMING 0
+#endif
+// Stream-mode clock marks of a measurement build, per workgroup: 0 start,
+// 1 lengths scanned, then for each of the first three segments i: 2+4i
+// start, 3+4i page ids staged, 4+4i tokens streamed, 5+4i result
+// published; 14 deferred arrivals start, 15 end.  Unwritten slots keep
+// what the workspace held.
+constexpr int kWgClockSlots = 16;
+#if FD_WG_TIMING
+#define FD_MARK(args, slot)                                                                              \
+    do {                                                                                                 \
+        if (threadIdx.x == 0 && (args).wg_clock && (slot) < kWgClockSlots)                               \
+            (args).wg_clock[(size_t)blockIdx.x * kWgClockSlots + (slot)] = __builtin_amdgcn_s_memrealtime(); \
+    } while (0)
+#else
+#define FD_MARK(args, slot) \
+    do {                    \
+    } while (0)
+#endif
 
 // Most sequences a stream-mode launch handles (its LDS prefix array).
 constexpr int kStreamMaxB = 2048;

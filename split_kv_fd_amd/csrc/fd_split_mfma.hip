@@ -349,11 +349,13 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void split_mfma(SplitArgs a) 
                 const long long e = ((long long)(r0 >> a.page_shift) + kMaxSplitPages) << a.page_shift;
                 r1 = e < e1 ? (int)e : e1;
                 stage_pages(r0, r1);
+                if (STREAM) FD_MARK(a, 3 + 4 * so.ord);
                 stream_range(r0, r1);
             }
         } else {
             if (c0 < e1) stream_range(c0, e1);
         }
+        if (STREAM) FD_MARK(a, 4 + 4 * so.ord);
 
         // A few tokens (count <= 16) as the first tile of wave 0: lane i16
         // loads token i16's K row and lane (i16, kb) token 4*kb + r's V rows.
@@ -432,7 +434,12 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void split_mfma(SplitArgs a) 
 
     if constexpr (STREAM) {
         __shared__ long long s_pref[kStreamMaxB + 1];
-        drive_stream<64 * WAVES, D>(a, s_pref, GB, segment);
+        drive_stream<64 * WAVES, D>(a, s_pref, GB, segment,
+                                    [&](int b, int kvh, int hb, const SegOut &so, bool fence) {
+                                        const int g0 = hb * GB;
+                                        arrive_and_merge<WAVES, GB, D>(a, sm, so, b, kvh, g0,
+                                                                       min(GB, a.R - g0), fence);
+                                    });
     } else {
         const int split = blockIdx.x;
         const int kvh = blockIdx.y / a.head_blocks;

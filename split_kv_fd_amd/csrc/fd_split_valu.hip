@@ -400,7 +400,12 @@ __global__ __launch_bounds__(256) void split_valu(SplitArgs a) {
 
     if constexpr (STREAM) {
         __shared__ long long s_pref[kStreamMaxB + 1];
-        drive_stream<64 * WAVES, D>(a, s_pref, GB, segment);
+        drive_stream<64 * WAVES, D>(a, s_pref, GB, segment,
+                                    [&](int b, int kvh, int hb, const SegOut &so, bool fence) {
+                                        const int g0 = hb * GB;
+                                        arrive_and_merge<WAVES, GB, D>(a, sm, so, b, kvh, g0,
+                                                                       min(GB, a.R - g0), fence);
+                                    });
     } else {
         const int split = blockIdx.x;
         const int kvh = blockIdx.y / a.head_blocks;
