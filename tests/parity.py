@@ -91,40 +91,6 @@ def check_full(case, n_splits=0, path=None, what="", fused_merge=None):
     return compare(case, out, lse, ref_out, ref_lse, max_abs_v(case), what or case.spec.name), plan
 
 
-def sampled_rows(case, rows, out, lse, what=""):
-    """Compare selected (b, h) rows of a large case against the oracle,
-    computed one sequence at a time from host copies."""
-    s = case.spec
-    orc = oracle_mod.default()
-    by_b = {}
-    for r in rows:
-        by_b.setdefault(r // s.Hq, []).append(r % s.Hq)
-    worst = (0.0, 0.0)
-    for b, hs in sorted(by_b.items()):
-        q = case.q[b:b + 1].cpu()
-        if case.page_table is None:
-            k = case.k[b:b + 1].cpu()
-            v = case.v[b:b + 1].cpu()
-            ro, rl = orc.decode(q, k, v, s.scale, rows=hs)
-        else:
-            n = -(-case.lengths()[b] // s.page_size)
-            pages = case.page_table[b, :n].long()
-            # the sequence's own pages, renumbered 0..n-1 (same values and order)
-            k = case.k[pages].cpu()
-            v = case.v[pages].cpu()
-            table = torch.arange(n, dtype=torch.int32)[None]
-            sl = case.seq_lens[b:b + 1].cpu()
-            ro, rl = orc.decode(q, k, v, s.scale, page_table=table, seq_lens=sl, rows=hs)
-        go = np.stack([out[b, h] for h in hs])
-        gl = np.array([lse[b, h] for h in hs])
-
-        class _Sub:  # the tolerance needs only spec and dtype
-            spec = s
-        e = compare(_Sub, go, gl, ro, rl, max_abs_v(case, b), f"{what} b={b} heads={hs}")
-        worst = (max(worst[0], e[0]), max(worst[1], e[1]))
-    return worst
-
-
 def run_gpu_append(case, k_new, v_new, n_splits=0, path=None, fused_merge=None, poison=False):
     """fd_append_decode on the GPU; returns host (out, lse, k_after, v_after,
     plan).  case.k / case.v are updated in place."""
@@ -169,3 +135,79 @@ def check_append(case, k_new, v_new, n_splits=0, path=None, fused_merge=None, wh
     rv = ref_v.view(np.int16) if ref_v.dtype == np.uint16 else ref_v
     assert np.array_equal(ka, rk) and np.array_equal(va, rv), f"{what}: caches after the append differ"
     return err, plan
+
+
+def seq_host(case, b):
+    """Host copies of sequence b of a case: (k, v, page_table, seq_lens) for
+    the oracle.  A paged sequence gets its own pages, renumbered 0..n-1
+    (same values, same order); a contiguous one its [1, Hkv, T, D] slice."""
+    s = case.spec
+    if case.page_table is None:
+        sl = None if case.seq_lens is None else case.seq_lens[b:b + 1].cpu()
+        return case.k[b:b + 1].cpu(), case.v[b:b + 1].cpu(), None, sl
+    n = max(1, -(-case.lengths()[b] // s.page_size))
+    pages = case.page_table[b, :n].long()
+    table = torch.arange(n, dtype=torch.int32)[None]
+    return case.k[pages].cpu(), case.v[pages].cpu(), table, case.seq_lens[b:b + 1].cpu()
+
+
+def all_rows(case, out, lse, what=""):
+    """Every (b, h) row of a large case against the oracle, one sequence at a
+    time from host copies.  Each sequence's error is taken relative to its
+    own max |V| (at most the whole case's).  Returns and reports the worst
+    max|d out|/max|V| and max|d lse| over all rows."""
+    s = case.spec
+    orc = oracle_mod.default()
+    worst = (0.0, 0.0)
+    for b in range(s.B):
+        k, v, table, sl = seq_host(case, b)
+        ro, rl = orc.decode(case.q[b:b + 1].cpu(), k, v, s.scale, page_table=table, seq_lens=sl)
+        vmax = max_abs_v(case, b)
+        go, gl = out[b:b + 1], lse[b:b + 1]
+        assert np.all(np.isfinite(go)), f"{what} b={b}: non-finite output"
+        fin = np.isfinite(rl)
+        assert np.array_equal(fin, np.isfinite(gl)) and np.all(gl[~fin] == rl[~fin]), f"{what} b={b}: lse infinities"
+        err = float(np.max(np.abs(go - ro))) / max(vmax, 1e-30)
+        lerr = float(np.max(np.abs(gl[fin] - rl[fin]), initial=0.0))
+        worst = (max(worst[0], err), max(worst[1], lerr))
+    tol, ltol = OUT_TOL[s.dtype], LSE_TOL[s.dtype]
+    announce(f"{what}: all {s.B * s.Hq} rows: max|d out|/max|V| = {worst[0]:.3e} (tol {tol:.0e}), "
+             f"max|d lse| = {worst[1]:.3e} (tol {ltol:.0e})")
+    assert worst[0] <= tol, f"{what}: output error {worst[0]:.3e} > {tol:.0e}"
+    assert worst[1] <= ltol, f"{what}: lse error {worst[1]:.3e} > {ltol:.0e}"
+    return worst
+
+
+def all_queries(case, q, out, lse, bs, causal, what="", heads=None):
+    """Every query of the sequences bs (all query heads, or the kv groups
+    whose query heads are listed in `heads`) against the oracle's
+    several-query decode of that sequence alone."""
+    s = case.spec
+    orc = oracle_mod.default()
+    worst = (0.0, 0.0)
+    for b in bs:
+        k, v, table, sl = seq_host(case, b)
+        qb = q[b:b + 1].cpu()
+        hs = list(range(s.Hq)) if heads is None else list(heads)
+        if heads is not None:
+            # whole kv groups only: query heads j*G .. j*G+G-1 read kv head j
+            kvh = sorted(set(h // s.G for h in hs))
+            hs = [j * s.G + g for j in kvh for g in range(s.G)]
+            qb = qb[:, :, hs].contiguous()
+            # kv heads are axis 1 of a contiguous slice and of a page pool alike
+            k, v = k[:, kvh].contiguous(), v[:, kvh].contiguous()
+        ro, rl = orc.decode_multi(qb, k, v, s.scale, causal=causal, page_table=table, seq_lens=sl)
+        go = out[b:b + 1][:, :, hs]
+        gl = lse[b:b + 1][:, :, hs]
+        vmax = max_abs_v(case, b)
+        assert np.all(np.isfinite(go)), f"{what} b={b}: non-finite output"
+        fin = np.isfinite(rl)
+        assert np.array_equal(fin, np.isfinite(gl)) and np.all(gl[~fin] == rl[~fin]), f"{what} b={b}: lse infinities"
+        err = float(np.max(np.abs(go - ro))) / max(vmax, 1e-30)
+        lerr = float(np.max(np.abs(gl[fin] - rl[fin]), initial=0.0))
+        announce(f"{what} b={b}: {q.shape[1]} queries x {len(hs)} heads: err {err:.2e} lse {lerr:.2e}")
+        worst = (max(worst[0], err), max(worst[1], lerr))
+    tol, ltol = OUT_TOL[s.dtype], LSE_TOL[s.dtype]
+    assert worst[0] <= tol, f"{what}: output error {worst[0]:.3e} > {tol:.0e}"
+    assert worst[1] <= ltol, f"{what}: lse error {worst[1]:.3e} > {ltol:.0e}"
+    return worst

@@ -1,6 +1,5 @@
 """GPU parity of decode with several queries per sequence (q [B, n_q, Hq,
 D]), causal or not, against the oracle's per-query decode."""
-import numpy as np
 import pytest
 import torch
 
@@ -124,38 +123,14 @@ def test_multi_query_equals_single_query_decodes():
         assert torch.allclose(lse_m[:, i], lse_s, rtol=0, atol=2e-6)
 
 
-# ------------------------------------------------------------------ full-size workloads, sampled queries
-
-def _sampled_queries(case, q, out, lse, picks, what):
-    # each picked (sequence, query) against the oracle's one-query decode
-    # over the tokens that query sees (all heads of the query at once)
-    s = case.spec
-    nq = q.shape[1]
-    orc = oracle_mod.default()
-    lens = case.lengths()
-    for b, i in picks:
-        if case.page_table is None:
-            k_h, v_h, table = case.k[b:b + 1].cpu(), case.v[b:b + 1].cpu(), None
-        else:
-            n = -(-lens[b] // s.page_size)
-            pages = case.page_table[b, :n].long()
-            k_h, v_h = case.k[pages].cpu(), case.v[pages].cpu()
-            table = torch.arange(n, dtype=torch.int32)[None]
-        L = lens[b] - (nq - 1 - i)
-        ref, ref_l = orc.decode(q[b:b + 1, i].cpu(), k_h, v_h, s.scale, page_table=table,
-                                seq_lens=np.array([L], np.int32))
-        vmax = float(v_h.abs().max())
-        err = float(np.max(np.abs(out[b, i].cpu().double().numpy() - ref[0]))) / vmax
-        lerr = float(np.max(np.abs(lse[b, i].cpu().double().numpy() - ref_l[0])))
-        parity.announce(f"{what} b={b} query={i}: err {err:.2e} lse {lerr:.2e}")
-        assert err <= parity.OUT_TOL[s.dtype] and lerr <= parity.LSE_TOL[s.dtype]
-
+# ------------------------------------------------------------------ full-size workloads, every query of sampled sequences
 
 @pytest.mark.parametrize("name,nq", [("gqa_b64_bf16", 8), ("gqa128k_bf16", 16), ("paged_ragged_bf16", 16)])
 def test_full_size_many_rows(name, nq):
     # the workloads at full size with nq causal queries per sequence: 64
     # query rows per kv head, the query-tiled kernel with KV splits, as the
-    # benchmark runs them; sampled (sequence, query) pairs
+    # benchmark runs them; every query and head of the first, the last and
+    # two random sequences against the oracle
     s = inputs.spec(name)
     case = inputs.make_case(s, device=DEV)
     q = inputs.make_q_multi(s, nq, device=DEV)
@@ -167,7 +142,7 @@ def test_full_size_many_rows(name, nq):
     torch.cuda.synchronize()
     g = torch.Generator().manual_seed(s.seed + 11)
     bs = sorted(set([0, s.B - 1] + torch.randint(0, s.B, (2,), generator=g).tolist()))
-    picks = [(b, int(torch.randint(0, nq, (1,), generator=g))) for b in bs] + [(0, 0), (s.B - 1, nq - 1)]
-    _sampled_queries(case, q, out, lse, sorted(set(picks)), f"full {name} nq={nq}")
+    parity.all_queries(case, q, out.cpu().double().numpy(), lse.cpu().double().numpy(), bs, True,
+                       f"full {name} nq={nq}")
     del dec, out, lse, q, case
     torch.cuda.empty_cache()

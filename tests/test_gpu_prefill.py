@@ -1,6 +1,5 @@
 """GPU parity of the query-tiled kernel (many queries per sequence: the
 prefill phase) against the oracle's per-query decode, causal or not."""
-import numpy as np
 import pytest
 import torch
 
@@ -67,9 +66,9 @@ def test_prefill_kernel_for_few_queries(nq):
     assert torch.allclose(lse_a, lse_d, rtol=0, atol=1e-4)
 
 
-def test_prefill_full_size_sampled():
-    # a 2048-token prompt after a 2048-token prefix, GQA 32/8, bf16; sampled
-    # (sequence, query) rows against the oracle one query at a time
+def test_prefill_full_size_every_query():
+    # a 2048-token prompt after a 2048-token prefix, GQA 32/8, bf16: every
+    # query and head of both sequences against the oracle
     s = inputs.spec("gqa128k_bf16", B=2, T=4096)
     case = inputs.make_case(s, device=DEV)
     nq = 2048
@@ -79,20 +78,8 @@ def test_prefill_full_size_sampled():
     parity.announce(f"prefill full size nq={nq} plan={dec.plan}")
     out, lse = dec()
     torch.cuda.synchronize()
-    orc = oracle_mod.default()
-    g = torch.Generator().manual_seed(9)
-    for b in range(s.B):
-        k_h, v_h = case.k[b:b + 1].cpu(), case.v[b:b + 1].cpu()
-        vmax = float(v_h.abs().max())
-        for i in [0, 1, nq // 2, nq - 1] + torch.randint(0, nq, (3,), generator=g).tolist():
-            L = s.T - (nq - 1 - i)
-            ref, ref_l = orc.decode(q[b:b + 1, i].cpu(), k_h, v_h, s.scale,
-                                    seq_lens=np.array([L], np.int32))
-            got = out[b, i].cpu().double().numpy()
-            err = float(np.max(np.abs(got - ref[0]))) / vmax
-            lerr = float(np.max(np.abs(lse[b, i].cpu().double().numpy() - ref_l[0])))
-            parity.announce(f"prefill b={b} query={i}: err {err:.2e} lse {lerr:.2e}")
-            assert err <= parity.OUT_TOL["bf16"] and lerr <= parity.LSE_TOL["bf16"]
+    parity.all_queries(case, q, out.cpu().double().numpy(), lse.cpu().double().numpy(), [0, 1], True,
+                       f"prefill full size nq={nq}")
 
 
 @pytest.mark.parametrize("scale", [-0.3, 0.0, 0.35])
@@ -135,9 +122,9 @@ def test_prefill_sharp_softmax(dtype, scale):
                        parity.max_abs_v(host), f"prefill sharp dtype={dtype} scale={scale} causal={causal}")
 
 
-def test_prefill_full_size_sampled_f16():
-    # MHA 32 heads, f16 (one P product per tile): a 4096-token causal prompt,
-    # sampled query rows against the oracle one query at a time
+def test_prefill_full_size_f16_every_query():
+    # MHA 32 heads, f16 (one P product per tile): a 4096-token causal
+    # prompt; every query of four of the heads against the oracle
     s = inputs.spec("mha32k_f16", B=1, T=4096)
     case = inputs.make_case(s, device=DEV)
     nq = 4096
@@ -147,18 +134,8 @@ def test_prefill_full_size_sampled_f16():
     parity.announce(f"prefill f16 full size nq={nq} plan={dec.plan}")
     out, lse = dec()
     torch.cuda.synchronize()
-    orc = oracle_mod.default()
-    k_h, v_h = case.k.cpu(), case.v.cpu()
-    vmax = float(v_h.abs().max())
-    g = torch.Generator().manual_seed(11)
-    for i in [0, 1, nq // 2, nq - 1] + torch.randint(0, nq, (3,), generator=g).tolist():
-        L = s.T - (nq - 1 - i)
-        ref, ref_l = orc.decode(q[:, i].cpu(), k_h, v_h, s.scale, seq_lens=np.array([L], np.int32))
-        got = out[0, i].cpu().double().numpy()
-        err = float(np.max(np.abs(got - ref[0]))) / vmax
-        lerr = float(np.max(np.abs(lse[0, i].cpu().double().numpy() - ref_l[0])))
-        parity.announce(f"prefill f16 query={i}: err {err:.2e} lse {lerr:.2e}")
-        assert err <= parity.OUT_TOL["f16"] and lerr <= parity.LSE_TOL["f16"]
+    parity.all_queries(case, q, out.cpu().double().numpy(), lse.cpu().double().numpy(), [0], True,
+                       f"prefill f16 full size nq={nq}", heads=[0, 9, 22, 31])
 
 
 @pytest.mark.parametrize("vt", ["1", "0"])
@@ -366,10 +343,11 @@ def test_prefill_kv_splits_separate_entry_points():
     assert torch.equal(out_a, out_c) and torch.equal(lse_a, lse_c)
 
 
-def test_prefill_ragged_full_size_sampled():
+def test_prefill_ragged_full_size_every_query():
     # the paged ragged workload's shape (16-token pages, lengths from 1k to
     # 64k) with 512 causal queries per sequence, B=4: the automatic plan
-    # splits the KV axis; sampled (sequence, query) rows against the oracle
+    # splits the KV axis.  Every query of the shortest sequence (all heads)
+    # and of the longest (two kv groups, 8 heads) against the oracle
     s = inputs.spec("paged_ragged_bf16", B=4)
     case = inputs.make_case(s, device=DEV)
     nq = 512
@@ -380,24 +358,13 @@ def test_prefill_ragged_full_size_sampled():
     parity.announce(f"prefill ragged full size nq={nq} plan={dec.plan}")
     out, lse = dec()
     torch.cuda.synchronize()
-    orc = oracle_mod.default()
     lens = case.lengths()
-    g = torch.Generator().manual_seed(13)
-    for b in range(s.B):
-        n = -(-lens[b] // s.page_size)
-        pages = case.page_table[b, :n].long()
-        k_h, v_h = case.k[pages].cpu(), case.v[pages].cpu()
-        table = torch.arange(n, dtype=torch.int32)[None]
-        vmax = float(v_h.abs().max())
-        for i in [0, nq - 1] + torch.randint(0, nq, (2,), generator=g).tolist():
-            L = lens[b] - (nq - 1 - i)
-            ref, ref_l = orc.decode(q[b:b + 1, i].cpu(), k_h, v_h, s.scale, page_table=table,
-                                    seq_lens=np.array([L], np.int32))
-            got = out[b, i].cpu().double().numpy()
-            err = float(np.max(np.abs(got - ref[0]))) / vmax
-            lerr = float(np.max(np.abs(lse[b, i].cpu().double().numpy() - ref_l[0])))
-            parity.announce(f"prefill ragged b={b} T_b={lens[b]} query={i}: err {err:.2e} lse {lerr:.2e}")
-            assert err <= parity.OUT_TOL["bf16"] and lerr <= parity.LSE_TOL["bf16"]
+    out_h, lse_h = out.cpu().double().numpy(), lse.cpu().double().numpy()
+    shortest = min(range(s.B), key=lambda b: lens[b])
+    longest = max(range(s.B), key=lambda b: lens[b])
+    parity.all_queries(case, q, out_h, lse_h, [shortest], True, f"prefill ragged T_b={lens[shortest]}")
+    parity.all_queries(case, q, out_h, lse_h, [longest], True, f"prefill ragged T_b={lens[longest]}",
+                       heads=[0, s.Hq - 1])
 
 
 @pytest.mark.parametrize("D", [128, 64])
