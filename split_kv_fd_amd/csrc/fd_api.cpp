@@ -254,10 +254,15 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
     // any lengths spread evenly and no workgroup is launched for an empty
     // split.  Taken on the automatic split count only; an explicit n_splits
     // keeps the split grid.
+    // One workgroup per compute unit: with two, the one dispatched second
+    // to a compute unit was measured to stream its equal share ~26% slower
+    // (the older waves win issue), and the call waits for it (paged ragged
+    // batch: 370.5 us with one per compute unit, 387.3 us with two; an
+    // 8-wave workgroup per compute unit, 388 us).
     const bool stream = paged && n_req == 0 && B <= fdk::kStreamMaxB && env_long("FD_STREAM", 1) == 1;
     if (stream) {
         const long rows = (long)B * Hkv * head_blocks;
-        const long nw = std::max(1L, env_long("FD_STREAM_WGS", 2L * cus));
+        const long nw = std::max(1L, env_long("FD_STREAM_WGS", (long)cus));
         p->n_splits = (int)nw;
         p->chunk = 0;
         p->path = path;

@@ -125,15 +125,16 @@ def test_plan_paged_chunks_align_to_pages(lib):
                                           (32, fd.FD_BF16, fd.FD_PATH_MFMA)])
 def test_plan_paged_stream_mode(lib, G, dtype, path):
     # automatic plans of paged (ragged) batches on the split kernels use the
-    # balanced stream mode: one workgroup per stream range, two per compute
-    # unit, merged in-launch (32 query rows per kv head would take the
-    # query-tiled kernel unless the matrix-core path is asked for)
+    # balanced stream mode: one workgroup per stream range and compute unit,
+    # merged in-launch (32 query rows per kv head would take the query-tiled
+    # kernel unless the matrix-core path is asked for)
     B, Hkv, D = 16, 2, 128
     st, p = plan(B, G * Hkv, Hkv, 65536, D, 0, dtype=dtype, page_size=16,
                  max_pages_per_seq=4096, num_pages=10, num_cus=100, path=path)
     assert st == fd.FD_OK, fd.fd_last_error()
     assert p.stream and p.fused and p.combine and p.chunk == 0
-    assert (p.n_splits, p.grid[0], p.grid[1], p.grid[2]) == (200, 200, 1, 1)
+    assert (p.n_splits, p.grid[0], p.grid[1], p.grid[2]) == (100, 100, 1, 1)
+    assert p.block == 256
     rows = B * Hkv * p.head_blocks
     slots = (rows + p.n_splits) * p.heads_per_block
     assert p.workspace_bytes >= rows * 8 + slots * (D + 2) * 4
