@@ -541,6 +541,11 @@ fd_status_t prepare(const void *q, const void *k, const void *v, const int32_t *
     f.scale_log2 = s.scale_log2;
     f.vt = nullptr; f.vmax = nullptr; f.vexp = nullptr;
     f.xcd_map = env_long("FD_PREFILL_XCD", 1) == 1 ? 1 : 0;
+    // paged pools below 4 GiB: 32-bit row offsets from the pool base
+    f.pool32 = paged && (unsigned long long)c->o.num_pages * (unsigned long long)Hkv *
+                                (unsigned long long)c->o.page_size * (unsigned long long)D * 2ull <
+                            (1ull << 32) &&
+               env_long("FD_PREFILL_POOL32", 1) == 1;
     f.vt_tiles = (int)ceil_div(T, fdk::kPrefillTokens);
     f.vmax_chunks = (int)ceil_div(T, fdk::kVconvChunk);
     f.n_splits = c->p.path == FD_PATH_PREFILL ? c->p.n_splits : 1;

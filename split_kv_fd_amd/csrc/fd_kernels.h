@@ -189,6 +189,8 @@ struct PrefillArgs {
     int vt_tiles;                // ceil(T / kPrefillTokens)
     int vmax_chunks;             // ceil(T / kVconvChunk)
     int xcd_map;                 // 1: each XCD walks a contiguous run of work items
+    int pool32;                  // paged: each pool is under 4 GiB, so rows are
+                                 // addressed with 32-bit byte offsets
 };
 constexpr int kVconvChunk = 256;                  // tokens per workgroup of the conversion passes
 

@@ -112,7 +112,10 @@ constexpr float kSlack = 8.f;
 // per-(batch, kv head) power-of-two scale, transposed in tile order; the
 // value product then runs on f16 with one P product, as for f16 inputs.
 // NB: 16-row blocks per wave (the workgroup's tile is 64 * NB query rows).
-template <int DT, int D, bool PAGED, bool VT, int NB>
+// P32: paged pools under 4 GiB, whose rows are loaded through buffer
+// resources over the pools with 32-bit byte offsets (as contiguous slices
+// are) instead of 64-bit addresses.
+template <int DT, int D, bool PAGED, bool VT, int NB, bool P32 = false>
 __global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void prefill(PrefillArgs a) {
     constexpr int ROWB = D * 2;              // bytes per K / V row
     constexpr int KS = D / 32;               // 32-wide k chunks of the logit product
@@ -297,6 +300,17 @@ __global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void prefill(PrefillArgs a) {
         ok = (tt < Tb) & valid;
         return ((size_t)(valid ? pg : 0) * a.Hkv + kvh) * a.page_size + (tc & (a.page_size - 1));
     };
+    // P32: the same row as a 32-bit byte offset into the pool (the host
+    // takes this form only when the pool is under 4 GiB).
+    [[maybe_unused]] const uint32_t page_rows = (uint32_t)(a.Hkv * a.page_size);
+    [[maybe_unused]] const uint32_t head_row = (uint32_t)(kvh * a.page_size);
+    auto page_off = [&](int pg, int tt, int &ok) -> uint32_t {
+        const int tc = tt < Tb ? tt : Tb - 1;
+        const bool valid = (unsigned)pg < (unsigned)a.num_pages;
+        ok = (tt < Tb) & valid;
+        return ((uint32_t)(valid ? pg : 0) * page_rows + head_row + (uint32_t)(tc & (a.page_size - 1))) *
+               (uint32_t)ROWB;
+    };
     // Contiguous caches: the (batch, kv head) slices of K and V as buffer
     // resources sized to the real tokens.  Rows past the end read as zeros
     // (and are masked), so no clamp is needed, and each load takes one
@@ -325,6 +339,14 @@ __global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void prefill(PrefillArgs a) {
                                                 0x00020000);
         vexp = a.vexp[sl];
     }
+    [[maybe_unused]] __amdgpu_buffer_rsrc_t rkp = rk, rvp = rv;
+    if constexpr (PAGED && P32) {
+        const uint32_t pool = (uint32_t)a.num_pages * page_rows * (uint32_t)ROWB;
+        rkp = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(static_cast<const char *>(a.k)), 0, (int)pool,
+                                                0x00020000);
+        rvp = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(static_cast<const char *>(a.v)), 0, (int)pool,
+                                                0x00020000);
+    }
     auto bload = [](__amdgpu_buffer_rsrc_t r, uint32_t off) -> uint4 {
         typedef unsigned u32x4_v __attribute__((ext_vector_type(4)));
         const u32x4_v x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
@@ -349,6 +371,21 @@ __global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void prefill(PrefillArgs a) {
         }
         int unused_ok;                           // the mask bits come from the V rows
         const int tv = j * NTOK + 2 * u, tk = j * NTOK + 2 * ku;
+        if constexpr (P32) {
+            [[maybe_unused]] const uint32_t oa = page_off(pp.v0, tv, g.ok0);
+            [[maybe_unused]] const uint32_t ob = page_off(pp.v1, tv + 1, g.ok1);
+            g.k0 = bload(rkp, page_off(pp.k0, tk, unused_ok) + (uint32_t)(kpiece * 16));
+            g.k1 = bload(rkp, page_off(pp.k1, tk + 1, unused_ok) + (uint32_t)(kpiece * 16));
+            if constexpr (VT) {
+                const uint32_t vb = (uint32_t)j * (uint32_t)(D * 64) + (uint32_t)(vtrow * 64 + vthalf * 32);
+                g.v0 = bload(rvt, vb);
+                g.v1 = bload(rvt, vb + 16);
+            } else {
+                g.v0 = bload(rvp, oa + (uint32_t)(piece * 16));
+                g.v1 = bload(rvp, ob + (uint32_t)(piece * 16));
+            }
+            return g;
+        }
         [[maybe_unused]] const size_t ra = page_row(pp.v0, tv, g.ok0);
         [[maybe_unused]] const size_t rb = page_row(pp.v1, tv + 1, g.ok1);
         const size_t ka = page_row(pp.k0, tk, unused_ok);
@@ -787,17 +824,25 @@ hipError_t launch_dim(const PrefillArgs &a, hipStream_t stream) {
                 hipLaunchKernelGGL((vmax_pass<D, false>), pgrid, dim3(256), 0, stream, a);
                 hipLaunchKernelGGL((vconv_pass<D, false>), pgrid, dim3(256), 0, stream, a);
             }
-            if (a.page_table) hipLaunchKernelGGL((prefill<DT, D, true, true, kPrefillNB>), grid, dim3(256), 0, stream, a);
+            if (a.page_table && a.pool32)
+                hipLaunchKernelGGL((prefill<DT, D, true, true, kPrefillNB, true>), grid, dim3(256), 0, stream, a);
+            else if (a.page_table)
+                hipLaunchKernelGGL((prefill<DT, D, true, true, kPrefillNB>), grid, dim3(256), 0, stream, a);
             else hipLaunchKernelGGL((prefill<DT, D, false, true, kPrefillNB>), grid, dim3(256), 0, stream, a);
             return hipGetLastError();
         }
     }
     if (a.tile_rows == 64 * kPrefillNB) {
-        if (a.page_table) hipLaunchKernelGGL((prefill<DT, D, true, false, kPrefillNB>), grid, dim3(256), 0, stream, a);
+        if (a.page_table && a.pool32)
+            hipLaunchKernelGGL((prefill<DT, D, true, false, kPrefillNB, true>), grid, dim3(256), 0, stream, a);
+        else if (a.page_table)
+            hipLaunchKernelGGL((prefill<DT, D, true, false, kPrefillNB>), grid, dim3(256), 0, stream, a);
         else hipLaunchKernelGGL((prefill<DT, D, false, false, kPrefillNB>), grid, dim3(256), 0, stream, a);
     } else if (a.tile_rows == kPrefillSmallRows) {
         // a 64-row tile for 33..64 query rows per kv head: no row block idles
-        if (a.page_table) hipLaunchKernelGGL((prefill<DT, D, true, false, 1>), grid, dim3(256), 0, stream, a);
+        if (a.page_table && a.pool32)
+            hipLaunchKernelGGL((prefill<DT, D, true, false, 1, true>), grid, dim3(256), 0, stream, a);
+        else if (a.page_table) hipLaunchKernelGGL((prefill<DT, D, true, false, 1>), grid, dim3(256), 0, stream, a);
         else hipLaunchKernelGGL((prefill<DT, D, false, false, 1>), grid, dim3(256), 0, stream, a);
     } else {
         return hipErrorInvalidValue;
