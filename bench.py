@@ -267,13 +267,12 @@ def measure(spec, case, args, overrides=None):
         roofline = query_tiled_roofline(flops, kv_bytes, split_avg)
         roofline.update({"traffic": None if overrides else read_traffic(spec.name, kernel),
                          "kernel": kernel, "launch_us_avg": round(split_avg * 1e3, 2)})
-        # the workspace holds the split partials and, when V is converted,
-        # the converted V: then the two conversion passes run inside the
-        # timed launch
-        a256 = lambda x: -(-x // 256) * 256
-        parts = spec.B * spec.Hkv * args.n_queries * spec.G * plan["n_splits"]
-        part_bytes = a256(parts * spec.D * 4) + 2 * a256(parts * 4) if plan["n_splits"] > 1 else 0
-        if plan["workspace_bytes"] > part_bytes:
+        # bf16 calls with at least 1024 query rows per kv head convert V
+        # to f16 by two passes ahead of the kernel (FD_PREFILL_VT forces
+        # either form): then those passes run inside the timed launch
+        rows = args.n_queries * spec.G
+        vt = os.environ.get("FD_PREFILL_VT", "1" if rows >= 1024 else "0") == "1"
+        if spec.dtype == "bf16" and vt:
             roofline["launch_includes"] = "V conversion passes + query-tiled kernel"
     del decs
     torch.cuda.synchronize()

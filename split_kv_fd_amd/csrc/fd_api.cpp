@@ -104,6 +104,16 @@ fd_status_t read_options(const fd_options_t *opt, fd_options_t *o) {
     return FD_OK;
 }
 
+// Ragged (paged) query-tiled calls with one row tile per kv head and
+// several splits run their (sequence, split) columns longest first: the
+// full-length splits, then each sequence's last, partial one by size, so
+// the dispatch ends on short work (measured on the paged ragged batch with
+// 16 causal queries; FD_PREFILL_ORDER=0 keeps the plain order).
+bool prefill_ordered(bool paged, long tiles, long n_splits, int B) {
+    return paged && tiles == 1 && n_splits > 1 && n_splits < 65536 && B <= fdk::kOrderMaxB &&
+           env_long("FD_PREFILL_ORDER", 1) == 1;
+}
+
 // Shape checks and the plan.  `paged` tells whether a page table is used.
 fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_options_t &o,
                       bool paged, fd_plan_t *p) {
@@ -211,6 +221,7 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
         p->combine = n > 1;
         if (vt) p->workspace_bytes = fdk::prefill_vt_bytes(B, Hkv, T, D);
         p->workspace_bytes += fdk::prefill_part_bytes(B, Hkv, R, D, (int)n);
+        if (prefill_ordered(paged, tiles, n, B)) p->workspace_bytes += fdk::prefill_order_bytes(B, (int)n);
         return FD_OK;
     }
     if (o.n_queries > kMaxDecodeQueries)
@@ -551,6 +562,7 @@ fd_status_t prepare(const void *q, const void *k, const void *v, const int32_t *
     f.n_splits = c->p.path == FD_PATH_PREFILL ? c->p.n_splits : 1;
     f.chunk = c->p.chunk;
     f.part_o = f.part_m = f.part_l = nullptr;
+    f.order = nullptr;
     if (c->p.path == FD_PATH_PREFILL && c->p.workspace_bytes > 0) {
         if (!c->o.workspace)
             return fail(FD_ERR_WORKSPACE, "query-tiled plan: a workspace of %zu bytes is required",
@@ -559,9 +571,14 @@ fd_status_t prepare(const void *q, const void *k, const void *v, const int32_t *
             return fail(FD_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", c->o.workspace_bytes,
                         c->p.workspace_bytes);
         if (!aligned(c->o.workspace, 256)) return fail(FD_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-        // converted V (bf16), then the split partials
-        const size_t vt_bytes = c->p.workspace_bytes - fdk::prefill_part_bytes(B, Hkv, s.R, D, c->p.n_splits);
+        // converted V (bf16), then the split partials, then the column order
+        const bool ordered = prefill_ordered(paged, c->p.head_blocks, c->p.n_splits, B);
+        const size_t order_bytes = ordered ? fdk::prefill_order_bytes(B, c->p.n_splits) : 0;
+        const size_t vt_bytes =
+            c->p.workspace_bytes - fdk::prefill_part_bytes(B, Hkv, s.R, D, c->p.n_splits) - order_bytes;
         char *w = static_cast<char *>(c->o.workspace);
+        if (ordered)
+            f.order = reinterpret_cast<uint32_t *>(w + (c->p.workspace_bytes - order_bytes));
         if (vt_bytes > 0) {
             const size_t sl = (size_t)B * Hkv;
             f.vexp = reinterpret_cast<int32_t *>(w);

@@ -191,7 +191,14 @@ struct PrefillArgs {
     int xcd_map;                 // 1: each XCD walks a contiguous run of work items
     int pool32;                  // paged: each pool is under 4 GiB, so rows are
                                  // addressed with 32-bit byte offsets
+    // Longest-first order of the (sequence, split) columns (ragged paged
+    // calls with one row tile per kv head and several splits; nullptr: the
+    // plain order).  Written by a one-workgroup pass ahead of the kernel:
+    // entry c is (b << 16 | split) of the c-th column to run, or ~0u for a
+    // column that holds no tokens.
+    uint32_t *order;
 };
+constexpr int kOrderMaxB = 1024;                 // sequences the order pass ranks
 constexpr int kVconvChunk = 256;                  // tokens per workgroup of the conversion passes
 
 // Workspace of a query-tiled call with converted V (bf16), 256-byte aligned
@@ -202,6 +209,11 @@ inline size_t prefill_vt_bytes(int B, int Hkv, int T, int D) {
     const size_t tiles = ((size_t)T + kPrefillTokens - 1) / kPrefillTokens;
     const size_t chunks = ((size_t)T + kVconvChunk - 1) / kVconvChunk;
     return a256(sl * 4) + a256(sl * chunks * 4) + a256(sl * tiles * D * kPrefillTokens * 2);
+}
+
+// The column order of a query-tiled call (after the partials).
+inline size_t prefill_order_bytes(int B, int n_splits) {
+    return ((size_t)B * n_splits * 4 + 255) / 256 * 256;
 }
 
 // Partials of a query-tiled call with n_splits > 1 (after the converted V

@@ -163,21 +163,35 @@ __global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void prefill(PrefillArgs a) {
     // different XCDs), however ragged the lengths.  Ranges past the last
     // multiple of 8 keep the plain order.  Within a range causal tiles run
     // longest first.
+    // With a column order (one row tile per kv head), consecutive
+    // workgroups take the kv heads of one (sequence, split) column, columns
+    // in the order the order pass wrote: longest first.
     const int lin = (int)(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
-    const int n_rng = a.B * a.Hkv * a.n_splits;
-    const int mapped = (n_rng / 8) * 8 * a.row_tiles;
-    int item = lin;
-    if (a.xcd_map && lin < mapped) {
-        const int g = lin / 8;
-        item = ((lin % 8) + 8 * (g / a.row_tiles)) * a.row_tiles + g % a.row_tiles;
+    int tile_i, split, kvh, b;
+    if (a.order) {
+        const uint32_t col = a.order[lin / a.Hkv];
+        if (col == ~0u) return;                    // a column without tokens
+        tile_i = 0;
+        kvh = lin % a.Hkv;
+        b = (int)(col >> 16);
+        split = (int)(col & 0xffffu);
+    } else {
+        const int n_rng = a.B * a.Hkv * a.n_splits;
+        const int mapped = (n_rng / 8) * 8 * a.row_tiles;
+        int item = lin;
+        if (a.xcd_map && lin < mapped) {
+            const int g = lin / 8;
+            item = ((lin % 8) + 8 * (g / a.row_tiles)) * a.row_tiles + g % a.row_tiles;
+        }
+        tile_i = item % a.row_tiles;
+        const int rng = item / a.row_tiles;
+        split = rng / (a.B * a.Hkv);
+        const int slc0 = rng - split * (a.B * a.Hkv);
+        kvh = slc0 % a.Hkv;
+        b = slc0 / a.Hkv;
     }
-    const int tile_i = item % a.row_tiles;
-    const int rng = item / a.row_tiles;
-    const int split = rng / (a.B * a.Hkv);
-    const int slc = rng - split * (a.B * a.Hkv);
+    const int slc = b * a.Hkv + kvh;
     const int tile = a.causal ? a.row_tiles - 1 - tile_i : tile_i;
-    const int kvh = slc % a.Hkv;
-    const int b = slc / a.Hkv;
     const int r0 = tile * ROWS;
 
     int Tb = a.seq_lens ? a.seq_lens[b] : a.T;
@@ -703,6 +717,51 @@ __global__ __launch_bounds__(256, NB > 2 ? 1 : 2) void prefill(PrefillArgs a) {
     }
 }
 
+// ---- the longest-first column order ----
+// One workgroup of kOrderMaxB threads, thread b for sequence b (B <=
+// kOrderMaxB): of the columns (b, s), s < n_splits, those holding a whole
+// chunk come first (sequence by sequence; they are all the same work), then
+// each sequence's last, partial column by descending token count (ties by
+// sequence), then the empty ones (~0u).  The sizes are the cached lengths;
+// a causal row tile sees at most that many tokens.
+__global__ __launch_bounds__(kOrderMaxB) void order_pass(PrefillArgs a) {
+    const int t = threadIdx.x;
+    __shared__ int s_rem[kOrderMaxB];
+    __shared__ int s_scan[kOrderMaxB];
+    int Tb = 0;
+    if (t < a.B) {
+        Tb = a.seq_lens ? a.seq_lens[t] : a.T;
+        Tb = Tb < 0 ? 0 : (Tb > a.T ? a.T : Tb);
+    }
+    const long long cap = (long long)a.n_splits * a.chunk;
+    const int full = t < a.B ? (int)((Tb < cap ? Tb : cap) / a.chunk) : 0;
+    const int rem = (t < a.B && full < a.n_splits) ? Tb - full * a.chunk : 0;
+    s_rem[t] = rem;
+    s_scan[t] = full;
+    __syncthreads();
+    // inclusive scan of the full-column counts
+    for (int off = 1; off < kOrderMaxB; off <<= 1) {
+        const int x = t >= off ? s_scan[t - off] : 0;
+        __syncthreads();
+        s_scan[t] += x;
+        __syncthreads();
+    }
+    const int nfull = s_scan[kOrderMaxB - 1];
+    const int first = s_scan[t] - full;
+    for (int s = 0; s < full; ++s) a.order[first + s] = ((uint32_t)t << 16) | (uint32_t)s;
+    if (rem > 0) {
+        int rank = 0;
+        for (int o = 0; o < a.B; ++o) {
+            const int r = s_rem[o];
+            rank += (r > rem) | ((r == rem) & (o < t));
+        }
+        a.order[nfull + rank] = ((uint32_t)t << 16) | (uint32_t)full;
+    }
+    int npart = 0;
+    for (int o = 0; o < a.B; ++o) npart += s_rem[o] > 0;
+    for (int c = nfull + npart + t; c < a.B * a.n_splits; c += kOrderMaxB) a.order[c] = ~0u;
+}
+
 // ---- bf16 V converted for the value product ----
 // A bf16 value v becomes the f16 value v * 2^k, with k chosen per (batch,
 // kv head) so that the sequence's largest |v| lands in [2^14, 2^15).  bf16
@@ -813,6 +872,10 @@ __global__ __launch_bounds__(256) void vconv_pass(PrefillArgs a) {
 template <int DT, int D>
 hipError_t launch_dim(const PrefillArgs &a, hipStream_t stream) {
     const dim3 grid(a.row_tiles * a.n_splits, a.Hkv, a.B);
+    if (a.order) {
+        if (a.row_tiles != 1 || a.B > kOrderMaxB || a.n_splits >= 65536) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(order_pass, dim3(1), dim3(kOrderMaxB), 0, stream, a);
+    }
     if constexpr (DT == FD_BF16) {
         if (a.vt) {
             if (a.tile_rows != kPrefillRows) return hipErrorInvalidValue;

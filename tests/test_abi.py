@@ -547,3 +547,21 @@ def test_noalloc_scratch_fits_the_decode_workloads(lib):
 def test_noalloc_without_device_reports_hip_error(lib):
     # a valid call that fits reaches the device lookup, which fails cleanly here
     assert noalloc(n=0) == fd.FD_ERR_HIP
+
+
+def test_plan_query_tiled_column_order_workspace(lib):
+    # ragged paged calls with one row tile per kv head and several splits
+    # reserve B * n_splits order entries after the partials; contiguous
+    # caches, several row tiles or more than 1024 sequences do not
+    kw = dict(n_queries=16, page_size=16, max_pages_per_seq=4096, num_pages=100)
+    st, p = plan(16, 32, 8, 65536, 128, 0, **kw)
+    assert st == fd.FD_OK and p.path == fd.FD_PATH_PREFILL and p.head_blocks == 1 and p.n_splits > 1
+    parts = 16 * 8 * 64 * p.n_splits
+    a256 = lambda x: -(-x // 256) * 256
+    want = a256(parts * 128 * 4) + 2 * a256(parts * 4)
+    assert p.workspace_bytes == want + a256(16 * p.n_splits * 4)
+    st, c = plan(16, 32, 8, 65536, 128, 0, n_queries=16)
+    assert st == fd.FD_OK and c.workspace_bytes == a256(16 * 8 * 64 * c.n_splits * 128 * 4) + 2 * a256(16 * 8 * 64 * c.n_splits * 4)
+    st, big = plan(1100, 32, 8, 2048, 128, 4, **dict(kw, max_pages_per_seq=128))
+    parts = 1100 * 8 * 64 * big.n_splits
+    assert st == fd.FD_OK and big.workspace_bytes == a256(parts * 128 * 4) + 2 * a256(parts * 4)
