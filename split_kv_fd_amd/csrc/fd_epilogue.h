@@ -394,20 +394,24 @@ __device__ void finish_split(const SplitArgs &a, EpilogueLds<WAVES, GB, D> &sm, 
 }
 
 // Stream mode.  Rows (batch, kv head, head block) are padded to
-// a.stream_align tokens and laid end to end; workgroup w takes the stream
-// range [w*per, (w+1)*per), which may cover the end of one row, whole rows
-// and the start of another.  Every workgroup scans the sequence lengths to
-// find its range (B <= kStreamMaxB).  The segment of row r taken by
+// a.stream_align tokens, each row is preceded by a.stream_row_cost positions
+// that hold no tokens, and the rows are laid end to end; workgroup w takes
+// the stream range [w*per, (w+1)*per), which may cover the end of one row,
+// whole rows and the start of another.  The positions before a row stand for
+// the fixed time a segment costs (page staging, the latency of its first
+// loads, the partial's write) in tokens' worth, so a range that holds more
+// row starts gets fewer tokens.  Every workgroup scans the sequence lengths
+// to find its range (B <= kStreamMaxB).  The segment of row r taken by
 // workgroup w writes partial slot r + w (distinct for all rows and
 // workgroups, and consecutive within a row); a row's last arriving segment
 // merges it, and a row covered by one segment writes out directly.
 // `seg(b, kvh, hb, c0, c1, so)` runs one segment (tokens [c0, c1) of the
-// row; c0 == c1 for a range that only covers padding).  A range cuts at
-// most two rows (its first and its last); their segments only publish
-// their partials, and after its last segment the workgroup counts both
-// arrivals behind one release fence, `arrive(b, kvh, hb, so, fence)`
-// merging a row it completes.  Sequences of length 0 have no segments:
-// their outputs are written here.
+// row; c0 == c1 for a range that only covers padding or the positions before
+// the tokens).  A range cuts at most two rows (its first and its last);
+// their segments only publish their partials, and after its last segment
+// the workgroup counts both arrivals behind one release fence,
+// `arrive(b, kvh, hb, so, fence)` merging a row it completes.  Sequences of
+// length 0 have no segments: their outputs are written here.
 template <int NT, int D, typename Seg, typename Arrive>
 __device__ void drive_stream(const SplitArgs &a, long long *pref, int hpb, Seg &&seg, Arrive &&arrive) {
     FD_MARK(a, 0);
@@ -416,14 +420,18 @@ __device__ void drive_stream(const SplitArgs &a, long long *pref, int hpb, Seg &
     const int align = a.stream_align;
     auto real_len = [&](int b) { return attended_len(a, b); };
     auto pad_len = [&](int b) { return (long long)((real_len(b) + align - 1) / align) * align; };
+    // a row's length in the stream: its padded tokens after row_cost
+    // positions that stand for the fixed cost of starting a segment
+    const long long V = a.stream_row_cost;
+    auto stride = [&](int b) { const long long lb = pad_len(b); return lb > 0 ? lb + V : 0; };
 
-    // exclusive prefix over sequences of RB * padded length, and the longest row
+    // exclusive prefix over sequences of RB * row stride, and the longest row
     __shared__ long long s_scan[NT];
     __shared__ long long s_max[NT];
     long long carry = 0, lmax = 0;
     for (int c = 0; c < a.B; c += NT) {
         const int b = c + t;
-        const long long v = b < a.B ? pad_len(b) : 0;
+        const long long v = b < a.B ? stride(b) : 0;
         lmax = v > lmax ? v : lmax;
         s_scan[t] = v * RB;
         __syncthreads();
@@ -479,19 +487,23 @@ __device__ void drive_stream(const SplitArgs &a, long long *pref, int hpb, Seg &
     int pb[2], pk[2], npend = 0, nseg = 0;
     bool done = false;
     for (int b = lo; b < a.B && pref[b] < g1 && !done; ++b) {
-        const long long lb = pad_len(b);
-        if (lb == 0) continue;
+        const long long sb = stride(b);
+        if (sb == 0) continue;
         const int Tb = real_len(b);
-        long long k = g0 > pref[b] ? (g0 - pref[b]) / lb : 0;
+        long long k = g0 > pref[b] ? (g0 - pref[b]) / sb : 0;
         for (; k < RB; ++k) {
-            const long long rs = pref[b] + k * lb;     // row start in the stream
+            const long long rs = pref[b] + k * sb;     // row start in the stream
             if (rs >= g1) { done = true; break; }
-            const long long c0 = g0 > rs ? g0 - rs : 0;
-            const long long c1p = g1 - rs < lb ? g1 - rs : lb;
+            // this range's part of the row, then of its tokens (which start
+            // V positions in)
+            const long long s0 = g0 > rs ? g0 - rs : 0;
+            const long long s1 = g1 - rs < sb ? g1 - rs : sb;
+            const long long c0 = s0 > V ? s0 - V : 0;
+            const long long c1p = s1 > V ? s1 - V : 0;
             const int c1 = (int)(c1p < Tb ? c1p : Tb);
             const int r = b * RB + (int)k;
             const int kvh = (int)k / a.head_blocks, hb = (int)k - kvh * a.head_blocks;
-            const long long wf = rs / per, wl = (rs + lb - 1) / per;
+            const long long wf = rs / per, wl = (rs + sb - 1) / per;
             SegOut so;
             so.final_out = wf == wl;
             so.base = (size_t)(r + wf) * hpb;

@@ -57,6 +57,7 @@ struct SplitArgs {
     // laid end to end, one equal range per workgroup (gridDim.x of them).
     int stream;
     int stream_align;
+    int stream_row_cost;         // stream positions before each row's tokens (multiple of stream_align)
     int merge_cap;               // most segments one row may have (fused merge)
     // Append (fused append-KV): the new token's rows k_new / v_new [B, Hkv,
     // D] are token T_b = seq_lens[b] of each sequence, which then has T_b + 1

@@ -234,6 +234,22 @@ def test_stream_mode_workgroup_counts(monkeypatch, path, wgs):
 
 
 @pytest.mark.parametrize("path", ["valu", "mfma"])
+@pytest.mark.parametrize("row_cost", [0, 64, 1000, 20000])
+def test_stream_mode_row_cost(monkeypatch, path, row_cost):
+    # Positions before each row's tokens move the range boundaries: ranges
+    # that end before a row's first token (an empty segment), rows shorter
+    # than the positions before them, and a cost longer than any range.
+    monkeypatch.setenv("FD_STREAM_WGS", "13")
+    monkeypatch.setenv("FD_STREAM_ROWCOST", str(row_cost))
+    case = small_case("paged_ragged_bf16", B=9, Hq=8, Hkv=2, T=3000, page_size=16, len_lo=0, len_hi=3000)
+    case.seq_lens[1] = 0
+    case.seq_lens[3] = 1
+    case.seq_lens[5] = 129
+    (_, _), plan = parity.check_full(case, path=path, what=f"stream row cost {row_cost} {path}")
+    assert plan["stream"] and plan["n_splits"] == 13
+
+
+@pytest.mark.parametrize("path", ["valu", "mfma"])
 def test_stream_mode_merge_cap(monkeypatch, path):
     # Many workgroups over one long row: ranges are widened so that no row
     # is cut into more pieces than the in-launch merge holds.
