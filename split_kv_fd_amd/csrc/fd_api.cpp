@@ -49,9 +49,11 @@ constexpr int kMaxDecodeQueries = 16;    // more take the query-tiled (prefill) 
 // More query rows per kv head than this take the query-tiled kernel too
 // (f16 / bf16), which reads K/V once for a tile of 64 or 128 rows.  The
 // matrix-core split kernel holds 32 rows in one K/V read (two 16-row
-// blocks), but from 17 rows on the query-tiled kernel is faster (measured,
-// contiguous and paged caches).
-constexpr int kMaxSplitRows = 16;
+// blocks, value product on 16x16x32 MFMAs), and there it is the faster one
+// (measured, bf16, 8 causal queries x 4 heads: GQA 128k 330 vs 368-376 us,
+// paged ragged batch 402 vs 480 us; 5 queries x 4 heads: 321 vs 367 us and
+// 388 vs 488 us; B=64 with 4 queries: 1225 vs 1432 us).
+constexpr int kMaxSplitRows = 32;
 // bf16 V is converted to f16 for the query-tiled kernel's value product
 // from this many query rows per kv head: the conversion reads V twice and
 // writes it once, which the cheaper product repays only when many rows

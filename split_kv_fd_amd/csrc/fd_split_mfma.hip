@@ -24,7 +24,10 @@
 //    token 4*kb+r, and V of that token as the A operand -- 8 (D=128) or 4
 //    (D=64) consecutive elements of the row, one per MFMA, so element i of
 //    lane i16 is dimension (D/16)*i16 + i.  Each V load instruction reads
-//    four whole rows.
+//    four whole rows.  With two row blocks (17-32 rows) the value product
+//    instead runs on v_mfma_f32_16x16x32_{bf16,f16}: V^T from LDS through
+//    transposing reads as the A operand, P in a high and a low 16-bit part
+//    as the B operand (see TRV below);
 // The next step's K/V pieces are prefetched into registers while the current
 // step is consumed (two buffers used in turn).
 #include <type_traits>
@@ -75,6 +78,35 @@ __device__ __forceinline__ void widen(const uint2 &p, float *f) {
 
 typedef unsigned int u32x4_v __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_v __attribute__((ext_vector_type(2)));
+typedef float f32x2_v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_v __attribute__((ext_vector_type(2)));
+typedef short i16x4_v __attribute__((ext_vector_type(4)));
+
+// Two probabilities as one word of the input type (round to nearest), and
+// that word's two values back in fp32 (exact).
+template <int DT>
+__device__ __forceinline__ uint32_t pack_p(float x, float y) {
+    if constexpr (DT == FD_BF16)
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_v{x, y}, bf16x2_v));
+    else
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_v{x, y}, f16x2_v));
+}
+
+template <int DT>
+__device__ __forceinline__ void unpack_p(uint32_t w, float &x, float &y) {
+    x = widen1<DT>(w, 0);
+    y = widen1<DT>(w, 1);
+}
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane j names 4
+// consecutive 16-bit values M[j][0..3]; lane i receives M[4k + i/4][i%4]
+// for k = 0..3 (checked on gfx950 with an index-filled LDS array).
+__device__ __forceinline__ uint2 lds_read_tr16(const unsigned char *p) {
+    const i16x4_v v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4_v *)(p));
+    return __builtin_bit_cast(uint2, v);
+}
 
 template <typename V>
 __device__ __forceinline__ V load_piece(const char *p);
@@ -130,6 +162,15 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void split_mfma(SplitArgs a) 
 
     __shared__ int s_pages[PAGED ? kMaxSplitPages : 1];
     __shared__ EpilogueLds<WAVES, GB, D> sm;
+    // Two row blocks: the value product runs on 16x16x32 MFMAs, whose A
+    // operand needs 8 tokens of one dimension per lane.  Each wave writes its
+    // step's V rows (as loaded) to its own LDS tile and reads them back with
+    // transposing reads.  Row stride 2D + 32 bytes: 8 x an odd number of
+    // dwords, so the 16 token rows one transposing read touches fall on
+    // disjoint 8-bank windows of the 128 banks.
+    constexpr bool TRV = NB >= 2;
+    constexpr int VROW = 2 * D + 32;
+    __shared__ __align__(16) unsigned char s_v[TRV ? WAVES : 1][TRV ? TOK * VROW : 16];
 
     // One segment: tokens [c0, c1) of row (b, kvh, hb) into `so`.
     auto segment = [&](int b, int kvh, int hb, int c0, int c1, const SegOut &so) {
@@ -230,6 +271,48 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void split_mfma(SplitArgs a) 
                 m[nb] = mn;
 #pragma unroll
                 for (int i = 0; i < PVE; ++i) acc[nb][i] *= alpha;
+            }
+            if constexpr (TRV) {
+                // O^T (16 dims x 16 rows per block) += V^T (dims x 32 tokens)
+                // . P^T (tokens x rows).  k slot 4h + r of lane (i16, kb) is
+                // token 16h + 4kb + r on both operands: the B operand is the
+                // lane's own probabilities, in a high and a low 16-bit part
+                // (P = hi + lo to ~2^-16 relative), and the A operand comes
+                // from two transposing reads of the wave's V tile.  acc[nb][dt]
+                // then holds dims 16*dt + 4*kb .. +3 of row i16.
+                unsigned char *wv = s_v[wave];
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        *reinterpret_cast<VP *>(wv + (16 * h + 4 * kb + r) * VROW + VB * i16) = f.v[h][r];
+                uint4 phi[NB], plo[NB];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    uint32_t hi[4], lo[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float x = p[nb][e >> 1][2 * (e & 1)], y = p[nb][e >> 1][2 * (e & 1) + 1];
+                        hi[e] = pack_p<DT>(x, y);
+                        float hx, hy;
+                        unpack_p<DT>(hi[e], hx, hy);
+                        lo[e] = pack_p<DT>(x - hx, y - hy);
+                    }
+                    phi[nb] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+                    plo[nb] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+                }
+                const unsigned char *rd = wv + (4 * kb + (i16 >> 2)) * VROW + 8 * (i16 & 3);
+#pragma unroll
+                for (int dt = 0; dt < PVE; ++dt) {
+                    const uint2 a0 = lds_read_tr16(rd + 32 * dt);
+                    const uint2 a1 = lds_read_tr16(rd + 16 * VROW + 32 * dt);
+                    const uint4 va = make_uint4(a0.x, a0.y, a1.x, a1.y);
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) acc[nb][dt] = mfma_logits<DT>(va, phi[nb], acc[nb][dt]);
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) acc[nb][dt] = mfma_logits<DT>(va, plo[nb], acc[nb][dt]);
+                }
+                return;
             }
 #pragma unroll
             for (int h = 0; h < 2; ++h)
@@ -425,7 +508,10 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void split_mfma(SplitArgs a) 
 #pragma unroll
             for (int i = 0; i < PVE; ++i)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) sm.o[wave][16 * nb + i16][PVE * (4 * kb + r) + i] = acc[nb][i][r];
+                for (int r = 0; r < 4; ++r) {
+                    if constexpr (TRV) sm.o[wave][16 * nb + i16][16 * i + 4 * kb + r] = acc[nb][i][r];
+                    else sm.o[wave][16 * nb + i16][PVE * (4 * kb + r) + i] = acc[nb][i][r];
+                }
             if (kb == 0) { sm.m[wave][16 * nb + i16] = m[nb]; sm.l[wave][16 * nb + i16] = l[nb]; }
         }
         __syncthreads();

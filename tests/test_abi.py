@@ -269,7 +269,7 @@ def test_plan_several_queries(lib, nq):
         st, p = plan(B, G * Hkv, Hkv, T, D, 0, dtype=dt, n_queries=nq)
         assert st == fd.FD_OK, fd.fd_last_error()
         R = nq * G
-        if dt != fd.FD_F32 and R > 16:      # contiguous: the query-tiled kernel from 17 rows
+        if dt != fd.FD_F32 and R > 32:      # contiguous: the query-tiled kernel from 33 rows
             assert p.path == fd.FD_PATH_PREFILL
             continue
         want_mfma = dt != fd.FD_F32 and R >= 4
@@ -419,17 +419,18 @@ def test_plan_query_tiled_size_limits(lib):
 
 @pytest.mark.parametrize("nq,G,dtype,want", [
     (1, 16, fd.FD_BF16, fd.FD_PATH_MFMA),        # 16 rows: split kernels
-    (1, 32, fd.FD_BF16, fd.FD_PATH_PREFILL),     # 32 rows
+    (1, 32, fd.FD_BF16, fd.FD_PATH_MFMA),        # 32 rows: two row blocks of the split kernel
     (1, 64, fd.FD_BF16, fd.FD_PATH_PREFILL),     # 64 rows of one query
     (4, 4, fd.FD_F16, fd.FD_PATH_MFMA),
-    (5, 4, fd.FD_BF16, fd.FD_PATH_PREFILL),      # 20 rows
+    (5, 4, fd.FD_BF16, fd.FD_PATH_MFMA),         # 20 rows
+    (8, 4, fd.FD_F16, fd.FD_PATH_MFMA),          # 32 rows
     (9, 4, fd.FD_F16, fd.FD_PATH_PREFILL),       # 36 rows
     (16, 8, fd.FD_BF16, fd.FD_PATH_PREFILL),
     (16, 8, fd.FD_F32, fd.FD_PATH_VALU),         # fp32 stays on the vector kernel
     (17, 1, fd.FD_F16, fd.FD_PATH_PREFILL),      # more than 16 queries
 ])
 def test_plan_rows_route(lib, nq, G, dtype, want):
-    # query rows per kv head (n_q * G) past 16 take the query-tiled kernel,
+    # query rows per kv head (n_q * G) past 32 take the query-tiled kernel,
     # which reads K/V once for a 64- or 128-row tile, contiguous or paged;
     # one-query calls with an appended token stay on the split kernels
     st, p = plan(2, G * 2, 2, 4096, 128, 0, n_queries=nq, causal=1 if nq > 1 else 0, dtype=dtype)

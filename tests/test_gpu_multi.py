@@ -123,6 +123,24 @@ def test_multi_query_equals_single_query_decodes():
         assert torch.allclose(lse_m[:, i], lse_s, rtol=0, atol=2e-6)
 
 
+@pytest.mark.parametrize("nq,G,dtype", [(1, 17, "bf16"), (3, 8, "f16"), (8, 4, "bf16"), (5, 4, "f16"), (1, 32, "f16")])
+def test_rows_17_to_32_take_two_row_blocks(nq, G, dtype):
+    # 17..32 query rows per kv head: the automatic plan takes the matrix-core
+    # split kernel with two 16-row blocks (value product on 16x16x32 MFMAs
+    # over V transposed through LDS), contiguous and paged, both masks
+    case = contiguous("gqa128k_bf16", [3000, 1500, 0], Hq=G * 2, Hkv=2, T=3000, dtype=dtype)
+    q = inputs.make_q_multi(case.spec, nq).to(DEV)
+    for causal in ((False, True) if nq > 1 else (False,)):
+        plan = check_multi(case, q, causal, what=f"two row blocks nq={nq} G={G} {dtype} causal={causal}")
+        assert plan["path"] == "mfma" and plan["heads_per_block"] == 32 and plan["head_blocks"] == 1
+    s = inputs.spec("paged_ragged_bf16", B=3, Hq=G * 2, Hkv=2, T=2500, page_size=16, len_lo=0, len_hi=2500,
+                    dtype=dtype)
+    pcase = inputs.make_case(s).to(DEV)
+    pq = inputs.make_q_multi(s, nq).to(DEV)
+    plan = check_multi(pcase, pq, nq > 1, what=f"two row blocks paged nq={nq} G={G} {dtype}")
+    assert plan["path"] == "mfma" and plan["stream"] and plan["heads_per_block"] == 32
+
+
 # ------------------------------------------------------------------ full-size workloads, every query of sampled sequences
 
 @pytest.mark.parametrize("name,nq", [("gqa_b64_bf16", 8), ("gqa128k_bf16", 16), ("paged_ragged_bf16", 16)])

@@ -365,7 +365,8 @@ def test_largest_contiguous_slice():
     # one (batch, kv head) slice just under 4 GiB -- the largest the kernels'
     # 32-bit offsets address (2^24 - 32 tokens x 128 x 2 bytes) -- through
     # the vector and matrix-core split kernels and, with 8 causal queries
-    # (32 rows per kv head), the query-tiled kernel with its KV splits;
+    # (32 rows per kv head), the split kernel's two row blocks and the
+    # query-tiled kernel with its KV splits;
     # sampled against the oracle
     T = (1 << 24) - 32
     s = inputs.spec("gqa128k_bf16", B=1, Hq=4, Hkv=1, T=T)
@@ -384,18 +385,23 @@ def test_largest_contiguous_slice():
         assert err <= parity.OUT_TOL["bf16"] and lerr <= parity.LSE_TOL["bf16"]
     nq = 8
     q = inputs.make_q_multi(s, nq, device=DEV)
-    dec = Decoder(q, case.k, case.v, scale=s.scale, causal=True)
-    assert dec.plan["path"] == "prefill" and dec.plan["n_splits"] > 1
-    parity.announce(f"largest slice query-tiled plan={dec.plan}")
-    out, lse = dec()
-    torch.cuda.synchronize()
-    for i in (0, nq - 1):
-        r, rl = orc.decode(q[:, i].cpu(), k_h, v_h, s.scale, seq_lens=np.array([T - (nq - 1 - i)], np.int32))
-        err = float(np.max(np.abs(out[0, i].cpu().double().numpy() - r[0]))) / vmax
-        lerr = float(np.max(np.abs(lse[0, i].cpu().double().numpy() - rl[0])))
-        parity.announce(f"largest slice query-tiled query={i}: err {err:.2e} lse {lerr:.2e}")
-        assert err <= parity.OUT_TOL["bf16"] and lerr <= parity.LSE_TOL["bf16"]
-    del dec, out, lse, q, case, k_h, v_h
+    refs = {i: orc.decode(q[:, i].cpu(), k_h, v_h, s.scale, seq_lens=np.array([T - (nq - 1 - i)], np.int32))
+            for i in (0, nq - 1)}
+    # 32 rows per kv head: the automatic plan takes the split kernel's two
+    # row blocks; the query-tiled kernel with its KV splits is asked for
+    for path, want in ((None, "mfma"), ("prefill", "prefill")):
+        dec = Decoder(q, case.k, case.v, scale=s.scale, causal=True, path=path)
+        assert dec.plan["path"] == want and dec.plan["n_splits"] > 1
+        parity.announce(f"largest slice {want} plan={dec.plan}")
+        out, lse = dec()
+        torch.cuda.synchronize()
+        for i, (r, rl) in refs.items():
+            err = float(np.max(np.abs(out[0, i].cpu().double().numpy() - r[0]))) / vmax
+            lerr = float(np.max(np.abs(lse[0, i].cpu().double().numpy() - rl[0])))
+            parity.announce(f"largest slice {want} query={i}: err {err:.2e} lse {lerr:.2e}")
+            assert err <= parity.OUT_TOL["bf16"] and lerr <= parity.LSE_TOL["bf16"]
+        del dec, out, lse
+    del q, case, k_h, v_h
     torch.cuda.empty_cache()
 
 

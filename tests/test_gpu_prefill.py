@@ -233,9 +233,9 @@ def test_prefill_kv_splits_converted_v(env_switch, causal, n):
 
 
 @pytest.mark.parametrize("nq,G,dtype", [(1, 64, "bf16"), (2, 20, "f16"), (9, 4, "bf16"), (16, 8, "bf16"),
-                                         (1, 17, "bf16"), (3, 8, "f16"), (8, 4, "bf16")])
+                                         (1, 33, "bf16"), (5, 8, "f16"), (12, 4, "bf16")])
 def test_many_rows_take_query_tiled_kernel(nq, G, dtype):
-    # more than 16 query rows per kv head (n_q * G) of a contiguous cache go
+    # more than 32 query rows per kv head (n_q * G) of a contiguous cache go
     # to the query-tiled kernel, which reads K/V once for a 64- or 128-row
     # tile (bf16 V unconverted at these row counts); ragged lengths, one
     # empty sequence, both masks
