@@ -50,8 +50,9 @@ __device__ __forceinline__ float ep_exp2(float x) { return __builtin_amdgcn_exp2
 // (all are RMWs on one word), so each earlier release fence synchronises
 // with this acquire fence (the C++ fence rules, which the AMDGPU model
 // follows), and the completing workgroup's other threads take that
-// ordering over through a barrier before they load the partials with
-// agent-scope atomic loads.  In the GFX942 sequences an agent-scope release
+// ordering over through a barrier before they load the partials (plain
+// 16-byte loads: the writes happen before them, so they race with nothing;
+// the acquire fence has also invalidated this compute unit's L1).  In the GFX942 sequences an agent-scope release
 // fence is a write-back of the L2's dirty lines plus vmcnt(0), and an
 // acquire fence vmcnt(0) plus an invalidate of the L2's non-local lines:
 // one of each per arriving workgroup and per group (a stream-mode
@@ -220,11 +221,21 @@ __device__ __forceinline__ SegOut split_segment(const SplitArgs &a, int b, int k
     return so;
 }
 
+// A partial's float4 in the merging workgroup.  With the release / acquire
+// fences the partials are ordered before these reads (see arrive_last), so
+// plain 16-byte loads serve; the fence-free measurement form keeps
+// agent-scope atomic loads.
+__device__ __forceinline__ float4 ld_part4(const float *p) {
+    if (FD_MERGE_RELEASE) return *reinterpret_cast<const float4 *>(p);
+    return make_float4(ld_agent(p), ld_agent(p + 1), ld_agent(p + 2), ld_agent(p + 3));
+}
+
 // Merge the last workgroup's group: for every valid head g of the block,
 // out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s over the n active
 // splits, read back from the workspace.  The loads of the split maxima and
-// sums and of each thread's first PRE partial rows are issued together, so
-// a merge of up to PRE*SG splits costs one memory round trip.  Thread t owns
+// sums and of each thread's first PRE partial rows are issued together, and
+// further splits are read PRE at a time, so a merge of n splits costs about
+// n / (PRE*SG) memory round trips per pass.  Thread t owns
 // one (head, float4 quad) pair and every SG-th split of it; sums run in
 // split order within a thread and in split-group order across threads
 // (deterministic).  ng * n <= kMergeMaxPairs.
@@ -267,10 +278,7 @@ __device__ void combine_group(const SplitArgs &a, EpilogueLds<WAVES, GB, D> &sm,
         for (int j = 0; j < PRE; ++j) {
             const int s = sg + j * SG;
             pre[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (active && s < n) {
-                const float *src = po + (size_t)s * srow;
-                pre[j] = make_float4(ld_agent(src), ld_agent(src + 1), ld_agent(src + 2), ld_agent(src + 3));
-            }
+            if (active && s < n) pre[j] = ld_part4(po + (size_t)s * srow);
         }
         if (p0 == 0) {
             // global max, weights and normaliser of each head (one wave per head)
@@ -310,11 +318,23 @@ __device__ void combine_group(const SplitArgs &a, EpilogueLds<WAVES, GB, D> &sm,
                     acc.z = fmaf(c, pre[j].z, acc.z); acc.w = fmaf(c, pre[j].w, acc.w);
                 }
             }
-            for (; s < n; s += SG) {
-                const float *src = po + (size_t)s * srow;
-                const float c = wg[s];
-                acc.x = fmaf(c, ld_agent(src), acc.x); acc.y = fmaf(c, ld_agent(src + 1), acc.y);
-                acc.z = fmaf(c, ld_agent(src + 2), acc.z); acc.w = fmaf(c, ld_agent(src + 3), acc.w);
+            // the rest, PRE splits per round trip (same order of sums)
+            for (; s < n; s += PRE * SG) {
+                float4 v[PRE];
+#pragma unroll
+                for (int j = 0; j < PRE; ++j) {
+                    const int sj = s + j * SG;
+                    v[j] = sj < n ? ld_part4(po + (size_t)sj * srow) : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+#pragma unroll
+                for (int j = 0; j < PRE; ++j) {
+                    const int sj = s + j * SG;
+                    if (sj < n) {
+                        const float c = wg[sj];
+                        acc.x = fmaf(c, v[j].x, acc.x); acc.y = fmaf(c, v[j].y, acc.y);
+                        acc.z = fmaf(c, v[j].z, acc.z); acc.w = fmaf(c, v[j].w, acc.w);
+                    }
+                }
             }
         }
         sm.red[sg * per_pass + (t / SG)] = acc;
