@@ -59,6 +59,9 @@ constexpr int kMaxSplitRows = 32;
 // writes it once, which the cheaper product repays only when many rows
 // share each V tile (measured crossover near 1024 rows).
 constexpr int kConvertRows = 1024;
+// K/V bytes of a call (its longest sequence for every one) up to which the
+// automatic plan merges splits in the launch (see make_plan).
+constexpr double kFusedMaxBytes = 48.0 * (1 << 20);
 
 // Compute units of the current device, cached per device id.
 fd_status_t device_cus(int *cus) {
@@ -351,11 +354,19 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
     p->block = 256;
     p->combine = n > 1;
     // The last workgroup of a group merges the splits itself when their
-    // maxima and sums fit its LDS (n * heads <= 1024).  By
-    // default this is chosen when the grid runs in about one round (at most
-    // two workgroups per compute unit): then it saves the combine launch,
-    // while with many rounds the per-workgroup publish latency costs more.
-    bool want_fused = (long)B * Hkv * head_blocks * n <= 2L * cus;
+    // maxima and sums fit its LDS (n * heads <= 1024).  By default this is
+    // chosen for small calls whose grid runs in about one round (at most two
+    // workgroups per compute unit): there it saves the combine launch.  With
+    // many rounds the per-workgroup publish latency costs more, and on large
+    // calls the in-launch merge (its fences and the completing workgroup's
+    // serial merge) costs more than the combine kernel.  Measured, wall time
+    // per call: MHA f16 32k tokens x 32 heads (537 MB of K/V) 78.0 us
+    // without any merge, 81.9 with the combine kernel, 83.6 fused; GQA 128k
+    // bf16 (1.07 GB) 303.7 / 307.2 / 311.6; MHA with 4096 tokens (67 MB)
+    // fused 18.3 vs 17.6 with the combine kernel, 2048 tokens (34 MB) 13.6
+    // vs 15.8, the tiny fp32 case 9.3 vs 16.2.
+    const double kv_call = 2.0 * B * Hkv * (double)Tp * D * elt;
+    bool want_fused = (long)B * Hkv * head_blocks * n <= 2L * cus && kv_call <= kFusedMaxBytes;
     if (o.flags & FD_FLAG_FUSED_MERGE) want_fused = true;
     if (o.flags & FD_FLAG_COMBINE_KERNEL) want_fused = false;
     const long env_fused = env_long("FD_FUSED", -1);

@@ -146,14 +146,21 @@ def test_plan_paged_stream_mode(lib, G, dtype, path):
 
 
 def test_plan_merge_choice(lib):
-    # one round of workgroups: fused merge; many rounds: combine kernel
-    st, p = plan(1, 32, 32, 32768, 128, 0, dtype=fd.FD_F16)
+    # a small call in one round of workgroups: fused merge; many rounds, or
+    # more than 48 MiB of K/V: combine kernel; the flags override either way
+    st, p = plan(1, 32, 32, 2048, 128, 0, dtype=fd.FD_F16)          # 32 MiB of K/V
     assert st == fd.FD_OK and p.n_splits > 1 and p.fused
-    st, p = plan(1, 32, 32, 32768, 128, 64, dtype=fd.FD_F16)
+    st, p = plan(1, 32, 32, 3072, 128, 0, dtype=fd.FD_F16)          # 48 MiB
+    assert st == fd.FD_OK and p.n_splits > 1 and p.fused
+    st, p = plan(1, 32, 32, 3200, 128, 0, dtype=fd.FD_F16)          # just over
+    assert st == fd.FD_OK and p.n_splits > 1 and not p.fused
+    st, p = plan(1, 32, 32, 32768, 128, 0, dtype=fd.FD_F16)         # 512 MiB
+    assert st == fd.FD_OK and p.n_splits > 1 and not p.fused
+    st, p = plan(1, 32, 32, 2048, 128, 64, dtype=fd.FD_F16)         # many rounds
     assert st == fd.FD_OK and not p.fused
     st, p = plan(1, 32, 32, 32768, 128, 64, dtype=fd.FD_F16, flags=fd.FD_FLAG_FUSED_MERGE)
     assert st == fd.FD_OK and p.fused
-    st, p = plan(1, 32, 32, 32768, 128, 0, dtype=fd.FD_F16, flags=fd.FD_FLAG_COMBINE_KERNEL)
+    st, p = plan(1, 32, 32, 2048, 128, 0, dtype=fd.FD_F16, flags=fd.FD_FLAG_COMBINE_KERNEL)
     assert st == fd.FD_OK and not p.fused
 
 
