@@ -269,8 +269,11 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void split_mfma(SplitArgs a) 
                     }
                 l[nb] = l[nb] * alpha + ps;
                 m[nb] = mn;
+                // (skipped when no lane's max moved: alpha is then 1 exactly)
+                if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
 #pragma unroll
-                for (int i = 0; i < PVE; ++i) acc[nb][i] *= alpha;
+                    for (int i = 0; i < PVE; ++i) acc[nb][i] *= alpha;
+                }
             }
             if constexpr (TRV) {
                 // O^T (16 dims x 16 rows per block) += V^T (dims x 32 tokens)
