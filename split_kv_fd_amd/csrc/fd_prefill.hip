@@ -25,6 +25,8 @@
 //    the value product can take 8 tokens of one dimension per lane in one
 //    16-byte read: within a row the tokens are stored in the order the
 //    lanes take them (position 8*((t%16)/4) + 4*(t/16) + t%4 for token t).
+//    (Paged 64-row tiles with V read as given store V rows as loaded and
+//    take the same operand through transposing LDS reads; see VROWS.)
 //    Both row strides are padded by 32 bytes: gfx950 serves a 16-byte LDS
 //    read 32 lanes at a time over 128 banks, and rows 8 dwords apart (mod
 //    128) keep the 16 rows x 2 chunks of such a read on distinct banks,
