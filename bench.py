@@ -203,44 +203,46 @@ def measure(spec, case, args, overrides=None):
     K = args.steps
     # fd_append_decode has no separate passes: its step is timed as a whole
     separate = plan["combine"] and not plan["fused"] and not args.append
-    # HIP events on the launch stream.  One launch per step (the split
-    # kernel with the fused merge): a pair of events brackets each block of
-    # EVERY consecutive launches, and a launch's duration is the block's
-    # time over its launch count, so the events' own cost is amortised.
-    # Two launches per step: the split and combine launches of every
-    # EVERY-th step are bracketed one by one.
+    # HIP events on the launch stream: a pair of events brackets each block
+    # of EVERY consecutive steps, and a step's duration is the block's time
+    # over its step count, so the events' own cost is amortised.  With one
+    # launch per step (the split kernel, the merge fused into it) that is the
+    # split launch's duration.  With two (split, then the combine kernel),
+    # the split and combine launches are timed the same way in loops of
+    # their own after the timed steps (K split launches back to back, then K
+    # combine launches over the last partials).
     every = max(1, args.event_every)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(0, K, every)]
-    in_block = [0] * len(ev)
+
+    def timed_blocks(n, launch):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(0, n, every)]
+        counts = [0] * len(ev)
+        for i in range(n):
+            e = ev[i // every]
+            if i % every == 0:
+                e[0].record()
+            launch(i)
+            counts[i // every] += 1
+            if i % every == every - 1 or i == n - 1:
+                e[1].record()
+        return ev, counts
+
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(K):
-        d = decs[i % copies]
-        e = ev[i // every]
-        if separate:
-            # the merge is its own kernel: time the two launches apart
-            if i % every == 0:
-                e[0].record()
-            d.split()
-            if i % every == 0:
-                e[1].record()
-            d.combine()
-            if i % every == 0:
-                e[2].record()
-                in_block[i // every] = 1
-        else:
-            if i % every == 0:
-                e[0].record()
-            d()
-            in_block[i // every] += 1
-            if i % every == every - 1 or i == K - 1:
-                e[1].record()
+    step_ev, step_n = timed_blocks(K, lambda i: decs[i % copies]())
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-
-    split_ms = [e[0].elapsed_time(e[1]) / n for e, n in zip(ev, in_block)]
-    comb_ms = [e[1].elapsed_time(e[2]) for e in ev] if separate else [0.0]
-    step_ms = ([e[0].elapsed_time(e[2]) for e in ev] if separate else split_ms)
+    step_ms = [e[0].elapsed_time(e[1]) / n for e, n in zip(step_ev, step_n)]
+    if separate:
+        split_ev, split_n = timed_blocks(K, lambda i: decs[i % copies].split())
+        torch.cuda.synchronize()
+        last = decs[(K - 1) % copies]
+        comb_ev, comb_n = timed_blocks(K, lambda i: last.combine())
+        torch.cuda.synchronize()
+        split_ms = [e[0].elapsed_time(e[1]) / n for e, n in zip(split_ev, split_n)]
+        comb_ms = [e[0].elapsed_time(e[1]) / n for e, n in zip(comb_ev, comb_n)]
+    else:
+        split_ms = step_ms
+        comb_ms = [0.0]
     ms_per_step = (t1 - t0) * 1e3 / K
     gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
     split_avg = statistics.mean(split_ms)
@@ -283,7 +285,8 @@ def measure(spec, case, args, overrides=None):
 
 def kernels_us(m) -> dict:
     return {"split_avg": round(m["split_avg"] * 1e3, 2),
-            "merge": "fused into the split launch" if not m["separate"] else "combine kernel",
+            "merge": ("none (one split)" if m["plan"]["n_splits"] <= 1 else
+                      "combine kernel" if m["separate"] else "fused into the split launch"),
             "split_median": round(statistics.median(m["split_ms"]) * 1e3, 2),
             "combine_avg": round(statistics.mean(m["comb_ms"]) * 1e3, 2),
             "step_events_median": round(statistics.median(m["step_ms"]) * 1e3, 2),
@@ -304,8 +307,8 @@ def main() -> int:
     ap.add_argument("--merge", default="auto", choices=["auto", "fused", "combine"],
                     help="force the fused merge or the combine kernel (default: library's choice)")
     ap.add_argument("--event-every", type=int, default=8,
-                    help="one-launch steps: events bracket blocks of N launches; two-launch steps: "
-                         "the launches of every N-th step")
+                    help="HIP events bracket blocks of N steps (and, for split + combine steps, blocks of N "
+                         "split launches and of N combine launches, timed in loops of their own)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true",
