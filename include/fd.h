@@ -106,10 +106,13 @@ typedef enum {
 } fd_path_t;
 
 /* fd_options_t.flags.  By default fd_decode merges the splits inside the
- * split launch (the last workgroup of each kv head combines its group, the
- * partials travelling through device-coherent stores and loads) when the
- * grid runs in about one round of workgroups, and launches the combine
- * kernel otherwise.  These flags force one or the other. */
+ * split launch (the last workgroup of each kv head combines its group; the
+ * partials are ordered by a release fence before each arrival and an
+ * acquire fence in the completing workgroup) for small calls -- at most 48
+ * MiB of K/V, counted at T for every sequence -- whose grid runs in about
+ * one round of workgroups, and launches the combine kernel otherwise;
+ * stream mode (paged batches, automatic split count) always merges in the
+ * launch.  These flags force one or the other. */
 #define FD_FLAG_FUSED_MERGE 0x1
 #define FD_FLAG_COMBINE_KERNEL 0x2
 /* Plan for fd_append_decode: every sequence attends to one more token than
