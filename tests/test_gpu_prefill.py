@@ -411,3 +411,27 @@ def test_query_tiled_column_order(env_switch, n_splits):
         torch.cuda.synchronize()
         res.append((out.clone(), lse.clone()))
     assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+
+
+@pytest.mark.parametrize("dtype,D,nq", [("bf16", 128, 16), ("f16", 128, 16), ("bf16", 64, 16), ("bf16", 128, 40)])
+def test_query_tiled_pool_offsets_agree(env_switch, dtype, D, nq):
+    # paged pools under 4 GiB are addressed with 32-bit byte offsets into a
+    # buffer resource; the 64-bit row addressing (FD_PREFILL_POOL32=0) loads
+    # the same rows, so the results are bit-identical, and both meet the
+    # oracle.  64-row tiles (V stored as loaded, transposing reads, three
+    # workgroups per CU) and 128-row tiles; 16-token pages, shuffled pool
+    s = inputs.spec("paged_ragged_bf16", B=4, Hq=8, Hkv=2, D=D, T=3000, page_size=16, len_lo=0, len_hi=3000,
+                    dtype=dtype)
+    case = inputs.make_case(s).to(DEV)
+    q = inputs.make_q_multi(s, nq).to(DEV)
+    res = []
+    for p32 in ("1", "0"):
+        env_switch.setenv("FD_PREFILL_POOL32", p32)
+        plan = check_multi(case, q, True, what=f"pool offsets p32={p32} {dtype} D={D} nq={nq}")
+        assert plan["path"] == "prefill" and plan["heads_per_block"] == (64 if nq * 4 <= 64 else 128)
+        dec = Decoder(q, case.k, case.v, scale=s.scale, page_table=case.page_table, seq_lens=case.seq_lens,
+                      T=s.T, causal=True)
+        out, lse = dec()
+        torch.cuda.synchronize()
+        res.append((out.clone(), lse.clone()))
+    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
