@@ -88,3 +88,37 @@ def test_graph_replays_of_fused_calls(kind):
     torch.cuda.synchronize()
     _check(kind, case, dec, q_host, f"graph {kind} replay after eager calls")
     del g
+
+
+def test_graph_replays_of_split_and_combine():
+    # a plan that merges with the combine kernel (the default for large
+    # calls) captured as two launches: every replay with a new q matches the
+    # oracle, and so does an eager call afterwards
+    case = _case("fused_gqa")
+    c = case.to(DEV)
+    dec = Decoder(c.q, c.k, c.v, scale=case.spec.scale, n_splits=12, fused_merge=False)
+    assert not dec.plan["fused"] and dec.plan["combine"] and dec.plan["n_splits"] > 1
+    q_dev = dec.inputs[0]
+    parity.announce(f"graph split+combine: plan={dec.plan}")
+    dec.workspace.fill_(0xFF)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dec()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        q_host = inputs.make_q(replace(case.spec, seed=case.spec.seed + 13 * rep + 5))
+        q_dev.copy_(q_host.to(DEV))
+        dec.out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        parity.announce(f"graph split+combine: replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        _check("fused_gqa", case, dec, q_host, f"graph split+combine replay {rep}")
+    q_host = inputs.make_q(replace(case.spec, seed=case.spec.seed + 501))
+    q_dev.copy_(q_host.to(DEV))
+    dec.out.fill_(float("nan"))
+    dec()
+    torch.cuda.synchronize()
+    _check("fused_gqa", case, dec, q_host, "graph split+combine eager after the replays")
+    del g
