@@ -140,7 +140,7 @@ typedef struct fd_options {
     void *stream;               /* hipStream_t to launch on; NULL = null stream */
     int32_t n_queries;          /* queries per sequence, 1 .. 65536 (0 = 1);  */
                                 /* > 1 gives q / out an n_q axis (see below); */
-                                /* > 16 (or > 16 query rows per kv head,     */
+                                /* > 16 (or > 32 query rows per kv head,     */
                                 /* f16 / bf16) runs the query-tiled kernel   */
     int32_t causal;             /* with n_queries > 1: 1 = query i sees the   */
                                 /* first T_b - (n_queries - 1 - i) tokens     */
