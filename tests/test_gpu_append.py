@@ -43,7 +43,7 @@ def paged_case(s, lens):
     ("mha32k_f16", dict(Hq=8, Hkv=2, T=700, dtype="bf16"), "valu"),
     ("gqa128k_bf16", dict(Hq=8, Hkv=2, T=700), "mfma"),
     ("gqa128k_bf16", dict(Hq=8, Hkv=2, T=700, dtype="f16"), "mfma"),
-    ("gqa128k_bf16", dict(Hq=64, Hkv=2, T=700), "mfma"),       # two head blocks per kv head
+    ("gqa128k_bf16", dict(Hq=64, Hkv=2, T=700), "mfma"),       # one workgroup, two 16-row blocks
     ("gqa128k_bf16", dict(Hq=64, Hkv=2, T=700), "valu"),       # four head blocks
     ("gqa128k_bf16", dict(Hq=8, Hkv=2, T=700, D=64), "mfma"),
 ])
@@ -79,6 +79,21 @@ def test_append_paged(path, P):
         _, plan = parity.check_append(case, kn.to(DEV), vn.to(DEV), n_splits=n, path=path,
                                       what=f"append paged P={P} n={n} {path}")
         assert plan["stream"] == (n == 0)
+
+
+@pytest.mark.parametrize("G,dtype", [(32, "bf16"), (24, "f16")])
+def test_append_paged_two_row_blocks(G, dtype):
+    # 17..32 query heads per kv head: the split kernel's two row blocks (value
+    # product over V transposed through LDS) in stream mode and on a split
+    # grid, with the appended token folded in as the last step
+    s = inputs.spec("paged_ragged_bf16", B=4, Hq=G * 2, Hkv=2, T=1024, page_size=16, dtype=dtype)
+    lens = [0, 48, 1024, 700]
+    for n in (0, 5):
+        case = paged_case(s, lens)
+        kn, vn = new_token(case, n)
+        _, plan = parity.check_append(case, kn.to(DEV), vn.to(DEV), n_splits=n, path="mfma",
+                                      what=f"append paged two blocks G={G} {dtype} n={n}")
+        assert plan["heads_per_block"] == 32 and plan["stream"] == (n == 0)
 
 
 def test_append_successive_steps():
