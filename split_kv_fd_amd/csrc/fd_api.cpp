@@ -119,6 +119,14 @@ bool prefill_ordered(bool paged, long tiles, long n_splits, int B) {
            env_long("FD_PREFILL_ORDER", 1) == 1;
 }
 
+// Ordered calls with the automatic split count also let the order pass pick
+// the chunk from the lengths (the host plans for T only): the plan then has
+// twice the columns a length-blind plan would use, and its chunk is the
+// smallest the pass may pick (FD_PREFILL_DEVCHUNK=0: the plan's chunk).
+bool prefill_devchunk(bool ordered, int n_req) {
+    return ordered && n_req == 0 && env_long("FD_PREFILL_DEVCHUNK", 1) == 1;
+}
+
 // Shape checks and the plan.  `paged` tells whether a page table is used.
 fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_options_t &o,
                       bool paged, fd_plan_t *p) {
@@ -209,8 +217,14 @@ fd_status_t make_plan(int B, int Hq, int Hkv, int T, int D, int n_req, const fd_
                 if (n > cap) n = cap;
             }
         }
-        const long chunk = ceil_div(ceil_div(T, n), fdk::kPrefillTokens) * fdk::kPrefillTokens;
+        long chunk = ceil_div(ceil_div(T, n), fdk::kPrefillTokens) * fdk::kPrefillTokens;
         n = ceil_div(T, chunk);
+        if (prefill_devchunk(prefill_ordered(paged, tiles, n, B), n_req)) {
+            const long ntiles_t = ceil_div(T, fdk::kPrefillTokens);
+            const long ncap = std::min(2 * n, ntiles_t);
+            chunk = ceil_div(ntiles_t, ncap) * fdk::kPrefillTokens;
+            n = ceil_div(T, chunk);
+        }
         if (tiles * n * Hkv * B > 0x7fffffffL) return fail(FD_ERR_UNSUPPORTED, "too many query-tiled workgroups");
         std::memset(p, 0, sizeof *p);
         p->n_splits = (int)n;
@@ -557,6 +571,7 @@ fd_status_t prepare(const void *q, const void *k, const void *v, const int32_t *
     cb.Hkv = Hkv; cb.G = s.G; cb.nq = s.nq; cb.R = s.R;
     cb.n_splits = c->p.n_splits;
     cb.chunk = c->p.chunk;
+    cb.dev_chunk = nullptr;
     cb.append = append ? 1 : 0;
     cb.causal = s.causal;
     // the query-tiled kernel's partials: many rows, few splits
@@ -586,6 +601,8 @@ fd_status_t prepare(const void *q, const void *k, const void *v, const int32_t *
     f.chunk = c->p.chunk;
     f.part_o = f.part_m = f.part_l = nullptr;
     f.order = nullptr;
+    f.dev_chunk = nullptr;
+    f.slots = 0;
     if (c->p.path == FD_PATH_PREFILL && c->p.workspace_bytes > 0) {
         if (!c->o.workspace)
             return fail(FD_ERR_WORKSPACE, "query-tiled plan: a workspace of %zu bytes is required",
@@ -600,8 +617,24 @@ fd_status_t prepare(const void *q, const void *k, const void *v, const int32_t *
         const size_t vt_bytes =
             c->p.workspace_bytes - fdk::prefill_part_bytes(B, Hkv, s.R, D, c->p.n_splits) - order_bytes;
         char *w = static_cast<char *>(c->o.workspace);
-        if (ordered)
+        if (ordered) {
             f.order = reinterpret_cast<uint32_t *>(w + (c->p.workspace_bytes - order_bytes));
+            if (prefill_devchunk(ordered, n_req)) {
+                // after the order entries; the workgroups resident at once:
+                // three per CU for the paged 64-row instance with V read as
+                // given, two for the others
+                f.dev_chunk = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(f.order) +
+                                                          align256((size_t)B * c->p.n_splits * 4));
+                int cus = c->o.num_cus;
+                if (cus == 0) {
+                    const fd_status_t cst = device_cus(&cus);
+                    if (cst != FD_OK) return cst;
+                }
+                const bool three = f.tile_rows == fdk::kPrefillSmallRows && vt_bytes == 0;
+                f.slots = (three ? 3 : 2) * cus;
+                cb.dev_chunk = f.dev_chunk;
+            }
+        }
         if (vt_bytes > 0) {
             const size_t sl = (size_t)B * Hkv;
             f.vexp = reinterpret_cast<int32_t *>(w);

@@ -170,7 +170,8 @@ __global__ __launch_bounds__(256) void combine_rows(CombineArgs a) {
         Tb -= a.nq - 1 - qr / a.G;
         Tb = Tb < 0 ? 0 : Tb;
     }
-    int n = (Tb + a.chunk - 1) / a.chunk;
+    const int chunk = a.dev_chunk ? *a.dev_chunk : a.chunk;
+    int n = (Tb + chunk - 1) / chunk;
     n = n < a.n_splits ? n : a.n_splits;
     if (!live) n = 0;
 

@@ -106,6 +106,7 @@ struct CombineArgs {
     int B, Hq, T, D;
     int Hkv, G, nq, R;           // partial row p = (b * Hkv + kv head) * R + row
     int n_splits, chunk;
+    const int32_t *dev_chunk;    // query-tiled partials: the chunk the order pass chose (nullptr: chunk)
     int append;                  // sequences hold seq_lens[b] + 1 tokens
     int causal;                  // query r / G sees T_b - (nq - 1 - r / G) tokens:
                                  // only splits that start below that are read
@@ -198,6 +199,13 @@ struct PrefillArgs {
     // entry c is (b << 16 | split) of the c-th column to run, or ~0u for a
     // column that holds no tokens.
     uint32_t *order;
+    // With `order`, the order pass may also choose the chunk from the
+    // lengths (nullptr: the plan's `chunk`): it writes it here, and the
+    // kernel and the combine read it.  `chunk` is then the smallest it may
+    // pick (n_splits columns cover T), and `slots` the workgroups resident at
+    // once that it balances over.
+    int32_t *dev_chunk;
+    int slots;
 };
 constexpr int kOrderMaxB = 1024;                 // sequences the order pass ranks
 constexpr int kVconvChunk = 256;                  // tokens per workgroup of the conversion passes
@@ -214,7 +222,7 @@ inline size_t prefill_vt_bytes(int B, int Hkv, int T, int D) {
 
 // The column order of a query-tiled call (after the partials).
 inline size_t prefill_order_bytes(int B, int n_splits) {
-    return ((size_t)B * n_splits * 4 + 255) / 256 * 256;
+    return ((size_t)B * n_splits * 4 + 255) / 256 * 256 + 256;   // + the chosen chunk
 }
 
 // Partials of a query-tiled call with n_splits > 1 (after the converted V

@@ -265,10 +265,11 @@ __global__ __launch_bounds__(256, (PAGED && NB == 1 && !VT) ? 3 : 2) void prefil
     int seen = a.causal ? Tb - (a.nq - 1 - r_last / a.G) : Tb;
     seen = seen < 0 ? 0 : seen;
     const bool parts = a.n_splits > 1;
-    const int j0 = parts ? split * (a.chunk / NTOK) : 0;
+    const int chunk_t = (a.dev_chunk ? *a.dev_chunk : a.chunk) / NTOK;   // tiles per split
+    const int j0 = parts ? split * chunk_t : 0;
     int j1 = (seen + NTOK - 1) / NTOK;
     if (parts) {
-        j1 = min(j1, j0 + a.chunk / NTOK);
+        j1 = min(j1, j0 + chunk_t);
         if (j1 <= j0) return;    // no row of the tile sees this split: never read
     }
     const int nt = j1 - j0;
@@ -767,14 +768,39 @@ __global__ __launch_bounds__(kOrderMaxB) void order_pass(PrefillArgs a) {
     const int t = threadIdx.x;
     __shared__ int s_rem[kOrderMaxB];
     __shared__ int s_scan[kOrderMaxB];
+    __shared__ long long s_sum[kOrderMaxB];
     int Tb = 0;
     if (t < a.B) {
         Tb = a.seq_lens ? a.seq_lens[t] : a.T;
         Tb = Tb < 0 ? 0 : (Tb > a.T ? a.T : Tb);
     }
-    const long long cap = (long long)a.n_splits * a.chunk;
-    const int full = t < a.B ? (int)((Tb < cap ? Tb : cap) / a.chunk) : 0;
-    const int rem = (t < a.B && full < a.n_splits) ? Tb - full * a.chunk : 0;
+    int chunk = a.chunk;
+    if (a.dev_chunk) {
+        // The chunk from the lengths: W tiles of work (every kv head of every
+        // sequence), `slots` workgroups at once.  Whole chunks of P tiles with
+        // W ~ m * slots * P for a whole number m of rounds pack the slots
+        // evenly under longest-first dispatch (the remainders fill in);
+        // P is at least the plan's chunk, so n_splits columns still cover
+        // every sequence.
+        s_sum[t] = t < a.B ? (long long)((Tb + kPrefillTokens - 1) / kPrefillTokens) * a.Hkv : 0;
+        __syncthreads();
+        for (int off = kOrderMaxB / 2; off > 0; off >>= 1) {
+            if (t < off) s_sum[t] += s_sum[t + off];
+            __syncthreads();
+        }
+        const long long W = s_sum[0];
+        const long long pmin = a.chunk / kPrefillTokens;
+        const long long S = a.slots > 0 ? a.slots : 1;
+        long long m = W / (pmin * S);
+        if (m < 1) m = 1;
+        long long P = (W + m * S - 1) / (m * S);
+        if (P < pmin) P = pmin;
+        chunk = (int)(P * kPrefillTokens);
+        if (t == 0) *a.dev_chunk = chunk;
+    }
+    const long long cap = (long long)a.n_splits * chunk;
+    const int full = t < a.B ? (int)((Tb < cap ? Tb : cap) / chunk) : 0;
+    const int rem = (t < a.B && full < a.n_splits) ? Tb - full * chunk : 0;
     s_rem[t] = rem;
     s_scan[t] = full;
     __syncthreads();

@@ -78,12 +78,15 @@ class Decoder:
     current stream; given k_new and v_new ([B, Hkv, D]) it launches
     fd_append_decode instead, which also stores them into k, v.  The
     benchmark and tests use it to keep allocation out of the timed region.
+    num_cus (0: the device's own count) plans and launches as if the device
+    had that many compute units.
     """
 
     def __init__(self, q, k, v, *, scale: Optional[float] = None, page_table=None,
                  seq_lens=None, T: Optional[int] = None, n_splits: int = 0,
                  path: Optional[str] = None, fused_merge: Optional[bool] = None, out=None, lse=None,
-                 want_lse: bool = True, k_new=None, v_new=None, causal: bool = False):
+                 want_lse: bool = True, k_new=None, v_new=None, causal: bool = False,
+                 num_cus: int = 0):
         if q.device.type != "cuda":
             raise ValueError("q, k and v must be GPU tensors")
         if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPE:
@@ -133,7 +136,8 @@ class Decoder:
         self.inputs = (q, k, v, page_table, seq_lens)
         self.opt = make_options(q.dtype, page_size=page_size, max_pages=max_pages,
                                 num_pages=num_pages, path=path, fused_merge=fused_merge,
-                                append=self.append, n_queries=self.n_queries, causal=causal)
+                                append=self.append, n_queries=self.n_queries, causal=causal,
+                                num_cus=num_cus)
         p = fd.fd_plan_t()
         st = fd.fd_plan(B, Hq, Hkv, T, D, n_splits, self.opt, p)
         if st != fd.FD_OK:

@@ -451,14 +451,23 @@ def test_plan_rows_route(lib, nq, G, dtype, want):
     assert st == fd.FD_OK and p.path == fd.FD_PATH_MFMA
 
 
-def test_plan_query_tiled_paged_splits(lib):
+def test_plan_query_tiled_paged_splits(lib, monkeypatch):
     # a paged (ragged) batch with one row tile per kv head is planned for
-    # four rounds of workgroups, a contiguous one for two
+    # four rounds of workgroups, a contiguous one for two; with the chunk
+    # chosen on the device from the lengths (the default for such ordered
+    # calls) the plan holds twice the columns and the smallest chunk
     B, Hq, Hkv, T = 16, 32, 8, 65536
     kw = dict(n_queries=16, causal=1)
-    st, p = plan(B, Hq, Hkv, T, 128, 0, page_size=16, max_pages_per_seq=T // 16, num_pages=10, **kw)
+    paged = dict(page_size=16, max_pages_per_seq=T // 16, num_pages=10)
+    monkeypatch.setenv("FD_PREFILL_DEVCHUNK", "0")
+    st, p = plan(B, Hq, Hkv, T, 128, 0, **paged, **kw)
     assert st == fd.FD_OK and p.path == fd.FD_PATH_PREFILL
-    assert p.n_splits == _query_tiled_splits(B * Hkv, T, tiles=2)[0] == 16
+    assert p.n_splits == _query_tiled_splits(B * Hkv, T, tiles=2)[0] == 16 and p.chunk == 4096
+    monkeypatch.delenv("FD_PREFILL_DEVCHUNK")
+    st, p = plan(B, Hq, Hkv, T, 128, 0, **paged, **kw)
+    assert st == fd.FD_OK and p.path == fd.FD_PATH_PREFILL and p.n_splits == 32 and p.chunk == 2048
+    st, p = plan(B, Hq, Hkv, T, 128, 5, **paged, **kw)          # an explicit count is kept
+    assert st == fd.FD_OK and p.n_splits == 5
     st, p = plan(B, Hq, Hkv, T, 128, 0, **kw)
     assert st == fd.FD_OK and p.n_splits == _query_tiled_splits(B * Hkv, T, tiles=1)[0] == 8
     # one row tile per kv head that already gives two workgroups per CU: no split
@@ -559,15 +568,16 @@ def test_noalloc_without_device_reports_hip_error(lib):
 
 def test_plan_query_tiled_column_order_workspace(lib):
     # ragged paged calls with one row tile per kv head and several splits
-    # reserve B * n_splits order entries after the partials; contiguous
-    # caches, several row tiles or more than 1024 sequences do not
+    # reserve B * n_splits order entries after the partials, then 256 bytes
+    # for the chunk the order pass picks; contiguous caches, several row
+    # tiles or more than 1024 sequences do not
     kw = dict(n_queries=16, page_size=16, max_pages_per_seq=4096, num_pages=100)
     st, p = plan(16, 32, 8, 65536, 128, 0, **kw)
     assert st == fd.FD_OK and p.path == fd.FD_PATH_PREFILL and p.head_blocks == 1 and p.n_splits > 1
     parts = 16 * 8 * 64 * p.n_splits
     a256 = lambda x: -(-x // 256) * 256
     want = a256(parts * 128 * 4) + 2 * a256(parts * 4)
-    assert p.workspace_bytes == want + a256(16 * p.n_splits * 4)
+    assert p.workspace_bytes == want + a256(16 * p.n_splits * 4) + 256
     st, c = plan(16, 32, 8, 65536, 128, 0, n_queries=16)
     assert st == fd.FD_OK and c.workspace_bytes == a256(16 * 8 * 64 * c.n_splits * 128 * 4) + 2 * a256(16 * 8 * 64 * c.n_splits * 4)
     st, big = plan(1100, 32, 8, 2048, 128, 4, **dict(kw, max_pages_per_seq=128))

@@ -400,6 +400,7 @@ def test_query_tiled_column_order(env_switch, n_splits):
     case = case.to(DEV)
     q = inputs.make_q_multi(s, 16).to(DEV)
     res = []
+    env_switch.setenv("FD_PREFILL_DEVCHUNK", "0")          # the plan's chunk both ways
     for order in ("1", "0"):
         env_switch.setenv("FD_PREFILL_ORDER", order)
         plan = check_multi(case, q, True, n_splits=n_splits, what=f"column order={order} n={n_splits}")
@@ -435,3 +436,51 @@ def test_query_tiled_pool_offsets_agree(env_switch, dtype, D, nq):
         torch.cuda.synchronize()
         res.append((out.clone(), lse.clone()))
     assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+
+
+@pytest.mark.parametrize("lens, grows", [([4096, 0, 5000, 700, 2048, 3333], True),   # ragged, one empty
+                                         ([5000] * 6, True),                           # all at T
+                                         ([5000, 1, 1, 1, 1, 1], False),               # one long, many short
+                                         ([31, 32, 33, 0, 64, 65], False)])            # a tile or two
+def test_query_tiled_device_chunk(lens, grows):
+    # Ragged paged calls on the automatic split count let the order pass pick
+    # the chunk from the lengths (about a whole number of rounds of the
+    # resident workgroups, never below the plan's chunk); the query-tiled
+    # kernel and the combine read it back.  Every query and head against the
+    # oracle, causal and not, the workspace poisoned first; planned as if for
+    # the device's CUs and for 4 CUs, where the first two length sets get a
+    # chunk above the plan's.
+    s = inputs.spec("paged_ragged_bf16", B=len(lens), Hq=8, Hkv=2, T=5000, page_size=16)
+    npages = [-(-n // s.page_size) for n in lens]
+    num_pages = max(1, sum(npages))
+    perm = torch.randperm(num_pages, generator=torch.Generator().manual_seed(7)).to(torch.int32)
+    table = torch.zeros((s.B, -(-s.T // s.page_size)), dtype=torch.int32)
+    off = 0
+    for b, n in enumerate(npages):
+        table[b, :n] = perm[off:off + n]
+        off += n
+    host = inputs.Case(s, inputs.make_q(s), inputs.make_pool(s, num_pages, inputs._K),
+                       inputs.make_pool(s, num_pages, inputs._V), table, torch.tensor(lens, dtype=torch.int32))
+    case = host.to(DEV)
+    q = inputs.make_q_multi(s, 16)
+    for causal in (True, False):
+        ref_out, ref_lse = oracle_mod.default().decode_multi(q, host.k, host.v, s.scale, causal=causal,
+                                                             page_table=host.page_table, seq_lens=host.seq_lens)
+        for cus in (0, 4):
+            dec = Decoder(q.to(DEV), case.k, case.v, scale=s.scale, page_table=case.page_table,
+                          seq_lens=case.seq_lens, T=s.T, causal=causal, num_cus=cus)
+            plan = dec.plan
+            assert plan["path"] == "prefill" and plan["head_blocks"] == 1 and plan["n_splits"] > 1
+            dec.workspace.fill_(0xFF)
+            what = f"device chunk lens={lens} causal={causal} cus={cus}"
+            parity.announce(f"{what} plan={plan}")
+            out, lse = dec()
+            torch.cuda.synchronize()
+            parity.compare(host, out.cpu().double().numpy(), lse.cpu().double().numpy(), ref_out, ref_lse,
+                           parity.max_abs_v(host), what)
+            # the chunk the order pass chose: the first word of the
+            # workspace's last 256 bytes
+            chunk = int(dec.workspace[-256:-252].cpu().view(torch.int32)[0])
+            assert chunk % 32 == 0 and chunk >= plan["chunk"] and chunk * plan["n_splits"] >= s.T, (chunk, plan)
+            if cus == 4:
+                assert (chunk > plan["chunk"]) == grows, (chunk, plan)
