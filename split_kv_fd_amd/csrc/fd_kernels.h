@@ -190,7 +190,8 @@ struct PrefillArgs {
     int32_t *vexp;               // [B, Hkv]: k
     int vt_tiles;                // ceil(T / kPrefillTokens)
     int vmax_chunks;             // ceil(T / kVconvChunk)
-    int xcd_map;                 // 1: each XCD walks a contiguous run of work items
+    int xcd_map;                 // 1: each XCD walks a contiguous run of work items;
+                                 // 2: the same in pairs of ranges, tiles interleaved
     int pool32;                  // paged: each pool is under 4 GiB, so rows are
                                  // addressed with 32-bit byte offsets
     // Longest-first order of the (sequence, split) columns (ragged paged

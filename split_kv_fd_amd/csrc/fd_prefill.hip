@@ -176,7 +176,13 @@ __global__ __launch_bounds__(256, (PAGED && NB == 1 && !VT) ? 3 : 2) void prefil
     // evenly over the XCDs (consecutive kv heads of one split land on
     // different XCDs), however ragged the lengths.  Ranges past the last
     // multiple of 8 keep the plain order.  Within a range causal tiles run
-    // longest first.
+    // longest first; causal calls (xcd_map 2) also take an XCD's ranges in
+    // pairs with their tiles interleaved (tile t of both ranges, then t - 1),
+    // so that the long tiles of the next ranges do not start behind a run of
+    // short ones (list scheduling on one XCD's slots: 4 ranges of 32 tiles
+    // end at 1.48x the average load one range after another, at the average
+    // load in interleaved pairs) while an XCD still holds about two ranges'
+    // K/V at a time.
     // With a column order (one row tile per kv head), consecutive
     // workgroups take the kv heads of one (sequence, split) column, columns
     // in the order the order pass wrote: longest first.
@@ -195,7 +201,15 @@ __global__ __launch_bounds__(256, (PAGED && NB == 1 && !VT) ? 3 : 2) void prefil
         int item = lin;
         if (a.xcd_map && lin < mapped) {
             const int g = lin / 8;
-            item = ((lin % 8) + 8 * (g / a.row_tiles)) * a.row_tiles + g % a.row_tiles;
+            if (a.xcd_map == 2) {
+                const int nr = n_rng / 8;                  // ranges of this XCD
+                const int pair = g / (2 * a.row_tiles);
+                const int w = g - pair * 2 * a.row_tiles;
+                const int gl = min(2, nr - 2 * pair);      // 1 for the last of an odd count
+                item = ((lin % 8) + 8 * (2 * pair + w % gl)) * a.row_tiles + w / gl;
+            } else {
+                item = ((lin % 8) + 8 * (g / a.row_tiles)) * a.row_tiles + g % a.row_tiles;
+            }
         }
         tile_i = item % a.row_tiles;
         const int rng = item / a.row_tiles;

@@ -184,21 +184,37 @@ def test_prefill_bf16_split_p_form(env_switch, causal):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-def test_prefill_work_order_does_not_change_results(env_switch, dtype):
-    # the XCD-aware work order only permutes which workgroup takes which
-    # (sequence, kv head, row tile): outputs are bit-identical
-    case = contiguous("gqa128k_bf16", [700, 333, 512], Hq=8, Hkv=2, T=700, dtype=dtype)
+@pytest.mark.parametrize("n_splits", [0, 2])
+def test_prefill_work_order_does_not_change_results(env_switch, dtype, n_splits):
+    # the XCD-aware work orders only permute which workgroup takes which
+    # (sequence, kv head, split, row tile): outputs are bit-identical.  24
+    # (48 split) ranges: 3 (6) per XCD, so the causal pairs end on a single
+    # range (or not), 5 row tiles each
+    case = contiguous("gqa128k_bf16", [700, 333, 512], Hq=16, Hkv=8, T=700, dtype=dtype)
     q = inputs.make_q_multi(case.spec, 300).to(DEV)
     res = []
-    for x in ("1", "0"):
+    for x, pairs in (("0", "1"), ("1", "0"), ("1", "2")):       # plain, ranges in turn, in pairs
         env_switch.setenv("FD_PREFILL_XCD", x)
-        dec = Decoder(q, case.k, case.v, scale=case.spec.scale, seq_lens=case.seq_lens, causal=True)
+        env_switch.setenv("FD_PREFILL_PAIRS", pairs)
+        dec = Decoder(q, case.k, case.v, scale=case.spec.scale, seq_lens=case.seq_lens, causal=True,
+                      n_splits=n_splits)
+        assert dec.plan["path"] == "prefill" and dec.plan["head_blocks"] == 5
         out, lse = dec()
         torch.cuda.synchronize()
         res.append((out.clone(), lse.clone()))
-    vmax = float(case.v.float().abs().max())
-    assert torch.allclose(res[0][0], res[1][0], rtol=0, atol=1e-3 * vmax)
-    assert torch.allclose(res[0][1], res[1][1], rtol=0, atol=1e-4)
+    for out, lse in res[1:]:
+        assert torch.equal(out, res[0][0]) and torch.equal(lse, res[0][1])
+    check_multi(case, q, True, n_splits=n_splits, what=f"paired causal order {dtype} n={n_splits}")
+
+
+def test_prefill_full_prompt_causal_pairs():
+    # causal queries covering the whole cache take the paired order by
+    # default (MHA, 64 ranges: 8 per XCD, 8 row tiles each); the oracle on
+    # every row
+    case = contiguous("mha32k_f16", [1024, 1000], Hq=32, Hkv=32, T=1024)
+    q = inputs.make_q_multi(case.spec, 1024).to(DEV)
+    plan = check_multi(case, q, True, what="full-prompt causal, paired order")
+    assert plan["path"] == "prefill" and plan["head_blocks"] == 8
 
 
 # ------------------------------------------------------------------ KV splits of the query-tiled kernel
