@@ -500,3 +500,12 @@ def test_query_tiled_device_chunk(lens, grows):
             assert chunk % 32 == 0 and chunk >= plan["chunk"] and chunk * plan["n_splits"] >= s.T, (chunk, plan)
             if cus == 4:
                 assert (chunk > plan["chunk"]) == grows, (chunk, plan)
+            # fd_split then fd_combine: the combine reads the chunk the split's
+            # order pass left in the workspace; bit for bit fd_decode's result
+            out_a, lse_a = out.clone(), lse.clone()
+            dec.out.fill_(float("nan"))
+            dec.lse.fill_(float("nan"))
+            dec.split()
+            dec.combine()
+            torch.cuda.synchronize()
+            assert torch.equal(out_a, dec.out) and torch.equal(lse_a, dec.lse)
