@@ -509,3 +509,29 @@ def test_query_tiled_device_chunk(lens, grows):
             dec.combine()
             torch.cuda.synchronize()
             assert torch.equal(out_a, dec.out) and torch.equal(lse_a, dec.lse)
+
+
+@pytest.mark.parametrize("B", [1024, 1025])
+def test_query_tiled_order_batch_limit(B):
+    # The column order pass takes at most 1024 sequences: B=1024 runs its
+    # columns longest first with the chunk chosen on the device, B=1025 in
+    # the plain order.  Planned as for 512 CUs, so the KV axis splits; the
+    # workspace poisoned first.  Every query of a sample of sequences (first,
+    # last, shortest, longest and 12 seeded others) against the oracle
+    s = inputs.spec("paged_ragged_bf16", B=B, Hq=4, Hkv=1, T=2048, page_size=16, len_lo=0, len_hi=2048)
+    case = inputs.make_case(s, device=DEV)
+    q = inputs.make_q_multi(s, 16, device=DEV)
+    dec = Decoder(q, case.k, case.v, scale=s.scale, page_table=case.page_table, seq_lens=case.seq_lens,
+                  T=s.T, causal=True, num_cus=512)
+    plan = dec.plan
+    assert plan["path"] == "prefill" and plan["head_blocks"] == 1 and plan["n_splits"] > 1
+    dec.workspace.fill_(0xFF)
+    parity.announce(f"order batch limit B={B} plan={plan}")
+    out, lse = dec()
+    torch.cuda.synchronize()
+    lens = case.lengths()
+    g = torch.Generator().manual_seed(B)
+    bs = {0, B - 1, min(range(B), key=lambda b: lens[b]), max(range(B), key=lambda b: lens[b])}
+    bs |= set(torch.randint(0, B, (12,), generator=g).tolist())
+    parity.all_queries(case, q, out.cpu().double().numpy(), lse.cpu().double().numpy(), sorted(bs), True,
+                       f"order batch limit B={B}")
