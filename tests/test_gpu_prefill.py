@@ -458,7 +458,8 @@ def test_query_tiled_pool_offsets_agree(env_switch, dtype, D, nq):
                                          ([5000] * 6, True),                           # all at T
                                          ([5000, 1, 1, 1, 1, 1], False),               # one long, many short
                                          ([31, 32, 33, 0, 64, 65], False)])            # a tile or two
-def test_query_tiled_device_chunk(lens, grows):
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f16", 64)])
+def test_query_tiled_device_chunk(lens, grows, dtype, D):
     # Ragged paged calls on the automatic split count let the order pass pick
     # the chunk from the lengths (about a whole number of rounds of the
     # resident workgroups, never below the plan's chunk); the query-tiled
@@ -466,7 +467,7 @@ def test_query_tiled_device_chunk(lens, grows):
     # oracle, causal and not, the workspace poisoned first; planned as if for
     # the device's CUs and for 4 CUs, where the first two length sets get a
     # chunk above the plan's.
-    s = inputs.spec("paged_ragged_bf16", B=len(lens), Hq=8, Hkv=2, T=5000, page_size=16)
+    s = inputs.spec("paged_ragged_bf16", B=len(lens), Hq=8, Hkv=2, T=5000, page_size=16, dtype=dtype, D=D)
     npages = [-(-n // s.page_size) for n in lens]
     num_pages = max(1, sum(npages))
     perm = torch.randperm(num_pages, generator=torch.Generator().manual_seed(7)).to(torch.int32)
@@ -488,7 +489,7 @@ def test_query_tiled_device_chunk(lens, grows):
             plan = dec.plan
             assert plan["path"] == "prefill" and plan["head_blocks"] == 1 and plan["n_splits"] > 1
             dec.workspace.fill_(0xFF)
-            what = f"device chunk lens={lens} causal={causal} cus={cus}"
+            what = f"device chunk {dtype} D={D} lens={lens} causal={causal} cus={cus}"
             parity.announce(f"{what} plan={plan}")
             out, lse = dec()
             torch.cuda.synchronize()
