@@ -417,14 +417,17 @@ void log_plan(const char *entry, int B, int Hq, int Hkv, int T, int D, int n_req
     if (!log_enabled()) return;
     static const char *const dt[] = {"f32", "f16", "bf16"};
     const char *merge = p.n_splits <= 1 ? "none" : (p.stream || p.fused) ? "fused" : "combine-kernel";
+    // 1: the order pass picks the split size on the device (at least `chunk`)
+    const int on_device = p.path == FD_PATH_PREFILL &&
+                          prefill_devchunk(prefill_ordered(o.page_size > 0, p.head_blocks, p.n_splits, B), n_req);
     std::fprintf(stderr,
                  "[fd] %s B=%d Hq=%d Hkv=%d T=%d D=%d dtype=%s n_queries=%d causal=%d paged=%d page_size=%d "
-                 "n_splits_req=%d -> path=%s n_splits=%d chunk=%d grid=%dx%dx%d rows_per_wg=%d head_blocks=%d "
-                 "merge=%s stream=%d workspace=%zu\n",
+                 "n_splits_req=%d -> path=%s n_splits=%d chunk=%d chunk_on_device=%d grid=%dx%dx%d rows_per_wg=%d "
+                 "head_blocks=%d merge=%s stream=%d workspace=%zu\n",
                  entry, B, Hq, Hkv, T, D, (o.dtype >= 0 && o.dtype <= 2) ? dt[o.dtype] : "?", (int)o.n_queries,
                  (int)o.causal, o.page_size > 0 ? 1 : 0, o.page_size > 0 ? (int)o.page_size : 0, n_req,
-                 path_name(p.path), p.n_splits, p.chunk, p.grid[0], p.grid[1], p.grid[2], p.heads_per_block,
-                 p.head_blocks, merge, p.stream, p.workspace_bytes);
+                 path_name(p.path), p.n_splits, p.chunk, on_device, p.grid[0], p.grid[1], p.grid[2],
+                 p.heads_per_block, p.head_blocks, merge, p.stream, p.workspace_bytes);
 }
 
 struct Call {

@@ -488,7 +488,10 @@ print("PLAN", p.path, p.n_splits, p.chunk, p.fused, p.stream, flush=True)
 o.page_size, o.max_pages_per_seq, o.num_pages = 16, 4096, 100
 assert fd.fd_plan(16, 32, 8, 65536, 128, 0, o, p) == fd.FD_OK
 print("PLAN", p.path, p.n_splits, p.chunk, p.fused, p.stream, flush=True)
-o.page_size = 0
+o.n_queries, o.causal = 16, 1
+assert fd.fd_plan(16, 32, 8, 65536, 128, 0, o, p) == fd.FD_OK
+print("PLAN", p.path, p.n_splits, p.chunk, p.fused, p.stream, flush=True)
+o.n_queries, o.causal, o.page_size = 1, 0, 0
 # fails validation: nothing is planned, nothing logged
 assert fd.fd_decode(None, 1 << 20, 1 << 20, None, None, 1 << 20, None, 1, 4, 4, 4096, 128, 0.1, 0, o) != fd.FD_OK
 """
@@ -511,7 +514,7 @@ def test_fd_log_prints_each_plan(lib, flag):
     if not flag:
         assert logs == []
         return
-    assert len(logs) == 2 and all(ln.startswith("[fd] fd_plan ") for ln in logs)
+    assert len(logs) == 3 and all(ln.startswith("[fd] fd_plan ") for ln in logs)
     names = {0: "valu", 1: "mfma", 2: "query-tiled"}
     for ln, (path, n, chunk, fused, stream) in zip(logs, plans):
         kv = dict(t.split("=", 1) for t in ln.split() if "=" in t)
@@ -519,6 +522,9 @@ def test_fd_log_prints_each_plan(lib, flag):
         assert kv["stream"] == stream
         assert kv["merge"] == ("none" if int(n) == 1 else "fused" if (int(fused) or int(stream)) else "combine-kernel")
     assert "paged=1" in logs[1] and "stream=1" in logs[1] and "B=16" in logs[1]
+    # a ragged paged few-query call: the order pass picks the split size
+    assert "n_queries=16" in logs[2] and "chunk_on_device=1" in logs[2]
+    assert "chunk_on_device=0" in logs[0] and "chunk_on_device=0" in logs[1]
 
 
 def noalloc(q=A, k=A, v=A, pt=None, sl=None, out=A, lse=A, shape=(1, 4, 4, 4096, 128), scale=0.1,
