@@ -122,3 +122,54 @@ def test_graph_replays_of_split_and_combine():
     torch.cuda.synchronize()
     _check("fused_gqa", case, dec, q_host, "graph split+combine eager after the replays")
     del g
+
+
+def test_graph_replays_of_query_tiled_ordered_call():
+    # a ragged paged call with 16 causal queries: the order pass, the
+    # query-tiled kernel and the row combine captured once; between replays
+    # eager work copies in new queries and new (shorter) lengths, so the
+    # split size the order pass picks on the device changes from replay to
+    # replay under the same host plan (planned as for 4 CUs, where it grows
+    # past the planned chunk).  Every replay against the oracle.
+    from oracle import oracle as oracle_mod
+    s = inputs.spec("paged_ragged_bf16", B=6, Hq=8, Hkv=2, T=6000, len_lo=2000, len_hi=6000)
+    case = inputs.make_case(s, device="cpu")
+    c = case.to(DEV)
+    nq = 16
+    q_dev = inputs.make_q_multi(s, nq).to(DEV)
+    dec = Decoder(q_dev, c.k, c.v, scale=s.scale, page_table=c.page_table, seq_lens=c.seq_lens, T=s.T,
+                  causal=True, num_cus=4)
+    plan = dec.plan
+    assert plan["path"] == "prefill" and plan["head_blocks"] == 1 and plan["n_splits"] > 1
+    lens_dev = dec.inputs[4]
+    parity.announce(f"graph query-tiled ordered: plan={plan}")
+    dec.workspace.fill_(0xFF)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dec()
+    torch.cuda.synchronize()
+    full = case.seq_lens.clone()
+    gen = torch.Generator().manual_seed(77)
+    chunks = set()
+    for rep in range(4):
+        q_host = inputs.make_q_multi(replace(s, seed=s.seed + 7 * rep + 3), nq)
+        # each sequence keeps between none and all of its cached tokens
+        lens = (full.double() * torch.rand(s.B, generator=gen, dtype=torch.float64)).to(torch.int32)
+        if rep == 0:
+            lens = full.clone()
+        q_dev.copy_(q_host.to(DEV))
+        lens_dev.copy_(lens.to(DEV))
+        dec.out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        parity.announce(f"graph query-tiled ordered: replay {rep} lens={lens.tolist()}")
+        g.replay()
+        torch.cuda.synchronize()
+        chunks.add(int(dec.workspace[-256:-252].cpu().view(torch.int32)[0]))
+        ref_out, ref_lse = oracle_mod.default().decode_multi(q_host, case.k, case.v, s.scale, causal=True,
+                                                             page_table=case.page_table, seq_lens=lens)
+        hc = replace(case, seq_lens=lens)
+        parity.compare(hc, dec.out.cpu().double().numpy(), dec.lse.cpu().double().numpy(), ref_out, ref_lse,
+                       parity.max_abs_v(hc), f"graph query-tiled ordered replay {rep}")
+    assert len(chunks) > 1, chunks
+    del g
