@@ -173,3 +173,42 @@ def test_graph_replays_of_query_tiled_ordered_call():
                        parity.max_abs_v(hc), f"graph query-tiled ordered replay {rep}")
     assert len(chunks) > 1, chunks
     del g
+
+
+def test_graph_replays_of_converted_v_prefill():
+    # bf16 prefill with 1024 query rows per kv head: the two V conversion
+    # passes and the query-tiled kernel captured once.  Between replays eager
+    # work writes a new V, scaled by a different power of two each time, so
+    # the exponent the passes pick changes under the same graph; every
+    # replay against the oracle.
+    from oracle import oracle as oracle_mod
+    s = inputs.spec("gqa128k_bf16", B=1, T=300)
+    case = inputs.make_case(s, device="cpu")
+    c = case.to(DEV)
+    nq = 256
+    q_host = inputs.make_q_multi(s, nq)
+    q_dev = q_host.to(DEV)
+    dec = Decoder(q_dev, c.k, c.v, scale=s.scale, causal=True)
+    assert dec.plan["path"] == "prefill" and dec.plan["workspace_bytes"] > 0
+    v_dev = dec.inputs[2]
+    parity.announce(f"graph converted-V prefill: plan={dec.plan}")
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dec()
+    torch.cuda.synchronize()
+    for rep, e in enumerate((0, 9, -13, 4)):
+        v_host = (case.v.float() * 2.0 ** e).to(case.v.dtype)     # exact: a power of two
+        qr = inputs.make_q_multi(replace(s, seed=s.seed + 5 * rep + 1), nq)
+        v_dev.copy_(v_host.to(DEV))
+        q_dev.copy_(qr.to(DEV))
+        dec.out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        parity.announce(f"graph converted-V prefill: replay {rep}, V x 2^{e}")
+        g.replay()
+        torch.cuda.synchronize()
+        ref_out, ref_lse = oracle_mod.default().decode_multi(qr, case.k, v_host, s.scale, causal=True)
+        hc = replace(case, v=v_host)
+        parity.compare(hc, dec.out.cpu().double().numpy(), dec.lse.cpu().double().numpy(), ref_out, ref_lse,
+                       parity.max_abs_v(hc), f"graph converted-V prefill replay {rep}")
+    del g
