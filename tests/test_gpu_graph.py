@@ -4,7 +4,10 @@ arguments, so every replay of a captured fused or stream-mode call counts its
 workgroups from zero and merges.  Each replay gets a new q (copied in by
 eager work between replays) and is compared with the fp64 oracle; the
 workspace starts full of foreign bytes.  An eager call after the replays
-must find the counters usable too."""
+must find the counters usable too.  Query-tiled calls are captured the same
+way: the order pass (whose split size follows the lengths written between
+replays) and the V conversion passes (whose exponent follows V) run inside
+the graph."""
 from dataclasses import replace
 
 import pytest
